@@ -1,0 +1,247 @@
+"""NF4 quantizer oracle (numpy, vectorized).  Test infrastructure only.
+
+What the pages fix, and where:
+
+* NF4 puts its 16 levels at quantiles of the normal distribution so that
+  every level stands for an equal share of normally distributed weights
+  ("QLoRA: fine-tuning a 65B model on one GPU", section "NormalFloat, double
+  quantization, paged optimizers"; "QLoRA: efficient finetuning of quantized
+  LLMs", Abstract, item (a)).
+* Blockwise quantization keeps one scaling constant per block of weights; the
+  constant is the block's absmax ("Qlora 4 Bit Quantization With Nf4 Fp4 Data
+  Types And Lora Adapters", entry on 4-bit quantization with the nf4 data
+  type).
+* Double quantization stores those constants in 8 bits under a second,
+  coarser level of constants (blog section "NormalFloat, double quantization,
+  paged optimizers"; CoChat Abstract, item (b)).
+* The base is quantized once and dequantized to 16 bits on every forward and
+  backward pass (blog section "Where the memory goes").
+
+Readings taken where the pages are silent (each is listed in the design
+notes): level offset delta = 1 - (1/30 + 1/32)/2 with 7 negative levels, an
+exact zero and 8 positive levels; blocks of 64 consecutive row-major
+elements; nearest level with ties to the lower index; even element in the
+low nibble; unsigned linear 8-bit constants per group of 256 consecutive
+blocks under an fp32 step max/255, rounded half-to-even; dequantization
+w = bf16_rne(fl32(level * fl32(q * step))).
+"""
+
+import math
+
+import numpy as np
+
+BLOCKSIZE = 64
+DQ_BLOCKSIZE = 256
+
+
+# --------------------------------------------------------------------------
+# Normal quantile function, from its definition
+# --------------------------------------------------------------------------
+
+def normal_cdf(x: float) -> float:
+    """Phi(x) = P(Z <= x) for a standard normal Z, via the complementary
+    error function: Phi(x) = erfc(-x / sqrt 2) / 2."""
+    return 0.5 * math.erfc(-x / math.sqrt(2.0))
+
+
+def normal_quantile(p: float) -> float:
+    """Phi^{-1}(p) for 0.5 <= p < 1, by bisection on the monotone Phi.
+
+    Bisection stops when the midpoint of the bracket equals one of its ends,
+    i.e. the bracket is two adjacent doubles.  The result is then within one
+    ulp of the root of the computed Phi, which is accurate to a few ulp.
+    """
+    if not (0.5 <= p < 1.0):
+        raise ValueError("normal_quantile is only needed on [0.5, 1)")
+    lo, hi = 0.0, 40.0
+    while True:
+        mid = 0.5 * (lo + hi)
+        if mid == lo or mid == hi:
+            break
+        if normal_cdf(mid) < p:
+            lo = mid
+        else:
+            hi = mid
+    # pick the end whose Phi is closer to p
+    return lo if abs(normal_cdf(lo) - p) <= abs(normal_cdf(hi) - p) else hi
+
+
+# --------------------------------------------------------------------------
+# The 16 NF4 levels
+# --------------------------------------------------------------------------
+
+NF4_DELTA = 1.0 - 0.5 * (1.0 / 30.0 + 1.0 / 32.0)
+
+
+def nf4_levels_f64() -> np.ndarray:
+    """The 16 NF4 levels in fp64, sorted ascending.
+
+    Levels sit at normal quantiles (blog section "NormalFloat, double
+    quantization, paged optimizers").  Phi^{-1}(1) is infinite, so the
+    outermost probability is pulled in to delta.  An exact zero splits the
+    levels into 8 positive ones at probabilities evenly spaced from delta
+    down to (but not including) 1/2, and 7 negative ones mirrored from 7
+    evenly spaced probabilities on the same interval.  Dividing by
+    Phi^{-1}(delta) puts the outermost levels at exactly -1 and +1.
+    """
+    d = NF4_DELTA
+    pos = [normal_quantile(d - (d - 0.5) * i / 8.0) for i in range(8)]
+    neg = [-normal_quantile(d - (d - 0.5) * j / 7.0) for j in range(7)]
+    top = normal_quantile(d)
+    vals = sorted(neg + [0.0] + pos)
+    return np.array([v / top for v in vals], dtype=np.float64)
+
+
+def nf4_levels() -> np.ndarray:
+    """The NF4 levels rounded once to fp32 (round to nearest even)."""
+    return nf4_levels_f64().astype(np.float32)
+
+
+# --------------------------------------------------------------------------
+# bf16 helpers
+# --------------------------------------------------------------------------
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round fp32 to bf16 (round to nearest, ties to even) and return the
+    16-bit patterns.  Written with integer operations on the fp32 bit
+    pattern: add 0x7FFF plus the lowest kept bit, then drop 16 bits.  Exact
+    for every finite input, subnormals included (NaN is outside the
+    contract)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    keep_lsb = (u >> np.uint64(16)) & np.uint64(1)
+    r = (u + np.uint64(0x7FFF) + keep_lsb) >> np.uint64(16)
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns to fp32 (exact)."""
+    u = np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32)
+
+
+# --------------------------------------------------------------------------
+# Quantizer
+# --------------------------------------------------------------------------
+
+def nearest_level(x: np.ndarray, levels_f32: np.ndarray) -> np.ndarray:
+    """Index of the level nearest to each fp32 x, ties to the lower index.
+
+    Distances are taken in fp64.  For fp32 operands of nearby magnitude the
+    difference is exact in fp64, which is the only case where two distances
+    can tie or nearly tie; far from a midpoint, rounding in fp64 cannot
+    change which distance is smaller.  ``argmin`` returns the first minimum,
+    which is the lower index.
+    """
+    L = levels_f32.astype(np.float64)
+    xs = np.asarray(x, dtype=np.float32).astype(np.float64)
+    out = np.empty(xs.shape, dtype=np.uint8)
+    flat_in = xs.reshape(-1)
+    flat_out = out.reshape(-1)
+    chunk = 1 << 20
+    for s in range(0, flat_in.size, chunk):
+        d = np.abs(flat_in[s:s + chunk, None] - L[None, :])
+        flat_out[s:s + chunk] = np.argmin(d, axis=1).astype(np.uint8)
+    return out
+
+
+def block_absmax(W: np.ndarray, blocksize: int = BLOCKSIZE) -> np.ndarray:
+    """c_b = max |w| over each block of ``blocksize`` consecutive elements
+    of row-major W (exact in fp32)."""
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    N, K = W.shape
+    if K % blocksize:
+        raise ValueError("K must be a multiple of the block size")
+    return np.max(np.abs(W.reshape(-1, blocksize)), axis=1)
+
+
+def normalize(W: np.ndarray, c: np.ndarray, blocksize: int = BLOCKSIZE) -> np.ndarray:
+    """x = fl32(w / c_b), IEEE fp32 division; x = 0 where c_b = 0."""
+    Wb = np.ascontiguousarray(W, dtype=np.float32).reshape(-1, blocksize)
+    cb = c.astype(np.float32)[:, None]
+    x = np.zeros_like(Wb)
+    nz = np.broadcast_to(cb != 0, Wb.shape)
+    np.divide(Wb, np.broadcast_to(cb, Wb.shape), out=x, where=nz)
+    return x
+
+
+def pack_codes(codes: np.ndarray) -> np.ndarray:
+    """Two 4-bit codes per byte, element 2j in the low nibble."""
+    c = np.ascontiguousarray(codes, dtype=np.uint8).reshape(-1)
+    return (c[0::2] | (c[1::2] << np.uint8(4))).astype(np.uint8)
+
+
+def unpack_codes(packed: np.ndarray) -> np.ndarray:
+    p = np.ascontiguousarray(packed, dtype=np.uint8).reshape(-1)
+    out = np.empty(p.size * 2, dtype=np.uint8)
+    out[0::2] = p & np.uint8(0x0F)
+    out[1::2] = p >> np.uint8(4)
+    return out
+
+
+def double_quantize(c: np.ndarray, dq_blocksize: int = DQ_BLOCKSIZE):
+    """Quantize the absmax constants to 8 bits under a coarser fp32 level.
+
+    Groups are ``dq_blocksize`` consecutive block indices (the last group may
+    be shorter).  Per group: s = max c_b; step = fl32(s / 255);
+    q_b = min(255, rint(fl32(c_b / step))) with round-half-to-even, and
+    q_b = 0 when step = 0.  Returns (q8 uint8 [nblocks], step fp32
+    [ngroups]).
+    """
+    c = np.asarray(c, dtype=np.float32)
+    nb = c.size
+    ng = (nb + dq_blocksize - 1) // dq_blocksize
+    step = np.empty(ng, dtype=np.float32)
+    q = np.empty(nb, dtype=np.uint8)
+    for g in range(ng):
+        cg = c[g * dq_blocksize:(g + 1) * dq_blocksize]
+        s = np.max(cg)
+        st = np.float32(s) / np.float32(255.0)
+        step[g] = st
+        if st == 0:
+            q[g * dq_blocksize:g * dq_blocksize + cg.size] = 0
+            continue
+        r = np.rint(cg / st)  # fp32 division, then half-to-even rounding
+        q[g * dq_blocksize:g * dq_blocksize + cg.size] = np.minimum(r, 255).astype(np.uint8)
+    return q, step
+
+
+def quantize(W: np.ndarray, blocksize: int = BLOCKSIZE, dq_blocksize: int = DQ_BLOCKSIZE):
+    """Full NF4 + double-quant encoding of W [N, K] fp32.
+
+    Returns (codes uint8 [N*K/2], q8 uint8 [N*K/64], step fp32
+    [ceil(N*K/64/256)]).
+    """
+    levels = nf4_levels()
+    c = block_absmax(W, blocksize)
+    x = normalize(W, c, blocksize)
+    codes = nearest_level(x, levels)
+    packed = pack_codes(codes)
+    q8, step = double_quantize(c, dq_blocksize)
+    return packed, q8, step
+
+
+def dequant_constants(q8: np.ndarray, step: np.ndarray, dq_blocksize: int = DQ_BLOCKSIZE) -> np.ndarray:
+    """c_hat_b = fl32(q_b * step_g) for every block b in group g."""
+    q8 = np.asarray(q8, dtype=np.uint8)
+    g = np.arange(q8.size) // dq_blocksize
+    return (q8.astype(np.float32) * np.asarray(step, dtype=np.float32)[g]).astype(np.float32)
+
+
+def dequantize_f32(packed, q8, step, N, K, blocksize=BLOCKSIZE, dq_blocksize=DQ_BLOCKSIZE) -> np.ndarray:
+    """fl32(level[code] * c_hat_b) as fp32 [N, K], before the bf16 rounding."""
+    levels = nf4_levels()
+    codes = unpack_codes(packed)
+    chat = dequant_constants(q8, step, dq_blocksize)
+    vals = levels[codes].reshape(-1, blocksize) * chat[:, None]
+    return vals.astype(np.float32).reshape(N, K)
+
+
+def dequantize(packed, q8, step, N, K, blocksize=BLOCKSIZE, dq_blocksize=DQ_BLOCKSIZE) -> np.ndarray:
+    """The dequantized weight W_hat as bf16 bit patterns [N, K] (uint16)."""
+    return f32_to_bf16_bits(dequantize_f32(packed, q8, step, N, K, blocksize, dq_blocksize))
+
+
+def storage_bytes(N: int, K: int, blocksize=BLOCKSIZE, dq_blocksize=DQ_BLOCKSIZE) -> int:
+    """Bytes of the quantized state: packed codes + 8-bit constants + fp32 steps."""
+    nb = N * K // blocksize
+    return N * K // 2 + nb + 4 * ((nb + dq_blocksize - 1) // dq_blocksize)

@@ -1,0 +1,107 @@
+"""Pure-Python scalar NF4 quantizer, for brute-force checks on tiny inputs.
+Test infrastructure only.
+
+It follows the same steps as :mod:`oracle.nf4` (blockwise absmax, divide,
+nearest level with ties to the lower index, pack, double quantization,
+dequantization) one element at a time, with no numpy in the arithmetic.
+Python floats are fp64; fp32 results are obtained by rounding the fp64 result
+of one operation on fp32 operands to fp32.  For a single division or
+multiplication of fp32 operands this gives the correctly rounded fp32 result
+(fp64 carries more than 2*24 + 2 significand bits, so the two roundings
+cannot disagree with one direct rounding).
+
+Page citations are those of :mod:`oracle.nf4` ("QLoRA: fine-tuning a 65B
+model on one GPU", section "NormalFloat, double quantization, paged
+optimizers"; "Qlora 4 Bit Quantization With Nf4 Fp4 Data Types And Lora
+Adapters", NF4 entry).
+"""
+
+import math
+import struct
+
+
+def f32(x: float) -> float:
+    """Round a Python float to the nearest fp32 (ties to even)."""
+    return struct.unpack("<f", struct.pack("<f", x))[0]
+
+
+def f32_bits(x: float) -> int:
+    return struct.unpack("<I", struct.pack("<f", x))[0]
+
+
+def bf16_bits(x: float) -> int:
+    """Round an fp32 value to bf16, ties to even, by comparing the two bf16
+    neighbours of x directly (no bit tricks)."""
+    b = f32_bits(x)
+    lo = b & 0xFFFF0000
+    hi = lo + 0x10000
+    vlo = struct.unpack("<f", struct.pack("<I", lo))[0]
+    if b == lo:
+        return lo >> 16
+    if (hi & 0x7F800000) == 0x7F800000 and (hi & 0x007FFFFF) == 0:
+        # rounding past the largest finite bf16: IEEE compares against the
+        # next value the format would have with an unbounded exponent, 2^128
+        vhi = math.copysign(2.0 ** 128, vlo)
+    else:
+        vhi = struct.unpack("<f", struct.pack("<I", hi & 0xFFFFFFFF))[0]
+    dlo = abs(x - vlo)
+    dhi = abs(vhi - x)
+    if dlo < dhi:
+        return lo >> 16
+    if dhi < dlo:
+        return (hi >> 16) & 0xFFFF
+    return (lo >> 16) if ((lo >> 16) & 1) == 0 else ((hi >> 16) & 0xFFFF)
+
+
+def quantize(W, levels, blocksize=64, dq_blocksize=256):
+    """W: list of rows (lists of fp32-representable floats).  levels: 16
+    fp32-representable floats, ascending.  Returns (codes bytes, q8 list,
+    step list)."""
+    flat = [float(v) for row in W for v in row]
+    n = len(flat)
+    assert n % blocksize == 0
+    nb = n // blocksize
+    c = []
+    codes = []
+    for b in range(nb):
+        blk = flat[b * blocksize:(b + 1) * blocksize]
+        cb = 0.0
+        for w in blk:
+            if abs(w) > cb:
+                cb = abs(w)
+        c.append(cb)
+        for w in blk:
+            x = 0.0 if cb == 0.0 else f32(w / cb)
+            best, bestd = 0, None
+            for i, lv in enumerate(levels):
+                d = abs(x - lv)
+                if bestd is None or d < bestd:
+                    best, bestd = i, d
+            codes.append(best)
+    packed = bytes(codes[2 * j] | (codes[2 * j + 1] << 4) for j in range(n // 2))
+    q8, steps = [], []
+    for g in range(0, nb, dq_blocksize):
+        grp = c[g:g + dq_blocksize]
+        s = max(grp)
+        st = f32(s / 255.0)
+        steps.append(st)
+        for cb in grp:
+            if st == 0.0:
+                q8.append(0)
+            else:
+                r = f32(cb / st)
+                q = round(r)  # Python round() is half-to-even
+                q8.append(min(255, int(q)))
+    return packed, q8, steps
+
+
+def dequantize(packed, q8, steps, levels, blocksize=64, dq_blocksize=256):
+    """Returns the bf16 bit patterns of W_hat, flat, row-major."""
+    out = []
+    for j, byte in enumerate(packed):
+        for code in (byte & 0xF, byte >> 4):
+            e = len(out)
+            b = e // blocksize
+            chat = f32(float(q8[b]) * steps[b // dq_blocksize])
+            out.append(bf16_bits(f32(levels[code] * chat)))
+    return out
