@@ -1,0 +1,174 @@
+/*
+ * qlora_nf4.h -- C ABI of the frozen-NF4-base + LoRA linear layer for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What the layer is (cited by page title and section):
+ *  - The frozen base weight is stored in 4-bit NormalFloat (NF4): 16 levels
+ *    at normal quantiles, one absmax scaling constant per block of weights,
+ *    and the constants themselves quantized to 8 bits under a coarser set of
+ *    constants ("QLoRA: fine-tuning a 65B model on one GPU", section
+ *    "NormalFloat, double quantization, paged optimizers"; "QLoRA: efficient
+ *    finetuning of quantized LLMs", Abstract, items (a) and (b)).
+ *  - The base is quantized once up front and dequantized to 16 bits on the
+ *    fly for every forward and backward pass; gradients reach only the
+ *    low-rank adapters, which stay in 16 bits (blog section "Where the memory
+ *    goes"; CoChat Abstract).
+ *  - The backward pass re-materializes the low-precision weight from the
+ *    quantized module instead of keeping a 16-bit copy ("ModuLoRA: Finetuning
+ *    2-Bit LLMs on Consumer GPUs by Integrating with Modular Quantizers",
+ *    abstract).
+ *
+ * Shapes (torch Linear convention, row-major, contiguous):
+ *   W [N, K]  frozen weight (fp32 only as quantizer input)
+ *   X [M, K]  input, bf16            Y  [M, N] output, bf16
+ *   A [r, K]  LoRA down, bf16        B  [N, r] LoRA up, bf16
+ *   s         LoRA scale (alpha / r), fp32
+ *   Forward:  Y  = X W^T + s (X A^T) B^T
+ *   Backward: dU = s dY B;  dX = dY W + dU A;  dA = dU^T X;  dB = s dY^T (X A^T)
+ *   where W is the dequantized weight; there is no gradient for W.
+ *
+ * NF4 storage of W (the "nf4 tensor"):
+ *   codes [N*K/2] uint8  two 4-bit level indices per byte, element 2j of the
+ *                        row-major flattening in the low nibble of byte j
+ *   q8    [N*K/64] uint8 8-bit absmax constant of each 64-element block
+ *   step  [ceil(N*K/64/256)] fp32  per group of 256 consecutive blocks:
+ *                        the group's largest absmax divided by 255
+ *   Dequantized weight: w = bf16_rne(level[code] * (q8 * step)), both
+ *   products rounded to fp32.
+ *
+ * Conventions for every call:
+ *   - bf16 tensors are passed as uint16_t bit patterns.
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the
+ *     library never allocates, frees or keeps them.  Scratch memory comes
+ *     from a caller-provided device workspace sized by
+ *     qlora_workspace_size().  Pointers must be 16-byte aligned.
+ *   - Work is enqueued on `stream` (0 = the null stream) and is
+ *     asynchronous; no call synchronizes.  The library keeps no mutable
+ *     global state: calls are reentrant and thread-safe.  Calls that share
+ *     a workspace must be ordered (same stream).
+ *   - Every call validates its arguments before launching anything and
+ *     returns a status code (QLORA_OK or a negative error, see below); on
+ *     error nothing has been enqueued and no output has been touched.
+ *   - Results are deterministic: the same inputs give bit-identical outputs.
+ */
+#ifndef QLORA_NF4_H_
+#define QLORA_NF4_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---- */
+#define QLORA_OK 0
+#define QLORA_ERR_INVALID (-1)     /* null pointer, bad size, misalignment   */
+#define QLORA_ERR_UNSUPPORTED (-2) /* block sizes other than 64 / 256, etc.  */
+#define QLORA_ERR_WORKSPACE (-3)   /* workspace smaller than required        */
+#define QLORA_ERR_LAUNCH (-4)      /* a HIP launch reported an error         */
+
+#define QLORA_NF4_BLOCKSIZE 64
+#define QLORA_NF4_DQ_BLOCKSIZE 256
+#define QLORA_MAX_RANK 256
+
+/* The quantized frozen weight.  All pointers are device pointers. */
+typedef struct nf4_tensor_t {
+  const uint8_t* codes; /* [N*K/2]  */
+  const uint8_t* q8;    /* [N*K/64] */
+  const float* step;    /* [ceil(N*K/16384)] */
+  int64_t N;
+  int64_t K;
+  int32_t blocksize;    /* must be 64  */
+  int32_t dq_blocksize; /* must be 256 */
+} nf4_tensor_t;
+
+/* Text for a status code (static storage, never NULL). */
+const char* qlora_status_str(int32_t status);
+
+/* Host-side copy of the 16 NF4 levels (ascending, fp32) and of the 15
+ * decision thresholds the quantizer compares against (a value x normalized
+ * by its block's absmax gets the code #{i : x > thresholds[i]}, which is the
+ * nearest level with ties going to the lower one).  No device work.  Either
+ * pointer may be NULL.  Levels: normal quantiles with an exact zero,
+ * normalized to [-1, 1] ("QLoRA: fine-tuning a 65B model on one GPU",
+ * section "NormalFloat, double quantization, paged optimizers"). */
+void nf4_code_table(float* levels16, float* thresholds15);
+
+/* Bytes of the three NF4 arrays for an N x K weight (closed form:
+ * N*K/2 + N*K/64 + 4*ceil(N*K/16384)); 0 for invalid sizes. */
+size_t nf4_storage_bytes(int64_t N, int64_t K);
+
+/* nf4_quantize -- blockwise NF4 quantization with double-quantized absmax
+ * constants, once per frozen weight (blog section "NormalFloat, double
+ * quantization, paged optimizers"; capability page "Qlora 4 Bit
+ * Quantization With Nf4 Fp4 Data Types And Lora Adapters", NF4 entry:
+ * block-wise absmax scaling and double quantization of the constants).
+ *
+ *   W      [N, K] fp32, device.  Must be finite.
+ *   N, K   N >= 1, K >= 64, K % 64 == 0.
+ *   blocksize, dq_blocksize   must be 64 and 256.
+ *   codes  [N*K/2] out;  q8 [N*K/64] out;  step [ceil(N*K/16384)] out.
+ * Per block b of 64 consecutive elements: c_b = max|w|; each element gets
+ * the level nearest to fl32(w / c_b) (ties to the lower level; an all-zero
+ * block gets the zero level).  Per group g of 256 consecutive blocks (the
+ * last group may be shorter): step_g = fl32(max_b c_b / 255),
+ * q_b = min(255, round_half_even(fl32(c_b / step_g))), q_b = 0 if step_g = 0.
+ */
+int32_t nf4_quantize(const float* W, int64_t N, int64_t K, int32_t blocksize,
+                     int32_t dq_blocksize, uint8_t* codes, uint8_t* q8,
+                     float* step, hipStream_t stream);
+
+/* nf4_dequantize -- materialize the bf16 weight [N, K] from its NF4 state
+ * (for checking and interop; the linear layer never does this: it
+ * dequantizes tiles on chip).  w->N, w->K as in nf4_quantize.
+ * W_bf16 [N*K] out. */
+int32_t nf4_dequantize(const nf4_tensor_t* w, uint16_t* W_bf16,
+                       hipStream_t stream);
+
+/* Workspace bytes needed by qlora_linear_fwd (for_bwd = 0) or
+ * qlora_linear_bwd (for_bwd = 1) at these sizes; 0 for invalid sizes. */
+size_t qlora_workspace_size(int64_t M, int64_t N, int64_t K, int32_t r,
+                            int32_t for_bwd);
+
+/* qlora_linear_fwd -- Y = X W^T + s (X A^T) B^T with W dequantized on the
+ * fly to bf16 (blog section "Where the memory goes").
+ *
+ *   w       quantized weight, N >= 1, N % 8 == 0, K % 64 == 0
+ *   X       [M, K] bf16, M >= 1
+ *   A       [r, K] bf16;  B [N, r] bf16;  1 <= r <= 256
+ *   s       LoRA scale
+ *   Y       [M, N] bf16 out
+ *   U_out   [M, r] bf16 out, may be NULL: X A^T rounded to bf16, which
+ *           qlora_linear_bwd can take back instead of recomputing it
+ *   ws      device workspace of ws_bytes >= qlora_workspace_size(M,N,K,r,0)
+ * Accumulation is fp32.  M <= 16 takes a bandwidth-bound path that
+ * streams the packed weight once; larger M takes an MFMA tile path.
+ */
+int32_t qlora_linear_fwd(const nf4_tensor_t* w, const uint16_t* X, int64_t M,
+                         const uint16_t* A, const uint16_t* B, int32_t r,
+                         float s, uint16_t* Y, uint16_t* U_out, void* ws,
+                         size_t ws_bytes, hipStream_t stream);
+
+/* qlora_linear_bwd -- gradients of the layer for the output gradient dY,
+ * re-dequantizing W on chip (ModuLoRA abstract: the backward pass
+ * materializes the low-precision weight from the quantized module):
+ *   dX = dY W + s (dY B) A      [M, K] bf16 out, may be NULL (skipped)
+ *   dA = s (dY B)^T X           [r, K] bf16 out
+ *   dB = s dY^T (X A^T)         [N, r] bf16 out
+ * Outputs are overwritten, not accumulated.  U is X A^T as returned by
+ * qlora_linear_fwd's U_out, or NULL to recompute it.  Other arguments as in
+ * qlora_linear_fwd; ws_bytes >= qlora_workspace_size(M,N,K,r,1).
+ */
+int32_t qlora_linear_bwd(const nf4_tensor_t* w, const uint16_t* X,
+                         const uint16_t* dY, int64_t M, const uint16_t* A,
+                         const uint16_t* B, const uint16_t* U, int32_t r,
+                         float s, uint16_t* dX, uint16_t* dA, uint16_t* dB,
+                         void* ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLORA_NF4_H_ */

@@ -27,6 +27,7 @@ w = bf16_rne(fl32(level * fl32(q * step))).
 """
 
 import math
+import os
 
 import numpy as np
 
@@ -130,17 +131,30 @@ def nearest_level(x: np.ndarray, levels_f32: np.ndarray) -> np.ndarray:
     difference is exact in fp64, which is the only case where two distances
     can tie or nearly tie; far from a midpoint, rounding in fp64 cannot
     change which distance is smaller.  ``argmin`` returns the first minimum,
-    which is the lower index.
+    which is the lower index.  Chunks are independent and are spread over a
+    few threads (numpy releases the GIL inside the ufuncs).
     """
     L = levels_f32.astype(np.float64)
-    xs = np.asarray(x, dtype=np.float32).astype(np.float64)
+    xs = np.asarray(x, dtype=np.float32)
     out = np.empty(xs.shape, dtype=np.uint8)
     flat_in = xs.reshape(-1)
     flat_out = out.reshape(-1)
-    chunk = 1 << 20
-    for s in range(0, flat_in.size, chunk):
-        d = np.abs(flat_in[s:s + chunk, None] - L[None, :])
+    chunk = 1 << 19
+
+    def work(s):
+        xc = flat_in[s:s + chunk].astype(np.float64)
+        d = np.abs(xc[:, None] - L[None, :])
         flat_out[s:s + chunk] = np.argmin(d, axis=1).astype(np.uint8)
+
+    starts = range(0, flat_in.size, chunk)
+    if flat_in.size <= 4 * chunk:
+        for s in starts:
+            work(s)
+    else:
+        from concurrent.futures import ThreadPoolExecutor
+        nthreads = max(1, min(8, len(os.sched_getaffinity(0))))
+        with ThreadPoolExecutor(nthreads) as ex:
+            list(ex.map(work, starts))
     return out
 
 

@@ -1,0 +1,64 @@
+// Internal launch interface between the C ABI (abi.hip) and the kernels.
+// Every launcher enqueues on `stream` and returns hipGetLastError().
+#pragma once
+
+#include "common.hpp"
+
+namespace qn {
+
+// ---- nf4_quant.hip ----
+hipError_t launch_nf4_quantize(const float* W, int64_t nblocks, uint8_t* codes, uint8_t* q8,
+                               float* step, hipStream_t stream);
+hipError_t launch_nf4_dequantize(const uint8_t* codes, const uint8_t* q8, const float* step,
+                                 int64_t nelem, uint16_t* out, hipStream_t stream);
+
+// ---- qgemm.hip: MFMA tile kernels with the NF4 dequantization in the prologue ----
+struct Nf4View {
+  const uint8_t* codes;
+  const uint8_t* q8;
+  const float* step;
+  int64_t N, K;
+};
+
+// Y[M,N] = X[M,K] W^T + bf16(s U)[M,r] B[N,r]^T.  U has row stride ldu (a
+// multiple of 8, zero-padded to ceil(r/64)*64 columns).
+hipError_t launch_qgemm_fwd(const Nf4View& w, const uint16_t* X, int64_t M, const uint16_t* U,
+                            int64_t ldu, const uint16_t* B, int32_t r, float s, uint16_t* Y,
+                            hipStream_t stream);
+
+// dX[M,K] = dY[M,N] W + dU[M,r] A[r,K].  dU has row stride lddu (zero-padded).
+hipError_t launch_qgemm_bwd(const Nf4View& w, const uint16_t* dY, int64_t M, const uint16_t* dU,
+                            int64_t lddu, const uint16_t* A, int32_t r, uint16_t* dX,
+                            hipStream_t stream);
+
+// ---- gemv.hip: bandwidth-bound forward for M <= 16 ----
+constexpr int kGemvMaxM = 16;
+// Partial sums part[S][M][N] (fp32) over S equal K ranges; returns S.
+int gemv_splits(int64_t N, int64_t K);
+hipError_t launch_qgemv_partial(const Nf4View& w, const uint16_t* X, int64_t M, int splits,
+                                float* part, hipStream_t stream);
+// Y[m,n] = sum_s part[s][m][n] + s * sum_j U[m][j] B[n][j]  (bf16 out)
+hipError_t launch_gemv_finish(const float* part, int splits, int64_t M, int64_t N,
+                              const uint16_t* U, int64_t ldu, const uint16_t* B, int32_t r,
+                              float s, uint16_t* Y, hipStream_t stream);
+
+// ---- lora.hip: small-rank GEMMs (fp32 split partials + ordered reduction) ----
+// Operand element access: A-op (i, c) at a[i*a_si + c*a_sc]; B-op (c, j) at
+// b[j*b_sj + c*b_sc]; one stride of each operand must be 1.
+struct SkinnyOp {
+  const uint16_t* a;
+  int64_t a_si, a_sc;
+  const uint16_t* b;
+  int64_t b_sj, b_sc;
+  int64_t I, J, C;
+};
+int skinny_splits(int64_t I, int64_t J, int64_t C);
+size_t skinny_partial_bytes(int64_t I, int64_t J, int64_t C);
+hipError_t launch_skinny_partial(const SkinnyOp& op, int splits, float* part, hipStream_t stream);
+// out[i*o_si + j] = bf16(scale * sum_s part[s][i][j]) for j < J, and 0 for
+// J <= j < Jw; optionally also out2[i*o2_si + j] for j < J.
+hipError_t launch_skinny_finish(const float* part, int splits, int64_t I, int64_t J, float scale,
+                                uint16_t* out, int64_t o_si, int64_t Jw, uint16_t* out2,
+                                int64_t o2_si, hipStream_t stream);
+
+}  // namespace qn

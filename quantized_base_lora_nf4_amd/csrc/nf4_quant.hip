@@ -1,0 +1,132 @@
+// NF4 quantizer with double-quantized absmax constants, and the standalone
+// dequantizer.
+//
+// Quantization follows "QLoRA: fine-tuning a 65B model on one GPU", section
+// "NormalFloat, double quantization, paged optimizers" (16 levels at normal
+// quantiles, one constant per block, constants stored in 8 bits under a
+// coarser level) and the capability page "Qlora 4 Bit Quantization With Nf4
+// Fp4 Data Types And Lora Adapters", NF4 entry (block-wise absmax scaling).
+//
+// Layout: one workgroup per group of 256 consecutive 64-element blocks
+// (16384 fp32 = 64 KB of W).  Each wave walks 64 blocks, four at a time:
+// sixteen lanes share a block and each lane owns four consecutive elements,
+// so every load instruction reads 1 KB of contiguous W and every store writes
+// 128 contiguous code bytes.  The kernel is bound by HBM (4 B read and
+// 0.52 B written per weight).
+#include "kernels.hpp"
+
+namespace qn {
+
+__device__ __forceinline__ uint32_t nf4_code(float x) {
+  // number of thresholds strictly below x = nearest level, ties low
+  uint32_t c = 0;
+#pragma unroll
+  for (int i = 0; i < 15; ++i) c += (x > __builtin_bit_cast(float, kThr.bits[i])) ? 1u : 0u;
+  return c;
+}
+
+__global__ __launch_bounds__(256) void k_nf4_quantize(const float* __restrict__ W,
+                                                      int64_t nblocks,
+                                                      uint8_t* __restrict__ codes,
+                                                      uint8_t* __restrict__ q8,
+                                                      float* __restrict__ step) {
+  __shared__ float cabs[256];
+  __shared__ float wmax[4];
+  const int64_t g = blockIdx.x;
+  const int64_t b0 = g * 256;
+  const int nb = (int)((nblocks - b0) < 256 ? (nblocks - b0) : 256);
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int sub = lane & 15;  // lane within the block: elements 4*sub .. 4*sub+3
+
+  for (int it = 0; it < 16; ++it) {
+    const int bi = wave * 64 + it * 4 + (lane >> 4);  // block within the group
+    if (bi < nb) {
+      const int64_t b = b0 + bi;
+      const f32x4 v = *reinterpret_cast<const f32x4*>(W + b * 64 + sub * 4);
+      float m = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+      m = fmaxf(m, __shfl_xor(m, 8, 16));
+      m = fmaxf(m, __shfl_xor(m, 4, 16));
+      m = fmaxf(m, __shfl_xor(m, 2, 16));
+      m = fmaxf(m, __shfl_xor(m, 1, 16));
+      uint32_t c0, c1, c2, c3;
+      if (m > 0.0f) {
+        // IEEE-correct fp32 division (the compiler's default for '/')
+        c0 = nf4_code(v[0] / m);
+        c1 = nf4_code(v[1] / m);
+        c2 = nf4_code(v[2] / m);
+        c3 = nf4_code(v[3] / m);
+      } else {
+        c0 = c1 = c2 = c3 = 7u;  // all-zero block: the exact zero level
+      }
+      const uint16_t packed = (uint16_t)(c0 | (c1 << 4) | (c2 << 8) | (c3 << 12));
+      *reinterpret_cast<uint16_t*>(codes + b * 32 + sub * 2) = packed;
+      if (sub == 0) cabs[bi] = m;
+    }
+  }
+  __syncthreads();
+
+  // Double quantization of this group's constants.
+  const int t = threadIdx.x;
+  float c = (t < nb) ? cabs[t] : 0.0f;
+  float m = c;
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  if (lane == 0) wmax[wave] = m;
+  __syncthreads();
+  const float smax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  const float st = smax / 255.0f;
+  if (t < nb) {
+    uint32_t q = 0;
+    if (st > 0.0f) {
+      const float r = __builtin_rintf(c / st);  // round half to even
+      q = (r >= 255.0f) ? 255u : (uint32_t)r;
+    }
+    q8[b0 + t] = (uint8_t)q;
+  }
+  if (t == 0) step[g] = st;
+}
+
+// Standalone dequantizer: w = bf16_rne(level[code] * fl32(q8 * step)).
+// Each thread expands four code bytes (eight weights) into 16 bytes of bf16.
+__global__ __launch_bounds__(256) void k_nf4_dequantize(const uint8_t* __restrict__ codes,
+                                                        const uint8_t* __restrict__ q8,
+                                                        const float* __restrict__ step,
+                                                        int64_t n8, uint16_t* __restrict__ out) {
+  __shared__ float lv[16];
+  if (threadIdx.x < 16) lv[threadIdx.x] = level_f32(threadIdx.x);
+  __syncthreads();
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n8;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(codes + i * 4);
+    const int64_t b = i >> 3;  // 8 groups of 8 weights per 64-element block
+    const float chat = (float)q8[b] * step[b >> 8];
+    u32x4 o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float lo = lv[(w >> (8 * j)) & 15u] * chat;
+      const float hi = lv[(w >> (8 * j + 4)) & 15u] * chat;
+      o[j] = pack_bf16x2(lo, hi);
+    }
+    *reinterpret_cast<u32x4*>(out + i * 8) = o;
+  }
+}
+
+hipError_t launch_nf4_quantize(const float* W, int64_t nblocks, uint8_t* codes, uint8_t* q8,
+                               float* step, hipStream_t stream) {
+  const int64_t ngroups = (nblocks + 255) / 256;
+  hipLaunchKernelGGL(k_nf4_quantize, dim3((unsigned)ngroups), dim3(256), 0, stream, W, nblocks,
+                     codes, q8, step);
+  return hipGetLastError();
+}
+
+hipError_t launch_nf4_dequantize(const uint8_t* codes, const uint8_t* q8, const float* step,
+                                 int64_t nelem, uint16_t* out, hipStream_t stream) {
+  const int64_t n8 = nelem / 8;
+  int64_t grid = (n8 + 255) / 256;
+  if (grid > 65536) grid = 65536;
+  hipLaunchKernelGGL(k_nf4_dequantize, dim3((unsigned)grid), dim3(256), 0, stream, codes, q8,
+                     step, n8, out);
+  return hipGetLastError();
+}
+
+}  // namespace qn

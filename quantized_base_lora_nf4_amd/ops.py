@@ -1,0 +1,200 @@
+"""Thin torch binding of the C ABI: argument marshalling only.
+
+Tensors are torch CUDA (HIP) tensors; bf16 tensors may be ``torch.bfloat16``
+or ``torch.int16``/``torch.uint16`` views of the bits.  Every call enqueues on
+``torch.cuda.current_stream()`` unless a stream is passed.  All arithmetic
+happens in the HIP kernels behind the C ABI.
+"""
+
+import ctypes
+from dataclasses import dataclass
+from typing import Optional, Tuple
+
+import torch
+
+from ._lib import Nf4Tensor, check, lib
+
+BLOCKSIZE = 64
+DQ_BLOCKSIZE = 256
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _bf16_view(t: torch.Tensor) -> torch.Tensor:
+    if t.dtype in (torch.bfloat16, torch.int16, torch.uint16):
+        return t
+    raise TypeError(f"expected a bf16 tensor (or its 16-bit view), got {t.dtype}")
+
+
+@dataclass
+class NF4Weight:
+    """Device storage of one quantized frozen weight."""
+    codes: torch.Tensor   # uint8 [N*K/2]
+    q8: torch.Tensor      # uint8 [N*K/64]
+    step: torch.Tensor    # float32 [ceil(N*K/16384)]
+    N: int
+    K: int
+
+    def struct(self) -> Nf4Tensor:
+        return Nf4Tensor(_ptr(self.codes), _ptr(self.q8), _ptr(self.step), self.N, self.K,
+                         BLOCKSIZE, DQ_BLOCKSIZE)
+
+    def nbytes(self) -> int:
+        return self.codes.numel() + self.q8.numel() + 4 * self.step.numel()
+
+
+def code_table() -> Tuple[list, list]:
+    """The library's NF4 levels (16) and decision thresholds (15), fp32."""
+    lv = (ctypes.c_float * 16)()
+    th = (ctypes.c_float * 15)()
+    lib().nf4_code_table(ctypes.cast(lv, ctypes.c_void_p), ctypes.cast(th, ctypes.c_void_p))
+    return list(lv), list(th)
+
+
+def storage_bytes(N: int, K: int) -> int:
+    return int(lib().nf4_storage_bytes(N, K))
+
+
+def alloc_nf4(N: int, K: int, device="cuda") -> NF4Weight:
+    nb = N * K // BLOCKSIZE
+    ng = (nb + DQ_BLOCKSIZE - 1) // DQ_BLOCKSIZE
+    return NF4Weight(
+        codes=torch.empty(N * K // 2, dtype=torch.uint8, device=device),
+        q8=torch.empty(nb, dtype=torch.uint8, device=device),
+        step=torch.empty(ng, dtype=torch.float32, device=device),
+        N=N, K=K)
+
+
+def nf4_quantize(W: torch.Tensor, out: Optional[NF4Weight] = None, stream=None) -> NF4Weight:
+    """Quantize an fp32 [N, K] device tensor to NF4 with double-quantized constants."""
+    if W.dtype != torch.float32 or W.dim() != 2:
+        raise TypeError("W must be a 2-D float32 tensor")
+    N, K = W.shape
+    if out is None:
+        out = alloc_nf4(N, K, W.device)
+    st = lib().nf4_quantize(_ptr(W), N, K, BLOCKSIZE, DQ_BLOCKSIZE, _ptr(out.codes), _ptr(out.q8),
+                            _ptr(out.step), _stream(stream))
+    check(st, "nf4_quantize")
+    return out
+
+
+def nf4_dequantize(w: NF4Weight, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Materialize the bf16 [N, K] weight (for checks and interop)."""
+    if out is None:
+        out = torch.empty(w.N, w.K, dtype=torch.bfloat16, device=w.codes.device)
+    s = w.struct()
+    check(lib().nf4_dequantize(ctypes.byref(s), _ptr(_bf16_view(out)), _stream(stream)),
+          "nf4_dequantize")
+    return out
+
+
+def workspace_size(M: int, N: int, K: int, r: int, for_bwd: bool) -> int:
+    return int(lib().qlora_workspace_size(M, N, K, r, 1 if for_bwd else 0))
+
+
+def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> torch.Tensor:
+    if ws is not None and ws.numel() * ws.element_size() >= nbytes:
+        return ws
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def qlora_linear_fwd(w: NF4Weight, X: torch.Tensor, A: torch.Tensor, B: torch.Tensor, s: float,
+                     Y: Optional[torch.Tensor] = None, U_out: Optional[torch.Tensor] = None,
+                     ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Y = X W^T + s (X A^T) B^T.  X [M, K], A [r, K], B [N, r] bf16."""
+    M = X.shape[0]
+    r = A.shape[0]
+    if Y is None:
+        Y = torch.empty(M, w.N, dtype=torch.bfloat16, device=X.device)
+    nbytes = workspace_size(M, w.N, w.K, r, False)
+    ws = _workspace(nbytes, X.device, ws)
+    s_ = w.struct()
+    st = lib().qlora_linear_fwd(ctypes.byref(s_), _ptr(_bf16_view(X)), M, _ptr(_bf16_view(A)),
+                                _ptr(_bf16_view(B)), r, float(s), _ptr(_bf16_view(Y)),
+                                _ptr(U_out), _ptr(ws), ws.numel() * ws.element_size(),
+                                _stream(stream))
+    check(st, "qlora_linear_fwd")
+    return Y
+
+
+def qlora_linear_bwd(w: NF4Weight, X: torch.Tensor, dY: torch.Tensor, A: torch.Tensor,
+                     B: torch.Tensor, s: float, U: Optional[torch.Tensor] = None,
+                     need_dX: bool = True, out: Optional[tuple] = None,
+                     ws: Optional[torch.Tensor] = None, stream=None):
+    """Returns (dX or None, dA, dB), all bf16."""
+    M = X.shape[0]
+    r = A.shape[0]
+    dev = X.device
+    if out is None:
+        dX = torch.empty(M, w.K, dtype=torch.bfloat16, device=dev) if need_dX else None
+        dA = torch.empty(r, w.K, dtype=torch.bfloat16, device=dev)
+        dB = torch.empty(w.N, r, dtype=torch.bfloat16, device=dev)
+    else:
+        dX, dA, dB = out
+    nbytes = workspace_size(M, w.N, w.K, r, True)
+    ws = _workspace(nbytes, dev, ws)
+    s_ = w.struct()
+    st = lib().qlora_linear_bwd(ctypes.byref(s_), _ptr(_bf16_view(X)), _ptr(_bf16_view(dY)), M,
+                                _ptr(_bf16_view(A)), _ptr(_bf16_view(B)), _ptr(U), r, float(s),
+                                _ptr(dX), _ptr(dA), _ptr(dB), _ptr(ws),
+                                ws.numel() * ws.element_size(), _stream(stream))
+    check(st, "qlora_linear_bwd")
+    return dX, dA, dB
+
+
+class QLoRALinearFunction(torch.autograd.Function):
+    """Autograd wrapper: gradients flow to X, A and B only (the NF4 base is frozen)."""
+
+    @staticmethod
+    def forward(ctx, X, A, B, w: NF4Weight, s: float):
+        M = X.shape[0]
+        U = torch.empty(M, A.shape[0], dtype=torch.bfloat16, device=X.device)
+        Y = qlora_linear_fwd(w, X.contiguous(), A.contiguous(), B.contiguous(), s, U_out=U)
+        ctx.save_for_backward(X, A, B, U)
+        ctx.w = w
+        ctx.s = s
+        return Y
+
+    @staticmethod
+    def backward(ctx, dY):
+        X, A, B, U = ctx.saved_tensors
+        dX, dA, dB = qlora_linear_bwd(ctx.w, X.contiguous(), dY.contiguous(), A.contiguous(),
+                                      B.contiguous(), ctx.s, U=U,
+                                      need_dX=ctx.needs_input_grad[0])
+        return dX, dA, dB, None, None
+
+
+class QLoRALinear(torch.nn.Module):
+    """A frozen NF4 weight with a trainable LoRA pair (A: r x K, B: N x r)."""
+
+    def __init__(self, weight_fp32: torch.Tensor, r: int, alpha: float, A=None, B=None):
+        super().__init__()
+        N, K = weight_fp32.shape
+        self.nf4 = nf4_quantize(weight_fp32.float().contiguous())
+        self.r, self.alpha = r, alpha
+        dev = weight_fp32.device
+        self.A = torch.nn.Parameter(A if A is not None else
+                                    (torch.randn(r, K, device=dev) * 0.01).bfloat16())
+        self.B = torch.nn.Parameter(B if B is not None else
+                                    torch.zeros(N, r, device=dev, dtype=torch.bfloat16))
+
+    @property
+    def s(self) -> float:
+        return self.alpha / self.r
+
+    def forward(self, X):
+        shp = X.shape
+        Y = QLoRALinearFunction.apply(X.reshape(-1, shp[-1]), self.A, self.B, self.nf4, self.s)
+        return Y.reshape(*shp[:-1], Y.shape[-1])

@@ -1,0 +1,146 @@
+"""Host-side checks of the C ABI (no GPU work): the library loads and exports
+every declared symbol, its NF4 table agrees with the oracle, and bad
+arguments are rejected before anything is launched."""
+
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import numpy as np
+import pytest
+
+import quantized_base_lora_nf4_amd as qn
+from quantized_base_lora_nf4_amd import _lib
+from oracle import nf4
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qlora_nf4.h")
+
+
+def header_symbols():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_0-9]+)\s*\(", txt)) - {"defined"})
+
+
+def test_header_symbols_are_exported():
+    syms = header_symbols()
+    assert set(syms) == set(_lib.EXPORTS), syms
+    L = qn.lib()
+    for s in syms:
+        assert hasattr(L, s), s
+    out = subprocess.run(["nm", "-D", "--defined-only", qn.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    for s in syms:
+        assert re.search(r"\bT %s$" % s, out, flags=re.M), s
+
+
+def test_code_table_matches_oracle():
+    lv, th = qn.code_table()
+    assert np.array_equal(np.array(lv, np.float32).view(np.uint32),
+                          nf4.nf4_levels().view(np.uint32))
+    # thresholds are the level midpoints rounded toward -inf
+    L = nf4.nf4_levels().astype(np.float64)
+    for i, t in enumerate(th):
+        mid = (L[i] + L[i + 1]) / 2
+        t32 = np.float32(t)
+        assert float(t32) <= mid < float(np.nextafter(t32, np.float32(np.inf)))
+
+
+def test_threshold_rule_is_nearest_level_for_every_fp32_in_unit_interval():
+    lv, th = qn.code_table()
+    with tempfile.TemporaryDirectory() as d:
+        so = os.path.join(d, "exh.so")
+        src = os.path.join(ROOT, "tests", "csrc", "exhaustive_nearest.c")
+        subprocess.run(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", src, "-o", so, "-lm"],
+                       check=True)
+        E = ctypes.CDLL(so)
+        E.nearest_mismatches.restype = ctypes.c_long
+        E.nearest_mismatches.argtypes = [ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.POINTER(ctypes.c_uint32)]
+        L = (ctypes.c_float * 16)(*lv)
+        T = (ctypes.c_float * 15)(*th)
+        first = ctypes.c_uint32(0)
+        bad = E.nearest_mismatches(ctypes.cast(L, ctypes.c_void_p), ctypes.cast(T, ctypes.c_void_p),
+                                   ctypes.byref(first))
+        assert bad == 0, hex(first.value)
+
+
+def test_storage_bytes_closed_form():
+    for N, K in [(1, 64), (3, 1024), (1024, 1024), (22016, 8192), (5120, 13824)]:
+        assert qn.storage_bytes(N, K) == nf4.storage_bytes(N, K)
+    assert qn.storage_bytes(4, 65) == 0 and qn.storage_bytes(0, 64) == 0
+
+
+def test_workspace_size_rules():
+    assert qn.workspace_size(256, 1024, 1024, 8, False) > 0
+    assert qn.workspace_size(256, 1024, 1024, 8, True) >= qn.workspace_size(256, 1024, 1024, 8, False) // 2
+    for bad in [(0, 64, 64, 8), (4, 64, 63, 8), (4, 60, 64, 8), (4, 64, 64, 0), (4, 64, 64, 257)]:
+        assert qn.workspace_size(*bad, False) == 0, bad
+
+
+FAKE = 1 << 20  # an aligned non-null address that is never dereferenced
+
+
+def _w(N=64, K=64, bs=64, dq=256, codes=FAKE):
+    return _lib.Nf4Tensor(codes, FAKE, FAKE, N, K, bs, dq)
+
+
+def test_quantize_rejects_bad_arguments_without_launching():
+    L = qn.lib()
+    ok = dict(W=FAKE, N=4, K=128, bs=64, dq=256, codes=FAKE, q8=FAKE, step=FAKE)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return L.nf4_quantize(a["W"], a["N"], a["K"], a["bs"], a["dq"], a["codes"], a["q8"],
+                              a["step"], None)
+    assert call(W=None) == _lib.QLORA_ERR_INVALID
+    assert call(codes=None) == _lib.QLORA_ERR_INVALID
+    assert call(K=96) == _lib.QLORA_ERR_INVALID
+    assert call(N=0) == _lib.QLORA_ERR_INVALID
+    assert call(bs=32) == _lib.QLORA_ERR_UNSUPPORTED
+    assert call(dq=128) == _lib.QLORA_ERR_UNSUPPORTED
+    assert call(W=FAKE + 4) == _lib.QLORA_ERR_INVALID
+
+
+def test_linear_rejects_bad_arguments_without_launching():
+    L = qn.lib()
+    need = qn.workspace_size(32, 64, 128, 8, False)
+
+    def fwd(w=None, X=FAKE, M=32, r=8, ws=FAKE, nbytes=need, s=1.0, Y=FAKE):
+        w = w or _w(64, 128)
+        return L.qlora_linear_fwd(ctypes.byref(w), X, M, FAKE, FAKE, r, s, Y, None, ws, nbytes, None)
+    assert fwd(X=None) == _lib.QLORA_ERR_INVALID
+    assert fwd(Y=None) == _lib.QLORA_ERR_INVALID
+    assert fwd(M=0) == _lib.QLORA_ERR_INVALID
+    assert fwd(r=0) == _lib.QLORA_ERR_INVALID
+    assert fwd(r=300) == _lib.QLORA_ERR_INVALID
+    assert fwd(w=_w(64, 100)) == _lib.QLORA_ERR_INVALID
+    assert fwd(w=_w(60, 128)) == _lib.QLORA_ERR_INVALID
+    assert fwd(w=_w(64, 128, bs=128)) == _lib.QLORA_ERR_UNSUPPORTED
+    assert fwd(w=_w(64, 128, codes=None)) == _lib.QLORA_ERR_INVALID
+    assert fwd(nbytes=need - 1) == _lib.QLORA_ERR_WORKSPACE
+    assert fwd(ws=None) == _lib.QLORA_ERR_INVALID
+    assert fwd(X=FAKE + 2) == _lib.QLORA_ERR_INVALID
+    assert fwd(s=float("nan")) == _lib.QLORA_ERR_INVALID
+
+    needb = qn.workspace_size(32, 64, 128, 8, True)
+
+    def bwd(dY=FAKE, dA=FAKE, nbytes=needb):
+        w = _w(64, 128)
+        return L.qlora_linear_bwd(ctypes.byref(w), FAKE, dY, 32, FAKE, FAKE, None, 8, 1.0, None,
+                                  dA, FAKE, FAKE, nbytes, None)
+    assert bwd(dY=None) == _lib.QLORA_ERR_INVALID
+    assert bwd(dA=None) == _lib.QLORA_ERR_INVALID
+    assert bwd(nbytes=needb - 1) == _lib.QLORA_ERR_WORKSPACE
+
+    w = _w(64, 128)
+    assert L.nf4_dequantize(ctypes.byref(w), None, None) == _lib.QLORA_ERR_INVALID
+
+
+def test_status_strings():
+    for st in (0, -1, -2, -3, -4):
+        assert qn.lib().qlora_status_str(st)
+    assert "workspace" in _lib.status_str(-3)
