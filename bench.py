@@ -1,0 +1,381 @@
+#!/usr/bin/env python3
+"""Throughput of the frozen-NF4-base + LoRA linear layer on one MI355X.
+
+Step = one forward + backward pass of the layer for every weight of the
+workload (default: the LLaMA-7B q_proj 4096x4096 and up_proj 11008x4096
+projections, 4096 tokens, LoRA r=64, alpha=16) with inputs resident in HBM.
+The quantized weights are built once before timing (quantization is a
+one-time cost of the frozen base); it is timed separately and reported
+under "extra", as is the few-token (M = 1, 4, 16) forward path on the
+8192x8192 and 28672x8192 weights.
+
+Prints ONE JSON line (rank 0, N = 1).  FLOPs per weight and step:
+4 M N K + 6 M r (N + K) (no gradient for the frozen W).
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E, published
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama7b_q_up_M4096_r64")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (for scaling HBM "
+                         "counters) and exit")
+    ap.add_argument("--cpu-rows", type=int, default=4096,
+                    help="token rows of the workload the CPU oracle runs on")
+    return ap.parse_args()
+
+
+class HipEvents:
+    """hipEvent_t pairs through the HIP runtime's C API (the library's
+    measurement calls record them around the dominant kernel)."""
+
+    def __init__(self):
+        import torch  # noqa: F401  (loads the HIP runtime)
+        self.rt = ctypes.CDLL("libamdhip64.so")
+        self.rt.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                ctypes.c_void_p]
+        self.rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.rt.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        e = ctypes.c_void_p()
+        assert self.rt.hipEventCreate(ctypes.byref(e)) == 0
+        return e
+
+    def elapsed_ms(self, a, b) -> float:
+        assert self.rt.hipEventSynchronize(b) == 0
+        ms = ctypes.c_float()
+        assert self.rt.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return ms.value
+
+    def destroy(self, e):
+        self.rt.hipEventDestroy(e)
+
+
+def kernel_source_hash(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "quantized_base_lora_nf4_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, workload: str, src_hash: str):
+    """HBM bytes per launch from rocprofv3 FETCH_SIZE/WRITE_SIZE runs, stored
+    in profiles/traffic.json together with the hash of the kernel sources the
+    counters were taken on; null once the sources have changed."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            d = json.load(f)
+        e = d[kernel][workload]
+        if e.get("src_hash") != src_hash:
+            return None
+        return e["bytes_per_launch"]
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build measures the layer on a single "
+              "MI355X (a data-parallel run would add an all-reduce of dA and dB).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": 1 << 30, "launches": 4}))
+        return
+    import quantized_base_lora_nf4_amd as qn
+    from quantized_base_lora_nf4_amd._lib import check
+    import workloads as wl_mod
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    qn.lib()
+    wl = {w.name: w for w in wl_mod.WORKLOADS}[args.workload]
+    assert not wl.fwd_only, "the headline workload is forward + backward"
+    M, r, s = wl.M[0], wl.r, wl.s
+    dev = "cuda"
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    L = qn.lib()
+    ev = HipEvents()
+
+    def d16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+
+    # ---- inputs (seeded, host-generated, then resident in HBM) ----
+    layers = []
+    host_inputs = []
+    for wi, spec in enumerate(wl.weights):
+        inp = wl_mod.draw_workload_weight(wl, wi)
+        host_inputs.append(inp)
+        W = torch.from_numpy(inp.W).to(dev)
+        w = qn.nf4_quantize(W)
+        N, K = spec.N, spec.K
+        t = dict(spec=spec, w=w, Wf32=W, X=d16(inp.X), dY=d16(inp.dY), A=d16(inp.A), B=d16(inp.B),
+                 U=torch.empty(M, r, dtype=torch.int16, device=dev),
+                 Y=torch.empty(M, N, dtype=torch.int16, device=dev),
+                 dX=torch.empty(M, K, dtype=torch.int16, device=dev),
+                 dA=torch.empty(r, K, dtype=torch.int16, device=dev),
+                 dB=torch.empty(N, r, dtype=torch.int16, device=dev))
+        t["wsf"] = torch.empty(qn.workspace_size(M, N, K, r, False), dtype=torch.uint8, device=dev)
+        t["wsb"] = torch.empty(qn.workspace_size(M, N, K, r, True), dtype=torch.uint8, device=dev)
+        t["st"] = w.struct()
+        # one set of 4 events per timed step: begin/end of the dominant
+        # forward kernel and of the dominant backward kernel
+        t["ev"] = [[ev.create() for _ in range(4)] for _ in range(args.steps)]
+        layers.append(t)
+    torch.cuda.synchronize()
+
+    def p(x):
+        return x.data_ptr() if x is not None else None
+
+    def step(i):
+        for t in layers:
+            e = t["ev"][i] if i is not None else [None] * 4
+            check(L.qlora_linear_fwd_ev(ctypes.byref(t["st"]), p(t["X"]), M, p(t["A"]), p(t["B"]), r,
+                                        s, p(t["Y"]), p(t["U"]), p(t["wsf"]), t["wsf"].numel(), sp,
+                                        e[0], e[1]), "fwd")
+            check(L.qlora_linear_bwd_ev(ctypes.byref(t["st"]), p(t["X"]), p(t["dY"]), M, p(t["A"]),
+                                        p(t["B"]), p(t["U"]), r, s, p(t["dX"]), p(t["dA"]),
+                                        p(t["dB"]), p(t["wsb"]), t["wsb"].numel(), sp, e[2], e[3]),
+                  "bwd")
+
+    for _ in range(args.warmup):
+        step(None)
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly `steps` steps, kernel events recorded live ----
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record()
+    for i in range(args.steps):
+        step(i)
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = t0.elapsed_time(t1)
+    ms_step = ms_total / args.steps
+
+    kt = {"fwd": [0.0, 0], "bwd": [0.0, 0]}  # summed kernel time (ms), launches
+    for t in layers:
+        for e in t["ev"]:
+            kt["fwd"][0] += ev.elapsed_ms(e[0], e[1])
+            kt["fwd"][1] += 1
+            kt["bwd"][0] += ev.elapsed_ms(e[2], e[3])
+            kt["bwd"][1] += 1
+
+    flops_step = 0.0
+    flops_fwd_kernel = 0.0
+    flops_bwd_kernel = 0.0
+    for t in layers:
+        N, K = t["spec"].N, t["spec"].K
+        flops_step += 4.0 * M * N * K + 6.0 * M * r * (N + K)
+        flops_fwd_kernel += 2.0 * M * N * (K + r)      # X W^T + (sU) B^T
+        flops_bwd_kernel += 2.0 * M * K * (N + r)      # dY W + dU A
+    tflops = flops_step / (ms_step * 1e-3) / 1e12
+
+    fwd_ms = kt["fwd"][0] / max(1, kt["fwd"][1]) * len(layers)   # per step
+    bwd_ms = kt["bwd"][0] / max(1, kt["bwd"][1]) * len(layers)
+    fwd_tf = flops_fwd_kernel / (fwd_ms * 1e-3) / 1e12
+    bwd_tf = flops_bwd_kernel / (bwd_ms * 1e-3) / 1e12
+    # dominant kernel = the one with the larger share of the step
+    if bwd_ms >= fwd_ms:
+        dom, dom_tf, dom_us = "k_qgemm_bwd", bwd_tf, bwd_ms / len(layers) * 1e3
+    else:
+        dom, dom_tf, dom_us = "k_qgemm_fwd", fwd_tf, fwd_ms / len(layers) * 1e3
+    src_hash = kernel_source_hash(["qgemm.hip", "common.hpp"])
+    roofline = {
+        "bound": "mfma", "kernel": dom, "achieved": round(dom_tf, 1),
+        "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+        "frac": round(dom_tf / MFMA_BF16_PEAK_TFLOPS, 4),
+        "traffic": load_traffic(dom, wl.name, src_hash),
+        "avg_launch_us": round(dom_us, 1),
+        "other": {"k_qgemm_fwd": {"TFLOP/s": round(fwd_tf, 1), "ms_per_step": round(fwd_ms, 4)},
+                  "k_qgemm_bwd": {"TFLOP/s": round(bwd_tf, 1), "ms_per_step": round(bwd_ms, 4)}},
+    }
+
+    extra = {}
+    if not args.no_extra:
+        extra = run_extras(qn, L, ev, torch, dev, sp, d16)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(host_inputs, wl, args.cpu_rows)
+
+    out = {
+        "metric": "fused NF4+LoRA linear fwd+bwd TFLOP/s (% bf16 MFMA peak); GEMV GB/s",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "tokens": M, "r": r, "alpha": wl.alpha,
+                   "weights": [f"{w_.name} {w_.N}x{w_.K}" for w_ in wl.weights],
+                   "nf4": "blocksize 64, double-quant 256 (8-bit constants, fp32 steps)",
+                   "pct_bf16_mfma_peak": round(100 * tflops / MFMA_BF16_PEAK_TFLOPS, 2),
+                   "wall_s_timed": round(wall, 4)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def run_extras(qn, L, ev, torch, dev, sp, d16):
+    """Few-token forward (GB/s on the packed weight stream) and one-time
+    quantization (GB/s), on rotated weight copies so that no call is served
+    from the 256 MB Infinity Cache."""
+    from quantized_base_lora_nf4_amd._lib import check
+    import workloads as wl_mod
+    res = {"gemv": [], "quantize": []}
+    g = wl_mod.SKINNY_GEMV
+    e0, e1, a0, a1 = ev.create(), ev.create(), ev.create(), ev.create()
+    for wi, spec in enumerate(g.weights):
+        N, K = spec.N, spec.K
+        inp = wl_mod.draw_workload_weight(g, wi, M=max(g.M))
+        W = torch.from_numpy(inp.W).to(dev)
+        wbytes = N * K // 2 + N * K // 64 + 4 * ((N * K // 64 + 255) // 256)
+        ncopy = max(3, int(np.ceil(768e6 / wbytes)))
+        copies = [qn.nf4_quantize(W) for _ in range(ncopy)]
+        structs = [c.struct() for c in copies]
+        # quantize GB/s (fp32 in, codes + constants out)
+        qt = []
+        for i in range(2 * ncopy):
+            ctypes_args = copies[i % ncopy]
+            torch.cuda.synchronize()
+            s0 = torch.cuda.Event(enable_timing=True)
+            s1 = torch.cuda.Event(enable_timing=True)
+            s0.record()
+            qn.nf4_quantize(W, out=ctypes_args)
+            s1.record()
+            torch.cuda.synchronize()
+            if i >= 2:
+                qt.append(s0.elapsed_time(s1))
+        qms = float(np.median(qt))
+        res["quantize"].append({"weight": f"{N}x{K}", "us": round(qms * 1e3, 1),
+                                "GB/s": round((4 * N * K + wbytes) / (qms * 1e-3) / 1e9, 1)})
+        A, B = d16(inp.A), d16(inp.B)
+        for M in g.M:
+            X = d16(inp.X[:M])
+            Y = torch.empty(M, N, dtype=torch.int16, device=dev)
+            ws = torch.empty(qn.workspace_size(M, N, K, g.r, False), dtype=torch.uint8, device=dev)
+            it, warm = 60, 6
+            kern, call = [], []
+            for i in range(it + warm):
+                st = structs[i % ncopy]
+                check(L.qlora_linear_fwd_ev(ctypes.byref(st), X.data_ptr(), M, A.data_ptr(),
+                                            B.data_ptr(), g.r, g.s, Y.data_ptr(), None,
+                                            ws.data_ptr(), ws.numel(), sp, e0, e1), "gemv")
+                torch.cuda.synchronize()
+                if i >= warm:
+                    kern.append(ev.elapsed_ms(e0, e1))
+            # whole call (all launches) on the stream
+            for i in range(it + warm):
+                st = structs[i % ncopy]
+                L.qlora_linear_fwd_ev(ctypes.byref(st), X.data_ptr(), M, A.data_ptr(), B.data_ptr(),
+                                      g.r, g.s, Y.data_ptr(), None, ws.data_ptr(), ws.numel(), sp,
+                                      None, None)
+                if i == warm - 1:
+                    torch.cuda.synchronize()
+                    c0 = torch.cuda.Event(enable_timing=True)
+                    c0.record()
+            c1 = torch.cuda.Event(enable_timing=True)
+            c1.record()
+            torch.cuda.synchronize()
+            call_ms = c0.elapsed_time(c1) / it
+            k_ms = float(np.median(kern))
+            res["gemv"].append({
+                "weight": f"{N}x{K}", "M": M, "r": g.r,
+                "kernel_us": round(k_ms * 1e3, 2),
+                "kernel_GB/s": round(wbytes / (k_ms * 1e-3) / 1e9, 1),
+                "kernel_frac_hbm": round(wbytes / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                "call_us": round(call_ms * 1e3, 2),
+                "call_GB/s": round(wbytes / (call_ms * 1e-3) / 1e9, 1),
+                "weight_bytes": wbytes, "copies_rotated": ncopy})
+        del copies, W
+        torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(host_inputs, wl, rows):
+    """The CPU oracle, as it stands, on a bounded sample of the same workload:
+    dequantize every weight from its (oracle-made) NF4 state, then fp64
+    forward + backward of the first `rows` token rows.  Reported in the
+    headline unit (TFLOP/s over that sample)."""
+    from oracle import linear, nf4
+    import workloads as wl_mod
+    states = []
+    for inp, spec in zip(host_inputs, wl.weights):
+        states.append((nf4.quantize(inp.W), spec))
+    cores = len(os.sched_getaffinity(0))
+    flops = 0.0
+    t0 = time.perf_counter()
+    for inp, (st, spec) in zip(host_inputs, states):
+        N, K = spec.N, spec.K
+        Wh = nf4.bf16_bits_to_f32(nf4.dequantize(*st, N, K))
+        X = nf4.bf16_bits_to_f32(inp.X[:rows])
+        dY = nf4.bf16_bits_to_f32(inp.dY[:rows])
+        A = nf4.bf16_bits_to_f32(inp.A)
+        B = nf4.bf16_bits_to_f32(inp.B)
+        linear.forward(X, Wh, A, B, wl.s)
+        linear.backward(X, dY, Wh, A, B, wl.s)
+        flops += 4.0 * rows * N * K + 6.0 * rows * wl.r * (N + K)
+    dt = time.perf_counter() - t0
+    try:
+        from threadpoolctl import threadpool_info
+        info = [d for d in threadpool_info() if d.get("user_api") == "blas"]
+        blas = ",".join(f"{d.get('internal_api')}" for d in info) or "?"
+        threads = max([d.get("num_threads", 0) for d in info] + [1])
+    except Exception:  # pragma: no cover
+        blas, threads = "?", cores
+    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": (f"{wl.name}: all {len(wl.weights)} weights, first {rows} of {wl.M[0]} "
+                       f"token rows; oracle dequantize + fp64 forward + backward "
+                       f"({dt:.1f} s, numpy BLAS {blas}, {threads} threads of {cores} "
+                       f"host cores)"),
+            "seconds": round(dt, 2)}
+
+
+if __name__ == "__main__":
+    main()

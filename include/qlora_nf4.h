@@ -167,6 +167,25 @@ int32_t qlora_linear_bwd(const nf4_tensor_t* w, const uint16_t* X,
                          float s, uint16_t* dX, uint16_t* dA, uint16_t* dB,
                          void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Measurement variants of the two layer calls: identical work, and in
+ * addition `ev_begin` is recorded on `stream` right before, and `ev_end`
+ * right after, the launch of the dequantizing main kernel (the MFMA tile
+ * GEMM, or for M <= 16 in the forward pass the weight-streaming kernel; in
+ * the backward pass the dX GEMM, so nothing is recorded when dX is NULL).
+ * hipEventElapsedTime over the pair is that kernel's duration.  Either
+ * event may be NULL.  The events are created and owned by the caller. */
+int32_t qlora_linear_fwd_ev(const nf4_tensor_t* w, const uint16_t* X,
+                            int64_t M, const uint16_t* A, const uint16_t* B,
+                            int32_t r, float s, uint16_t* Y, uint16_t* U_out,
+                            void* ws, size_t ws_bytes, hipStream_t stream,
+                            hipEvent_t ev_begin, hipEvent_t ev_end);
+int32_t qlora_linear_bwd_ev(const nf4_tensor_t* w, const uint16_t* X,
+                            const uint16_t* dY, int64_t M, const uint16_t* A,
+                            const uint16_t* B, const uint16_t* U, int32_t r,
+                            float s, uint16_t* dX, uint16_t* dA, uint16_t* dB,
+                            void* ws, size_t ws_bytes, hipStream_t stream,
+                            hipEvent_t ev_begin, hipEvent_t ev_end);
+
 #ifdef __cplusplus
 }
 #endif

@@ -26,6 +26,8 @@ EXPORTS = (
     "qlora_workspace_size",
     "qlora_linear_fwd",
     "qlora_linear_bwd",
+    "qlora_linear_fwd_ev",
+    "qlora_linear_bwd_ev",
 )
 
 
@@ -79,6 +81,10 @@ def lib() -> ctypes.CDLL:
     L.qlora_linear_bwd.restype = i32
     L.qlora_linear_bwd.argtypes = [ctypes.POINTER(Nf4Tensor), vp, vp, i64, vp, vp, vp, i32, f32,
                                    vp, vp, vp, vp, sz, vp]
+    L.qlora_linear_fwd_ev.restype = i32
+    L.qlora_linear_fwd_ev.argtypes = L.qlora_linear_fwd.argtypes + [vp, vp]
+    L.qlora_linear_bwd_ev.restype = i32
+    L.qlora_linear_bwd_ev.argtypes = L.qlora_linear_bwd.argtypes + [vp, vp]
     _lib = L
     return L
 

@@ -147,9 +147,17 @@ size_t qlora_workspace_size(int64_t M, int64_t N, int64_t K, int32_t r, int32_t 
   return for_bwd ? plan_bwd(M, N, K, r).total : plan_fwd(M, N, K, r).total;
 }
 
-int32_t qlora_linear_fwd(const nf4_tensor_t* w, const uint16_t* X, int64_t M, const uint16_t* A,
-                         const uint16_t* B, int32_t r, float s, uint16_t* Y, uint16_t* U_out,
-                         void* ws, size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+inline hipError_t record(hipEvent_t ev, hipStream_t stream) {
+  return ev ? hipEventRecord(ev, stream) : hipSuccess;
+}
+
+int32_t linear_fwd(const nf4_tensor_t* w, const uint16_t* X, int64_t M, const uint16_t* A,
+                   const uint16_t* B, int32_t r, float s, uint16_t* Y, uint16_t* U_out, void* ws,
+                   size_t ws_bytes, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   if (!nf4_ok(w) || !X || !A || !B || !Y || !ws) return QLORA_ERR_INVALID;
   const int32_t sup = nf4_supported(w);
   if (sup != QLORA_OK) return sup;
@@ -169,20 +177,22 @@ int32_t qlora_linear_fwd(const nf4_tensor_t* w, const uint16_t* X, int64_t M, co
 
   hipError_t e = run_lora_down(X, M, K, A, r, ws_u, U_out, part, stream);
   if (e != hipSuccess) return QLORA_ERR_LAUNCH;
+  if (record(ev0, stream) != hipSuccess) return QLORA_ERR_LAUNCH;
   if (M <= kGemvMaxM) {
     e = launch_qgemv_partial(v, X, M, pl.gemv_splits_n, part, stream);
-    if (e != hipSuccess) return QLORA_ERR_LAUNCH;
+    if (e != hipSuccess || record(ev1, stream) != hipSuccess) return QLORA_ERR_LAUNCH;
     e = launch_gemv_finish(part, pl.gemv_splits_n, M, N, ws_u, rank_pad(r), B, r, s, Y, stream);
   } else {
     e = launch_qgemm_fwd(v, X, M, ws_u, rank_pad(r), B, r, s, Y, stream);
+    if (e == hipSuccess) e = record(ev1, stream);
   }
   return launch_status(e);
 }
 
-int32_t qlora_linear_bwd(const nf4_tensor_t* w, const uint16_t* X, const uint16_t* dY, int64_t M,
-                         const uint16_t* A, const uint16_t* B, const uint16_t* U, int32_t r,
-                         float s, uint16_t* dX, uint16_t* dA, uint16_t* dB, void* ws,
-                         size_t ws_bytes, hipStream_t stream) {
+int32_t linear_bwd(const nf4_tensor_t* w, const uint16_t* X, const uint16_t* dY, int64_t M,
+                   const uint16_t* A, const uint16_t* B, const uint16_t* U, int32_t r, float s,
+                   uint16_t* dX, uint16_t* dA, uint16_t* dB, void* ws, size_t ws_bytes,
+                   hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   if (!nf4_ok(w) || !X || !dY || !A || !B || !dA || !dB || !ws) return QLORA_ERR_INVALID;
   const int32_t sup = nf4_supported(w);
   if (sup != QLORA_OK) return sup;
@@ -239,10 +249,45 @@ int32_t qlora_linear_bwd(const nf4_tensor_t* w, const uint16_t* X, const uint16_
   // dX = dY W + dU A
   if (dX) {
     const Nf4View v{w->codes, w->q8, w->step, N, K};
+    if (record(ev0, stream) != hipSuccess) return QLORA_ERR_LAUNCH;
     e = launch_qgemm_bwd(v, dY, M, ws_du, rp, A, r, dX, stream);
-    if (e != hipSuccess) return QLORA_ERR_LAUNCH;
+    if (e != hipSuccess || record(ev1, stream) != hipSuccess) return QLORA_ERR_LAUNCH;
   }
   return QLORA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t qlora_linear_fwd(const nf4_tensor_t* w, const uint16_t* X, int64_t M, const uint16_t* A,
+                         const uint16_t* B, int32_t r, float s, uint16_t* Y, uint16_t* U_out,
+                         void* ws, size_t ws_bytes, hipStream_t stream) {
+  return linear_fwd(w, X, M, A, B, r, s, Y, U_out, ws, ws_bytes, stream, nullptr, nullptr);
+}
+
+int32_t qlora_linear_fwd_ev(const nf4_tensor_t* w, const uint16_t* X, int64_t M,
+                            const uint16_t* A, const uint16_t* B, int32_t r, float s, uint16_t* Y,
+                            uint16_t* U_out, void* ws, size_t ws_bytes, hipStream_t stream,
+                            hipEvent_t ev_begin, hipEvent_t ev_end) {
+  return linear_fwd(w, X, M, A, B, r, s, Y, U_out, ws, ws_bytes, stream, ev_begin, ev_end);
+}
+
+int32_t qlora_linear_bwd(const nf4_tensor_t* w, const uint16_t* X, const uint16_t* dY, int64_t M,
+                         const uint16_t* A, const uint16_t* B, const uint16_t* U, int32_t r,
+                         float s, uint16_t* dX, uint16_t* dA, uint16_t* dB, void* ws,
+                         size_t ws_bytes, hipStream_t stream) {
+  return linear_bwd(w, X, dY, M, A, B, U, r, s, dX, dA, dB, ws, ws_bytes, stream, nullptr,
+                    nullptr);
+}
+
+int32_t qlora_linear_bwd_ev(const nf4_tensor_t* w, const uint16_t* X, const uint16_t* dY,
+                            int64_t M, const uint16_t* A, const uint16_t* B, const uint16_t* U,
+                            int32_t r, float s, uint16_t* dX, uint16_t* dA, uint16_t* dB,
+                            void* ws, size_t ws_bytes, hipStream_t stream, hipEvent_t ev_begin,
+                            hipEvent_t ev_end) {
+  return linear_bwd(w, X, dY, M, A, B, U, r, s, dX, dA, dB, ws, ws_bytes, stream, ev_begin,
+                    ev_end);
 }
 
 }  // extern "C"

@@ -27,15 +27,46 @@ struct SkinnyArgs {
   SkinnyOp op;
   int64_t c_split;  // contraction length per split (multiple of 64)
   float* part;
+  bool a_vec, b_vec;
 };
 
 // Stage a 64 x 64 operand tile into T[x][c] (c contiguous in LDS).
 // Element (x, c) is at src[x * sx + c * sc]; rows x >= X or columns
-// c >= cend are zero.
+// c >= cend are zero.  One of sx, sc is 1.  When the other stride and the
+// base are 16-byte aligned (`vec`), every thread moves two 16-byte chunks of
+// eight contiguous elements: along c they go to LDS as one 16-byte store;
+// along x they are scattered as eight 2-byte stores (the transpose).
+// Otherwise elements are moved one at a time.  The contraction length of
+// every caller is a multiple of 8, so a chunk is either wholly inside or
+// wholly outside [c0, cend) and [0, X) when X is a multiple of 8.
 __device__ __forceinline__ void stage_op(uint16_t* T, const uint16_t* src, int64_t sx, int64_t sc,
                                          int64_t x0, int64_t X, int64_t c0, int64_t cend,
-                                         int tid) {
+                                         bool vec, int tid) {
   const bool c_fast = (sc == 1);
+  if (vec) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int e = tid + 256 * q;
+      if (c_fast) {
+        const int xi = e >> 3, ci = (e & 7) * 8;
+        const int64_t gx = x0 + xi, gc = c0 + ci;
+        u32x4 v = u32x4{0u, 0u, 0u, 0u};
+        if (gx < X && gc < cend) v = *reinterpret_cast<const u32x4*>(src + gx * sx + gc);
+        *reinterpret_cast<u32x4*>(T + xi * SLD + ci) = v;
+      } else {
+        const int ci = e >> 3, xi = (e & 7) * 8;
+        const int64_t gx = x0 + xi, gc = c0 + ci;
+        u32x4 v = u32x4{0u, 0u, 0u, 0u};
+        if (gx < X && gc < cend) v = *reinterpret_cast<const u32x4*>(src + gc * sc + gx);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          T[(xi + 2 * j) * SLD + ci] = (uint16_t)(v[j] & 0xffffu);
+          T[(xi + 2 * j + 1) * SLD + ci] = (uint16_t)(v[j] >> 16);
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll 4
   for (int q = 0; q < 16; ++q) {
     const int e = tid + 256 * q;
@@ -62,8 +93,8 @@ __global__ __launch_bounds__(256) void k_skinny_partial(SkinnyArgs p) {
   f32x16 acc = f32x16{};
   const int r32 = lane & 31, kh = (lane >> 5) * 8;
   for (int64_t c0 = cs; c0 < ce; c0 += kSkinnyStep) {
-    stage_op(As, op.a, op.a_si, op.a_sc, i0, op.I, c0, ce, tid);
-    stage_op(Bs, op.b, op.b_sj, op.b_sc, j0, op.J, c0, ce, tid);
+    stage_op(As, op.a, op.a_si, op.a_sc, i0, op.I, c0, ce, p.a_vec, tid);
+    stage_op(Bs, op.b, op.b_sj, op.b_sc, j0, op.J, c0, ce, p.b_vec, tid);
     __syncthreads();
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
@@ -129,11 +160,18 @@ size_t skinny_partial_bytes(int64_t I, int64_t J, int64_t C) {
 
 hipError_t launch_skinny_partial(const SkinnyOp& op, int splits, float* part, hipStream_t stream) {
   const int64_t cl = split_len(op.C, splits);
-  const int64_t used = (op.C + cl - 1) / cl;  // splits actually covering C
-  SkinnyArgs a{op, cl, part};
+  // 16-byte chunks need an aligned base and an aligned outer stride, a
+  // contraction length that is a multiple of 8 and (for chunks along the
+  // output dimension) an output extent that is a multiple of 8.
+  auto vec_ok = [&](const uint16_t* ptr, int64_t sx, int64_t sc, int64_t X) {
+    const int64_t outer = (sc == 1) ? sx : sc;
+    const bool along_x = (sc != 1);
+    return ((uintptr_t)ptr & 15u) == 0 && (outer % 8) == 0 && (op.C % 8) == 0 &&
+           (!along_x || (X % 8) == 0);
+  };
+  SkinnyArgs a{op, cl, part, vec_ok(op.a, op.a_si, op.a_sc, op.I), vec_ok(op.b, op.b_sj, op.b_sc, op.J)};
   dim3 grid((unsigned)((op.J + 63) / 64), (unsigned)((op.I + 63) / 64), (unsigned)splits);
   hipLaunchKernelGGL(k_skinny_partial, grid, dim3(256), 0, stream, a);
-  (void)used;
   return hipGetLastError();
 }
 

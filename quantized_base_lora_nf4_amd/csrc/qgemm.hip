@@ -12,80 +12,281 @@
 //   Y  = [X | s U] [W | B]^T          (forward, contraction over K then r)
 //   dX = [dY | dU] [W ; A]            (backward, contraction over N then r)
 //
-// The dequantized tile is bit-identical to nf4_dequantize:
-// w = bf16_rne(level[code] * fl32(q8 * step)).
+// Tiling (both kernels): a 256 x 256 output tile per workgroup of 4 waves
+// (2 x 2), each wave owning 128 x 128 outputs as 4 x 4 MFMA 32x32x16 tiles
+// (256 fp32 accumulators per lane, held in AGPRs); 64-deep contraction steps;
+// both operand tiles double-buffered in LDS (147 KB) so that one barrier per
+// step separates filling the next buffer from the MFMAs on the current one.
+//
+// Dequantization: each thread owns one 64-weight block row per step.  It
+// builds that block's 16 possible bf16 values, bf16_rne(level[i] * c_hat),
+// once (16 multiplies), splits them into a low-byte and a high-byte plane of
+// 4 registers each, and then resolves every code with byte permutes
+// (v_perm_b32) in registers: no LDS lookups, and the tile is bit-identical to
+// nf4_dequantize.
+//
+// Backward: the weight slice is written to LDS in its natural [n][k] layout
+// and read as the MFMA B operand with ds_read_b64_tr_b16, which hands each
+// lane 4 consecutive rows of one column.
 #include "kernels.hpp"
 
 namespace qn {
 
 namespace {
 
-constexpr int LD = 72;  // LDS row stride in bf16 elements (64 + 8 pad: 144 B)
+constexpr int BK = 64;    // contraction per step (one NF4 block)
+constexpr int LDA = 72;   // LDS row stride (bf16) of [row][k] tiles: 64 + 8
 
-// One 64-deep slice of MFMA work for a 4-wave workgroup arranged 2 x 2, each
-// wave owning a 128 x 64 output tile (4 x 2 tiles of 32 x 32).
-// As: [256][LD] rows = output rows, Bs: [128][LD] rows = output columns; both
-// store the contraction index contiguously.
-__device__ __forceinline__ void mma_slice(const uint16_t* As, const uint16_t* Bs, int wm, int wn,
-                                          int lane, f32x16 (&acc)[4][2]) {
-  const int r32 = lane & 31;
-  const int kh = (lane >> 5) * 8;
+// Workgroups are handed to the 8 XCDs round-robin by linear id, and each XCD
+// has its own L2.  Remap so that each XCD receives a contiguous range of
+// output tiles (tiles that share an operand tile then share an L2): linear
+// id p runs on XCD p % 8, and becomes tile (p % 8) * (total / 8) + p / 8.
+// The ids past the last full round of 8 keep their own index.
+__device__ __forceinline__ int64_t xcd_tile(int64_t p, int64_t total) {
+  const int64_t per = total >> 3;
+  if (p >= per * 8) return p;
+  return (p & 7) * per + (p >> 3);
+}
+
+__device__ __forceinline__ uint32_t perm(uint32_t s0, uint32_t s1, uint32_t sel) {
+  return __builtin_amdgcn_perm(s0, s1, sel);
+}
+
+// Byte planes of the 16 candidate bf16 values of one block:
+// lo[q] byte e = low byte of value 4q + e, hi[q] byte e = high byte.
+struct LevelTable {
+  uint32_t lo[4], hi[4];
+};
+
+__device__ __forceinline__ LevelTable make_table(float chat) {
+  LevelTable t;
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    bf16x8 a[4], b[2];
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t p0 = pack_bf16x2(level_f32(4 * q) * chat, level_f32(4 * q + 1) * chat);
+    const uint32_t p1 = pack_bf16x2(level_f32(4 * q + 2) * chat, level_f32(4 * q + 3) * chat);
+    t.lo[q] = perm(p1, p0, 0x06040200u);
+    t.hi[q] = perm(p1, p0, 0x07050301u);
+  }
+  return t;
+}
+
+// Eight codes (one 32-bit word; element order = nibble order) -> four packed
+// bf16 pairs (element 2i in the low half of word i).
+__device__ __forceinline__ u32x4 lookup8(uint32_t w, const LevelTable& t) {
+  const uint32_t se = w & 0x07070707u;            // even elements, index bits 0..2
+  const uint32_t so = (w >> 4) & 0x07070707u;     // odd elements
+  // 0xFF in each byte whose index has bit 3 set (selector 13 -> 0xFF, 12 -> 0x00)
+  const uint32_t me = perm(0u, 0u, ((w >> 3) & 0x01010101u) | 0x0c0c0c0cu);
+  const uint32_t mo = perm(0u, 0u, ((w >> 7) & 0x01010101u) | 0x0c0c0c0cu);
+  const uint32_t le = (me & perm(t.lo[3], t.lo[2], se)) | (~me & perm(t.lo[1], t.lo[0], se));
+  const uint32_t he = (me & perm(t.hi[3], t.hi[2], se)) | (~me & perm(t.hi[1], t.hi[0], se));
+  const uint32_t lo = (mo & perm(t.lo[3], t.lo[2], so)) | (~mo & perm(t.lo[1], t.lo[0], so));
+  const uint32_t ho = (mo & perm(t.hi[3], t.hi[2], so)) | (~mo & perm(t.hi[1], t.hi[0], so));
+  const uint32_t t0 = perm(he, le, 0x05010400u);  // elements 0, 2
+  const uint32_t t1 = perm(he, le, 0x07030602u);  // elements 4, 6
+  const uint32_t u0 = perm(ho, lo, 0x05010400u);  // elements 1, 3
+  const uint32_t u1 = perm(ho, lo, 0x07030602u);  // elements 5, 7
+  return u32x4{perm(u0, t0, 0x05040100u), perm(u0, t0, 0x07060302u),
+               perm(u1, t1, 0x05040100u), perm(u1, t1, 0x07060302u)};
+}
+
+
+// ---------------------------------------------------------------------------
+// Tile configuration.  WM x WN waves, each owning FM x FN MFMA 32x32 tiles;
+// workgroup tile BM x BN = (WM FM 32) x (WN FN 32); 64-deep steps.
+// ---------------------------------------------------------------------------
+template <int WM_, int WN_, int FM_, int FN_>
+struct Cfg {
+  static constexpr int WM = WM_, WN = WN_, FM = FM_, FN = FN_;
+  static constexpr int NT = WM * WN * 64;           // threads
+  static constexpr int BM = WM * FM * 32;           // output rows
+  static constexpr int BN = WN * FN * 32;           // output columns
+  static constexpr int TILE_A = BM * 64;            // [BM][64] activation tile (swizzled)
+  static constexpr int TILE_BF = BN * LDA;          // forward weight tile [BN][LDA]
+  static constexpr int BSTR = 72;                   // backward slice: stride of a 64-column block
+  static constexpr int LDTB = (BN / 64) * BSTR;     // backward weight slice row stride
+  static constexpr int TILE_BB = BK * LDTB;         // backward weight slice [64][LDTB]
+  static constexpr int SMEM_F = 2 * (TILE_A + TILE_BF);
+  static constexpr int SMEM_B = 2 * (TILE_A + TILE_BB);
+  static constexpr int XCH = BM * 8 / NT;           // 16-byte activation chunks per thread
+  static constexpr int XLD = BM / 8 / (NT / 64);    // direct-to-LDS loads per wave per step
+  static constexpr int WPT = BN * 64 / NT;          // forward weights dequantized per thread
+  static_assert(SMEM_F * 2 <= 160 * 1024 && SMEM_B * 2 <= 160 * 1024, "LDS budget");
+  static_assert(WPT == 64 || WPT == 32, "a thread dequantizes a whole or half block row");
+};
+
+// Activation tiles are [rows][64] bf16 with no padding; the eight 16-byte
+// chunks of row r are stored in the order chunk ^ ((r >> 1) & 7), which keeps
+// the MFMA fragment reads (16 consecutive rows, one chunk) free of LDS bank
+// conflicts.  Offset (in elements) of chunk c of row r:
+__device__ __forceinline__ int a_off(int r, int c) { return r * 64 + ((c ^ ((r >> 1) & 7)) << 3); }
+
+// Direct global -> LDS load of a BM x 64 bf16 tile of a row-major matrix
+// (row stride ld, columns c0..c0+63; rows past `rows` clamp to the last row,
+// columns at or past `cols` are replaced by column 0 of the same row and must
+// be zeroed by the caller's data layout, see below).  Each wave instruction
+// fills 8 consecutive tile rows (1 KB); lane l writes row 8 e + l / 8, slot
+// l % 8, so it fetches the chunk that the swizzle puts in that slot.
+template <class C>
+__device__ __forceinline__ void load_rows_lds(uint16_t* As, const uint16_t* src, int64_t ld,
+                                              int64_t row0, int64_t rows, int64_t c0, int wave,
+                                              int lane) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      a[i] = *reinterpret_cast<const bf16x8*>(As + (wm * 128 + i * 32 + r32) * LD + kk * 16 + kh);
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-      b[j] = *reinterpret_cast<const bf16x8*>(Bs + (wn * 64 + j * 32 + r32) * LD + kk * 16 + kh);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
+  for (int q = 0; q < C::XLD; ++q) {
+    const int e = q * (C::NT / 64) + wave;  // 8-row group
+    const int r = 8 * e + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    int64_t gr = row0 + r;
+    if (gr >= rows) gr = rows - 1;
+    __builtin_amdgcn_global_load_lds((const void*)(src + gr * ld + c0 + c * 8),
+                                     (__attribute__((address_space(3))) void*)(As + 8 * e * 64),
+                                     16, 0, 0);
   }
 }
 
-// Store a 256 x 128 fp32 accumulator tile as bf16 into out[row][col] with row
-// stride ld, skipping rows >= rows and columns >= cols.
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+template <class C>
+struct AccT {
+  f32x16 v[C::FM][C::FN];
+};
+
+template <class C>
+__device__ __forceinline__ void zero_acc(AccT<C>& acc) {
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) acc.v[i][j] = f32x16{};
+}
+
+// MFMA operand fragments of one 16-deep sub-step.
+template <class C>
+struct Frags {
+  bf16x8 a[C::FM], b[C::FN];
+};
+
+// Read the fragments of sub-step kk.  As: [BM][LDA] (rows = output rows, k
+// contiguous).  B operand from Bs: forward [BN][LDA] (rows = output columns,
+// k contiguous); backward [64][LDTB] (rows = k, columns = output columns in
+// 64-column blocks of stride BSTR) read with the transposing LDS load.
+template <class C, bool kTransB>
+__device__ __forceinline__ void read_frags(Frags<C>& f, const uint16_t* As, const uint16_t* Bs,
+                                           int wm, int wn, int lane, int kk) {
+  const int r32 = lane & 31;
+  const int kh = (lane >> 5) * 8;
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+    f.a[i] = *reinterpret_cast<const bf16x8*>(As + a_off(wm * C::FM * 32 + i * 32 + r32, 2 * kk + (kh >> 3)));
+  if (!kTransB) {
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+      f.b[j] = *reinterpret_cast<const bf16x8*>(Bs + (wn * C::FN * 32 + j * 32 + r32) * LDA + kk * 16 + kh);
+  } else {
+    // Lane group g = lane / 16 covers columns 16 (g % 2) + 0..15 and
+    // contraction rows 8 (g / 2) + 0..7; within the group, lane i reads the
+    // 4-element chunk at row 4 h + i / 4, column 4 (i % 4) (h = 0, 1) and
+    // receives 4 consecutive rows of column i.
+    const int g = lane >> 4, i = lane & 15;
+    const int row = kk * 16 + 8 * (g >> 1) + (i >> 2);
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) {
+      typedef short v4i16 __attribute__((ext_vector_type(4)));
+      typedef short v8i16 __attribute__((ext_vector_type(8)));
+      typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+      const int col = wn * C::FN * 32 + j * 32 + 16 * (g & 1) + 4 * (i & 3);
+      const uint16_t* p0 = Bs + row * C::LDTB + (col >> 6) * C::BSTR + (col & 63);
+      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p0);
+      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p0 + 4 * C::LDTB));
+      const v8i16 v = v8i16{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      f.b[j] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void mfma_frags(const Frags<C>& f, AccT<C>& acc) {
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) acc.v[i][j] = mfma32(f.a[i], f.b[j], acc.v[i][j]);
+}
+
+// A whole 64-deep step without other work (used for the LoRA steps and an
+// odd last step).
+template <class C, bool kTransB>
+__device__ __forceinline__ void mma_step(const uint16_t* As, const uint16_t* Bs, int wm, int wn,
+                                         int lane, AccT<C>& acc) {
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    Frags<C> f;
+    read_frags<C, kTransB>(f, As, Bs, wm, wn, lane, kk);
+    mfma_frags(f, acc);
+  }
+}
+
+// Store the workgroup's accumulator tile as bf16 (row stride ld), skipping
+// rows >= rows and columns >= cols.
+template <class C>
 __device__ __forceinline__ void store_tile(uint16_t* out, int64_t ld, int64_t row0, int64_t col0,
                                            int64_t rows, int64_t cols, int wm, int wn, int lane,
-                                           const f32x16 (&acc)[4][2]) {
+                                           const AccT<C>& acc) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t col = col0 + wn * 64 + j * 32 + (lane & 31);
+    for (int j = 0; j < C::FN; ++j) {
+      const int64_t col = col0 + wn * C::FN * 32 + j * 32 + (lane & 31);
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int64_t row = row0 + wm * 128 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (row < rows && col < cols) out[row * ld + col] = f32_to_bf16(acc[i][j][v]);
+        const int64_t row = row0 + wm * C::FM * 32 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if (row < rows && col < cols) out[row * ld + col] = f32_to_bf16(acc.v[i][j][v]);
       }
     }
 }
 
-// Eight NF4 codes (one 32-bit word, element order = nibble order) scaled by
-// chat, as four packed bf16 pairs.
-__device__ __forceinline__ u32x4 dequant8(uint32_t w, float chat, const float* lv) {
-  u32x4 o;
+// Global -> register loader for a BM x 64 bf16 tile of a row-major matrix
+// (row stride ld, columns c0..c0+63; rows past `rows` clamp to the last row,
+// columns at or past `cols` read as zero; cols is a multiple of 8).
+template <class C>
+struct RowTileRegs {
+  u32x4 v[C::XCH];
+};
+
+template <class C>
+__device__ __forceinline__ void load_rows(RowTileRegs<C>& r, const uint16_t* src, int64_t ld,
+                                          int64_t row0, int64_t rows, int64_t c0, int64_t cols,
+                                          int tid) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const float lo = lv[(w >> (8 * j)) & 15u] * chat;
-    const float hi = lv[(w >> (8 * j + 4)) & 15u] * chat;
-    o[j] = pack_bf16x2(lo, hi);
+  for (int q = 0; q < C::XCH; ++q) {
+    const int e = tid + C::NT * q;
+    int64_t gr = row0 + (e >> 3);
+    if (gr >= rows) gr = rows - 1;
+    int64_t c = c0 + (e & 7) * 8;
+    const bool ok = c < cols;
+    if (!ok) c = 0;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(src + gr * ld + c);
+    r.v[q] = ok ? v : u32x4{0u, 0u, 0u, 0u};
   }
-  return o;
 }
 
-// Stage a 256 x 64 tile of a bf16 matrix with zero-padded columns (row
-// stride ld, a multiple of 8; the tile's columns c0..c0+63 all exist) into
-// As, multiplying by `scale` in fp32 and rounding back to bf16 when scale != 1.
+template <class C>
+__device__ __forceinline__ void store_rows(uint16_t* As, const RowTileRegs<C>& r, int tid) {
+#pragma unroll
+  for (int q = 0; q < C::XCH; ++q) {
+    const int e = tid + C::NT * q;
+    *reinterpret_cast<u32x4*>(As + a_off(e >> 3, e & 7)) = r.v[q];
+  }
+}
+
+// Stage a BM x 64 tile of a zero-padded bf16 matrix whose columns
+// c0..c0+63 all exist (row stride a multiple of 8), scaling each element by
+// `scale` in fp32 and rounding back to bf16 when do_scale is set.
+template <class C>
 __device__ __forceinline__ void stage_rows_scaled(uint16_t* As, const uint16_t* src, int64_t ld,
                                                   int64_t row0, int64_t rows, int64_t c0,
                                                   float scale, bool do_scale, int tid) {
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int e = tid + 256 * q;
+  for (int q = 0; q < C::XCH; ++q) {
+    const int e = tid + C::NT * q;
     const int row = e >> 3, c8 = e & 7;
     int64_t gr = row0 + row;
     if (gr >= rows) gr = rows - 1;
@@ -95,8 +296,54 @@ __device__ __forceinline__ void stage_rows_scaled(uint16_t* As, const uint16_t* 
       for (int j = 0; j < 4; ++j)
         v[j] = pack_bf16x2(bf16_lo_to_f32(v[j]) * scale, bf16_hi_to_f32(v[j]) * scale);
     }
-    *reinterpret_cast<u32x4*>(As + row * LD + c8 * 8) = v;
+    *reinterpret_cast<u32x4*>(As + a_off(row, c8)) = v;
   }
+}
+
+// What one thread loads of the weights for one contraction step: the codes
+// (a whole or half block row), their 8-bit constant and group step.
+template <class C>
+struct StepRegs {
+  u32x4 c[C::WPT / 32];
+  uint32_t q;
+  float st;
+};
+
+template <class C>
+__device__ __forceinline__ void dequant_codes(uint16_t* dst, const StepRegs<C>& r) {
+  const LevelTable t = make_table((float)r.q * r.st);
+#pragma unroll
+  for (int h = 0; h < C::WPT / 32; ++h)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) *reinterpret_cast<u32x4*>(dst + 32 * h + 8 * q) = lookup8(r.c[h][q], t);
+}
+
+// One pipelined contraction step: the MFMAs on the current buffers (As, Bs)
+// while this thread writes its dequantized weights for the next step (codes
+// loaded two steps earlier, in rn) at Bw_n.  (The next activation tile is
+// already on its way into the other buffer by direct-to-LDS loads.)  The
+// four 16-deep sub-steps each read the next sub-step's fragments first, then
+// alternate their 16 MFMAs with the VALU work of expanding two code words,
+// then write those weight chunks.
+template <class C, bool kTransB>
+__device__ __forceinline__ void step_interleaved(const uint16_t* As, const uint16_t* Bs,
+                                                 uint16_t* As_n, uint16_t* Bw_n,
+                                                 const StepRegs<C>& rn, int wm, int wn, int lane,
+                                                 AccT<C>& acc) {
+  constexpr int NW = C::WPT / 8;  // code words to expand
+  (void)As_n;
+  Frags<C> f[2];
+  read_frags<C, kTransB>(f[0], As, Bs, wm, wn, lane, 0);
+  const LevelTable t = make_table((float)rn.q * rn.st);
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    if (kk < 3) read_frags<C, kTransB>(f[(kk + 1) & 1], As, Bs, wm, wn, lane, kk + 1);
+    mfma_frags(f[kk & 1], acc);
+#pragma unroll
+    for (int w = kk * NW / 4; w < (kk + 1) * NW / 4; ++w)
+      *reinterpret_cast<u32x4*>(Bw_n + 8 * w) = lookup8(rn.c[w / 4][w % 4], t);
+  }
+
 }
 
 // ---------------------------------------------------------------------------
@@ -116,97 +363,108 @@ struct FwdArgs {
   int64_t M, N, K;
 };
 
-__global__ __launch_bounds__(256, 2) void k_qgemm_fwd(FwdArgs p) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[256 * LD];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[128 * LD];
-  __shared__ float lv[16];
+template <class C>
+__global__ __launch_bounds__(C::NT, 1) void k_qgemm_fwd(FwdArgs p) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem[C::SMEM_F];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int64_t m0 = (int64_t)blockIdx.y * 256, n0 = (int64_t)blockIdx.x * 128;
+  const int wm = wave / C::WN, wn = wave % C::WN;
   const int64_t M = p.M, N = p.N, K = p.K;
+  const int64_t tiles_n = (N + C::BN - 1) / C::BN;
+  const int64_t tile = xcd_tile(blockIdx.x, tiles_n * ((M + C::BM - 1) / C::BM));
+  const int64_t m0 = (tile / tiles_n) * C::BM, n0 = (tile % tiles_n) * C::BN;
   const int64_t kblocks = K >> 6;
-  if (tid < 16) lv[tid] = level_f32(tid);
 
-  // X loader: 8 chunks of 16 B per thread, 8 consecutive threads per row.
-  // W loader: thread -> (row tid/2, half tid%2): 32 codes = 16 bytes.
-  const int wrow = tid >> 1, whalf = tid & 1;
+  // This thread's weight row and part of the block (clamped; rows past N
+  // are computed and dropped).
+  constexpr int PARTS = 64 / C::WPT;
+  const int wrow = tid / PARTS, wpart = tid % PARTS;
   int64_t gn = n0 + wrow;
   if (gn >= N) gn = N - 1;
-  const uint8_t* wcodes = p.codes + gn * (K >> 1) + whalf * 16;
+  const uint8_t* wcodes = p.codes + gn * (K >> 1) + wpart * (C::WPT / 2);
   const int64_t wblk0 = gn * kblocks;
 
-  f32x16 acc[4][2];
+  AccT<C> acc;
+  zero_acc(acc);
+  // Two register sets of loads in flight: step t's loads are issued while
+  // the MFMAs of step t - 2 run, and turned into LDS tiles while those of
+  // step t - 1 run.  Steps past the end reload the last step (harmless).
+  // Weights are loaded two steps ahead (two register sets) and dequantized
+  // into the other LDS buffer while the MFMAs of the current step run;
+  // activations go straight from global memory into that buffer.  Steps
+  // past the end reload the last step (harmless).
+  StepRegs<C> ra, rb;
+  auto load_w = [&](StepRegs<C>& r, int64_t kt) {
+    if (kt >= kblocks) kt = kblocks - 1;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
-
-  u32x4 xr[8];
-  u32x4 wr;
-  float chat_r;
-  auto load = [&](int64_t kt) {
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int e = tid + 256 * q;
-      int64_t gm = m0 + (e >> 3);
-      if (gm >= M) gm = M - 1;
-      xr[q] = *reinterpret_cast<const u32x4*>(p.X + gm * K + kt * 64 + (e & 7) * 8);
-    }
-    wr = *reinterpret_cast<const u32x4*>(wcodes + kt * 32);
+    for (int h = 0; h < C::WPT / 32; ++h)
+      r.c[h] = *reinterpret_cast<const u32x4*>(wcodes + kt * 32 + 16 * h);
     const int64_t blk = wblk0 + kt;
-    chat_r = (float)p.q8[blk] * p.step[blk >> 8];
+    r.q = p.q8[blk];
+    r.st = p.step[blk >> 8];
   };
-  auto stage = [&]() {
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int e = tid + 256 * q;
-      *reinterpret_cast<u32x4*>(As + (e >> 3) * LD + (e & 7) * 8) = xr[q];
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<u32x4*>(Bs + wrow * LD + whalf * 32 + j * 8) = dequant8(wr[j], chat_r, lv);
+  auto load_x = [&](uint16_t* As_dst, int64_t kt) {
+    if (kt >= kblocks) kt = kblocks - 1;
+    load_rows_lds<C>(As_dst, p.X, K, m0, M, kt * BK, wave, lane);
+  };
+  auto body = [&](StepRegs<C>& rnext, StepRegs<C>& rload, int64_t kt, int cur) {
+    const uint16_t* As = smem + cur * (C::TILE_A + C::TILE_BF);
+    uint16_t* As_n = smem + (cur ^ 1) * (C::TILE_A + C::TILE_BF);
+    load_x(As_n, kt + 1);
+    load_w(rload, kt + 2);
+    step_interleaved<C, false>(As, As + C::TILE_A, As_n,
+                               As_n + C::TILE_A + wrow * LDA + wpart * C::WPT, rnext, wm, wn,
+                               lane, acc);
+    wait_vmem();
+    __syncthreads();
   };
 
-  load(0);
-  __syncthreads();  // lv ready
-  for (int64_t kt = 0; kt < kblocks; ++kt) {
-    stage();
-    __syncthreads();
-    if (kt + 1 < kblocks) load(kt + 1);
-    mma_slice(As, Bs, wm, wn, lane, acc);
+  load_w(ra, 0);
+  load_w(rb, 1);
+  load_x(smem, 0);
+  dequant_codes<C>(smem + C::TILE_A + wrow * LDA + wpart * C::WPT, ra);
+  wait_vmem();
+  __syncthreads();
+  int64_t kt = 0;
+  for (; kt + 2 <= kblocks; kt += 2) {
+    body(rb, ra, kt, 0);      // MFMA step kt (buffer 0), stage kt+1 from rb, load kt+2 into ra
+    body(ra, rb, kt + 1, 1);  // MFMA step kt+1 (buffer 1), stage kt+2 from ra, load kt+3 into rb
+  }
+  if (kt < kblocks) {  // odd number of steps: the last one is in buffer 0
+    mma_step<C, false>(smem, smem + C::TILE_A, wm, wn, lane, acc);
     __syncthreads();
   }
 
   // LoRA: extra contraction over r with A-side bf16(s U) and B-side B.
   const bool bvec = (p.r & 7) == 0;
   for (int j0 = 0; j0 < p.r; j0 += 64) {
-    stage_rows_scaled(As, p.U, p.ldu, m0, M, j0, p.s, true, tid);
-    if (bvec) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int e = tid + 256 * q;
-        const int row = e >> 3, c8 = e & 7;
-        int64_t g = n0 + row;
-        if (g >= N) g = N - 1;
-        u32x4 v = u32x4{0u, 0u, 0u, 0u};
+    uint16_t* As = smem;
+    uint16_t* Bs = smem + C::TILE_A;
+    stage_rows_scaled<C>(As, p.U, p.ldu, m0, M, j0, p.s, true, tid);
+    for (int e = tid; e < C::BN * 8; e += C::NT) {
+      const int row = e >> 3, c8 = e & 7;
+      int64_t g = n0 + row;
+      if (g >= N) g = N - 1;
+      u32x4 v = u32x4{0u, 0u, 0u, 0u};
+      if (bvec) {
         if (j0 + c8 * 8 < p.r) v = *reinterpret_cast<const u32x4*>(p.B + g * p.r + j0 + c8 * 8);
-        *reinterpret_cast<u32x4*>(Bs + row * LD + c8 * 8) = v;
+      } else {
+        uint16_t t[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int jj = j0 + c8 * 8 + q;
+          t[q] = (jj < p.r) ? p.B[g * p.r + jj] : (uint16_t)0;
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = (uint32_t)t[2 * q] | ((uint32_t)t[2 * q + 1] << 16);
       }
-    } else {
-      for (int e = tid; e < 128 * 64; e += 256) {
-        const int row = e >> 6, c = e & 63;
-        int64_t g = n0 + row;
-        if (g >= N) g = N - 1;
-        const int jj = j0 + c;
-        Bs[row * LD + c] = (jj < p.r) ? p.B[g * p.r + jj] : (uint16_t)0;
-      }
+      *reinterpret_cast<u32x4*>(Bs + row * LDA + c8 * 8) = v;
     }
     __syncthreads();
-    mma_slice(As, Bs, wm, wn, lane, acc);
+    mma_step<C, false>(As, Bs, wm, wn, lane, acc);
     __syncthreads();
   }
 
-  store_tile(p.Y, N, m0, n0, M, N, wm, wn, lane, acc);
+  store_tile<C>(p.Y, N, m0, n0, M, N, wm, wn, lane, acc);
 }
 
 // ---------------------------------------------------------------------------
@@ -225,125 +483,137 @@ struct BwdArgs {
   int64_t M, N, K;
 };
 
-// Output tile 256 (tokens) x 128 (input features); contraction over the
-// weight's rows in slices of 64.  The weight slice (64 rows x 128 columns)
-// is dequantized transposed into Bs[column][row] so that the MFMA B operand
-// reads 8 consecutive rows.
-__global__ __launch_bounds__(256, 2) void k_qgemm_bwd(BwdArgs p) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[256 * LD];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[128 * LD];
-  __shared__ float lv[16];
+// Output tile BM tokens x BN input features; contraction over the weight's
+// rows in steps of 64.  The step's weight slice, rows n..n+63 and columns
+// k0..k0+BN-1, is dequantized into Bs[64][LDTB] in its natural layout.
+template <class C>
+__global__ __launch_bounds__(C::NT, 1) void k_qgemm_bwd(BwdArgs p) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem[C::SMEM_B];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int64_t m0 = (int64_t)blockIdx.y * 256, k0 = (int64_t)blockIdx.x * 128;
+  const int wm = wave / C::WN, wn = wave % C::WN;
   const int64_t M = p.M, N = p.N, K = p.K;
+  const int64_t tiles_k = (K + C::BN - 1) / C::BN;
+  const int64_t tile = xcd_tile(blockIdx.x, tiles_k * ((M + C::BM - 1) / C::BM));
+  const int64_t m0 = (tile / tiles_k) * C::BM, k0 = (tile % tiles_k) * C::BN;
   const int64_t kblocks = K >> 6;
-  const int64_t nsteps = (N + 63) >> 6;
-  if (tid < 16) lv[tid] = level_f32(tid);
+  const int64_t nsteps = (N + BK - 1) / BK;
 
-  // W loader: thread -> rows 4*rg .. 4*rg+3 of the slice, columns 8*cg .. 8*cg+7.
-  const int rg = tid >> 4, cg = tid & 15;
-  const int64_t kcol = k0 + cg * 8;
+  // Weight slice work split: 64 rows x (BN / 64) blocks, each thread a whole
+  // or half block row.
+  constexpr int BPR = C::BN / 64;                 // blocks per slice row
+  constexpr int WPTB = 64 * C::BN / C::NT;        // weights per thread in the slice
+  static_assert(WPTB == 64 || WPTB == 32, "backward split");
+  constexpr int HP = 64 / WPTB;                   // threads per block row
+  const int wr = tid / (BPR * HP);
+  const int wb = (tid / HP) % BPR;
+  const int wh = tid % HP;
+  const int64_t kcol = k0 + wb * 64;
   const bool kvalid = kcol < K;
 
-  f32x16 acc[4][2];
+  AccT<C> acc;
+  zero_acc(acc);
+  StepRegs<C> ra, rb;
+  auto load_w = [&](StepRegs<C>& r, int64_t ns) {
+    if (ns >= nsteps) ns = nsteps - 1;
+    int64_t n = ns * BK + wr;
+    const bool ok = n < N && kvalid;
+    if (!ok) n = 0;
+    const uint8_t* src = p.codes + ((n * K + (ok ? kcol : 0)) >> 1) + wh * (WPTB / 2);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
-
-  u32x4 dr[8];
-  uint32_t wr[4];
-  float chat_r[4];
-  auto load = [&](int64_t ns) {
-    const int64_t nc = ns * 64;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int e = tid + 256 * q;
-      int64_t gm = m0 + (e >> 3);
-      if (gm >= M) gm = M - 1;
-      const int64_t col = nc + (e & 7) * 8;
-      dr[q] = (col < N) ? *reinterpret_cast<const u32x4*>(p.dY + gm * N + col)
-                        : u32x4{0u, 0u, 0u, 0u};
+    for (int h = 0; h < WPTB / 32; ++h) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(src + 16 * h);
+      r.c[h] = ok ? v : u32x4{0u, 0u, 0u, 0u};
     }
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int64_t n = nc + rg * 4 + rr;
-      if (n < N && kvalid) {
-        wr[rr] = *reinterpret_cast<const uint32_t*>(p.codes + ((n * K + kcol) >> 1));
-        const int64_t blk = n * kblocks + (kcol >> 6);
-        chat_r[rr] = (float)p.q8[blk] * p.step[blk >> 8];
-      } else {
-        wr[rr] = 0u;
-        chat_r[rr] = 0.0f;
-      }
+    const int64_t blk = n * kblocks + ((ok ? kcol : 0) >> 6);
+    const uint32_t q = p.q8[blk];
+    r.q = ok ? q : 0u;  // rows past N contribute +-0
+    r.st = p.step[blk >> 8];
+  };
+  // dY columns past N (a partial last step) must read as zero: those steps
+  // take the register path, which zero-fills; every other step is loaded
+  // straight into LDS.
+  auto load_x = [&](uint16_t* As_dst, int64_t ns) {
+    if (ns >= nsteps) ns = nsteps - 1;
+    if ((ns + 1) * BK <= N) {
+      load_rows_lds<C>(As_dst, p.dY, N, m0, M, ns * BK, wave, lane);
+    } else {
+      RowTileRegs<C> dr;
+      load_rows(dr, p.dY, N, m0, M, ns * BK, N, tid);
+      store_rows<C>(As_dst, dr, tid);
     }
   };
-  auto stage = [&]() {
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int e = tid + 256 * q;
-      *reinterpret_cast<u32x4*>(As + (e >> 3) * LD + (e & 7) * 8) = dr[q];
-    }
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      float v[4];
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) v[rr] = lv[(wr[rr] >> (4 * c)) & 15u] * chat_r[rr];
-      u32x2 o = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-      *reinterpret_cast<u32x2*>(Bs + (cg * 8 + c) * LD + rg * 4) = o;
-    }
-  };
-
-  load(0);
-  __syncthreads();
-  for (int64_t ns = 0; ns < nsteps; ++ns) {
-    stage();
+  auto body = [&](StepRegs<C>& rnext, StepRegs<C>& rload, int64_t ns, int cur) {
+    const uint16_t* As = smem + cur * (C::TILE_A + C::TILE_BB);
+    uint16_t* As_n = smem + (cur ^ 1) * (C::TILE_A + C::TILE_BB);
+    load_x(As_n, ns + 1);
+    load_w(rload, ns + 2);
+    step_interleaved<C, true>(As, As + C::TILE_A, As_n,
+                              As_n + C::TILE_A + wr * C::LDTB + wb * C::BSTR + wh * WPTB, rnext,
+                              wm, wn, lane, acc);
+    wait_vmem();
     __syncthreads();
-    if (ns + 1 < nsteps) load(ns + 1);
-    mma_slice(As, Bs, wm, wn, lane, acc);
+  };
+
+  load_w(ra, 0);
+  load_w(rb, 1);
+  load_x(smem, 0);
+  dequant_codes<C>(smem + C::TILE_A + wr * C::LDTB + wb * C::BSTR + wh * WPTB, ra);
+  wait_vmem();
+  __syncthreads();
+  int64_t ns = 0;
+  for (; ns + 2 <= nsteps; ns += 2) {
+    body(rb, ra, ns, 0);
+    body(ra, rb, ns + 1, 1);
+  }
+  if (ns < nsteps) {
+    mma_step<C, true>(smem, smem + C::TILE_A, wm, wn, lane, acc);
     __syncthreads();
   }
 
-  // LoRA: dX += dU A, contraction over r.  A[j][k] is staged transposed.
+  // LoRA: dX += dU A, contraction over r.  A[j][k] is already [contraction][column].
   for (int j0 = 0; j0 < p.r; j0 += 64) {
-    stage_rows_scaled(As, p.dU, p.lddu, m0, M, j0, 1.0f, false, tid);
-    for (int e = tid; e < 64 * 16; e += 256) {
-      const int jr = e >> 4, c8 = e & 15;  // adapter row j0+jr, columns 8*c8..
+    uint16_t* As = smem;
+    uint16_t* Bs = smem + C::TILE_A;
+    stage_rows_scaled<C>(As, p.dU, p.lddu, m0, M, j0, 1.0f, false, tid);
+    for (int e = tid; e < 64 * (C::BN / 8); e += C::NT) {
+      const int jr = e / (C::BN / 8), c8 = e % (C::BN / 8);  // adapter row j0 + jr
       const int64_t col = k0 + c8 * 8;
       u32x4 v = u32x4{0u, 0u, 0u, 0u};
       if (j0 + jr < p.r && col < K) v = *reinterpret_cast<const u32x4*>(p.A + (j0 + jr) * K + col);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        Bs[(c8 * 8 + 2 * q) * LD + jr] = (uint16_t)(v[q] & 0xffffu);
-        Bs[(c8 * 8 + 2 * q + 1) * LD + jr] = (uint16_t)(v[q] >> 16);
-      }
+      *reinterpret_cast<u32x4*>(Bs + jr * C::LDTB + (c8 >> 3) * C::BSTR + (c8 & 7) * 8) = v;
     }
     __syncthreads();
-    mma_slice(As, Bs, wm, wn, lane, acc);
+    mma_step<C, true>(As, Bs, wm, wn, lane, acc);
     __syncthreads();
   }
 
-  store_tile(p.dX, K, m0, k0, M, K, wm, wn, lane, acc);
+  store_tile<C>(p.dX, K, m0, k0, M, K, wm, wn, lane, acc);
 }
+
+#ifndef QN_GEMM_CFG
+#define QN_GEMM_CFG 2, 4, 4, 2
+#endif
+using GemmCfg = Cfg<QN_GEMM_CFG>;
 
 }  // namespace
 
 hipError_t launch_qgemm_fwd(const Nf4View& w, const uint16_t* X, int64_t M, const uint16_t* U,
                             int64_t ldu, const uint16_t* B, int32_t r, float s, uint16_t* Y,
                             hipStream_t stream) {
+  using C = GemmCfg;
   FwdArgs a{X, w.codes, w.q8, w.step, U, ldu, B, r, s, Y, M, w.N, w.K};
-  dim3 grid((unsigned)((w.N + 127) / 128), (unsigned)((M + 255) / 256));
-  hipLaunchKernelGGL(k_qgemm_fwd, grid, dim3(256), 0, stream, a);
+  dim3 grid((unsigned)(((w.N + C::BN - 1) / C::BN) * ((M + C::BM - 1) / C::BM)));
+  hipLaunchKernelGGL(k_qgemm_fwd<C>, grid, dim3(C::NT), 0, stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_qgemm_bwd(const Nf4View& w, const uint16_t* dY, int64_t M, const uint16_t* dU,
                             int64_t lddu, const uint16_t* A, int32_t r, uint16_t* dX,
                             hipStream_t stream) {
+  using C = GemmCfg;
   BwdArgs a{dY, w.codes, w.q8, w.step, dU, lddu, A, r, dX, M, w.N, w.K};
-  dim3 grid((unsigned)((w.K + 127) / 128), (unsigned)((M + 255) / 256));
-  hipLaunchKernelGGL(k_qgemm_bwd, grid, dim3(256), 0, stream, a);
+  dim3 grid((unsigned)(((w.K + C::BN - 1) / C::BN) * ((M + C::BM - 1) / C::BM)));
+  hipLaunchKernelGGL(k_qgemm_bwd<C>, grid, dim3(C::NT), 0, stream, a);
   return hipGetLastError();
 }
 
