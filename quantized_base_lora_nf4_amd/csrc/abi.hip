@@ -5,6 +5,8 @@
 
 #include <math.h>
 
+#include <algorithm>
+
 #include "kernels.hpp"
 
 using namespace qn;
@@ -20,12 +22,14 @@ inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 struct FwdPlan {
   size_t u_off, part_off, total;
-  int u_splits;
   int gemv_splits_n;
 };
 
+// Backward: with U given, [dU | dB] then [dA]; otherwise [U | dU] then
+// [dB | dA].  Slot 0 and slot 1 of a launch pair have their own partial
+// buffer; the second pair reuses them.
 struct BwdPlan {
-  size_t u_off, du_off, part_off, total;
+  size_t u_off, du_off, part0_off, part1_off, total;
 };
 
 bool sizes_ok(int64_t M, int64_t N, int64_t K, int32_t r) {
@@ -38,17 +42,15 @@ FwdPlan plan_fwd(int64_t M, int64_t N, int64_t K, int32_t r) {
   FwdPlan p{};
   const int64_t rp = rank_pad(r);
   p.u_off = 0;
-  size_t off = align_up((size_t)M * rp * 2);
-  p.part_off = off;
+  p.part_off = align_up((size_t)M * rp * 2);
   size_t part = skinny_partial_bytes(M, r, K);
-  p.u_splits = skinny_splits(M, r, K);
   p.gemv_splits_n = 0;
   if (M <= kGemvMaxM) {
     p.gemv_splits_n = gemv_splits(N, K);
     const size_t g = (size_t)p.gemv_splits_n * M * N * sizeof(float);
     if (g > part) part = g;
   }
-  p.total = off + align_up(part);
+  p.total = p.part_off + align_up(part);
   return p;
 }
 
@@ -57,15 +59,14 @@ BwdPlan plan_bwd(int64_t M, int64_t N, int64_t K, int32_t r) {
   const int64_t rp = rank_pad(r);
   p.u_off = 0;
   p.du_off = align_up((size_t)M * rp * 2);
-  p.part_off = p.du_off + align_up((size_t)M * rp * 2);
-  size_t part = skinny_partial_bytes(M, r, K);            // U = X A^T
-  size_t t = skinny_partial_bytes(M, r, N);               // dU = s dY B
-  if (t > part) part = t;
-  t = skinny_partial_bytes(N, r, M);                      // dB = s dY^T U
-  if (t > part) part = t;
-  t = skinny_partial_bytes(r, K, M);                      // dA = dU^T X
-  if (t > part) part = t;
-  p.total = p.part_off + align_up(part);
+  // slot 0: U or dU, then dB;  slot 1: dU or dB, then dA
+  const size_t b_u = skinny_partial_bytes(M, r, K), b_du = skinny_partial_bytes(M, r, N),
+               b_db = skinny_partial_bytes(N, r, M), b_da = skinny_partial_bytes(r, K, M);
+  const size_t part0 = std::max(std::max(b_u, b_du), b_db);
+  const size_t part1 = std::max(std::max(b_du, b_db), b_da);
+  p.part0_off = p.du_off + align_up((size_t)M * rp * 2);
+  p.part1_off = p.part0_off + align_up(part0);
+  p.total = p.part1_off + align_up(part1);
   return p;
 }
 
@@ -81,16 +82,6 @@ int32_t nf4_supported(const nf4_tensor_t* w) {
 
 inline int32_t launch_status(hipError_t e) { return e == hipSuccess ? QLORA_OK : QLORA_ERR_LAUNCH; }
 
-// U = X A^T (unscaled), into ws_u [M][rp] (zero-padded) and optionally U_out [M][r].
-hipError_t run_lora_down(const uint16_t* X, int64_t M, int64_t K, const uint16_t* A, int32_t r,
-                         uint16_t* ws_u, uint16_t* U_out, float* part, hipStream_t stream) {
-  SkinnyOp op{X, K, 1, A, K, 1, M, r, K};
-  const int sp = skinny_splits(M, r, K);
-  hipError_t e = launch_skinny_partial(op, sp, part, stream);
-  if (e != hipSuccess) return e;
-  return launch_skinny_finish(part, sp, M, r, 1.0f, ws_u, rank_pad(r), rank_pad(r), U_out, r,
-                              stream);
-}
 
 }  // namespace
 
@@ -174,16 +165,20 @@ int32_t linear_fwd(const nf4_tensor_t* w, const uint16_t* X, int64_t M, const ui
   uint16_t* ws_u = reinterpret_cast<uint16_t*>(base + pl.u_off);
   float* part = reinterpret_cast<float*>(base + pl.part_off);
   const Nf4View v{w->codes, w->q8, w->step, N, K};
+  const int64_t rp = rank_pad(r);
 
-  hipError_t e = run_lora_down(X, M, K, A, r, ws_u, U_out, part, stream);
+  // U = X A^T into ws_u [M][rp] (zero-padded) and U_out [M][r].
+  const SkinnyJob ju = make_job(SkinnyOp{X, K, 1, A, K, 1, M, r, K}, 1.0f, ws_u, rp, rp, U_out, r,
+                                part);
+  hipError_t e = launch_skinny(&ju, 1, stream);
   if (e != hipSuccess) return QLORA_ERR_LAUNCH;
   if (record(ev0, stream) != hipSuccess) return QLORA_ERR_LAUNCH;
   if (M <= kGemvMaxM) {
     e = launch_qgemv_partial(v, X, M, pl.gemv_splits_n, part, stream);
     if (e != hipSuccess || record(ev1, stream) != hipSuccess) return QLORA_ERR_LAUNCH;
-    e = launch_gemv_finish(part, pl.gemv_splits_n, M, N, ws_u, rank_pad(r), B, r, s, Y, stream);
+    e = launch_gemv_finish(part, pl.gemv_splits_n, M, N, ws_u, rp, B, r, s, Y, stream);
   } else {
-    e = launch_qgemm_fwd(v, X, M, ws_u, rank_pad(r), B, r, s, Y, stream);
+    e = launch_qgemm_fwd(v, X, M, ws_u, rp, B, r, s, Y, stream);
     if (e == hipSuccess) e = record(ev1, stream);
   }
   return launch_status(e);
@@ -208,44 +203,35 @@ int32_t linear_bwd(const nf4_tensor_t* w, const uint16_t* X, const uint16_t* dY,
   char* base = static_cast<char*>(ws);
   uint16_t* ws_u = reinterpret_cast<uint16_t*>(base + pl.u_off);
   uint16_t* ws_du = reinterpret_cast<uint16_t*>(base + pl.du_off);
-  float* part = reinterpret_cast<float*>(base + pl.part_off);
+  float* part0 = reinterpret_cast<float*>(base + pl.part0_off);
+  float* part1 = reinterpret_cast<float*>(base + pl.part1_off);
   const int64_t rp = rank_pad(r);
   hipError_t e;
 
-  // U = X A^T unless the caller kept it from the forward pass.
-  const uint16_t* Uuse = U;
-  int64_t ldu = r;
-  if (!Uuse) {
-    e = run_lora_down(X, M, K, A, r, ws_u, nullptr, part, stream);
-    if (e != hipSuccess) return QLORA_ERR_LAUNCH;
-    Uuse = ws_u;
-    ldu = rp;
+  // dU = s dY B -> ws_du [M][rp] (zero-padded)
+  const SkinnyOp op_du{dY, N, 1, B, 1, r, M, r, N};
+  // dA = dU^T X -> dA [r][K]
+  const SkinnyOp op_da{ws_du, 1, rp, X, 1, K, r, K, M};
+  if (U) {
+    // dB = s dY^T U -> dB [N][r], with the caller's U [M][r]
+    const SkinnyJob j1[2] = {
+        make_job(op_du, s, ws_du, rp, rp, nullptr, 0, part0),
+        make_job(SkinnyOp{dY, 1, N, U, 1, r, N, r, M}, s, dB, r, r, nullptr, 0, part1)};
+    if ((e = launch_skinny(j1, 2, stream)) != hipSuccess) return QLORA_ERR_LAUNCH;
+    const SkinnyJob j2 = make_job(op_da, 1.0f, dA, K, K, nullptr, 0, part1);
+    if ((e = launch_skinny(&j2, 1, stream)) != hipSuccess) return QLORA_ERR_LAUNCH;
+  } else {
+    // U = X A^T -> ws_u, then dB with ws_u
+    const SkinnyJob j1[2] = {
+        make_job(SkinnyOp{X, K, 1, A, K, 1, M, r, K}, 1.0f, ws_u, rp, rp, nullptr, 0, part0),
+        make_job(op_du, s, ws_du, rp, rp, nullptr, 0, part1)};
+    if ((e = launch_skinny(j1, 2, stream)) != hipSuccess) return QLORA_ERR_LAUNCH;
+    const SkinnyJob j2[2] = {
+        make_job(SkinnyOp{dY, 1, N, ws_u, 1, rp, N, r, M}, s, dB, r, r, nullptr, 0, part0),
+        make_job(op_da, 1.0f, dA, K, K, nullptr, 0, part1)};
+    if ((e = launch_skinny(j2, 2, stream)) != hipSuccess) return QLORA_ERR_LAUNCH;
   }
 
-  // dU = s dY B  -> ws_du [M][rp]
-  {
-    SkinnyOp op{dY, N, 1, B, 1, r, M, r, N};
-    const int sp = skinny_splits(M, r, N);
-    if ((e = launch_skinny_partial(op, sp, part, stream)) != hipSuccess) return QLORA_ERR_LAUNCH;
-    if ((e = launch_skinny_finish(part, sp, M, r, s, ws_du, rp, rp, nullptr, 0, stream)) != hipSuccess)
-      return QLORA_ERR_LAUNCH;
-  }
-  // dB = s dY^T U -> dB [N][r]
-  {
-    SkinnyOp op{dY, 1, N, Uuse, 1, ldu, N, r, M};
-    const int sp = skinny_splits(N, r, M);
-    if ((e = launch_skinny_partial(op, sp, part, stream)) != hipSuccess) return QLORA_ERR_LAUNCH;
-    if ((e = launch_skinny_finish(part, sp, N, r, s, dB, r, r, nullptr, 0, stream)) != hipSuccess)
-      return QLORA_ERR_LAUNCH;
-  }
-  // dA = dU^T X -> dA [r][K]
-  {
-    SkinnyOp op{ws_du, 1, rp, X, 1, K, r, K, M};
-    const int sp = skinny_splits(r, K, M);
-    if ((e = launch_skinny_partial(op, sp, part, stream)) != hipSuccess) return QLORA_ERR_LAUNCH;
-    if ((e = launch_skinny_finish(part, sp, r, K, 1.0f, dA, K, K, nullptr, 0, stream)) != hipSuccess)
-      return QLORA_ERR_LAUNCH;
-  }
   // dX = dY W + dU A
   if (dX) {
     const Nf4View v{w->codes, w->q8, w->step, N, K};

@@ -42,7 +42,7 @@ hipError_t launch_gemv_finish(const float* part, int splits, int64_t M, int64_t 
                               const uint16_t* U, int64_t ldu, const uint16_t* B, int32_t r,
                               float s, uint16_t* Y, hipStream_t stream);
 
-// ---- lora.hip: small-rank GEMMs (fp32 split partials + ordered reduction) ----
+// ---- lora.hip: small-rank products with in-kernel reduction of contraction slices ----
 // Operand element access: A-op (i, c) at a[i*a_si + c*a_sc]; B-op (c, j) at
 // b[j*b_sj + c*b_sc]; one stride of each operand must be 1.
 struct SkinnyOp {
@@ -52,13 +52,26 @@ struct SkinnyOp {
   int64_t b_sj, b_sc;
   int64_t I, J, C;
 };
+// One product: out[i*o_si + j] = bf16(scale * sum_c Aop(i,c) Bop(c,j)) for
+// j < J, zero for J <= j < Jw, optionally also out2[i*o2_si + j] for j < J.
+// part: fp32 slice partials (size from skinny_partial_bytes; unused when the
+// product has one slice).
+struct SkinnyJob {
+  SkinnyOp op;
+  float scale;
+  uint16_t* out;
+  int64_t o_si, Jw;
+  uint16_t* out2;
+  int64_t o2_si;
+  float* part;
+};
+int skinny_tiles(int64_t I, int64_t J);
 int skinny_splits(int64_t I, int64_t J, int64_t C);
 size_t skinny_partial_bytes(int64_t I, int64_t J, int64_t C);
-hipError_t launch_skinny_partial(const SkinnyOp& op, int splits, float* part, hipStream_t stream);
-// out[i*o_si + j] = bf16(scale * sum_s part[s][i][j]) for j < J, and 0 for
-// J <= j < Jw; optionally also out2[i*o2_si + j] for j < J.
-hipError_t launch_skinny_finish(const float* part, int splits, int64_t I, int64_t J, float scale,
-                                uint16_t* out, int64_t o_si, int64_t Jw, uint16_t* out2,
-                                int64_t o2_si, hipStream_t stream);
+SkinnyJob make_job(const SkinnyOp& op, float scale, uint16_t* out, int64_t o_si, int64_t Jw,
+                   uint16_t* out2, int64_t o2_si, float* part);
+// Run one or two independent products: one launch for the partial products
+// and, if any product has several contraction slices, one finish launch.
+hipError_t launch_skinny(const SkinnyJob* jobs, int njobs, hipStream_t stream);
 
 }  // namespace qn

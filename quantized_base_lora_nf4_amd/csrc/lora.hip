@@ -2,18 +2,24 @@
 // dA = dU^T X.  LoRA trains only a low-rank pair beside the frozen weight
 // ("QLoRA: fine-tuning a 65B model on one GPU", section "Where the memory
 // goes"), so one side of each of these products is the rank r (<= 256) and
-// the contraction is long (K, N or M).
+// the contraction is long (K, N or M): they are bound by reading X or dY.
 //
-// One generic MFMA kernel computes C[I, J] = sum_c Aop(i, c) Bop(c, j) over
-// a slice of the contraction and writes fp32 partial sums; a second kernel
-// adds the slices in a fixed order, scales and rounds to bf16.  No atomics,
-// so results are bit-reproducible.
+// One generic MFMA kernel computes C[I, J] = scale * sum_c Aop(i, c) Bop(c, j)
+// for up to two independent products in one launch.  Each product's output
+// is cut into 64 x 64 tiles and its contraction into `splits` equal slices;
+// a workgroup computes one (tile, slice) partial in fp32.  A product with one
+// slice is finished in place; otherwise the partials go to the workspace and
+// a second launch adds the slices in slice order, scales and rounds to bf16
+// (for both products of the first launch at once).  No atomics and no
+// cross-workgroup fences (a device-scope fence writes back and invalidates
+// the per-XCD L2s), and the summation order is fixed, so results are
+// bit-reproducible.
 //
 // Tiles are 64 x 64 outputs per 256-thread workgroup (2 x 2 waves of one
 // 32 x 32 MFMA tile each), 64-deep contraction steps staged through LDS.
-// Operands are read element-wise with the thread order chosen so that
-// consecutive lanes touch consecutive addresses in whichever dimension is
-// contiguous.
+// Operands move as 16-byte chunks: kept whole along the contraction, or
+// scattered element-wise when the chunk runs along the output dimension (the
+// transpose).  Misaligned operands fall back to element loads.
 #include "kernels.hpp"
 
 namespace qn {
@@ -23,79 +29,134 @@ namespace {
 constexpr int SLD = 72;
 constexpr int kSkinnyStep = 64;
 
-struct SkinnyArgs {
+struct Prob {
   SkinnyOp op;
-  int64_t c_split;  // contraction length per split (multiple of 64)
-  float* part;
+  int64_t c_split;   // contraction length per slice (multiple of 64)
+  float scale;
+  uint16_t* out;     // out[i * o_si + j]; zero for J <= j < Jw
+  int64_t o_si, Jw;
+  uint16_t* out2;    // optional copy without the padding
+  int64_t o2_si;
+  float* part;       // [tiles][splits][64 * 64]
+  int splits, tiles_j, tiles;
+  int wg_begin;      // first workgroup id of this product
   bool a_vec, b_vec;
 };
 
-// Stage a 64 x 64 operand tile into T[x][c] (c contiguous in LDS).
-// Element (x, c) is at src[x * sx + c * sc]; rows x >= X or columns
-// c >= cend are zero.  One of sx, sc is 1.  When the other stride and the
-// base are 16-byte aligned (`vec`), every thread moves two 16-byte chunks of
-// eight contiguous elements: along c they go to LDS as one 16-byte store;
-// along x they are scattered as eight 2-byte stores (the transpose).
-// Otherwise elements are moved one at a time.  The contraction length of
-// every caller is a multiple of 8, so a chunk is either wholly inside or
-// wholly outside [c0, cend) and [0, X) when X is a multiple of 8.
-__device__ __forceinline__ void stage_op(uint16_t* T, const uint16_t* src, int64_t sx, int64_t sc,
-                                         int64_t x0, int64_t X, int64_t c0, int64_t cend,
-                                         bool vec, int tid) {
+struct Launch {
+  Prob p[2];
+  int nprob;
+};
+
+// Operand tile staging, split into a global-load half (into registers, so
+// the next step's loads are in flight while the current step computes) and
+// an LDS-store half.  The tile is 64 x 64: element (x, c) of the operand is
+// at src[x * sx + c * sc] and lands in T[x][c] (c contiguous in LDS); rows
+// x >= X or columns c >= cend read as zero.  One of sx, sc is 1.  With
+// `vec`, each thread moves two 16-byte chunks of eight contiguous elements:
+// along c they are stored whole, along x they are scattered element-wise (a
+// transpose).  Otherwise each thread moves 16 single elements.
+struct OpRegs {
+  u32x4 v[2];  // vec: two chunks; otherwise 16 elements packed in pairs
+};
+
+__device__ __forceinline__ void load_op(OpRegs& R, const uint16_t* src, int64_t sx, int64_t sc,
+                                        int64_t x0, int64_t X, int64_t c0, int64_t cend,
+                                        bool vec, int tid) {
   const bool c_fast = (sc == 1);
   if (vec) {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const int e = tid + 256 * q;
-      if (c_fast) {
-        const int xi = e >> 3, ci = (e & 7) * 8;
-        const int64_t gx = x0 + xi, gc = c0 + ci;
-        u32x4 v = u32x4{0u, 0u, 0u, 0u};
-        if (gx < X && gc < cend) v = *reinterpret_cast<const u32x4*>(src + gx * sx + gc);
-        *reinterpret_cast<u32x4*>(T + xi * SLD + ci) = v;
-      } else {
-        const int ci = e >> 3, xi = (e & 7) * 8;
-        const int64_t gx = x0 + xi, gc = c0 + ci;
-        u32x4 v = u32x4{0u, 0u, 0u, 0u};
-        if (gx < X && gc < cend) v = *reinterpret_cast<const u32x4*>(src + gc * sc + gx);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          T[(xi + 2 * j) * SLD + ci] = (uint16_t)(v[j] & 0xffffu);
-          T[(xi + 2 * j + 1) * SLD + ci] = (uint16_t)(v[j] >> 16);
-        }
-      }
+      const int xi = c_fast ? (e >> 3) : ((e & 7) * 8);
+      const int ci = c_fast ? ((e & 7) * 8) : (e >> 3);
+      const int64_t gx = x0 + xi, gc = c0 + ci;
+      R.v[q] = u32x4{0u, 0u, 0u, 0u};
+      if (gx < X && gc < cend)
+        R.v[q] = *reinterpret_cast<const u32x4*>(src + (c_fast ? gx * sx + gc : gc * sc + gx));
     }
     return;
   }
-#pragma unroll 4
   for (int q = 0; q < 16; ++q) {
     const int e = tid + 256 * q;
     const int xi = c_fast ? (e >> 6) : (e & 63);
     const int ci = c_fast ? (e & 63) : (e >> 6);
     const int64_t gx = x0 + xi, gc = c0 + ci;
-    uint16_t v = 0;
-    if (gx < X && gc < cend) v = src[gx * sx + gc * sc];
-    T[xi * SLD + ci] = v;
+    const uint32_t v = (gx < X && gc < cend) ? src[gx * sx + gc * sc] : 0u;
+    const uint32_t w = R.v[q >> 3][(q >> 1) & 3];
+    R.v[q >> 3][(q >> 1) & 3] = (q & 1) ? ((w & 0xffffu) | (v << 16)) : v;
   }
 }
 
-__global__ __launch_bounds__(256) void k_skinny_partial(SkinnyArgs p) {
+__device__ __forceinline__ void store_op(uint16_t* T, const OpRegs& R, bool c_fast, bool vec,
+                                         int tid) {
+  if (vec) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int e = tid + 256 * q;
+      if (c_fast) {
+        *reinterpret_cast<u32x4*>(T + (e >> 3) * SLD + (e & 7) * 8) = R.v[q];
+      } else {
+        const int ci = e >> 3, xi = (e & 7) * 8;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          T[(xi + 2 * j) * SLD + ci] = (uint16_t)(R.v[q][j] & 0xffffu);
+          T[(xi + 2 * j + 1) * SLD + ci] = (uint16_t)(R.v[q][j] >> 16);
+        }
+      }
+    }
+    return;
+  }
+  for (int q = 0; q < 16; ++q) {
+    const int e = tid + 256 * q;
+    const int xi = c_fast ? (e >> 6) : (e & 63);
+    const int ci = c_fast ? (e & 63) : (e >> 6);
+    const uint32_t w = R.v[q >> 3][(q >> 1) & 3];
+    T[xi * SLD + ci] = (uint16_t)((q & 1) ? (w >> 16) : (w & 0xffffu));
+  }
+}
+
+// Write one finished output element (and the optional unpadded copy).
+__device__ __forceinline__ void put(const Prob& P, int64_t i, int64_t j, float v) {
+  const uint16_t b = f32_to_bf16(v * P.scale);
+  P.out[i * P.o_si + j] = b;
+  if (P.out2) P.out2[i * P.o2_si + j] = b;
+}
+
+// kVec: every operand of every product in the launch moves as 16-byte
+// chunks (the common case); the element-wise path is compiled separately so
+// that it does not inflate the register budget of the chunked one.
+template <bool kVec>
+__global__ __launch_bounds__(256) void k_skinny(Launch L) {
   __shared__ __attribute__((aligned(16))) uint16_t As[64 * SLD];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[64 * SLD];
+  const int pi = (L.nprob > 1 && (int)blockIdx.x >= L.p[1].wg_begin) ? 1 : 0;
+  const Prob& P = L.p[pi];
+  const SkinnyOp& op = P.op;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wi = wave >> 1, wj = wave & 1;
-  const int64_t j0 = (int64_t)blockIdx.x * 64, i0 = (int64_t)blockIdx.y * 64;
-  const int64_t cs = (int64_t)blockIdx.z * p.c_split;
-  int64_t ce = cs + p.c_split;
-  if (ce > p.op.C) ce = p.op.C;
-  const SkinnyOp& op = p.op;
+  const int local = (int)blockIdx.x - P.wg_begin;
+  const int tile = local / P.splits, split = local % P.splits;
+  const int64_t i0 = (int64_t)(tile / P.tiles_j) * 64, j0 = (int64_t)(tile % P.tiles_j) * 64;
+  const int64_t cs = (int64_t)split * P.c_split;
+  int64_t ce = cs + P.c_split;
+  if (ce > op.C) ce = op.C;
 
   f32x16 acc = f32x16{};
   const int r32 = lane & 31, kh = (lane >> 5) * 8;
+  OpRegs ra, rb;
+  if (cs < ce) {
+    load_op(ra, op.a, op.a_si, op.a_sc, i0, op.I, cs, ce, kVec || P.a_vec, tid);
+    load_op(rb, op.b, op.b_sj, op.b_sc, j0, op.J, cs, ce, kVec || P.b_vec, tid);
+  }
   for (int64_t c0 = cs; c0 < ce; c0 += kSkinnyStep) {
-    stage_op(As, op.a, op.a_si, op.a_sc, i0, op.I, c0, ce, p.a_vec, tid);
-    stage_op(Bs, op.b, op.b_sj, op.b_sc, j0, op.J, c0, ce, p.b_vec, tid);
+    store_op(As, ra, op.a_sc == 1, kVec || P.a_vec, tid);
+    store_op(Bs, rb, op.b_sc == 1, kVec || P.b_vec, tid);
     __syncthreads();
+    if (c0 + kSkinnyStep < ce) {  // next step's loads fly while this one computes
+      load_op(ra, op.a, op.a_si, op.a_sc, i0, op.I, c0 + kSkinnyStep, ce, kVec || P.a_vec, tid);
+      load_op(rb, op.b, op.b_sj, op.b_sc, j0, op.J, c0 + kSkinnyStep, ce, kVec || P.b_vec, tid);
+    }
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(As + (wi * 32 + r32) * SLD + kk * 16 + kh);
@@ -105,86 +166,149 @@ __global__ __launch_bounds__(256) void k_skinny_partial(SkinnyArgs p) {
     __syncthreads();
   }
 
-  float* out = p.part + (int64_t)blockIdx.z * op.I * op.J;
-  const int64_t j = j0 + wj * 32 + r32;
+  // Tile-local coordinates of this lane's accumulators.
+  const int tj = wj * 32 + r32;
+  if (P.splits == 1) {
+    const int64_t j = j0 + tj;
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int64_t i = i0 + wi * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-    if (i < op.I && j < op.J) out[i * op.J + j] = acc[v];
-  }
-}
-
-__global__ __launch_bounds__(256) void k_skinny_finish(const float* __restrict__ part, int splits,
-                                                       int64_t I, int64_t J, float scale,
-                                                       uint16_t* __restrict__ out, int64_t o_si,
-                                                       int64_t Jw, uint16_t* __restrict__ out2,
-                                                       int64_t o2_si) {
-  const int64_t total = I * Jw;
-  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
-       e += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t i = e / Jw, j = e - i * Jw;
-    if (j < J) {
-      float acc = 0.0f;
-      for (int s = 0; s < splits; ++s) acc += part[(int64_t)s * I * J + i * J + j];
-      const uint16_t v = f32_to_bf16(acc * scale);
-      out[i * o_si + j] = v;
-      if (out2) out2[i * o2_si + j] = v;
-    } else {
-      out[i * o_si + j] = 0;
+    for (int v = 0; v < 16; ++v) {
+      const int64_t i = i0 + wi * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      if (i < op.I && j < op.J) put(P, i, j, acc[v]);
+    }
+    // Zero padding columns J <= j < Jw (only tiles in the last tile column).
+    if (P.Jw > op.J && (tile % P.tiles_j) == P.tiles_j - 1) {
+      for (int e = tid; e < 64 * (int)(P.Jw - op.J); e += 256) {
+        const int64_t i = i0 + e / (P.Jw - op.J), j = op.J + e % (P.Jw - op.J);
+        if (i < op.I) P.out[i * P.o_si + j] = 0;
+      }
+    }
+  } else {
+    float* mine = P.part + ((int64_t)tile * P.splits + split) * 4096;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int ti = wi * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      mine[ti * 64 + tj] = acc[v];
     }
   }
 }
 
-}  // namespace
-
-int skinny_splits(int64_t I, int64_t J, int64_t C) {
-  const int64_t tiles = ((I + 63) / 64) * ((J + 63) / 64);
-  const int64_t steps = (C + kSkinnyStep - 1) / kSkinnyStep;
-  int64_t s = (1024 + tiles - 1) / tiles;  // aim for ~4 workgroups per CU
-  const int64_t max_s = (steps + 3) / 4;   // at least 4 steps per split
-  if (s > max_s) s = max_s;
-  if (s < 1) s = 1;
-  if (s > 64) s = 64;
-  return (int)s;
+// Second launch for products with several slices: four consecutive outputs
+// of one tile row per thread; slices added in order.
+__global__ __launch_bounds__(256) void k_skinny_finish(Launch L) {
+  const int pi = (L.nprob > 1 && (int)blockIdx.x >= L.p[1].wg_begin) ? 1 : 0;
+  const Prob& P = L.p[pi];
+  const int64_t q = ((int64_t)blockIdx.x - P.wg_begin) * 256 + threadIdx.x;  // quad index
+  const int64_t tile = q >> 10, off = (q & 1023) * 4;
+  if (tile >= P.tiles) return;
+  const f32x4* base = reinterpret_cast<const f32x4*>(P.part + tile * P.splits * 4096 + off);
+  f32x4 s = base[0];
+  for (int k = 1; k < P.splits; ++k) s += base[(int64_t)k * 1024];
+  const int64_t i = (tile / P.tiles_j) * 64 + (off >> 6);
+  const int64_t j = (tile % P.tiles_j) * 64 + (off & 63);
+  if (i >= P.op.I) return;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if (j + e < P.op.J) put(P, i, j + e, s[e]);
+    else if (j + e < P.Jw) P.out[i * P.o_si + j + e] = 0;
+  }
 }
 
-static int64_t split_len(int64_t C, int s) {
+
+int64_t split_len(int64_t C, int s) {
   const int64_t steps = (C + kSkinnyStep - 1) / kSkinnyStep;
   return ((steps + s - 1) / s) * kSkinnyStep;
 }
 
+bool vec_ok(const uint16_t* ptr, int64_t sx, int64_t sc, int64_t X, int64_t C) {
+  // 16-byte chunks need an aligned base and outer stride, a contraction
+  // length that is a multiple of 8 and, for chunks along the output
+  // dimension, an output extent that is a multiple of 8.
+  const int64_t outer = (sc == 1) ? sx : sc;
+  const bool along_x = (sc != 1);
+  return ((uintptr_t)ptr & 15u) == 0 && (outer % 8) == 0 && (C % 8) == 0 &&
+         (!along_x || (X % 8) == 0);
+}
+
+}  // namespace
+
+int skinny_tiles(int64_t I, int64_t J) { return (int)(((I + 63) / 64) * ((J + 63) / 64)); }
+
+int skinny_splits(int64_t I, int64_t J, int64_t C) {
+  const int64_t tiles = skinny_tiles(I, J);
+  const int64_t steps = (C + kSkinnyStep - 1) / kSkinnyStep;
+  int64_t s = (1024 + tiles - 1) / tiles;  // aim for ~4 workgroups per CU
+  const int64_t max_s = (steps + 7) / 8;   // keep >= 8 steps per slice
+  if (s > max_s) s = max_s;
+  if (s > 16) s = 16;
+  if (s < 1) s = 1;
+  return (int)s;
+}
+
 size_t skinny_partial_bytes(int64_t I, int64_t J, int64_t C) {
   const int s = skinny_splits(I, J, C);
-  return (size_t)s * (size_t)I * (size_t)J * sizeof(float);
+  return s > 1 ? (size_t)skinny_tiles(I, J) * s * 4096 * sizeof(float) : 0;
 }
 
-hipError_t launch_skinny_partial(const SkinnyOp& op, int splits, float* part, hipStream_t stream) {
-  const int64_t cl = split_len(op.C, splits);
-  // 16-byte chunks need an aligned base and an aligned outer stride, a
-  // contraction length that is a multiple of 8 and (for chunks along the
-  // output dimension) an output extent that is a multiple of 8.
-  auto vec_ok = [&](const uint16_t* ptr, int64_t sx, int64_t sc, int64_t X) {
-    const int64_t outer = (sc == 1) ? sx : sc;
-    const bool along_x = (sc != 1);
-    return ((uintptr_t)ptr & 15u) == 0 && (outer % 8) == 0 && (op.C % 8) == 0 &&
-           (!along_x || (X % 8) == 0);
-  };
-  SkinnyArgs a{op, cl, part, vec_ok(op.a, op.a_si, op.a_sc, op.I), vec_ok(op.b, op.b_sj, op.b_sc, op.J)};
-  dim3 grid((unsigned)((op.J + 63) / 64), (unsigned)((op.I + 63) / 64), (unsigned)splits);
-  hipLaunchKernelGGL(k_skinny_partial, grid, dim3(256), 0, stream, a);
+SkinnyJob make_job(const SkinnyOp& op, float scale, uint16_t* out, int64_t o_si, int64_t Jw,
+                   uint16_t* out2, int64_t o2_si, float* part) {
+  SkinnyJob j;
+  j.op = op;
+  j.scale = scale;
+  j.out = out;
+  j.o_si = o_si;
+  j.Jw = Jw;
+  j.out2 = out2;
+  j.o2_si = o2_si;
+  j.part = part;
+  return j;
+}
+
+hipError_t launch_skinny(const SkinnyJob* jobs, int njobs, hipStream_t stream) {
+  Launch L{};
+  L.nprob = njobs;
+  int wg = 0;
+  for (int k = 0; k < njobs; ++k) {
+    const SkinnyJob& j = jobs[k];
+    Prob& P = L.p[k];
+    P.op = j.op;
+    P.splits = skinny_splits(j.op.I, j.op.J, j.op.C);
+    P.c_split = split_len(j.op.C, P.splits);
+    P.scale = j.scale;
+    P.out = j.out;
+    P.o_si = j.o_si;
+    P.Jw = j.Jw;
+    P.out2 = j.out2;
+    P.o2_si = j.o2_si;
+    P.part = j.part;
+    P.tiles_j = (int)((j.op.J + 63) / 64);
+    P.tiles = skinny_tiles(j.op.I, j.op.J);
+    P.wg_begin = wg;
+    P.a_vec = vec_ok(j.op.a, j.op.a_si, j.op.a_sc, j.op.I, j.op.C);
+    P.b_vec = vec_ok(j.op.b, j.op.b_sj, j.op.b_sc, j.op.J, j.op.C);
+    wg += P.tiles * P.splits;
+  }
+  bool all_vec = true;
+  for (int k = 0; k < njobs; ++k) all_vec = all_vec && L.p[k].a_vec && L.p[k].b_vec;
+  if (all_vec)
+    hipLaunchKernelGGL(k_skinny<true>, dim3((unsigned)wg), dim3(256), 0, stream, L);
+  else
+    hipLaunchKernelGGL(k_skinny<false>, dim3((unsigned)wg), dim3(256), 0, stream, L);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // finish launch for the products with several slices: 4 quads of 1024 per tile
+  Launch F{};
+  int fwg = 0;
+  for (int k = 0; k < njobs; ++k) {
+    if (L.p[k].splits == 1) continue;
+    F.p[F.nprob] = L.p[k];
+    F.p[F.nprob].wg_begin = fwg;
+    fwg += L.p[k].tiles * 4;
+    ++F.nprob;
+  }
+  if (F.nprob == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_skinny_finish, dim3((unsigned)fwg), dim3(256), 0, stream, F);
   return hipGetLastError();
 }
 
-hipError_t launch_skinny_finish(const float* part, int splits, int64_t I, int64_t J, float scale,
-                                uint16_t* out, int64_t o_si, int64_t Jw, uint16_t* out2,
-                                int64_t o2_si, hipStream_t stream) {
-  const int64_t total = I * Jw;
-  int64_t grid = (total + 255) / 256;
-  if (grid > 16384) grid = 16384;
-  if (grid < 1) grid = 1;
-  hipLaunchKernelGGL(k_skinny_finish, dim3((unsigned)grid), dim3(256), 0, stream, part, splits, I,
-                     J, scale, out, o_si, Jw, out2, o2_si);
-  return hipGetLastError();
-}
 
 }  // namespace qn
