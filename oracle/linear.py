@@ -78,3 +78,14 @@ def forward_rows(X, W_hat, A, B, s: float, rows):
     """Y restricted to the given rows."""
     rows = np.asarray(rows)
     return forward(as_f64(X)[rows], W_hat, A, B, s)
+
+
+def adapter_grads(X, dY, A, B, s: float):
+    """dA and dB alone, in full, without the M x N x K product of dX
+    (same chain rule as ``backward``); for checking large shapes."""
+    X = as_f64(X)
+    dY = as_f64(dY)
+    s = float(s)
+    U = X @ as_f64(A).T
+    dU = s * (dY @ as_f64(B))
+    return dU.T @ X, s * (dY.T @ U)

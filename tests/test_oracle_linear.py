@@ -35,6 +35,9 @@ def test_backward_matches_torch_autograd(shape):
     np.testing.assert_allclose(dX, tX.grad.numpy(), rtol=1e-12, atol=1e-13)
     np.testing.assert_allclose(dA, tA.grad.numpy(), rtol=1e-12, atol=1e-13)
     np.testing.assert_allclose(dB, tB.grad.numpy(), rtol=1e-12, atol=1e-13)
+    gA, gB = linear.adapter_grads(X, dY, A, B, s)
+    np.testing.assert_allclose(gA, tA.grad.numpy(), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(gB, tB.grad.numpy(), rtol=1e-12, atol=1e-13)
 
 
 def test_backward_matches_finite_differences():
