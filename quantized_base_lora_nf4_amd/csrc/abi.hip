@@ -22,7 +22,6 @@ inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 struct FwdPlan {
   size_t u_off, part_off, total;
-  int gemv_splits_n;
 };
 
 // Backward: with U given, [dU | dB] then [dA]; otherwise [U | dU] then
@@ -43,13 +42,8 @@ FwdPlan plan_fwd(int64_t M, int64_t N, int64_t K, int32_t r) {
   const int64_t rp = rank_pad(r);
   p.u_off = 0;
   p.part_off = align_up((size_t)M * rp * 2);
-  size_t part = skinny_partial_bytes(M, r, K);
-  p.gemv_splits_n = 0;
-  if (M <= kGemvMaxM) {
-    p.gemv_splits_n = gemv_splits(N, K);
-    const size_t g = (size_t)p.gemv_splits_n * M * N * sizeof(float);
-    if (g > part) part = g;
-  }
+  (void)N;
+  const size_t part = gemv_fits(M, r, K) ? gemv_workspace_bytes(M, r, K) : skinny_partial_bytes(M, r, K);
   p.total = p.part_off + align_up(part);
   return p;
 }
@@ -167,20 +161,17 @@ int32_t linear_fwd(const nf4_tensor_t* w, const uint16_t* X, int64_t M, const ui
   const Nf4View v{w->codes, w->q8, w->step, N, K};
   const int64_t rp = rank_pad(r);
 
+  if (gemv_fits(M, r, K))
+    return launch_status(launch_qgemv(v, X, M, A, B, r, s, Y, U_out, part, stream, ev0, ev1));
+
   // U = X A^T into ws_u [M][rp] (zero-padded) and U_out [M][r].
   const SkinnyJob ju = make_job(SkinnyOp{X, K, 1, A, K, 1, M, r, K}, 1.0f, ws_u, rp, rp, U_out, r,
                                 part);
   hipError_t e = launch_skinny(&ju, 1, stream);
   if (e != hipSuccess) return QLORA_ERR_LAUNCH;
   if (record(ev0, stream) != hipSuccess) return QLORA_ERR_LAUNCH;
-  if (M <= kGemvMaxM) {
-    e = launch_qgemv_partial(v, X, M, pl.gemv_splits_n, part, stream);
-    if (e != hipSuccess || record(ev1, stream) != hipSuccess) return QLORA_ERR_LAUNCH;
-    e = launch_gemv_finish(part, pl.gemv_splits_n, M, N, ws_u, rp, B, r, s, Y, stream);
-  } else {
-    e = launch_qgemm_fwd(v, X, M, ws_u, rp, B, r, s, Y, stream);
-    if (e == hipSuccess) e = record(ev1, stream);
-  }
+  e = launch_qgemm_fwd(v, X, M, ws_u, rp, B, r, s, Y, stream);
+  if (e == hipSuccess) e = record(ev1, stream);
   return launch_status(e);
 }
 

@@ -4,158 +4,439 @@
 // MFMA throughput.
 //
 // Dequantize-on-the-fly as in "QLoRA: fine-tuning a 65B model on one GPU",
-// section "Where the memory goes".  To stay within the VALU budget of a
-// memory-bound stream (~2.5 lane-ops per weight at 8 TB/s on 256 CUs), the
-// codes are expanded to *unscaled* bf16 levels through a 256-entry byte
-// table (one LDS read yields two bf16 values in MFMA operand order), the
-// MFMA sums one 64-element block at a time, and the block constant
-// fl32(q8 * step) multiplies that block's fp32 partial sum.  The result
-// differs from using the bf16-rounded dequantized weight only by the bf16
-// rounding of the levels (relative 2^-9 per weight); accumulation is fp32.
+// section "Where the memory goes".  A memory-bound stream leaves only a few
+// lane operations per weight, so the codes are expanded to *unscaled* bf16
+// levels (a 256-entry byte table in LDS, or byte permutes over the level
+// table held in registers), the MFMA sums one 64-element block at a time,
+// and the block constant fl32(q8 * step) multiplies that block's fp32
+// partial sum.  The result differs from using the bf16-rounded dequantized
+// weight only by the bf16 rounding of the levels (relative 2^-9 per weight);
+// accumulation is fp32.
 //
-// Work split: a workgroup of 4 waves owns 64 weight rows and one of S equal
-// slices of K; each wave owns 16 rows.  In a 64-column block, lane l reads 8
-// bytes (16 codes) of row l % 16 at byte 8 (l / 16); MFMA j (0, 1) of the
-// block contracts codes 8 j .. 8 j + 7 of every lane's 16, with the matching
-// X elements on the A side.  Every MFMA therefore stays inside one block.
+// Two launches per call:
+//  1. k_lora_down_part: fp32 partial sums of U = X A^T over S slices of K.
+//  2. k_qgemv: Y = X W^T + s U B^T.  A workgroup owns 16 G weight rows and
+//     all of K; its KW waves each take a contiguous range of K, and their
+//     partial sums are added in LDS.  The epilogue sums the U partials,
+//     adds the LoRA term and stores bf16 Y (and bf16 U when asked for).
+//
+// Operand layout (MFMA 16x16x32 bf16, A = X rows, B = weight rows, so that
+// the four results of a lane share one weight row and one block constant):
+// per double step (blocks kb, kb+1) lane l loads 16 bytes of weight row
+// l % 16 at byte 32 kb + 16 (l / 16), i.e. lanes 0-31 hold block kb and
+// lanes 32-63 block kb+1.  One cross-half swap of two code words
+// (v_permlane32_swap) leaves every lane with two 8-code words of each
+// block, so each MFMA contracts codes of a single block.  Word j of lane
+// group q then holds codes 32 (q & 1) + 16 (q >> 1) + 8 (j & 1) .. +7 of
+// block kb + (j >> 1); the X fragment of MFMA j uses the same positions.
 #include "kernels.hpp"
 
 namespace qn {
 
 namespace {
 
-constexpr int kUnroll = 4;  // blocks in flight per lane
+// bf16 bits of an fp32 value (round to nearest even; finite input)
+constexpr uint32_t bf16_rne_bits(uint32_t f) { return (f + 0x7fffu + ((f >> 16) & 1u)) >> 16; }
 
-__global__ __launch_bounds__(256) void k_qgemv_partial(const uint8_t* __restrict__ codes,
-                                                       const uint8_t* __restrict__ q8,
-                                                       const float* __restrict__ step,
-                                                       const uint16_t* __restrict__ X, int64_t M,
-                                                       int64_t N, int64_t K, int64_t blocks_per_split,
-                                                       float* __restrict__ part) {
-  __shared__ uint32_t lut[256];
-  {
-    const int b = threadIdx.x;  // byte value -> (level[lo nibble], level[hi nibble]) as bf16
-    lut[b] = pack_bf16x2(level_f32(b & 15), level_f32(b >> 4));
+__device__ __forceinline__ uint32_t perm(uint32_t s0, uint32_t s1, uint32_t sel) {
+  return __builtin_amdgcn_perm(s0, s1, sel);
+}
+
+// Byte planes of the 16 unscaled bf16 levels: kLo[q] byte e = low byte of
+// level 4 q + e, kHi[q] byte e = high byte.
+struct UnscaledPlanes {
+  uint32_t lo[4], hi[4];
+};
+constexpr UnscaledPlanes make_planes() {
+  UnscaledPlanes p{};
+  for (int q = 0; q < 4; ++q) {
+    uint32_t lo = 0, hi = 0;
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t b = bf16_rne_bits(kLevelBits[4 * q + e]);
+      lo |= (b & 0xffu) << (8 * e);
+      hi |= ((b >> 8) & 0xffu) << (8 * e);
+    }
+    p.lo[q] = lo;
+    p.hi[q] = hi;
   }
-  __syncthreads();
+  return p;
+}
+constexpr UnscaledPlanes kPlanes = make_planes();
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int col = lane & 15, q = lane >> 4;
-  const int64_t kblocks = K >> 6;
-  int64_t n = (int64_t)blockIdx.x * 64 + wave * 16 + col;
-  const bool nvalid = n < N;
-  if (!nvalid) n = N - 1;
-  const int64_t kb0 = (int64_t)blockIdx.y * blocks_per_split;
-  int64_t kb1 = kb0 + blocks_per_split;
-  if (kb1 > kblocks) kb1 = kblocks;
+// Eight codes (nibble order) -> four packed bf16 level pairs, by permutes.
+__device__ __forceinline__ u32x4 levels8_perm(uint32_t w) {
+  const uint32_t se = w & 0x07070707u;
+  const uint32_t so = (w >> 4) & 0x07070707u;
+  const uint32_t me = perm(0u, 0u, ((w >> 3) & 0x01010101u) | 0x0c0c0c0cu);
+  const uint32_t mo = perm(0u, 0u, ((w >> 7) & 0x01010101u) | 0x0c0c0c0cu);
+  const uint32_t le = (me & perm(kPlanes.lo[3], kPlanes.lo[2], se)) |
+                      (~me & perm(kPlanes.lo[1], kPlanes.lo[0], se));
+  const uint32_t he = (me & perm(kPlanes.hi[3], kPlanes.hi[2], se)) |
+                      (~me & perm(kPlanes.hi[1], kPlanes.hi[0], se));
+  const uint32_t lo = (mo & perm(kPlanes.lo[3], kPlanes.lo[2], so)) |
+                      (~mo & perm(kPlanes.lo[1], kPlanes.lo[0], so));
+  const uint32_t ho = (mo & perm(kPlanes.hi[3], kPlanes.hi[2], so)) |
+                      (~mo & perm(kPlanes.hi[1], kPlanes.hi[0], so));
+  const uint32_t t0 = perm(he, le, 0x05010400u);
+  const uint32_t t1 = perm(he, le, 0x07030602u);
+  const uint32_t u0 = perm(ho, lo, 0x05010400u);
+  const uint32_t u1 = perm(ho, lo, 0x07030602u);
+  return u32x4{perm(u0, t0, 0x05040100u), perm(u0, t0, 0x07060302u), perm(u1, t1, 0x05040100u),
+               perm(u1, t1, 0x07060302u)};
+}
 
-  const bool mvalid = col < M;  // this lane's A-side row
-  const uint16_t* xrow = X + (mvalid ? col : 0) * K + q * 16;
-  const uint8_t* crow = codes + n * (K >> 1) + q * 8;
-  const int64_t blk_row = n * kblocks;
+// Eight codes -> four packed bf16 level pairs, by a byte-indexed LDS table.
+// The table is replicated 16 times, entry b of copy l at word 16 b + l, and
+// lane l reads copy l % 16 (lutl = table + l % 16): the 16 lanes that the
+// LDS serves together then always hit 16 different banks, whatever the codes
+// (random indices into a single copy stall the LDS on bank conflicts).
+__device__ __forceinline__ u32x4 levels8_lut(uint32_t w, const uint32_t* lutl) {
+  return u32x4{lutl[16 * (w & 0xffu)], lutl[16 * ((w >> 8) & 0xffu)],
+               lutl[16 * ((w >> 16) & 0xffu)], lutl[16 * (w >> 24)]};
+}
+constexpr int kLutWords = 256 * 16;
 
+// ---------------------------------------------------------------------------
+// U partial sums: part[s][m][j] = sum over k in slice s of X[m][k] A[j][k].
+// Grid (S, ceil(r / 64)); wave w of a workgroup owns adapter rows
+// 64 blockIdx.y + 16 w .. +15.  MFMA 16x16x32: A = X rows, B = A rows.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_lora_down_part(const uint16_t* __restrict__ X, int64_t M,
+                                                        const uint16_t* __restrict__ A, int32_t r,
+                                                        int64_t K, int64_t slice,
+                                                        float* __restrict__ part) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i16 = lane & 15, q = lane >> 4;
+  const int64_t j = (int64_t)blockIdx.y * 64 + wave * 16 + i16;
+  const bool mvalid = i16 < M, jvalid = j < r;
+  const int64_t k0 = (int64_t)blockIdx.x * slice;
+  int64_t k1 = k0 + slice;
+  if (k1 > K) k1 = K;
+  const uint16_t* xr = X + (mvalid ? i16 : 0) * K + 8 * q;
+  const uint16_t* ar = A + (jvalid ? j : 0) * K + 8 * q;
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  int64_t kb = kb0;
-  for (; kb + kUnroll <= kb1; kb += kUnroll) {
-    u32x2 cw[kUnroll];
-    u32x4 xa[kUnroll][2];
-    float chat[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      cw[u] = *reinterpret_cast<const u32x2*>(crow + (kb + u) * 32);
-      const int64_t blk = blk_row + kb + u;
-      chat[u] = (float)q8[blk] * step[blk >> 8];
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        xa[u][j] = mvalid ? *reinterpret_cast<const u32x4*>(xrow + (kb + u) * 64 + j * 8)
-                          : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      f32x4 pb = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const uint32_t w = cw[u][j];
-        const u32x4 bw = u32x4{lut[w & 0xffu], lut[(w >> 8) & 0xffu], lut[(w >> 16) & 0xffu],
-                               lut[w >> 24]};
-        pb = mfma16(as_bf16x8(xa[u][j]), as_bf16x8(bw), pb);
-      }
-#pragma unroll
-      for (int v = 0; v < 4; ++v) acc[v] += chat[u] * pb[v];
-    }
+  for (int64_t k = k0; k < k1; k += 32) {
+    const u32x4 xa = mvalid ? *reinterpret_cast<const u32x4*>(xr + k) : u32x4{0u, 0u, 0u, 0u};
+    const u32x4 aa = jvalid ? *reinterpret_cast<const u32x4*>(ar + k) : u32x4{0u, 0u, 0u, 0u};
+    acc = mfma16(as_bf16x8(xa), as_bf16x8(aa), acc);
   }
-  for (; kb < kb1; ++kb) {
-    const u32x2 cw = *reinterpret_cast<const u32x2*>(crow + kb * 32);
-    const int64_t blk = blk_row + kb;
-    const float chat = (float)q8[blk] * step[blk >> 8];
-    f32x4 pb = f32x4{0.f, 0.f, 0.f, 0.f};
+  // D[m = 4 q + v][j]
+  float* out = part + (int64_t)blockIdx.x * M * r;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const u32x4 xa = mvalid ? *reinterpret_cast<const u32x4*>(xrow + kb * 64 + j * 8)
-                              : u32x4{0u, 0u, 0u, 0u};
-      const uint32_t w = cw[j];
-      const u32x4 bw = u32x4{lut[w & 0xffu], lut[(w >> 8) & 0xffu], lut[(w >> 16) & 0xffu],
-                             lut[w >> 24]};
-      pb = mfma16(as_bf16x8(xa), as_bf16x8(bw), pb);
-    }
-#pragma unroll
-    for (int v = 0; v < 4; ++v) acc[v] += chat * pb[v];
-  }
-
-  if (nvalid) {
-    float* out = part + (int64_t)blockIdx.y * M * N;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int m = 4 * q + v;
-      if (m < M) out[m * N + n] = acc[v];
-    }
+  for (int v = 0; v < 4; ++v) {
+    const int m = 4 * q + v;
+    if (m < M && jvalid) out[m * r + j] = acc[v];
   }
 }
 
-__global__ __launch_bounds__(256) void k_gemv_finish(const float* __restrict__ part, int splits,
-                                                     int64_t M, int64_t N,
-                                                     const uint16_t* __restrict__ U, int64_t ldu,
-                                                     const uint16_t* __restrict__ B, int32_t r,
-                                                     float s, uint16_t* __restrict__ Y) {
-  const int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (e >= M * N) return;
-  const int64_t m = e / N, n = e - m * N;
-  float acc = 0.0f;
-  for (int sp = 0; sp < splits; ++sp) acc += part[(int64_t)sp * M * N + e];
-  float lora = 0.0f;
-  for (int j = 0; j < r; ++j) lora += bf16_to_f32(U[m * ldu + j]) * bf16_to_f32(B[n * r + j]);
-  Y[e] = f32_to_bf16(acc + s * lora);
+struct GemvArgs {
+  const uint8_t* codes;
+  const uint8_t* q8;
+  const float* step;
+  const uint16_t* X;
+  int64_t M, N, K;
+  const float* upart;  // [us][M][r]
+  int32_t us;
+  const uint16_t* B;
+  int32_t r;
+  float s;
+  uint16_t* Y;
+  uint16_t* U_out;  // nullable, bf16 [M][r]
+};
+
+#ifndef QN_GEMV_PERM
+#define QN_GEMV_PERM false
+#endif
+#ifndef QN_GEMV_PD
+#define QN_GEMV_PD 3
+#endif
+
+// Dynamic LDS of k_qgemv, in 4-byte words: the byte table (kLutWords), the U sums
+// (M r), then a region holding the block constants of the workgroup's rows
+// during the main loop (16 G rows of odd stride kblocks | 1, so that the 16
+// rows a wave reads at once sit in 16 different banks) and the waves'
+// partial sums after it (KW G 256).
+__host__ __device__ constexpr int64_t gemv_lds_words(int G, int KW, int64_t M, int64_t r,
+                                                     int64_t kblocks) {
+  const int64_t chat = 16 * G * (kblocks | 1), red = (int64_t)KW * G * 256;
+  return kLutWords + M * r + (chat > red ? chat : red);
+}
+
+template <int G, int KW, int PD, bool kPerm>
+__global__ __launch_bounds__(64 * KW) void k_qgemv(GemvArgs p) {
+  constexpr int NT = 64 * KW;
+  extern __shared__ float lds[];
+  uint32_t* lut = reinterpret_cast<uint32_t*>(lds);
+  float* ush = lds + kLutWords;
+  float* chat_t = ush + p.M * p.r;  // [16 G][kblocks | 1] during the main loop
+  float* red = chat_t;              // [KW][G][4][64] after it
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int i16 = lane & 15, q = lane >> 4;
+  const int64_t M = p.M, N = p.N, K = p.K;
+  const int64_t kblocks = K >> 6;
+  const int64_t kbs = kblocks | 1;  // row stride of the constant table
+  const int64_t n0 = (int64_t)blockIdx.x * 16 * G;
+
+  // Full double steps [d0, d1) of this wave, out of T = kblocks / 2; an odd
+  // last block is a separate tail step of the last wave.
+  const int64_t T = kblocks >> 1;
+  const int64_t d0 = T * wave / KW, d1 = T * (wave + 1) / KW;
+  const bool odd_tail = (kblocks & 1) && wave == KW - 1;
+
+  const uint8_t* crow[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    int64_t n = n0 + 16 * g + i16;
+    if (n >= N) n = N - 1;  // computed and dropped
+    crow[g] = p.codes + n * (K >> 1) + 16 * q;
+  }
+  // X fragment of word j: row i16, columns 64 (kb + (j >> 1)) + xo + 8 (j & 1).
+  // Rows past M re-read row 0; their results are never stored.
+  const int xo = 32 * (q & 1) + 16 * (q >> 1);
+  const uint16_t* xrow = p.X + (i16 < M ? i16 : 0) * K + xo;
+  // this lane's rows of the block-constant table
+  const float* crow_t[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) crow_t[g] = chat_t + (16 * g + i16) * kbs;
+
+  // Raw loads of one double step (codes, X fragments).  Nothing is computed
+  // from them at issue, so issuing never waits for a load.
+  struct Slot {
+    u32x4 c[G];
+    u32x4 x[4];
+  };
+  Slot sl[PD];
+
+  // Every call issues the same loads (no branches), so that the compiler can
+  // count them and wait only for the step being consumed.  Steps past the
+  // end re-read the last one.  The tail form covers the single block kb:
+  // lanes 32-63 re-read it (its second half gets constant 0).
+  auto issue = [&](Slot& S, int64_t d, bool tail) {
+    if (d >= d1 && !tail) d = d1 - 1;
+    const int64_t kb = 2 * d;
+    const int64_t off = (tail && q >= 2) ? kb * 32 - 32 : kb * 32;
+    const int64_t kb2 = tail ? kb : kb + 1;
+#pragma unroll
+    for (int g = 0; g < G; ++g) S.c[g] = *reinterpret_cast<const u32x4*>(crow[g] + off);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      S.x[j] = *reinterpret_cast<const u32x4*>(xrow + 64 * ((j >> 1) ? kb2 : kb) + 8 * (j & 1));
+  };
+
+  f32x4 acc[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const Slot& S, int64_t d, bool tail) {
+    const int64_t kb = 2 * d;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      u32x4 c = S.c[g];
+      // lanes 0-31: (block kb words 0, 1 | words 2, 3) -> keep 0, 1, take the
+      // other half's 0, 1 into 2, 3; lanes 32-63 the mirror image.
+      const auto s02 = __builtin_amdgcn_permlane32_swap(c[0], c[2], false, false);
+      const auto s13 = __builtin_amdgcn_permlane32_swap(c[1], c[3], false, false);
+      c[0] = s02[0];
+      c[2] = s02[1];
+      c[1] = s13[0];
+      c[3] = s13[1];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        u32x4 w0, w1;
+        if (kPerm) {
+          w0 = levels8_perm(c[2 * h]);
+          w1 = levels8_perm(c[2 * h + 1]);
+        } else {
+          w0 = levels8_lut(c[2 * h], lut + i16);
+          w1 = levels8_lut(c[2 * h + 1], lut + i16);
+        }
+        f32x4 pb = mfma16(as_bf16x8(S.x[2 * h]), as_bf16x8(w0), f32x4{0.f, 0.f, 0.f, 0.f});
+        pb = mfma16(as_bf16x8(S.x[2 * h + 1]), as_bf16x8(w1), pb);
+        const float chat = (h && tail) ? 0.0f : crow_t[g][kb + h];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[g][v] += chat * pb[v];
+      }
+    }
+  };
+
+  const bool active = d0 < d1;  // the wave has full steps (uniform)
+  if (active) {
+#pragma unroll
+    for (int u = 0; u < PD - 1; ++u) issue(sl[u], d0 + u, false);
+  }
+  // Prologue, overlapping the first loads: the byte table, the block
+  // constants fl32(q8 * step) of rows n0 .. n0 + 16 G - 1, and the U sums of
+  // the partial slices written by the previous launch on this stream.  All
+  // of a thread's loads are issued before any is used (one latency).
+  if (!kPerm) {
+    for (int e = tid; e < kLutWords; e += NT) {
+      const int b = e >> 4;  // copy e % 16 of entry b
+      lut[e] = pack_bf16x2(level_f32(b & 15), level_f32(b >> 4));
+    }
+  }
+  {
+    // The workgroup's constants are the contiguous q8 range starting at
+    // n0 kblocks (a multiple of 16 bytes), 16 G kblocks bytes long; rows
+    // past N read clamped bytes (their results are dropped).
+    const int64_t qtot = N * kblocks, qbase = n0 * kblocks;
+    const int64_t nchunk = (16 * G * kblocks + 15) / 16;
+    for (int64_t c = tid; c < nchunk; c += NT) {
+      const int64_t o = qbase + 16 * c;
+      u32x4 qv;
+      if (o + 16 <= qtot) {
+        qv = *reinterpret_cast<const u32x4*>(p.q8 + o);
+      } else {
+        uint32_t b[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) b[i] = p.q8[o + i < qtot ? o + i : qtot - 1];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          qv[i] = b[4 * i] | (b[4 * i + 1] << 8) | (b[4 * i + 2] << 16) | (b[4 * i + 3] << 24);
+      }
+      const int64_t ng = (qtot + 255) >> 8;
+      const int64_t g0 = o >> 8 < ng ? o >> 8 : ng - 1;
+      const int64_t g1 = (o + 15) >> 8 < ng ? (o + 15) >> 8 : ng - 1;
+      const float st0 = p.step[g0], st1 = p.step[g1];
+      const int64_t split = (g0 + 1) << 8;  // first block of group g0 + 1
+      float cv[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        cv[i] = (float)((qv[i >> 2] >> (8 * (i & 3))) & 0xffu) * (o + i < split ? st0 : st1);
+      // element 16 c + i is block kb of table row `row`
+      int64_t row = (16 * c) / kblocks, kb = 16 * c - row * kblocks;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (row < 16 * G) chat_t[row * kbs + kb] = cv[i];
+        if (++kb == kblocks) {
+          kb = 0;
+          ++row;
+        }
+      }
+    }
+  }
+  {
+    const int64_t ur = (int64_t)M * p.r;
+    constexpr int kMaxSlices = 8;
+    for (int64_t e = tid; e < ur; e += NT) {
+      float v[kMaxSlices];
+#pragma unroll
+      for (int sp = 0; sp < kMaxSlices; ++sp)
+        v[sp] = p.upart[(int64_t)(sp < p.us ? sp : 0) * ur + e];
+      float u = 0.0f;
+#pragma unroll
+      for (int sp = 0; sp < kMaxSlices; ++sp)
+        if (sp < p.us) u += v[sp];
+      ush[e] = u;
+    }
+  }
+  __syncthreads();
+
+  // A ring of PD register slots keeps PD - 1 steps of loads in flight while
+  // a step is consumed.  Loads are counted in issue order, so codes and X
+  // fragments travel in the same slot, and the scheduling barriers keep each
+  // step's loads ahead of the arithmetic of the step before it: the wait
+  // before a step then covers that step's own loads only.
+  int64_t d = d0;
+  for (; d + PD <= d1; d += PD) {  // slots 0 .. PD-2 hold steps d .. d+PD-2 on entry
+#pragma unroll
+    for (int u = 0; u < PD; ++u) {
+      issue(sl[(u + PD - 1) % PD], d + u + PD - 1, false);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(sl[u], d + u, false);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < PD - 1; ++u)
+    if (d + u < d1) compute(sl[u], d + u, false);
+  if (odd_tail) {
+    issue(sl[PD - 1], T, true);
+    compute(sl[PD - 1], T, true);
+  }
+  __syncthreads();  // the constant table becomes the reduction buffer
+
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) red[((wave * G + g) * 4 + v) * 64 + lane] = acc[g][v];
+  __syncthreads();
+
+  for (int o = tid; o < G * 4 * 64; o += NT) {
+    const int l = o & 63, v = (o >> 6) & 3, g = o >> 8;
+    float y = 0.0f;
+#pragma unroll
+    for (int w = 0; w < KW; ++w) y += red[((w * G + g) * 4 + v) * 64 + l];
+    const int64_t m = 4 * (l >> 4) + v, n = n0 + 16 * g + (l & 15);
+    if (m < M && n < N) {
+      float lora = 0.0f;
+      const uint16_t* brw = p.B + n * p.r;
+      for (int j = 0; j < p.r; ++j) lora += ush[m * p.r + j] * bf16_to_f32(brw[j]);
+      p.Y[m * N + n] = f32_to_bf16(y + p.s * lora);
+    }
+  }
+  if (p.U_out && blockIdx.x == 0) {
+    for (int64_t e = tid; e < (int64_t)M * p.r; e += NT) p.U_out[e] = f32_to_bf16(ush[e]);
+  }
 }
 
 }  // namespace
 
-int gemv_splits(int64_t N, int64_t K) {
-  const int64_t tiles = (N + 63) / 64;
-  const int64_t kblocks = K / 64;
-  int64_t s = (768 + tiles - 1) / tiles;  // aim for ~3 workgroups per CU
-  const int64_t max_s = (kblocks + 7) / 8;  // keep >= 8 blocks per split
-  if (s > max_s) s = max_s;
+bool gemv_fits(int64_t M, int32_t r, int64_t K) {
+  // the workgroup's LDS within 96 KB (K up to about 24000 at rank 256)
+  return M <= kGemvMaxM && 4 * gemv_lds_words(2, 8, M, r, K / 64) <= 96 * 1024;
+}
+
+int gemv_lora_slices(int64_t K) {
+  // slices of at least 1024 columns, at most 8 of them (k_qgemv sums them)
+  int64_t s = K / 1024;
+  if (s > 8) s = 8;
   if (s < 1) s = 1;
   return (int)s;
 }
 
-hipError_t launch_qgemv_partial(const Nf4View& w, const uint16_t* X, int64_t M, int splits,
-                                float* part, hipStream_t stream) {
-  const int64_t kblocks = w.K / 64;
-  const int64_t bps = (kblocks + splits - 1) / splits;
-  dim3 grid((unsigned)((w.N + 63) / 64), (unsigned)splits);
-  hipLaunchKernelGGL(k_qgemv_partial, grid, dim3(256), 0, stream, w.codes, w.q8, w.step, X, M,
-                     w.N, w.K, bps, part);
-  return hipGetLastError();
+size_t gemv_workspace_bytes(int64_t M, int32_t r, int64_t K) {
+  return (size_t)gemv_lora_slices(K) * M * r * sizeof(float);
 }
 
-hipError_t launch_gemv_finish(const float* part, int splits, int64_t M, int64_t N,
-                              const uint16_t* U, int64_t ldu, const uint16_t* B, int32_t r,
-                              float s, uint16_t* Y, hipStream_t stream) {
-  const int64_t total = M * N;
-  hipLaunchKernelGGL(k_gemv_finish, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
-                     part, splits, M, N, U, ldu, B, r, s, Y);
-  return hipGetLastError();
+hipError_t launch_qgemv(const Nf4View& w, const uint16_t* X, int64_t M, const uint16_t* A,
+                        const uint16_t* B, int32_t r, float s, uint16_t* Y, uint16_t* U_out,
+                        float* upart, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+  const int us = gemv_lora_slices(w.K);
+  const int64_t slice = (w.K / us + 31) / 32 * 32;
+  dim3 gu((unsigned)((w.K + slice - 1) / slice), (unsigned)((r + 63) / 64));
+  hipLaunchKernelGGL(k_lora_down_part, gu, dim3(256), 0, stream, X, M, A, r, w.K, slice, upart);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
+  const GemvArgs a{w.codes, w.q8, w.step, X, M, w.N, w.K, upart, (int32_t)gu.x, B, r, s, Y, U_out};
+  // about 16 waves per CU: 16-row groups x K-splitting waves
+  const int64_t kblocks = w.K / 64;
+  constexpr int G = 2, PD = QN_GEMV_PD;
+  // dynamic LDS above the default 64 KB needs the limit raised, once
+  static const hipError_t attr = [] {
+    hipError_t a = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_qgemv<G, 4, PD, QN_GEMV_PERM>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
+    hipError_t b = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_qgemv<G, 8, PD, QN_GEMV_PERM>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
+    return a != hipSuccess ? a : b;
+  }();
+  if (attr != hipSuccess) return attr;
+  if (w.N >= 16384) {
+    constexpr int KW = 4;
+    const size_t lds = 4 * (size_t)gemv_lds_words(G, KW, M, r, kblocks);
+    hipLaunchKernelGGL((k_qgemv<G, KW, PD, QN_GEMV_PERM>), dim3((unsigned)((w.N + 16 * G - 1) / (16 * G))),
+                       dim3(64 * KW), lds, stream, a);
+  } else {
+    constexpr int KW = 8;
+    const size_t lds = 4 * (size_t)gemv_lds_words(G, KW, M, r, kblocks);
+    hipLaunchKernelGGL((k_qgemv<G, KW, PD, QN_GEMV_PERM>), dim3((unsigned)((w.N + 16 * G - 1) / (16 * G))),
+                       dim3(64 * KW), lds, stream, a);
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (ev1) e = hipEventRecord(ev1, stream);
+  return e;
 }
 
 }  // namespace qn

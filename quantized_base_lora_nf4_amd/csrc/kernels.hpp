@@ -33,14 +33,17 @@ hipError_t launch_qgemm_bwd(const Nf4View& w, const uint16_t* dY, int64_t M, con
 
 // ---- gemv.hip: bandwidth-bound forward for M <= 16 ----
 constexpr int kGemvMaxM = 16;
-// Partial sums part[S][M][N] (fp32) over S equal K ranges; returns S.
-int gemv_splits(int64_t N, int64_t K);
-hipError_t launch_qgemv_partial(const Nf4View& w, const uint16_t* X, int64_t M, int splits,
-                                float* part, hipStream_t stream);
-// Y[m,n] = sum_s part[s][m][n] + s * sum_j U[m][j] B[n][j]  (bf16 out)
-hipError_t launch_gemv_finish(const float* part, int splits, int64_t M, int64_t N,
-                              const uint16_t* U, int64_t ldu, const uint16_t* B, int32_t r,
-                              float s, uint16_t* Y, hipStream_t stream);
+// Whether launch_qgemv takes these sizes (its per-workgroup table of block
+// constants must fit in LDS: K up to about 24000 at rank 256).
+bool gemv_fits(int64_t M, int32_t r, int64_t K);
+// Workspace of launch_qgemv: fp32 partial sums of U = X A^T.
+size_t gemv_workspace_bytes(int64_t M, int32_t r, int64_t K);
+// Y = X W^T + s (X A^T) B^T for M <= kGemvMaxM, and bf16 U into U_out when
+// it is not null.  Two launches (U partial sums, then the weight stream);
+// ev0 / ev1 (nullable) are recorded around the second one.
+hipError_t launch_qgemv(const Nf4View& w, const uint16_t* X, int64_t M, const uint16_t* A,
+                        const uint16_t* B, int32_t r, float s, uint16_t* Y, uint16_t* U_out,
+                        float* upart, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
 
 // ---- lora.hip: small-rank products with in-kernel reduction of contraction slices ----
 // Operand element access: A-op (i, c) at a[i*a_si + c*a_sc]; B-op (c, j) at
