@@ -410,29 +410,16 @@ hipError_t launch_qgemv(const Nf4View& w, const uint16_t* X, int64_t M, const ui
   if (e != hipSuccess) return e;
   if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
   const GemvArgs a{w.codes, w.q8, w.step, X, M, w.N, w.K, upart, (int32_t)gu.x, B, r, s, Y, U_out};
-  // about 16 waves per CU: 16-row groups x K-splitting waves
   const int64_t kblocks = w.K / 64;
-  constexpr int G = 2, PD = QN_GEMV_PD;
-  // dynamic LDS above the default 64 KB needs the limit raised, once
-  static const hipError_t attr = [] {
-    hipError_t a = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_qgemv<G, 4, PD, QN_GEMV_PERM>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
-    hipError_t b = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_qgemv<G, 8, PD, QN_GEMV_PERM>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
-    return a != hipSuccess ? a : b;
-  }();
+  // 32 weight rows per workgroup, K split over its 8 waves
+  constexpr int G = 2, KW = 8, PD = QN_GEMV_PD;
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&k_qgemv<G, KW, PD, QN_GEMV_PERM>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);  // above the default 64 KB, once
   if (attr != hipSuccess) return attr;
-  if (w.N >= 16384) {
-    constexpr int KW = 4;
-    const size_t lds = 4 * (size_t)gemv_lds_words(G, KW, M, r, kblocks);
-    hipLaunchKernelGGL((k_qgemv<G, KW, PD, QN_GEMV_PERM>), dim3((unsigned)((w.N + 16 * G - 1) / (16 * G))),
-                       dim3(64 * KW), lds, stream, a);
-  } else {
-    constexpr int KW = 8;
-    const size_t lds = 4 * (size_t)gemv_lds_words(G, KW, M, r, kblocks);
-    hipLaunchKernelGGL((k_qgemv<G, KW, PD, QN_GEMV_PERM>), dim3((unsigned)((w.N + 16 * G - 1) / (16 * G))),
-                       dim3(64 * KW), lds, stream, a);
-  }
+  const size_t lds = 4 * (size_t)gemv_lds_words(G, KW, M, r, kblocks);
+  hipLaunchKernelGGL((k_qgemv<G, KW, PD, QN_GEMV_PERM>), dim3((unsigned)((w.N + 16 * G - 1) / (16 * G))),
+                     dim3(64 * KW), lds, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (ev1) e = hipEventRecord(ev1, stream);
