@@ -192,6 +192,216 @@ __global__ __launch_bounds__(256) void k_skinny(Launch L) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Vectorized path (every operand aligned, contiguous extents multiples of 8).
+// Each operand tile of a 64-deep step is staged in LDS in its natural layout
+// (16-byte chunks along the operand's contiguous dimension): [x][c] when the
+// contraction runs along memory, [c][x] when the output dimension does.  The
+// MFMA fragments are read directly from the first and with the transposing
+// LDS read (ds_read_b64_tr_b16) from the second, so no element is ever
+// scattered.  Loads run three steps ahead in a register ring; every load is
+// issued unconditionally (out-of-range chunks re-read the tile origin and
+// are zeroed when stored), so the compiler waits only for the step consumed.
+// ---------------------------------------------------------------------------
+constexpr int kRing = 3;
+
+struct VecSlot {
+  u32x4 a[2], b[2];
+};
+
+// The two 16-byte chunks of one operand tile that a thread moves each step.
+// Tile element (t, c) of natural row t: for a c-fast operand t is the output
+// index and the columns are the contraction; otherwise t is the contraction
+// index and the columns the output.  Chunk pointers advance by a fixed
+// amount per step; a chunk is valid while its output index is in range and
+// its contraction offset within the step is below the step's valid length.
+struct VecOp {
+  const uint16_t* ptr[2];  // chunk pointers at step 0 (the tile origin if out of range)
+  const uint16_t* src;
+  int64_t delta;           // per-step advance (elements)
+  int coff[2];             // contraction offset of each chunk within a step
+  bool xok[2];
+};
+
+template <bool kCFast>
+__device__ __forceinline__ VecOp vec_op(const uint16_t* src, int64_t rstride, int64_t x0, int64_t X,
+                                        int64_t cs, int tid) {
+  VecOp o;
+  o.src = src;
+  o.delta = kCFast ? kSkinnyStep : kSkinnyStep * rstride;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int e = tid + 256 * q, r = e >> 3, cc = (e & 7) * 8;
+    const int64_t x = kCFast ? x0 + r : x0 + cc;
+    o.xok[q] = x < X;
+    o.coff[q] = kCFast ? cc : r;
+    o.ptr[q] = o.xok[q] ? src + (kCFast ? x * rstride + cs + cc : (cs + r) * rstride + x) : src;
+  }
+  return o;
+}
+
+// clen: valid contraction length of this step (0 .. 64)
+__device__ __forceinline__ void vec_issue(u32x4 (&v)[2], const VecOp& o, int64_t step_off,
+                                          int clen) {
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const bool ok = o.xok[q] & (o.coff[q] < clen);
+    const uint16_t* pq = ok ? o.ptr[q] + step_off : o.src;
+    v[q] = *reinterpret_cast<const u32x4*>(pq);
+  }
+}
+
+__device__ __forceinline__ void vec_store(uint16_t* T, const u32x4 (&v)[2], const VecOp& o, int clen,
+                                          int tid) {
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int e = tid + 256 * q;
+    const bool ok = o.xok[q] & (o.coff[q] < clen);
+    *reinterpret_cast<u32x4*>(T + (e >> 3) * SLD + (e & 7) * 8) = ok ? v[q] : u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+// MFMA 32x32x16 fragment of sub-step kk: lane l gets output index base + l % 32
+// and contraction rows 16 kk + 8 (l / 32) .. +7.
+template <bool kCFast>
+__device__ __forceinline__ bf16x8 vec_frag(const uint16_t* T, int base, int lane, int kk) {
+  if (kCFast)
+    return *reinterpret_cast<const bf16x8*>(T + (base + (lane & 31)) * SLD + kk * 16 + (lane >> 5) * 8);
+  // [c][x]: within each 16-lane group g, lane i reads the 4-element chunk at
+  // row 8 (g / 2) + i / 4 (+4 for the upper half), column 16 (g % 2) + 4 (i % 4)
+  // and receives 4 consecutive rows of column i.
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  typedef short v8i16 __attribute__((ext_vector_type(8)));
+  typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+  const int g = lane >> 4, i = lane & 15;
+  const int row = kk * 16 + 8 * (g >> 1) + (i >> 2);
+  const int col = base + 16 * (g & 1) + 4 * (i & 3);
+  const uint16_t* p0 = T + row * SLD + col;
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p0);
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p0 + 4 * SLD));
+  const v8i16 v = v8i16{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+template <bool kACF, bool kBCF>
+__device__ __forceinline__ void lora_vec_body(const Prob& P, int local,
+                                              uint16_t (&Ts)[2][2][64 * SLD]) {
+  const SkinnyOp op = P.op;
+  const int splits = P.splits, tiles_j = P.tiles_j;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wi = wave >> 1, wj = wave & 1;
+  const int tile = local / splits, split = local % splits;
+  const int64_t i0 = (int64_t)(tile / tiles_j) * 64, j0 = (int64_t)(tile % tiles_j) * 64;
+  const int64_t cs = (int64_t)split * P.c_split;
+  int64_t ce = cs + P.c_split;
+  if (ce > op.C) ce = op.C;
+  // operand A (i, c) at a[i a_si + c a_sc], B (c, j) at b[j b_sj + c b_sc]
+  const VecOp oa = vec_op<kACF>(op.a, kACF ? op.a_si : op.a_sc, i0, op.I, cs, tid);
+  const VecOp ob = vec_op<kBCF>(op.b, kBCF ? op.b_sj : op.b_sc, j0, op.J, cs, tid);
+  const int64_t nsteps = ce > cs ? (ce - cs + kSkinnyStep - 1) / kSkinnyStep : 0;
+
+  VecSlot sl[kRing];
+  // valid contraction length of step st (64 except on a ragged last step)
+  auto step_len = [&](int64_t st) {
+    const int64_t rem = ce - cs - st * kSkinnyStep;
+    return rem >= kSkinnyStep ? kSkinnyStep : (int)rem;
+  };
+  auto issue = [&](VecSlot& S, int64_t st) {
+    if (st >= nsteps) st = nsteps - 1;  // past the end: re-read the last step
+    const int clen = step_len(st);
+    vec_issue(S.a, oa, st * oa.delta, clen);
+    vec_issue(S.b, ob, st * ob.delta, clen);
+  };
+  f32x16 acc = f32x16{};
+  auto consume = [&](const VecSlot& S, int64_t st) {
+    const int clen = step_len(st);
+    uint16_t* TA = Ts[st & 1][0];
+    uint16_t* TB = Ts[st & 1][1];
+    vec_store(TA, S.a, oa, clen, tid);
+    vec_store(TB, S.b, ob, clen, tid);
+    // LDS writes visible to the workgroup; loads stay in flight
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const bf16x8 a = vec_frag<kACF>(TA, wi * 32, lane, kk);
+      const bf16x8 b = vec_frag<kBCF>(TB, wj * 32, lane, kk);
+      acc = mfma32(a, b, acc);
+    }
+  };
+
+  if (nsteps > 0) {
+#pragma unroll
+    for (int u = 0; u < kRing - 1; ++u) issue(sl[u], u);
+  }
+  int64_t st = 0;
+  for (; st + kRing <= nsteps; st += kRing) {
+#pragma unroll
+    for (int u = 0; u < kRing; ++u) {
+      issue(sl[(u + kRing - 1) % kRing], st + u + kRing - 1);
+      consume(sl[u], st + u);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kRing - 1; ++u)
+    if (st + u < nsteps) consume(sl[u], st + u);
+
+  const int r32 = lane & 31;
+  const int tj = wj * 32 + r32;
+  if (splits == 1) {
+    const int64_t j = j0 + tj;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int64_t i = i0 + wi * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      if (i < op.I && j < op.J) put(P, i, j, acc[v]);
+    }
+    if (P.Jw > op.J && (tile % tiles_j) == tiles_j - 1) {
+      for (int e = tid; e < 64 * (int)(P.Jw - op.J); e += 256) {
+        const int64_t i = i0 + e / (P.Jw - op.J), j = op.J + e % (P.Jw - op.J);
+        if (i < op.I) P.out[i * P.o_si + j] = 0;
+      }
+    }
+  } else {
+    float* mine = P.part + ((int64_t)tile * splits + split) * 4096;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int ti = wi * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      mine[ti * 64 + tj] = acc[v];
+    }
+  }
+}
+
+// Operand layouts of up to two products (c-fast A, c-fast B for each).
+template <bool kA0, bool kB0, bool kA1, bool kB1>
+__global__ __launch_bounds__(256) void k_lora_vec(Launch L) {
+  __shared__ __attribute__((aligned(16))) uint16_t Ts[2][2][64 * SLD];  // [buffer][A, B]
+  if (L.nprob > 1 && (int)blockIdx.x >= L.p[1].wg_begin)
+    lora_vec_body<kA1, kB1>(L.p[1], (int)blockIdx.x - L.p[1].wg_begin, Ts);
+  else
+    lora_vec_body<kA0, kB0>(L.p[0], (int)blockIdx.x - L.p[0].wg_begin, Ts);
+}
+
+// Launch the vectorized kernel instance for the launch's operand layouts.
+hipError_t launch_lora_vec(const Launch& L, int wg, hipStream_t stream) {
+  auto cf = [&](int k, bool b) {
+    const SkinnyOp& o = L.p[k < L.nprob ? k : 0].op;
+    return b ? o.b_sc == 1 : o.a_sc == 1;
+  };
+  const int key = (cf(0, false) << 3) | (cf(0, true) << 2) | (cf(1, false) << 1) | cf(1, true);
+  switch (key) {
+#define QN_LORA_CASE(k)                                                                       \
+  case k:                                                                                     \
+    hipLaunchKernelGGL((k_lora_vec<(k >> 3) & 1, (k >> 2) & 1, (k >> 1) & 1, k & 1>),         \
+                       dim3((unsigned)wg), dim3(256), 0, stream, L);                          \
+    break;
+    QN_LORA_CASE(0) QN_LORA_CASE(1) QN_LORA_CASE(2) QN_LORA_CASE(3)
+    QN_LORA_CASE(4) QN_LORA_CASE(5) QN_LORA_CASE(6) QN_LORA_CASE(7)
+    QN_LORA_CASE(8) QN_LORA_CASE(9) QN_LORA_CASE(10) QN_LORA_CASE(11)
+    QN_LORA_CASE(12) QN_LORA_CASE(13) QN_LORA_CASE(14) QN_LORA_CASE(15)
+#undef QN_LORA_CASE
+  }
+  return hipGetLastError();
+}
+
 // Second launch for products with several slices: four consecutive outputs
 // of one tile row per thread; slices added in order.
 __global__ __launch_bounds__(256) void k_skinny_finish(Launch L) {
@@ -289,11 +499,13 @@ hipError_t launch_skinny(const SkinnyJob* jobs, int njobs, hipStream_t stream) {
   }
   bool all_vec = true;
   for (int k = 0; k < njobs; ++k) all_vec = all_vec && L.p[k].a_vec && L.p[k].b_vec;
-  if (all_vec)
-    hipLaunchKernelGGL(k_skinny<true>, dim3((unsigned)wg), dim3(256), 0, stream, L);
-  else
+  hipError_t e;
+  if (all_vec) {
+    e = launch_lora_vec(L, wg, stream);
+  } else {
     hipLaunchKernelGGL(k_skinny<false>, dim3((unsigned)wg), dim3(256), 0, stream, L);
-  hipError_t e = hipGetLastError();
+    e = hipGetLastError();
+  }
   if (e != hipSuccess) return e;
   // finish launch for the products with several slices: 4 quads of 1024 per tile
   Launch F{};
