@@ -35,8 +35,11 @@ HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E, published
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--events-every", type=int, default=2,
+                    help="record the kernel events on every n-th timed step (the event "
+                         "records themselves cost a few microseconds of stream time)")
     ap.add_argument("--workload", default="llama7b_q_up_M4096_r64")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
@@ -163,7 +166,8 @@ def main():
 
     def step(i):
         for t in layers:
-            e = t["ev"][i] if i is not None else [None] * 4
+            timed = i is not None and i % args.events_every == 0
+            e = t["ev"][i] if timed else [None] * 4
             check(L.qlora_linear_fwd_ev(ctypes.byref(t["st"]), p(t["X"]), M, p(t["A"]), p(t["B"]), r,
                                         s, p(t["Y"]), p(t["U"]), p(t["wsf"]), t["wsf"].numel(), sp,
                                         e[0], e[1]), "fwd")
@@ -191,12 +195,21 @@ def main():
     ms_step = ms_total / args.steps
 
     kt = {"fwd": [0.0, 0], "bwd": [0.0, 0]}  # summed kernel time (ms), launches
+    per_launch = {"fwd": [], "bwd": []}      # per layer and step (us)
     for t in layers:
-        for e in t["ev"]:
-            kt["fwd"][0] += ev.elapsed_ms(e[0], e[1])
+        lf, lb = [], []
+        for i, e in enumerate(t["ev"]):
+            if i % args.events_every:
+                continue
+            f_ms, b_ms = ev.elapsed_ms(e[0], e[1]), ev.elapsed_ms(e[2], e[3])
+            kt["fwd"][0] += f_ms
             kt["fwd"][1] += 1
-            kt["bwd"][0] += ev.elapsed_ms(e[2], e[3])
+            kt["bwd"][0] += b_ms
             kt["bwd"][1] += 1
+            lf.append(f_ms * 1e3)
+            lb.append(b_ms * 1e3)
+        per_launch["fwd"].append(lf)
+        per_launch["bwd"].append(lb)
 
     flops_step = 0.0
     flops_fwd_kernel = 0.0
@@ -225,7 +238,13 @@ def main():
         "traffic": load_traffic(dom, wl.name, src_hash),
         "avg_launch_us": round(dom_us, 1),
         "other": {"k_qgemm_fwd": {"TFLOP/s": round(fwd_tf, 1), "ms_per_step": round(fwd_ms, 4)},
-                  "k_qgemm_bwd": {"TFLOP/s": round(bwd_tf, 1), "ms_per_step": round(bwd_ms, 4)}},
+                  "k_qgemm_bwd": {"TFLOP/s": round(bwd_tf, 1), "ms_per_step": round(bwd_ms, 4)},
+                  "launch_us_p10_p50_p90": {
+                      f"{kn} {t['spec'].name}": [round(float(np.percentile(v, q)), 1)
+                                                for q in (10, 50, 90)]
+                      for kn, key in (("k_qgemm_fwd", "fwd"), ("k_qgemm_bwd", "bwd"))
+                      for t, v in zip(layers, per_launch[key])},
+                  "events_on_every_nth_step": args.events_every},
     }
 
     extra = {}

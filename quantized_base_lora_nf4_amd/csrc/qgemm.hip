@@ -123,14 +123,15 @@ __device__ __forceinline__ int a_off(int r, int c) { return r * 64 + ((c ^ ((r >
 
 // Direct global -> LDS load of a BM x 64 bf16 tile of a row-major matrix
 // (row stride ld, columns c0..c0+63; rows past `rows` clamp to the last row,
-// columns at or past `cols` are replaced by column 0 of the same row and must
-// be zeroed by the caller's data layout, see below).  Each wave instruction
-// fills 8 consecutive tile rows (1 KB); lane l writes row 8 e + l / 8, slot
-// l % 8, so it fetches the chunk that the swizzle puts in that slot.
-template <class C>
+// and a 16-byte chunk at or past column `cols` (a multiple of 8) re-reads
+// column 0 of its row: the caller multiplies those columns by zero weights).
+// Each wave instruction fills 8 consecutive tile rows (1 KB); lane l writes
+// row 8 e + l / 8, slot l % 8, so it fetches the chunk that the swizzle puts
+// in that slot.
+template <class C, bool kClampCols>
 __device__ __forceinline__ void load_rows_lds(uint16_t* As, const uint16_t* src, int64_t ld,
-                                              int64_t row0, int64_t rows, int64_t c0, int wave,
-                                              int lane) {
+                                              int64_t row0, int64_t rows, int64_t c0, int64_t cols,
+                                              int wave, int lane) {
 #pragma unroll
   for (int q = 0; q < C::XLD; ++q) {
     const int e = q * (C::NT / 64) + wave;  // 8-row group
@@ -138,13 +139,32 @@ __device__ __forceinline__ void load_rows_lds(uint16_t* As, const uint16_t* src,
     const int c = (lane & 7) ^ ((r >> 1) & 7);
     int64_t gr = row0 + r;
     if (gr >= rows) gr = rows - 1;
-    __builtin_amdgcn_global_load_lds((const void*)(src + gr * ld + c0 + c * 8),
+    int64_t gc = c0 + c * 8;
+    if (kClampCols && gc >= cols) gc = 0;
+    __builtin_amdgcn_global_load_lds((const void*)(src + gr * ld + gc),
                                      (__attribute__((address_space(3))) void*)(As + 8 * e * 64),
                                      16, 0, 0);
   }
 }
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// End of a pipelined step: this wave's direct-to-LDS tile loads (issued
+// first in the step) and LDS writes are complete, then the workgroup
+// barrier.  The step's kWLoads weight loads (issued after the tile loads)
+// stay in flight into the next step, where they are consumed; vector memory
+// loads complete in issue order, so vmcnt(kWLoads) covers the tile loads.
+// The wait is issued through the builtin (s_waitcnt simm16: vmcnt in bits
+// 3:0, expcnt 6:4, lgkmcnt 11:8) so that the compiler's own wait tracking
+// knows the tile loads are complete; the empty asm statements keep memory
+// operations from moving across it.
+constexpr int kWLoads = 3;  // codes (one 16-byte load), q8 byte, step
+__device__ __forceinline__ void step_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0070 | kWLoads);  // vmcnt(kWLoads) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 template <class C>
 struct AccT {
@@ -243,40 +263,6 @@ __device__ __forceinline__ void store_tile(uint16_t* out, int64_t ld, int64_t ro
     }
 }
 
-// Global -> register loader for a BM x 64 bf16 tile of a row-major matrix
-// (row stride ld, columns c0..c0+63; rows past `rows` clamp to the last row,
-// columns at or past `cols` read as zero; cols is a multiple of 8).
-template <class C>
-struct RowTileRegs {
-  u32x4 v[C::XCH];
-};
-
-template <class C>
-__device__ __forceinline__ void load_rows(RowTileRegs<C>& r, const uint16_t* src, int64_t ld,
-                                          int64_t row0, int64_t rows, int64_t c0, int64_t cols,
-                                          int tid) {
-#pragma unroll
-  for (int q = 0; q < C::XCH; ++q) {
-    const int e = tid + C::NT * q;
-    int64_t gr = row0 + (e >> 3);
-    if (gr >= rows) gr = rows - 1;
-    int64_t c = c0 + (e & 7) * 8;
-    const bool ok = c < cols;
-    if (!ok) c = 0;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(src + gr * ld + c);
-    r.v[q] = ok ? v : u32x4{0u, 0u, 0u, 0u};
-  }
-}
-
-template <class C>
-__device__ __forceinline__ void store_rows(uint16_t* As, const RowTileRegs<C>& r, int tid) {
-#pragma unroll
-  for (int q = 0; q < C::XCH; ++q) {
-    const int e = tid + C::NT * q;
-    *reinterpret_cast<u32x4*>(As + a_off(e >> 3, e & 7)) = r.v[q];
-  }
-}
-
 // Stage a BM x 64 tile of a zero-padded bf16 matrix whose columns
 // c0..c0+63 all exist (row stride a multiple of 8), scaling each element by
 // `scale` in fp32 and rounding back to bf16 when do_scale is set.
@@ -305,13 +291,14 @@ __device__ __forceinline__ void stage_rows_scaled(uint16_t* As, const uint16_t* 
 template <class C>
 struct StepRegs {
   u32x4 c[C::WPT / 32];
-  uint32_t q;
+  uint32_t q;   // 8-bit constant as loaded
+  uint32_t qm;  // ~0, or 0 for weight rows past N (their values become 0)
   float st;
 };
 
 template <class C>
 __device__ __forceinline__ void dequant_codes(uint16_t* dst, const StepRegs<C>& r) {
-  const LevelTable t = make_table((float)r.q * r.st);
+  const LevelTable t = make_table((float)(r.q & r.qm) * r.st);
 #pragma unroll
   for (int h = 0; h < C::WPT / 32; ++h)
 #pragma unroll
@@ -334,7 +321,7 @@ __device__ __forceinline__ void step_interleaved(const uint16_t* As, const uint1
   (void)As_n;
   Frags<C> f[2];
   read_frags<C, kTransB>(f[0], As, Bs, wm, wn, lane, 0);
-  const LevelTable t = make_table((float)rn.q * rn.st);
+  const LevelTable t = make_table((float)(rn.q & rn.qm) * rn.st);
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
     if (kk < 3) read_frags<C, kTransB>(f[(kk + 1) & 1], As, Bs, wm, wn, lane, kk + 1);
@@ -400,12 +387,16 @@ __global__ __launch_bounds__(C::NT, 1) void k_qgemm_fwd(FwdArgs p) {
       r.c[h] = *reinterpret_cast<const u32x4*>(wcodes + kt * 32 + 16 * h);
     const int64_t blk = wblk0 + kt;
     r.q = p.q8[blk];
+    r.qm = ~0u;
     r.st = p.step[blk >> 8];
   };
   auto load_x = [&](uint16_t* As_dst, int64_t kt) {
     if (kt >= kblocks) kt = kblocks - 1;
-    load_rows_lds<C>(As_dst, p.X, K, m0, M, kt * BK, wave, lane);
+    load_rows_lds<C, false>(As_dst, p.X, K, m0, M, kt * BK, K, wave, lane);  // K % 64 == 0
   };
+  // (Measured: keeping the weight loads in flight across the barrier, as
+  // the backward kernel does, is slower here; the forward step waits for
+  // all of its loads.)
   auto body = [&](StepRegs<C>& rnext, StepRegs<C>& rload, int64_t kt, int cur) {
     const uint16_t* As = smem + cur * (C::TILE_A + C::TILE_BF);
     uint16_t* As_n = smem + (cur ^ 1) * (C::TILE_A + C::TILE_BF);
@@ -513,45 +504,40 @@ __global__ __launch_bounds__(C::NT, 1) void k_qgemm_bwd(BwdArgs p) {
   AccT<C> acc;
   zero_acc(acc);
   StepRegs<C> ra, rb;
+  // Rows past N get constant 0 (their dequantized values are +-0, so the
+  // dY columns they meet add nothing); columns past K are computed from
+  // clamped codes and dropped on store.  Every load is unconditional.
   auto load_w = [&](StepRegs<C>& r, int64_t ns) {
     if (ns >= nsteps) ns = nsteps - 1;
-    int64_t n = ns * BK + wr;
-    const bool ok = n < N && kvalid;
-    if (!ok) n = 0;
-    const uint8_t* src = p.codes + ((n * K + (ok ? kcol : 0)) >> 1) + wh * (WPTB / 2);
+    const int64_t n = ns * BK + wr;
+    const bool nok = n < N;
+    const int64_t nc = nok ? n : 0, kc = kvalid ? kcol : 0;
+    const uint8_t* src = p.codes + ((nc * K + kc) >> 1) + wh * (WPTB / 2);
 #pragma unroll
-    for (int h = 0; h < WPTB / 32; ++h) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(src + 16 * h);
-      r.c[h] = ok ? v : u32x4{0u, 0u, 0u, 0u};
-    }
-    const int64_t blk = n * kblocks + ((ok ? kcol : 0) >> 6);
-    const uint32_t q = p.q8[blk];
-    r.q = ok ? q : 0u;  // rows past N contribute +-0
+    for (int h = 0; h < WPTB / 32; ++h) r.c[h] = *reinterpret_cast<const u32x4*>(src + 16 * h);
+    const int64_t blk = nc * kblocks + (kc >> 6);
+    r.q = p.q8[blk];
+    r.qm = nok ? ~0u : 0u;
     r.st = p.step[blk >> 8];
   };
-  // dY columns past N (a partial last step) must read as zero: those steps
-  // take the register path, which zero-fills; every other step is loaded
-  // straight into LDS.
+  // dY tile of step ns straight into LDS; on a partial last step the chunks
+  // past column N re-read column 0 and meet the zero rows above.
   auto load_x = [&](uint16_t* As_dst, int64_t ns) {
     if (ns >= nsteps) ns = nsteps - 1;
-    if ((ns + 1) * BK <= N) {
-      load_rows_lds<C>(As_dst, p.dY, N, m0, M, ns * BK, wave, lane);
-    } else {
-      RowTileRegs<C> dr;
-      load_rows(dr, p.dY, N, m0, M, ns * BK, N, tid);
-      store_rows<C>(As_dst, dr, tid);
-    }
+    load_rows_lds<C, true>(As_dst, p.dY, N, m0, M, ns * BK, N, wave, lane);
   };
+  static_assert(WPTB / 32 + 2 == kWLoads, "weight loads per step");
   auto body = [&](StepRegs<C>& rnext, StepRegs<C>& rload, int64_t ns, int cur) {
     const uint16_t* As = smem + cur * (C::TILE_A + C::TILE_BB);
     uint16_t* As_n = smem + (cur ^ 1) * (C::TILE_A + C::TILE_BB);
-    load_x(As_n, ns + 1);
-    load_w(rload, ns + 2);
+    load_x(As_n, ns + 1);    // tile loads first ...
+    __builtin_amdgcn_sched_barrier(0);
+    load_w(rload, ns + 2);   // ... then the weight loads, which outlive the step
+    __builtin_amdgcn_sched_barrier(0);
     step_interleaved<C, true>(As, As + C::TILE_A, As_n,
                               As_n + C::TILE_A + wr * C::LDTB + wb * C::BSTR + wh * WPTB, rnext,
                               wm, wn, lane, acc);
-    wait_vmem();
-    __syncthreads();
+    step_barrier();
   };
 
   load_w(ra, 0);
