@@ -286,7 +286,26 @@ def run_extras(qn, L, ev, torch, dev, sp, d16):
     from the 256 MB Infinity Cache."""
     from quantized_base_lora_nf4_amd._lib import check
     import workloads as wl_mod
-    res = {"gemv": [], "quantize": []}
+    res = {"gemv": [], "quantize": [], "copy": None}
+    # measured streaming reference next to the 8 TB/s spec: a plain 1 GiB
+    # device copy (reads 1 GiB, writes 1 GiB; larger than the Infinity Cache)
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    c0 = torch.cuda.Event(enable_timing=True)
+    c1 = torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    c1.record()
+    torch.cuda.synchronize()
+    cms = c0.elapsed_time(c1) / 5
+    res["copy"] = {"bytes_read_plus_written": 2 << 30, "us": round(cms * 1e3, 1),
+                   "GB/s": round((2 << 30) / (cms * 1e-3) / 1e9, 1)}
+    del src, dst
+    torch.cuda.empty_cache()
     g = wl_mod.SKINNY_GEMV
     e0, e1, a0, a1 = ev.create(), ev.create(), ev.create(), ev.create()
     for wi, spec in enumerate(g.weights):
