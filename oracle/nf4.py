@@ -17,6 +17,14 @@ What the pages fix, and where:
 * The base is quantized once and dequantized to 16 bits on every forward and
   backward pass (blog section "Where the memory goes").
 
+FP4, the other data type the capability page "Qlora 4 Bit Quantization With
+Nf4 Fp4 Data Types And Lora Adapters" names in its title (and the plain
+4-bit float NF4 is compared against in the blog section "NormalFloat, double
+quantization, paged optimizers"), goes through the same blockwise absmax,
+double quantization and storage; only the 16 values behind the codes differ.
+The pages give no bit layout for it; it is read as the E2M1 format (see
+``fp4_values``).
+
 Readings taken where the pages are silent (each is listed in the design
 notes): level offset delta = 1 - (1/30 + 1/32)/2 with 7 negative levels, an
 exact zero and 8 positive levels; blocks of 64 consecutive row-major
@@ -99,6 +107,47 @@ def nf4_levels() -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
+# FP4 (E2M1) values
+# --------------------------------------------------------------------------
+
+def fp4_values_f64() -> np.ndarray:
+    """The value of each 4-bit FP4 code, in code order, in fp64.
+
+    Reading of "fp4" (the pages name the type without a layout): the E2M1
+    format.  Bit 3 is the sign, bits 2..1 an exponent e with bias 1, bit 0 a
+    mantissa bit m.  e = 0 is subnormal, m / 2; otherwise 2^(e-1) (1 + m/2).
+    The magnitudes are then 0, 1/2, 1, 3/2, 2, 3, 4, 6; they are divided by
+    6 so that the largest is 1, like the NF4 levels, since a block is scaled
+    by its absmax.  Code 8 is -0.
+    """
+    out = []
+    for code in range(16):
+        sign = -1.0 if code & 8 else 1.0
+        e = (code >> 1) & 3
+        m = code & 1
+        mag = m / 2.0 if e == 0 else 2.0 ** (e - 1) * (1.0 + m / 2.0)
+        out.append(sign * mag / 6.0)
+    return np.array(out, dtype=np.float64)
+
+
+def fp4_values() -> np.ndarray:
+    """The FP4 values rounded once to fp32 (round to nearest even)."""
+    return fp4_values_f64().astype(np.float32)
+
+
+CODE_TYPES = ("nf4", "fp4")
+
+
+def code_values(code: str = "nf4") -> np.ndarray:
+    """fp32 value of each of the 16 codes of a code type, in code order."""
+    if code == "nf4":
+        return nf4_levels()
+    if code == "fp4":
+        return fp4_values()
+    raise ValueError(f"unknown code type {code!r}")
+
+
+# --------------------------------------------------------------------------
 # bf16 helpers
 # --------------------------------------------------------------------------
 
@@ -156,6 +205,17 @@ def nearest_level(x: np.ndarray, levels_f32: np.ndarray) -> np.ndarray:
         with ThreadPoolExecutor(nthreads) as ex:
             list(ex.map(work, starts))
     return out
+
+
+def nearest_code(x: np.ndarray, values_f32: np.ndarray) -> np.ndarray:
+    """Code whose value is nearest to each fp32 x, for values in any code
+    order: ties go to the lower value, and of two codes with the same value
+    (FP4's +0 and -0) the lower code is taken.  The codes are put in
+    ascending order of (value, code) and ``nearest_level`` picks in that
+    order; for the ascending NF4 levels this is ``nearest_level`` itself."""
+    v = np.asarray(values_f32, dtype=np.float32)
+    order = np.lexsort((np.arange(v.size), v.astype(np.float64)))
+    return order[nearest_level(x, v[order])].astype(np.uint8)
 
 
 def block_absmax(W: np.ndarray, blocksize: int = BLOCKSIZE) -> np.ndarray:
@@ -219,16 +279,17 @@ def double_quantize(c: np.ndarray, dq_blocksize: int = DQ_BLOCKSIZE):
     return q, step
 
 
-def quantize(W: np.ndarray, blocksize: int = BLOCKSIZE, dq_blocksize: int = DQ_BLOCKSIZE):
-    """Full NF4 + double-quant encoding of W [N, K] fp32.
+def quantize(W: np.ndarray, blocksize: int = BLOCKSIZE, dq_blocksize: int = DQ_BLOCKSIZE,
+             code: str = "nf4"):
+    """Full 4-bit (NF4 by default, or FP4) + double-quant encoding of W
+    [N, K] fp32.
 
     Returns (codes uint8 [N*K/2], q8 uint8 [N*K/64], step fp32
     [ceil(N*K/64/256)]).
     """
-    levels = nf4_levels()
     c = block_absmax(W, blocksize)
     x = normalize(W, c, blocksize)
-    codes = nearest_level(x, levels)
+    codes = nearest_code(x, code_values(code))
     packed = pack_codes(codes)
     q8, step = double_quantize(c, dq_blocksize)
     return packed, q8, step
@@ -241,18 +302,20 @@ def dequant_constants(q8: np.ndarray, step: np.ndarray, dq_blocksize: int = DQ_B
     return (q8.astype(np.float32) * np.asarray(step, dtype=np.float32)[g]).astype(np.float32)
 
 
-def dequantize_f32(packed, q8, step, N, K, blocksize=BLOCKSIZE, dq_blocksize=DQ_BLOCKSIZE) -> np.ndarray:
-    """fl32(level[code] * c_hat_b) as fp32 [N, K], before the bf16 rounding."""
-    levels = nf4_levels()
+def dequantize_f32(packed, q8, step, N, K, blocksize=BLOCKSIZE, dq_blocksize=DQ_BLOCKSIZE,
+                   code="nf4") -> np.ndarray:
+    """fl32(value[code] * c_hat_b) as fp32 [N, K], before the bf16 rounding."""
+    levels = code_values(code)
     codes = unpack_codes(packed)
     chat = dequant_constants(q8, step, dq_blocksize)
     vals = levels[codes].reshape(-1, blocksize) * chat[:, None]
     return vals.astype(np.float32).reshape(N, K)
 
 
-def dequantize(packed, q8, step, N, K, blocksize=BLOCKSIZE, dq_blocksize=DQ_BLOCKSIZE) -> np.ndarray:
+def dequantize(packed, q8, step, N, K, blocksize=BLOCKSIZE, dq_blocksize=DQ_BLOCKSIZE,
+               code="nf4") -> np.ndarray:
     """The dequantized weight W_hat as bf16 bit patterns [N, K] (uint16)."""
-    return f32_to_bf16_bits(dequantize_f32(packed, q8, step, N, K, blocksize, dq_blocksize))
+    return f32_to_bf16_bits(dequantize_f32(packed, q8, step, N, K, blocksize, dq_blocksize, code))
 
 
 def storage_bytes(N: int, K: int, blocksize=BLOCKSIZE, dq_blocksize=DQ_BLOCKSIZE) -> int:

@@ -2,7 +2,7 @@
 Test infrastructure only.
 
 It follows the same steps as :mod:`oracle.nf4` (blockwise absmax, divide,
-nearest level with ties to the lower index, pack, double quantization,
+nearest code value with ties to the lower value, pack, double quantization,
 dequantization) one element at a time, with no numpy in the arithmetic.
 Python floats are fp64; fp32 results are obtained by rounding the fp64 result
 of one operation on fp32 operands to fp32.  For a single division or
@@ -54,9 +54,12 @@ def bf16_bits(x: float) -> int:
 
 
 def quantize(W, levels, blocksize=64, dq_blocksize=256):
-    """W: list of rows (lists of fp32-representable floats).  levels: 16
-    fp32-representable floats, ascending.  Returns (codes bytes, q8 list,
-    step list)."""
+    """W: list of rows (lists of fp32-representable floats).  levels: the 16
+    fp32-representable code values in code order (ascending for NF4; for
+    FP4 the E2M1 order, with +0 and -0).  Each element gets the code of the
+    nearest value; a tie between two values goes to the lower value, and
+    two codes with the same value to the lower code.  Returns (codes bytes,
+    q8 list, step list)."""
     flat = [float(v) for row in W for v in row]
     n = len(flat)
     assert n % blocksize == 0
@@ -75,7 +78,7 @@ def quantize(W, levels, blocksize=64, dq_blocksize=256):
             best, bestd = 0, None
             for i, lv in enumerate(levels):
                 d = abs(x - lv)
-                if bestd is None or d < bestd:
+                if bestd is None or d < bestd or (d == bestd and lv < levels[best]):
                     best, bestd = i, d
             codes.append(best)
     packed = bytes(codes[2 * j] | (codes[2 * j + 1] << 4) for j in range(n // 2))
