@@ -250,6 +250,8 @@ def main():
     extra = {}
     if not args.no_extra:
         extra = run_extras(qn, L, ev, torch, dev, sp, d16)
+        extra["fp4"] = fp4_step(qn, L, torch, layers, M, r, s, sp, args.steps, args.warmup,
+                                flops_step)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -278,6 +280,40 @@ def main():
         "extra": extra,
     }
     print(json.dumps(out), flush=True)
+
+
+def fp4_step(qn, L, torch, layers, M, r, s, sp, steps, warmup, flops_step):
+    """The same fused forward + backward step with the weights quantized to
+    the FP4 code type instead of NF4 (same kernels, other code table)."""
+    from quantized_base_lora_nf4_amd._lib import check
+    fp4 = [qn.nf4_quantize(t["Wf32"], code="fp4") for t in layers]
+    sts = [w.struct() for w in fp4]
+
+    def p(x):
+        return x.data_ptr() if x is not None else None
+
+    def one():
+        for t, st in zip(layers, sts):
+            check(L.qlora_linear_fwd(ctypes.byref(st), p(t["X"]), M, p(t["A"]), p(t["B"]), r, s,
+                                     p(t["Y"]), p(t["U"]), p(t["wsf"]), t["wsf"].numel(), sp),
+                  "fp4 fwd")
+            check(L.qlora_linear_bwd(ctypes.byref(st), p(t["X"]), p(t["dY"]), M, p(t["A"]),
+                                     p(t["B"]), p(t["U"]), r, s, p(t["dX"]), p(t["dA"]),
+                                     p(t["dB"]), p(t["wsb"]), t["wsb"].numel(), sp), "fp4 bwd")
+    for _ in range(warmup):
+        one()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        one()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    del fp4
+    return {"code": "fp4 (E2M1 / 6)", "ms_per_step": round(ms, 4),
+            "TFLOP/s": round(flops_step / (ms * 1e-3) / 1e12, 2), "steps": steps}
 
 
 def run_extras(qn, L, ev, torch, dev, sp, d16):
@@ -334,45 +370,68 @@ def run_extras(qn, L, ev, torch, dev, sp, d16):
                                 "GB/s": round((4 * N * K + wbytes) / (qms * 1e-3) / 1e9, 1)})
         A, B = d16(inp.A), d16(inp.B)
         for M in g.M:
-            X = d16(inp.X[:M])
-            Y = torch.empty(M, N, dtype=torch.int16, device=dev)
-            ws = torch.empty(qn.workspace_size(M, N, K, g.r, False), dtype=torch.uint8, device=dev)
-            it, warm = 60, 6
-            kern, call = [], []
-            for i in range(it + warm):
-                st = structs[i % ncopy]
-                check(L.qlora_linear_fwd_ev(ctypes.byref(st), X.data_ptr(), M, A.data_ptr(),
-                                            B.data_ptr(), g.r, g.s, Y.data_ptr(), None,
-                                            ws.data_ptr(), ws.numel(), sp, e0, e1), "gemv")
-                torch.cuda.synchronize()
-                if i >= warm:
-                    kern.append(ev.elapsed_ms(e0, e1))
-            # whole call (all launches) on the stream
-            for i in range(it + warm):
-                st = structs[i % ncopy]
-                L.qlora_linear_fwd_ev(ctypes.byref(st), X.data_ptr(), M, A.data_ptr(), B.data_ptr(),
-                                      g.r, g.s, Y.data_ptr(), None, ws.data_ptr(), ws.numel(), sp,
-                                      None, None)
-                if i == warm - 1:
-                    torch.cuda.synchronize()
-                    c0 = torch.cuda.Event(enable_timing=True)
-                    c0.record()
-            c1 = torch.cuda.Event(enable_timing=True)
-            c1.record()
-            torch.cuda.synchronize()
-            call_ms = c0.elapsed_time(c1) / it
-            k_ms = float(np.median(kern))
-            res["gemv"].append({
-                "weight": f"{N}x{K}", "M": M, "r": g.r,
-                "kernel_us": round(k_ms * 1e3, 2),
-                "kernel_GB/s": round(wbytes / (k_ms * 1e-3) / 1e9, 1),
-                "kernel_frac_hbm": round(wbytes / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-                "call_us": round(call_ms * 1e3, 2),
-                "call_GB/s": round(wbytes / (call_ms * 1e-3) / 1e9, 1),
-                "weight_bytes": wbytes, "copies_rotated": ncopy})
+            res["gemv"].append(_time_gemv(L, torch, ev, structs, inp, M, N, K, g, A, B, d16, dev,
+                                          sp, wbytes, e0, e1))
+        if wi == 0:
+            # the FP4 code type on the same kernel, one token
+            del copies, structs
+            torch.cuda.empty_cache()
+            copies = [qn.nf4_quantize(W, code="fp4") for _ in range(ncopy)]
+            structs = [c.struct() for c in copies]
+            row = _time_gemv(L, torch, ev, structs, inp, 1, N, K, g, A, B, d16, dev, sp, wbytes,
+                             e0, e1)
+            row["code"] = "fp4"
+            res["gemv_fp4"] = [row]
         del copies, W
         torch.cuda.empty_cache()
     return res
+
+
+def _time_gemv(L, torch, ev, structs, inp, M, N, K, g, A, B, d16, dev, sp, wbytes, e0, e1):
+    """Few-token forward on rotated weight copies: the weight-streaming
+    kernel alone (events around its launch) and the whole call."""
+    from quantized_base_lora_nf4_amd._lib import check
+    ncopy = len(structs)
+    X = d16(inp.X[:M])
+    Y = torch.empty(M, N, dtype=torch.int16, device=dev)
+    ws = torch.empty(qn_ws(L, M, N, K, g.r), dtype=torch.uint8, device=dev)
+    it, warm = 60, 6
+    kern = []
+    for i in range(it + warm):
+        st = structs[i % ncopy]
+        check(L.qlora_linear_fwd_ev(ctypes.byref(st), X.data_ptr(), M, A.data_ptr(),
+                                    B.data_ptr(), g.r, g.s, Y.data_ptr(), None,
+                                    ws.data_ptr(), ws.numel(), sp, e0, e1), "gemv")
+        torch.cuda.synchronize()
+        if i >= warm:
+            kern.append(ev.elapsed_ms(e0, e1))
+    # whole call (all launches) on the stream
+    for i in range(it + warm):
+        st = structs[i % ncopy]
+        L.qlora_linear_fwd_ev(ctypes.byref(st), X.data_ptr(), M, A.data_ptr(), B.data_ptr(),
+                              g.r, g.s, Y.data_ptr(), None, ws.data_ptr(), ws.numel(), sp,
+                              None, None)
+        if i == warm - 1:
+            torch.cuda.synchronize()
+            c0 = torch.cuda.Event(enable_timing=True)
+            c0.record()
+    c1 = torch.cuda.Event(enable_timing=True)
+    c1.record()
+    torch.cuda.synchronize()
+    call_ms = c0.elapsed_time(c1) / it
+    k_ms = float(np.median(kern))
+    return {
+        "weight": f"{N}x{K}", "M": M, "r": g.r,
+        "kernel_us": round(k_ms * 1e3, 2),
+        "kernel_GB/s": round(wbytes / (k_ms * 1e-3) / 1e9, 1),
+        "kernel_frac_hbm": round(wbytes / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "call_us": round(call_ms * 1e3, 2),
+        "call_GB/s": round(wbytes / (call_ms * 1e-3) / 1e9, 1),
+        "weight_bytes": wbytes, "copies_rotated": ncopy}
+
+
+def qn_ws(L, M, N, K, r):
+    return int(L.qlora_workspace_size(M, N, K, r, 0))
 
 
 def cpu_baseline(host_inputs, wl, rows):

@@ -36,6 +36,18 @@
  *   Dequantized weight: w = bf16_rne(level[code] * (q8 * step)), both
  *   products rounded to fp32.
  *
+ * Code types (the table `level[16]` behind the 4-bit codes; the capability
+ * page "Qlora 4 Bit Quantization With Nf4 Fp4 Data Types And Lora Adapters"
+ * names both data types, and the blog section "NormalFloat, double
+ * quantization, paged optimizers" compares NF4 against a plain 4-bit float):
+ *   QLORA_CODE_NF4  the 16 NF4 levels, ascending with the code, zero = code 7
+ *   QLORA_CODE_FP4  4-bit float E2M1 read as: bit 3 sign, bits 2..1 exponent
+ *                   (bias 1, exponent 0 subnormal), bit 0 mantissa, i.e.
+ *                   magnitudes {0, 1/2, 1, 3/2, 2, 3, 4, 6}, divided by 6
+ *                   so the largest is 1, rounded once to fp32; code 8 is -0
+ *                   and the quantizer writes code 0 for zero.
+ *   Block scaling, double quantization and storage are the same for both.
+ *
  * Conventions for every call:
  *   - bf16 tensors are passed as uint16_t bit patterns.
  *   - All tensor pointers are DEVICE pointers owned by the caller; the
@@ -69,6 +81,9 @@ extern "C" {
 #define QLORA_ERR_WORKSPACE (-3)   /* workspace smaller than required        */
 #define QLORA_ERR_LAUNCH (-4)      /* a HIP launch reported an error         */
 
+#define QLORA_CODE_NF4 0
+#define QLORA_CODE_FP4 1
+
 #define QLORA_NF4_BLOCKSIZE 64
 #define QLORA_NF4_DQ_BLOCKSIZE 256
 #define QLORA_MAX_RANK 256
@@ -82,6 +97,8 @@ typedef struct nf4_tensor_t {
   int64_t K;
   int32_t blocksize;    /* must be 64  */
   int32_t dq_blocksize; /* must be 256 */
+  int32_t code_type;    /* QLORA_CODE_NF4 or QLORA_CODE_FP4 (the type it was
+                           quantized with); others give QLORA_ERR_UNSUPPORTED */
 } nf4_tensor_t;
 
 /* Text for a status code (static storage, never NULL). */
@@ -95,6 +112,14 @@ const char* qlora_status_str(int32_t status);
  * normalized to [-1, 1] ("QLoRA: fine-tuning a 65B model on one GPU",
  * section "NormalFloat, double quantization, paged optimizers"). */
 void nf4_code_table(float* levels16, float* thresholds15);
+
+/* Host-side copy of the value of each of the 16 codes of `code_type` (in
+ * code order, fp32) and of its decision thresholds: the fp32 midpoint of
+ * each pair of consecutive distinct values, rounded toward -inf, ascending
+ * (NF4: 15; FP4: 14, since +0 and -0 are one value, and thresholds15[14] is
+ * set to 0).  Returns the number of thresholds, or QLORA_ERR_UNSUPPORTED for
+ * an unknown code type.  Either pointer may be NULL; no device work. */
+int32_t qlora_code_table(int32_t code_type, float* levels16, float* thresholds15);
 
 /* Bytes of the three NF4 arrays for an N x K weight (closed form:
  * N*K/2 + N*K/64 + 4*ceil(N*K/16384)); 0 for invalid sizes. */
@@ -120,10 +145,20 @@ int32_t nf4_quantize(const float* W, int64_t N, int64_t K, int32_t blocksize,
                      int32_t dq_blocksize, uint8_t* codes, uint8_t* q8,
                      float* step, hipStream_t stream);
 
-/* nf4_dequantize -- materialize the bf16 weight [N, K] from its NF4 state
- * (for checking and interop; the linear layer never does this: it
- * dequantizes tiles on chip).  w->N, w->K as in nf4_quantize.
- * W_bf16 [N*K] out. */
+/* qlora_quantize -- nf4_quantize for either code type: identical except that
+ * each element gets the code of the value of `code_type` nearest to
+ * fl32(w / c_b) (ties to the lower value; zero, and an all-zero block, get
+ * the code of zero: 7 for NF4, 0 for FP4).  An unknown code type gives
+ * QLORA_ERR_UNSUPPORTED.  nf4_quantize(...) is
+ * qlora_quantize(..., QLORA_CODE_NF4, ...). */
+int32_t qlora_quantize(const float* W, int64_t N, int64_t K, int32_t code_type,
+                       int32_t blocksize, int32_t dq_blocksize, uint8_t* codes,
+                       uint8_t* q8, float* step, hipStream_t stream);
+
+/* nf4_dequantize -- materialize the bf16 weight [N, K] from its quantized
+ * state, with the code table of w->code_type (for checking and interop; the
+ * linear layer never does this: it dequantizes tiles on chip).  w->N, w->K
+ * as in nf4_quantize.  W_bf16 [N*K] out. */
 int32_t nf4_dequantize(const nf4_tensor_t* w, uint16_t* W_bf16,
                        hipStream_t stream);
 

@@ -16,12 +16,17 @@ QLORA_ERR_UNSUPPORTED = -2
 QLORA_ERR_WORKSPACE = -3
 QLORA_ERR_LAUNCH = -4
 
+QLORA_CODE_NF4 = 0
+QLORA_CODE_FP4 = 1
+
 # Every symbol the header declares.
 EXPORTS = (
     "qlora_status_str",
     "nf4_code_table",
+    "qlora_code_table",
     "nf4_storage_bytes",
     "nf4_quantize",
+    "qlora_quantize",
     "nf4_dequantize",
     "qlora_workspace_size",
     "qlora_linear_fwd",
@@ -41,6 +46,7 @@ class Nf4Tensor(ctypes.Structure):
         ("K", ctypes.c_int64),
         ("blocksize", ctypes.c_int32),
         ("dq_blocksize", ctypes.c_int32),
+        ("code_type", ctypes.c_int32),
     ]
 
 
@@ -67,10 +73,14 @@ def lib() -> ctypes.CDLL:
     L.qlora_status_str.argtypes = [i32]
     L.nf4_code_table.restype = None
     L.nf4_code_table.argtypes = [vp, vp]
+    L.qlora_code_table.restype = i32
+    L.qlora_code_table.argtypes = [i32, vp, vp]
     L.nf4_storage_bytes.restype = sz
     L.nf4_storage_bytes.argtypes = [i64, i64]
     L.nf4_quantize.restype = i32
     L.nf4_quantize.argtypes = [vp, i64, i64, i32, i32, vp, vp, vp, vp]
+    L.qlora_quantize.restype = i32
+    L.qlora_quantize.argtypes = [vp, i64, i64, i32, i32, i32, vp, vp, vp, vp]
     L.nf4_dequantize.restype = i32
     L.nf4_dequantize.argtypes = [ctypes.POINTER(Nf4Tensor), vp, vp]
     L.qlora_workspace_size.restype = sz

@@ -13,6 +13,8 @@ using namespace qn;
 
 namespace {
 
+inline int32_t launch_status(hipError_t e) { return e == hipSuccess ? QLORA_OK : QLORA_ERR_LAUNCH; }
+
 constexpr size_t kAlign = 256;
 
 inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -68,14 +70,42 @@ bool nf4_ok(const nf4_tensor_t* w) {
   return w && w->codes && w->q8 && w->step;
 }
 
+inline bool code_ok(int32_t code_type) {
+  return code_type == QLORA_CODE_NF4 || code_type == QLORA_CODE_FP4;
+}
+
 int32_t nf4_supported(const nf4_tensor_t* w) {
-  return (w->blocksize == QLORA_NF4_BLOCKSIZE && w->dq_blocksize == QLORA_NF4_DQ_BLOCKSIZE)
+  return (w->blocksize == QLORA_NF4_BLOCKSIZE && w->dq_blocksize == QLORA_NF4_DQ_BLOCKSIZE &&
+          code_ok(w->code_type))
              ? QLORA_OK
              : QLORA_ERR_UNSUPPORTED;
 }
 
-inline int32_t launch_status(hipError_t e) { return e == hipSuccess ? QLORA_OK : QLORA_ERR_LAUNCH; }
+static_assert(CodeNF4::kId == QLORA_CODE_NF4 && CodeFP4::kId == QLORA_CODE_FP4,
+              "code type ids of the ABI and of the kernels agree");
 
+template <class CT>
+int32_t copy_table(float* levels16, float* thresholds15) {
+  if (levels16)
+    for (int i = 0; i < 16; ++i) levels16[i] = code_value<CT>(i);
+  if (thresholds15)
+    for (int i = 0; i < 15; ++i)
+      thresholds15[i] = i + 1 < CT::table.ndist ? __builtin_bit_cast(float, CT::table.thr[i]) : 0.0f;
+  return CT::table.ndist - 1;
+}
+
+int32_t quantize(const float* W, int64_t N, int64_t K, int32_t code_type, int32_t blocksize,
+                 int32_t dq_blocksize, uint8_t* codes, uint8_t* q8, float* step,
+                 hipStream_t stream) {
+  if (!W || !codes || !q8 || !step) return QLORA_ERR_INVALID;
+  if (N < 1 || K < 64 || (K % 64) != 0 || N > ((int64_t)1 << 40) / K) return QLORA_ERR_INVALID;
+  if (blocksize != QLORA_NF4_BLOCKSIZE || dq_blocksize != QLORA_NF4_DQ_BLOCKSIZE ||
+      !code_ok(code_type))
+    return QLORA_ERR_UNSUPPORTED;
+  if (!aligned16(W) || !aligned16(codes) || !aligned16(q8) || !aligned16(step))
+    return QLORA_ERR_INVALID;
+  return launch_status(launch_nf4_quantize(W, N * K / 64, codes, q8, step, code_type, stream));
+}
 
 }  // namespace
 
@@ -85,7 +115,8 @@ const char* qlora_status_str(int32_t status) {
   switch (status) {
     case QLORA_OK: return "ok";
     case QLORA_ERR_INVALID: return "invalid argument (null pointer, size or alignment)";
-    case QLORA_ERR_UNSUPPORTED: return "unsupported configuration (block sizes must be 64 and 256)";
+    case QLORA_ERR_UNSUPPORTED:
+      return "unsupported configuration (block sizes must be 64 and 256, code type NF4 or FP4)";
     case QLORA_ERR_WORKSPACE: return "workspace too small";
     case QLORA_ERR_LAUNCH: return "HIP launch error";
     default: return "unknown status";
@@ -93,10 +124,13 @@ const char* qlora_status_str(int32_t status) {
 }
 
 void nf4_code_table(float* levels16, float* thresholds15) {
-  if (levels16)
-    for (int i = 0; i < 16; ++i) levels16[i] = level_f32(i);
-  if (thresholds15)
-    for (int i = 0; i < 15; ++i) thresholds15[i] = __builtin_bit_cast(float, kThr.bits[i]);
+  copy_table<CodeNF4>(levels16, thresholds15);
+}
+
+int32_t qlora_code_table(int32_t code_type, float* levels16, float* thresholds15) {
+  if (code_type == QLORA_CODE_NF4) return copy_table<CodeNF4>(levels16, thresholds15);
+  if (code_type == QLORA_CODE_FP4) return copy_table<CodeFP4>(levels16, thresholds15);
+  return QLORA_ERR_UNSUPPORTED;
 }
 
 size_t nf4_storage_bytes(int64_t N, int64_t K) {
@@ -108,13 +142,13 @@ size_t nf4_storage_bytes(int64_t N, int64_t K) {
 int32_t nf4_quantize(const float* W, int64_t N, int64_t K, int32_t blocksize,
                      int32_t dq_blocksize, uint8_t* codes, uint8_t* q8, float* step,
                      hipStream_t stream) {
-  if (!W || !codes || !q8 || !step) return QLORA_ERR_INVALID;
-  if (N < 1 || K < 64 || (K % 64) != 0 || N > ((int64_t)1 << 40) / K) return QLORA_ERR_INVALID;
-  if (blocksize != QLORA_NF4_BLOCKSIZE || dq_blocksize != QLORA_NF4_DQ_BLOCKSIZE)
-    return QLORA_ERR_UNSUPPORTED;
-  if (!aligned16(W) || !aligned16(codes) || !aligned16(q8) || !aligned16(step))
-    return QLORA_ERR_INVALID;
-  return launch_status(launch_nf4_quantize(W, N * K / 64, codes, q8, step, stream));
+  return quantize(W, N, K, QLORA_CODE_NF4, blocksize, dq_blocksize, codes, q8, step, stream);
+}
+
+int32_t qlora_quantize(const float* W, int64_t N, int64_t K, int32_t code_type,
+                       int32_t blocksize, int32_t dq_blocksize, uint8_t* codes, uint8_t* q8,
+                       float* step, hipStream_t stream) {
+  return quantize(W, N, K, code_type, blocksize, dq_blocksize, codes, q8, step, stream);
 }
 
 int32_t nf4_dequantize(const nf4_tensor_t* w, uint16_t* W_bf16, hipStream_t stream) {
@@ -124,7 +158,8 @@ int32_t nf4_dequantize(const nf4_tensor_t* w, uint16_t* W_bf16, hipStream_t stre
   if (sup != QLORA_OK) return sup;
   if (!aligned16(w->codes) || !aligned16(w->q8) || !aligned16(w->step) || !aligned16(W_bf16))
     return QLORA_ERR_INVALID;
-  return launch_status(launch_nf4_dequantize(w->codes, w->q8, w->step, w->N * w->K, W_bf16, stream));
+  return launch_status(
+      launch_nf4_dequantize(w->codes, w->q8, w->step, w->N * w->K, W_bf16, w->code_type, stream));
 }
 
 size_t qlora_workspace_size(int64_t M, int64_t N, int64_t K, int32_t r, int32_t for_bwd) {
@@ -158,7 +193,7 @@ int32_t linear_fwd(const nf4_tensor_t* w, const uint16_t* X, int64_t M, const ui
   char* base = static_cast<char*>(ws);
   uint16_t* ws_u = reinterpret_cast<uint16_t*>(base + pl.u_off);
   float* part = reinterpret_cast<float*>(base + pl.part_off);
-  const Nf4View v{w->codes, w->q8, w->step, N, K};
+  const Nf4View v{w->codes, w->q8, w->step, N, K, w->code_type};
   const int64_t rp = rank_pad(r);
 
   if (gemv_fits(M, r, K))
@@ -225,7 +260,7 @@ int32_t linear_bwd(const nf4_tensor_t* w, const uint16_t* X, const uint16_t* dY,
 
   // dX = dY W + dU A
   if (dX) {
-    const Nf4View v{w->codes, w->q8, w->step, N, K};
+    const Nf4View v{w->codes, w->q8, w->step, N, K, w->code_type};
     if (record(ev0, stream) != hipSuccess) return QLORA_ERR_LAUNCH;
     e = launch_qgemm_bwd(v, dY, M, ws_du, rp, A, r, dX, stream);
     if (e != hipSuccess || record(ev1, stream) != hipSuccess) return QLORA_ERR_LAUNCH;

@@ -27,14 +27,19 @@ constexpr uint32_t kLevelBits[16] = {
     0xbdba7869u, 0x00000000u, 0x3da2fb01u, 0x3e24cadfu, 0x3e7c04dau, 0x3ead0336u,
     0x3ee1a4b5u, 0x3f1007a9u, 0x3f3913b0u, 0x3f800000u};
 
-constexpr float level_f32(int i) { return __builtin_bit_cast(float, kLevelBits[i]); }
-
-// Decision threshold between level i and level i + 1: their exact midpoint
-// (exact in double) rounded toward -inf to fp32.  For an fp32 x,
-// x > T_i  <=>  x is strictly nearer to level i + 1, so
-// code = #{i : x > T_i} is the nearest level with ties to the lower one.
-constexpr uint32_t threshold_bits(int i) {
-  double mid = ((double)level_f32(i) + (double)level_f32(i + 1)) * 0.5;
+// ---------------------------------------------------------------------------
+// 4-bit code tables.  A table gives the value of each of the 16 codes (fp32
+// bits, in code order) and the quantizer's rule: the distinct values in
+// ascending order, the decision threshold between consecutive ones, and the
+// code written for "x lies above exactly `count` thresholds".
+//
+// Decision threshold between distinct values v_i < v_{i+1}: their exact
+// midpoint (exact in double) rounded toward -inf to fp32.  For an fp32 x,
+// x > T_i  <=>  x is strictly nearer to v_{i+1}, so count = #{i : x > T_i}
+// picks the nearest value with ties to the lower one.
+// ---------------------------------------------------------------------------
+constexpr uint32_t midpoint_down_bits(float lo, float hi) {
+  double mid = ((double)lo + (double)hi) * 0.5;
   float f = (float)mid;  // round to nearest
   uint32_t b = __builtin_bit_cast(uint32_t, f);
   if ((double)f > mid) {  // step one ulp toward -inf
@@ -45,28 +50,108 @@ constexpr uint32_t threshold_bits(int i) {
   return b;
 }
 
-struct ThresholdTable {
-  uint32_t bits[15];
-  constexpr ThresholdTable() : bits{} {
-    for (int i = 0; i < 15; ++i) bits[i] = threshold_bits(i);
-  }
+struct CodeTable {
+  uint32_t level[16];    // value of each code (fp32 bits)
+  int ndist;             // distinct values (equal values, e.g. +0 and -0, count once)
+  uint32_t dist[16];     // distinct values, ascending (fp32 bits)
+  uint8_t dist_code[16]; // code written for distinct value i (the lowest such code)
+  uint32_t thr[15];      // ndist - 1 thresholds (fp32 bits)
+  uint8_t zero_code;     // code of an all-zero block
 };
-constexpr ThresholdTable kThr{};
 
-constexpr bool thresholds_sound() {
-  for (int i = 0; i < 15; ++i) {
-    double mid = ((double)level_f32(i) + (double)level_f32(i + 1)) * 0.5;
-    float t = __builtin_bit_cast(float, kThr.bits[i]);
-    if ((double)t > mid) return false;                       // at or below mid
-    uint32_t nb = kThr.bits[i] + ((t >= 0.0f) ? 1u : (uint32_t)-1);
-    if (t == 0.0f) return false;
-    float nx = __builtin_bit_cast(float, nb);
-    if ((double)nx <= mid) return false;                     // next float above mid
-    if (!(level_f32(i) <= t && t < level_f32(i + 1))) return false;
+constexpr CodeTable make_code_table(const uint32_t (&lv)[16]) {
+  CodeTable t{};
+  for (int c = 0; c < 16; ++c) t.level[c] = lv[c];
+  // distinct values in ascending order (selection by value, lowest code wins)
+  t.ndist = 0;
+  float last = 0.0f;
+  for (int k = 0; k < 16; ++k) {
+    int best = -1;
+    for (int c = 0; c < 16; ++c) {
+      const float v = __builtin_bit_cast(float, lv[c]);
+      if (t.ndist > 0 && !(v > last)) continue;
+      if (best < 0 || v < __builtin_bit_cast(float, lv[best])) best = c;
+    }
+    if (best < 0) break;
+    last = __builtin_bit_cast(float, lv[best]);
+    t.dist[t.ndist] = lv[best];
+    t.dist_code[t.ndist] = (uint8_t)best;
+    if (last == 0.0f) t.zero_code = (uint8_t)best;
+    ++t.ndist;
+  }
+  for (int i = 0; i + 1 < t.ndist; ++i)
+    t.thr[i] = midpoint_down_bits(__builtin_bit_cast(float, t.dist[i]),
+                                  __builtin_bit_cast(float, t.dist[i + 1]));
+  return t;
+}
+
+constexpr bool code_table_sound(const CodeTable& t) {
+  for (int i = 0; i + 1 < t.ndist; ++i) {
+    const float lo = __builtin_bit_cast(float, t.dist[i]);
+    const float hi = __builtin_bit_cast(float, t.dist[i + 1]);
+    if (!(lo < hi)) return false;
+    const double mid = ((double)lo + (double)hi) * 0.5;
+    const float th = __builtin_bit_cast(float, t.thr[i]);
+    if ((double)th > mid || th == 0.0f) return false;  // at or below the midpoint
+    const uint32_t nb = t.thr[i] + ((th >= 0.0f) ? 1u : (uint32_t)-1);
+    if ((double)__builtin_bit_cast(float, nb) <= mid) return false;  // next float above it
+    if (!(lo <= th && th < hi)) return false;
   }
   return true;
 }
-static_assert(thresholds_sound(), "NF4 thresholds must be the midpoints rounded down");
+
+// FP4: the E2M1 format (bit 3 sign, bits 2..1 exponent with bias 1, bit 0
+// mantissa; exponent 0 is subnormal), magnitudes 0, 1/2, 1, 3/2, 2, 3, 4, 6,
+// divided by 6 so that the largest magnitude is 1 like the NF4 levels, and
+// rounded once to fp32.  Code 8 is -0.
+constexpr uint32_t fp4_level_bits(int c) {
+  const int e = (c >> 1) & 3, m = c & 1;
+  const double mag = (e == 0) ? 0.5 * m : (double)(1 << (e - 1)) * (1.0 + 0.5 * m);
+  const float v = (float)(mag / 6.0);
+  return __builtin_bit_cast(uint32_t, (c & 8) ? -v : v);
+}
+struct Fp4Bits {
+  uint32_t b[16];
+  constexpr Fp4Bits() : b{} {
+    for (int c = 0; c < 16; ++c) b[c] = fp4_level_bits(c);
+  }
+};
+constexpr Fp4Bits kFp4Bits{};
+
+// Each code type also gives the code for a threshold count in closed form
+// (checked against the table below).
+struct CodeNF4 {
+  static constexpr int kId = 0;
+  static constexpr CodeTable table = make_code_table(kLevelBits);
+  __host__ __device__ static constexpr uint32_t code_of_count(uint32_t n) { return n; }
+};
+struct CodeFP4 {
+  static constexpr int kId = 1;
+  static constexpr CodeTable table = make_code_table(kFp4Bits.b);
+  // counts 0..6 are -1 .. -1/12 (codes 15..9), 7 is zero (code 0), 8..14 are
+  // 1/12 .. 1 (codes 1..7)
+  __host__ __device__ static constexpr uint32_t code_of_count(uint32_t n) {
+    return n >= 7 ? n - 7 : 15 - n;
+  }
+};
+template <class CT>
+constexpr bool count_map_sound() {
+  for (int n = 0; n < CT::table.ndist; ++n)
+    if (CT::code_of_count((uint32_t)n) != CT::table.dist_code[n]) return false;
+  return true;
+}
+static_assert(count_map_sound<CodeNF4>() && count_map_sound<CodeFP4>(), "count -> code maps");
+static_assert(CodeNF4::table.ndist == 16 && CodeNF4::table.zero_code == 7 &&
+                  code_table_sound(CodeNF4::table),
+              "NF4: 16 distinct levels, zero is code 7, thresholds are the midpoints rounded down");
+static_assert(CodeFP4::table.ndist == 15 && CodeFP4::table.zero_code == 0 &&
+                  code_table_sound(CodeFP4::table),
+              "FP4: 15 distinct values (+0 and -0), zero is code 0");
+
+template <class CT>
+__host__ __device__ constexpr float code_value(int c) {
+  return __builtin_bit_cast(float, CT::table.level[c]);
+}
 
 // ---------------------------------------------------------------------------
 // bf16 helpers

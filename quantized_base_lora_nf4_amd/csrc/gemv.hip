@@ -42,17 +42,18 @@ __device__ __forceinline__ uint32_t perm(uint32_t s0, uint32_t s1, uint32_t sel)
   return __builtin_amdgcn_perm(s0, s1, sel);
 }
 
-// Byte planes of the 16 unscaled bf16 levels: kLo[q] byte e = low byte of
-// level 4 q + e, kHi[q] byte e = high byte.
+// Byte planes of the 16 unscaled bf16 code values: lo[q] byte e = low byte
+// of the value of code 4 q + e, hi[q] byte e = high byte.
 struct UnscaledPlanes {
   uint32_t lo[4], hi[4];
 };
+template <class CT>
 constexpr UnscaledPlanes make_planes() {
   UnscaledPlanes p{};
   for (int q = 0; q < 4; ++q) {
     uint32_t lo = 0, hi = 0;
     for (int e = 0; e < 4; ++e) {
-      const uint32_t b = bf16_rne_bits(kLevelBits[4 * q + e]);
+      const uint32_t b = bf16_rne_bits(CT::table.level[4 * q + e]);
       lo |= (b & 0xffu) << (8 * e);
       hi |= ((b >> 8) & 0xffu) << (8 * e);
     }
@@ -61,10 +62,15 @@ constexpr UnscaledPlanes make_planes() {
   }
   return p;
 }
-constexpr UnscaledPlanes kPlanes = make_planes();
+template <class CT>
+struct Planes {
+  static constexpr UnscaledPlanes v = make_planes<CT>();
+};
 
 // Eight codes (nibble order) -> four packed bf16 level pairs, by permutes.
+template <class CT>
 __device__ __forceinline__ u32x4 levels8_perm(uint32_t w) {
+  constexpr UnscaledPlanes kPlanes = Planes<CT>::v;
   const uint32_t se = w & 0x07070707u;
   const uint32_t so = (w >> 4) & 0x07070707u;
   const uint32_t me = perm(0u, 0u, ((w >> 3) & 0x01010101u) | 0x0c0c0c0cu);
@@ -162,7 +168,7 @@ __host__ __device__ constexpr int64_t gemv_lds_words(int G, int KW, int64_t M, i
   return kLutWords + M * r + (chat > red ? chat : red);
 }
 
-template <int G, int KW, int PD, bool kPerm>
+template <int G, int KW, int PD, bool kPerm, class CT>
 __global__ __launch_bounds__(64 * KW) void k_qgemv(GemvArgs p) {
   constexpr int NT = 64 * KW;
   extern __shared__ float lds[];
@@ -245,8 +251,8 @@ __global__ __launch_bounds__(64 * KW) void k_qgemv(GemvArgs p) {
       for (int h = 0; h < 2; ++h) {
         u32x4 w0, w1;
         if (kPerm) {
-          w0 = levels8_perm(c[2 * h]);
-          w1 = levels8_perm(c[2 * h + 1]);
+          w0 = levels8_perm<CT>(c[2 * h]);
+          w1 = levels8_perm<CT>(c[2 * h + 1]);
         } else {
           w0 = levels8_lut(c[2 * h], lut + i16);
           w1 = levels8_lut(c[2 * h + 1], lut + i16);
@@ -272,7 +278,7 @@ __global__ __launch_bounds__(64 * KW) void k_qgemv(GemvArgs p) {
   if (!kPerm) {
     for (int e = tid; e < kLutWords; e += NT) {
       const int b = e >> 4;  // copy e % 16 of entry b
-      lut[e] = pack_bf16x2(level_f32(b & 15), level_f32(b >> 4));
+      lut[e] = pack_bf16x2(code_value<CT>(b & 15), code_value<CT>(b >> 4));
     }
   }
   {
@@ -413,13 +419,25 @@ hipError_t launch_qgemv(const Nf4View& w, const uint16_t* X, int64_t M, const ui
   const int64_t kblocks = w.K / 64;
   // 32 weight rows per workgroup, K split over its 8 waves
   constexpr int G = 2, KW = 8, PD = QN_GEMV_PD;
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&k_qgemv<G, KW, PD, QN_GEMV_PERM>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);  // above the default 64 KB, once
+  static const hipError_t attr = [] {
+    // dynamic LDS above the default 64 KB needs the limit raised, once
+    const hipError_t a = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&k_qgemv<G, KW, PD, QN_GEMV_PERM, CodeNF4>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
+    const hipError_t b = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&k_qgemv<G, KW, PD, QN_GEMV_PERM, CodeFP4>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
+    return a != hipSuccess ? a : b;
+  }();
   if (attr != hipSuccess) return attr;
   const size_t lds = 4 * (size_t)gemv_lds_words(G, KW, M, r, kblocks);
-  hipLaunchKernelGGL((k_qgemv<G, KW, PD, QN_GEMV_PERM>), dim3((unsigned)((w.N + 16 * G - 1) / (16 * G))),
-                     dim3(64 * KW), lds, stream, a);
+  const dim3 grid((unsigned)((w.N + 16 * G - 1) / (16 * G)));
+  if (w.code == CodeFP4::kId)
+    hipLaunchKernelGGL((k_qgemv<G, KW, PD, QN_GEMV_PERM, CodeFP4>), grid, dim3(64 * KW), lds,
+                       stream, a);
+  else
+    hipLaunchKernelGGL((k_qgemv<G, KW, PD, QN_GEMV_PERM, CodeNF4>), grid, dim3(64 * KW), lds,
+                       stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (ev1) e = hipEventRecord(ev1, stream);

@@ -6,11 +6,11 @@
 
 namespace qn {
 
-// ---- nf4_quant.hip ----
+// ---- nf4_quant.hip ----  (code: CodeNF4::kId or CodeFP4::kId)
 hipError_t launch_nf4_quantize(const float* W, int64_t nblocks, uint8_t* codes, uint8_t* q8,
-                               float* step, hipStream_t stream);
+                               float* step, int code, hipStream_t stream);
 hipError_t launch_nf4_dequantize(const uint8_t* codes, const uint8_t* q8, const float* step,
-                                 int64_t nelem, uint16_t* out, hipStream_t stream);
+                                 int64_t nelem, uint16_t* out, int code, hipStream_t stream);
 
 // ---- qgemm.hip: MFMA tile kernels with the NF4 dequantization in the prologue ----
 struct Nf4View {
@@ -18,6 +18,7 @@ struct Nf4View {
   const uint8_t* q8;
   const float* step;
   int64_t N, K;
+  int code;  // CodeNF4::kId or CodeFP4::kId
 };
 
 // Y[M,N] = X[M,K] W^T + bf16(s U)[M,r] B[N,r]^T.  U has row stride ldu (a

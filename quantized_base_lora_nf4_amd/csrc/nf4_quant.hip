@@ -1,5 +1,5 @@
-// NF4 quantizer with double-quantized absmax constants, and the standalone
-// dequantizer.
+// 4-bit quantizer (NF4 or FP4 code table) with double-quantized absmax
+// constants, and the standalone dequantizer.
 //
 // Quantization follows "QLoRA: fine-tuning a 65B model on one GPU", section
 // "NormalFloat, double quantization, paged optimizers" (16 levels at normal
@@ -17,14 +17,17 @@
 
 namespace qn {
 
-__device__ __forceinline__ uint32_t nf4_code(float x) {
-  // number of thresholds strictly below x = nearest level, ties low
-  uint32_t c = 0;
+template <class CT>
+__device__ __forceinline__ uint32_t quant_code(float x) {
+  // number of thresholds strictly below x = nearest value, ties low
+  uint32_t n = 0;
 #pragma unroll
-  for (int i = 0; i < 15; ++i) c += (x > __builtin_bit_cast(float, kThr.bits[i])) ? 1u : 0u;
-  return c;
+  for (int i = 0; i < CT::table.ndist - 1; ++i)
+    n += (x > __builtin_bit_cast(float, CT::table.thr[i])) ? 1u : 0u;
+  return CT::code_of_count(n);
 }
 
+template <class CT>
 __global__ __launch_bounds__(256) void k_nf4_quantize(const float* __restrict__ W,
                                                       int64_t nblocks,
                                                       uint8_t* __restrict__ codes,
@@ -52,12 +55,12 @@ __global__ __launch_bounds__(256) void k_nf4_quantize(const float* __restrict__ 
       uint32_t c0, c1, c2, c3;
       if (m > 0.0f) {
         // IEEE-correct fp32 division (the compiler's default for '/')
-        c0 = nf4_code(v[0] / m);
-        c1 = nf4_code(v[1] / m);
-        c2 = nf4_code(v[2] / m);
-        c3 = nf4_code(v[3] / m);
+        c0 = quant_code<CT>(v[0] / m);
+        c1 = quant_code<CT>(v[1] / m);
+        c2 = quant_code<CT>(v[2] / m);
+        c3 = quant_code<CT>(v[3] / m);
       } else {
-        c0 = c1 = c2 = c3 = 7u;  // all-zero block: the exact zero level
+        c0 = c1 = c2 = c3 = CT::table.zero_code;  // all-zero block: the zero level
       }
       const uint16_t packed = (uint16_t)(c0 | (c1 << 4) | (c2 << 8) | (c3 << 12));
       *reinterpret_cast<uint16_t*>(codes + b * 32 + sub * 2) = packed;
@@ -86,14 +89,15 @@ __global__ __launch_bounds__(256) void k_nf4_quantize(const float* __restrict__ 
   if (t == 0) step[g] = st;
 }
 
-// Standalone dequantizer: w = bf16_rne(level[code] * fl32(q8 * step)).
+// Standalone dequantizer: w = bf16_rne(value[code] * fl32(q8 * step)).
 // Each thread expands four code bytes (eight weights) into 16 bytes of bf16.
+template <class CT>
 __global__ __launch_bounds__(256) void k_nf4_dequantize(const uint8_t* __restrict__ codes,
                                                         const uint8_t* __restrict__ q8,
                                                         const float* __restrict__ step,
                                                         int64_t n8, uint16_t* __restrict__ out) {
   __shared__ float lv[16];
-  if (threadIdx.x < 16) lv[threadIdx.x] = level_f32(threadIdx.x);
+  if (threadIdx.x < 16) lv[threadIdx.x] = code_value<CT>(threadIdx.x);
   __syncthreads();
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n8;
        i += (int64_t)gridDim.x * blockDim.x) {
@@ -112,20 +116,28 @@ __global__ __launch_bounds__(256) void k_nf4_dequantize(const uint8_t* __restric
 }
 
 hipError_t launch_nf4_quantize(const float* W, int64_t nblocks, uint8_t* codes, uint8_t* q8,
-                               float* step, hipStream_t stream) {
+                               float* step, int code, hipStream_t stream) {
   const int64_t ngroups = (nblocks + 255) / 256;
-  hipLaunchKernelGGL(k_nf4_quantize, dim3((unsigned)ngroups), dim3(256), 0, stream, W, nblocks,
-                     codes, q8, step);
+  if (code == CodeFP4::kId)
+    hipLaunchKernelGGL(k_nf4_quantize<CodeFP4>, dim3((unsigned)ngroups), dim3(256), 0, stream, W,
+                       nblocks, codes, q8, step);
+  else
+    hipLaunchKernelGGL(k_nf4_quantize<CodeNF4>, dim3((unsigned)ngroups), dim3(256), 0, stream, W,
+                       nblocks, codes, q8, step);
   return hipGetLastError();
 }
 
 hipError_t launch_nf4_dequantize(const uint8_t* codes, const uint8_t* q8, const float* step,
-                                 int64_t nelem, uint16_t* out, hipStream_t stream) {
+                                 int64_t nelem, uint16_t* out, int code, hipStream_t stream) {
   const int64_t n8 = nelem / 8;
   int64_t grid = (n8 + 255) / 256;
   if (grid > 65536) grid = 65536;
-  hipLaunchKernelGGL(k_nf4_dequantize, dim3((unsigned)grid), dim3(256), 0, stream, codes, q8,
-                     step, n8, out);
+  if (code == CodeFP4::kId)
+    hipLaunchKernelGGL(k_nf4_dequantize<CodeFP4>, dim3((unsigned)grid), dim3(256), 0, stream,
+                       codes, q8, step, n8, out);
+  else
+    hipLaunchKernelGGL(k_nf4_dequantize<CodeNF4>, dim3((unsigned)grid), dim3(256), 0, stream,
+                       codes, q8, step, n8, out);
   return hipGetLastError();
 }
 

@@ -58,12 +58,15 @@ struct LevelTable {
   uint32_t lo[4], hi[4];
 };
 
+template <class CT>
 __device__ __forceinline__ LevelTable make_table(float chat) {
   LevelTable t;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const uint32_t p0 = pack_bf16x2(level_f32(4 * q) * chat, level_f32(4 * q + 1) * chat);
-    const uint32_t p1 = pack_bf16x2(level_f32(4 * q + 2) * chat, level_f32(4 * q + 3) * chat);
+    const uint32_t p0 =
+        pack_bf16x2(code_value<CT>(4 * q) * chat, code_value<CT>(4 * q + 1) * chat);
+    const uint32_t p1 =
+        pack_bf16x2(code_value<CT>(4 * q + 2) * chat, code_value<CT>(4 * q + 3) * chat);
     t.lo[q] = perm(p1, p0, 0x06040200u);
     t.hi[q] = perm(p1, p0, 0x07050301u);
   }
@@ -296,9 +299,9 @@ struct StepRegs {
   float st;
 };
 
-template <class C>
+template <class C, class CT>
 __device__ __forceinline__ void dequant_codes(uint16_t* dst, const StepRegs<C>& r) {
-  const LevelTable t = make_table((float)(r.q & r.qm) * r.st);
+  const LevelTable t = make_table<CT>((float)(r.q & r.qm) * r.st);
 #pragma unroll
   for (int h = 0; h < C::WPT / 32; ++h)
 #pragma unroll
@@ -312,7 +315,7 @@ __device__ __forceinline__ void dequant_codes(uint16_t* dst, const StepRegs<C>& 
 // four 16-deep sub-steps each read the next sub-step's fragments first, then
 // alternate their 16 MFMAs with the VALU work of expanding two code words,
 // then write those weight chunks.
-template <class C, bool kTransB>
+template <class C, bool kTransB, class CT>
 __device__ __forceinline__ void step_interleaved(const uint16_t* As, const uint16_t* Bs,
                                                  uint16_t* As_n, uint16_t* Bw_n,
                                                  const StepRegs<C>& rn, int wm, int wn, int lane,
@@ -321,7 +324,7 @@ __device__ __forceinline__ void step_interleaved(const uint16_t* As, const uint1
   (void)As_n;
   Frags<C> f[2];
   read_frags<C, kTransB>(f[0], As, Bs, wm, wn, lane, 0);
-  const LevelTable t = make_table((float)(rn.q & rn.qm) * rn.st);
+  const LevelTable t = make_table<CT>((float)(rn.q & rn.qm) * rn.st);
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
     if (kk < 3) read_frags<C, kTransB>(f[(kk + 1) & 1], As, Bs, wm, wn, lane, kk + 1);
@@ -350,7 +353,7 @@ struct FwdArgs {
   int64_t M, N, K;
 };
 
-template <class C>
+template <class C, class CT>
 __global__ __launch_bounds__(C::NT, 1) void k_qgemm_fwd(FwdArgs p) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[C::SMEM_F];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -402,7 +405,7 @@ __global__ __launch_bounds__(C::NT, 1) void k_qgemm_fwd(FwdArgs p) {
     uint16_t* As_n = smem + (cur ^ 1) * (C::TILE_A + C::TILE_BF);
     load_x(As_n, kt + 1);
     load_w(rload, kt + 2);
-    step_interleaved<C, false>(As, As + C::TILE_A, As_n,
+    step_interleaved<C, false, CT>(As, As + C::TILE_A, As_n,
                                As_n + C::TILE_A + wrow * LDA + wpart * C::WPT, rnext, wm, wn,
                                lane, acc);
     wait_vmem();
@@ -412,7 +415,7 @@ __global__ __launch_bounds__(C::NT, 1) void k_qgemm_fwd(FwdArgs p) {
   load_w(ra, 0);
   load_w(rb, 1);
   load_x(smem, 0);
-  dequant_codes<C>(smem + C::TILE_A + wrow * LDA + wpart * C::WPT, ra);
+  dequant_codes<C, CT>(smem + C::TILE_A + wrow * LDA + wpart * C::WPT, ra);
   wait_vmem();
   __syncthreads();
   int64_t kt = 0;
@@ -477,7 +480,7 @@ struct BwdArgs {
 // Output tile BM tokens x BN input features; contraction over the weight's
 // rows in steps of 64.  The step's weight slice, rows n..n+63 and columns
 // k0..k0+BN-1, is dequantized into Bs[64][LDTB] in its natural layout.
-template <class C>
+template <class C, class CT>
 __global__ __launch_bounds__(C::NT, 1) void k_qgemm_bwd(BwdArgs p) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[C::SMEM_B];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -534,7 +537,7 @@ __global__ __launch_bounds__(C::NT, 1) void k_qgemm_bwd(BwdArgs p) {
     __builtin_amdgcn_sched_barrier(0);
     load_w(rload, ns + 2);   // ... then the weight loads, which outlive the step
     __builtin_amdgcn_sched_barrier(0);
-    step_interleaved<C, true>(As, As + C::TILE_A, As_n,
+    step_interleaved<C, true, CT>(As, As + C::TILE_A, As_n,
                               As_n + C::TILE_A + wr * C::LDTB + wb * C::BSTR + wh * WPTB, rnext,
                               wm, wn, lane, acc);
     step_barrier();
@@ -543,7 +546,7 @@ __global__ __launch_bounds__(C::NT, 1) void k_qgemm_bwd(BwdArgs p) {
   load_w(ra, 0);
   load_w(rb, 1);
   load_x(smem, 0);
-  dequant_codes<C>(smem + C::TILE_A + wr * C::LDTB + wb * C::BSTR + wh * WPTB, ra);
+  dequant_codes<C, CT>(smem + C::TILE_A + wr * C::LDTB + wb * C::BSTR + wh * WPTB, ra);
   wait_vmem();
   __syncthreads();
   int64_t ns = 0;
@@ -589,7 +592,10 @@ hipError_t launch_qgemm_fwd(const Nf4View& w, const uint16_t* X, int64_t M, cons
   using C = GemmCfg;
   FwdArgs a{X, w.codes, w.q8, w.step, U, ldu, B, r, s, Y, M, w.N, w.K};
   dim3 grid((unsigned)(((w.N + C::BN - 1) / C::BN) * ((M + C::BM - 1) / C::BM)));
-  hipLaunchKernelGGL(k_qgemm_fwd<C>, grid, dim3(C::NT), 0, stream, a);
+  if (w.code == CodeFP4::kId)
+    hipLaunchKernelGGL((k_qgemm_fwd<C, CodeFP4>), grid, dim3(C::NT), 0, stream, a);
+  else
+    hipLaunchKernelGGL((k_qgemm_fwd<C, CodeNF4>), grid, dim3(C::NT), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -599,7 +605,10 @@ hipError_t launch_qgemm_bwd(const Nf4View& w, const uint16_t* dY, int64_t M, con
   using C = GemmCfg;
   BwdArgs a{dY, w.codes, w.q8, w.step, dU, lddu, A, r, dX, M, w.N, w.K};
   dim3 grid((unsigned)(((w.K + C::BN - 1) / C::BN) * ((M + C::BM - 1) / C::BM)));
-  hipLaunchKernelGGL(k_qgemm_bwd<C>, grid, dim3(C::NT), 0, stream, a);
+  if (w.code == CodeFP4::kId)
+    hipLaunchKernelGGL((k_qgemm_bwd<C, CodeFP4>), grid, dim3(C::NT), 0, stream, a);
+  else
+    hipLaunchKernelGGL((k_qgemm_bwd<C, CodeNF4>), grid, dim3(C::NT), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -12,10 +12,18 @@ from typing import Optional, Tuple
 
 import torch
 
-from ._lib import Nf4Tensor, check, lib
+from ._lib import QLORA_CODE_FP4, QLORA_CODE_NF4, Nf4Tensor, check, lib
 
 BLOCKSIZE = 64
 DQ_BLOCKSIZE = 256
+CODE_TYPES = {"nf4": QLORA_CODE_NF4, "fp4": QLORA_CODE_FP4}
+
+
+def _code_id(code: str) -> int:
+    try:
+        return CODE_TYPES[code]
+    except KeyError:
+        raise ValueError(f"code must be one of {sorted(CODE_TYPES)}, got {code!r}") from None
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -46,46 +54,59 @@ class NF4Weight:
     step: torch.Tensor    # float32 [ceil(N*K/16384)]
     N: int
     K: int
+    code: str = "nf4"     # the code table the codes index: "nf4" or "fp4"
 
     def struct(self) -> Nf4Tensor:
         return Nf4Tensor(_ptr(self.codes), _ptr(self.q8), _ptr(self.step), self.N, self.K,
-                         BLOCKSIZE, DQ_BLOCKSIZE)
+                         BLOCKSIZE, DQ_BLOCKSIZE, _code_id(self.code))
 
     def nbytes(self) -> int:
         return self.codes.numel() + self.q8.numel() + 4 * self.step.numel()
 
 
-def code_table() -> Tuple[list, list]:
-    """The library's NF4 levels (16) and decision thresholds (15), fp32."""
+def code_table(code: str = "nf4") -> Tuple[list, list]:
+    """The library's 16 code values (in code order) and its decision
+    thresholds (15 for NF4, 14 for FP4), fp32."""
     lv = (ctypes.c_float * 16)()
     th = (ctypes.c_float * 15)()
-    lib().nf4_code_table(ctypes.cast(lv, ctypes.c_void_p), ctypes.cast(th, ctypes.c_void_p))
-    return list(lv), list(th)
+    n = lib().qlora_code_table(_code_id(code), ctypes.cast(lv, ctypes.c_void_p),
+                               ctypes.cast(th, ctypes.c_void_p))
+    check(min(n, 0), "qlora_code_table")
+    return list(lv), list(th)[:n]
 
 
 def storage_bytes(N: int, K: int) -> int:
     return int(lib().nf4_storage_bytes(N, K))
 
 
-def alloc_nf4(N: int, K: int, device="cuda") -> NF4Weight:
+def alloc_nf4(N: int, K: int, device="cuda", code: str = "nf4") -> NF4Weight:
     nb = N * K // BLOCKSIZE
     ng = (nb + DQ_BLOCKSIZE - 1) // DQ_BLOCKSIZE
     return NF4Weight(
         codes=torch.empty(N * K // 2, dtype=torch.uint8, device=device),
         q8=torch.empty(nb, dtype=torch.uint8, device=device),
         step=torch.empty(ng, dtype=torch.float32, device=device),
-        N=N, K=K)
+        N=N, K=K, code=code)
 
 
-def nf4_quantize(W: torch.Tensor, out: Optional[NF4Weight] = None, stream=None) -> NF4Weight:
-    """Quantize an fp32 [N, K] device tensor to NF4 with double-quantized constants."""
+def nf4_quantize(W: torch.Tensor, out: Optional[NF4Weight] = None, stream=None,
+                 code: str = "nf4") -> NF4Weight:
+    """Quantize an fp32 [N, K] device tensor to 4-bit codes (NF4 by default,
+    or FP4) with double-quantized constants."""
     if W.dtype != torch.float32 or W.dim() != 2:
         raise TypeError("W must be a 2-D float32 tensor")
     N, K = W.shape
+    cid = _code_id(code)
     if out is None:
-        out = alloc_nf4(N, K, W.device)
-    st = lib().nf4_quantize(_ptr(W), N, K, BLOCKSIZE, DQ_BLOCKSIZE, _ptr(out.codes), _ptr(out.q8),
-                            _ptr(out.step), _stream(stream))
+        out = alloc_nf4(N, K, W.device, code)
+    else:
+        out.code = code
+    if cid == QLORA_CODE_NF4:
+        st = lib().nf4_quantize(_ptr(W), N, K, BLOCKSIZE, DQ_BLOCKSIZE, _ptr(out.codes),
+                                _ptr(out.q8), _ptr(out.step), _stream(stream))
+    else:
+        st = lib().qlora_quantize(_ptr(W), N, K, cid, BLOCKSIZE, DQ_BLOCKSIZE, _ptr(out.codes),
+                                  _ptr(out.q8), _ptr(out.step), _stream(stream))
     check(st, "nf4_quantize")
     return out
 
@@ -179,10 +200,11 @@ class QLoRALinearFunction(torch.autograd.Function):
 class QLoRALinear(torch.nn.Module):
     """A frozen NF4 weight with a trainable LoRA pair (A: r x K, B: N x r)."""
 
-    def __init__(self, weight_fp32: torch.Tensor, r: int, alpha: float, A=None, B=None):
+    def __init__(self, weight_fp32: torch.Tensor, r: int, alpha: float, A=None, B=None,
+                 code: str = "nf4"):
         super().__init__()
         N, K = weight_fp32.shape
-        self.nf4 = nf4_quantize(weight_fp32.float().contiguous())
+        self.nf4 = nf4_quantize(weight_fp32.float().contiguous(), code=code)
         self.r, self.alpha = r, alpha
         dev = weight_fp32.device
         self.A = torch.nn.Parameter(A if A is not None else

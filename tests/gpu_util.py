@@ -31,9 +31,9 @@ def f32(b: np.ndarray) -> np.ndarray:
     return nf4.bf16_bits_to_f32(b)
 
 
-def gpu_quantize(W: np.ndarray):
+def gpu_quantize(W: np.ndarray, code: str = "nf4"):
     Wd = torch.from_numpy(np.ascontiguousarray(W, dtype=np.float32)).cuda()
-    w = qn.nf4_quantize(Wd)
+    w = qn.nf4_quantize(Wd, code=code)
     torch.cuda.synchronize()
     return w
 
@@ -57,10 +57,10 @@ def assert_close(name: str, got: np.ndarray, ref: np.ndarray, tol: float = TOL) 
     return e
 
 
-def oracle_what(W: np.ndarray) -> np.ndarray:
+def oracle_what(W: np.ndarray, code: str = "nf4") -> np.ndarray:
     """Oracle-side quantize + dequantize, as fp32 values of the bf16 W_hat."""
-    packed, q8, step = nf4.quantize(W)
-    return f32(nf4.dequantize(packed, q8, step, *W.shape))
+    packed, q8, step = nf4.quantize(W, code=code)
+    return f32(nf4.dequantize(packed, q8, step, *W.shape, code=code))
 
 
 def oracle_what_from_state(codes, q8, step, N, K) -> np.ndarray:

@@ -68,6 +68,37 @@ def test_threshold_rule_is_nearest_level_for_every_fp32_in_unit_interval():
         assert bad == 0, hex(first.value)
 
 
+@pytest.mark.parametrize("code", ["nf4", "fp4"])
+def test_code_table_values_match_oracle(code):
+    lv, th = qn.code_table(code)
+    assert np.array_equal(np.array(lv, np.float32).view(np.uint32),
+                          nf4.code_values(code).view(np.uint32))
+    assert len(th) == (15 if code == "nf4" else 14)
+    with tempfile.TemporaryDirectory() as d:
+        so = os.path.join(d, "exh.so")
+        src = os.path.join(ROOT, "tests", "csrc", "exhaustive_nearest.c")
+        subprocess.run(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", src, "-o", so, "-lm"],
+                       check=True)
+        E = ctypes.CDLL(so)
+        E.nearest_value_mismatches.restype = ctypes.c_long
+        E.nearest_value_mismatches.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                               ctypes.POINTER(ctypes.c_uint32)]
+        L = (ctypes.c_float * 16)(*lv)
+        T = (ctypes.c_float * 15)(*(th + [0.0] * (15 - len(th))))
+        first = ctypes.c_uint32(0)
+        bad = E.nearest_value_mismatches(ctypes.cast(L, ctypes.c_void_p),
+                                         ctypes.cast(T, ctypes.c_void_p), len(th),
+                                         ctypes.byref(first))
+        assert bad == 0, hex(first.value)
+
+
+def test_code_table_rejects_unknown_type():
+    L = qn.lib()
+    assert L.qlora_code_table(7, None, None) == _lib.QLORA_ERR_UNSUPPORTED
+    with pytest.raises(ValueError):
+        qn.code_table("int4")
+
+
 def test_storage_bytes_closed_form():
     for N, K in [(1, 64), (3, 1024), (1024, 1024), (22016, 8192), (5120, 13824)]:
         assert qn.storage_bytes(N, K) == nf4.storage_bytes(N, K)
@@ -84,8 +115,8 @@ def test_workspace_size_rules():
 FAKE = 1 << 20  # an aligned non-null address that is never dereferenced
 
 
-def _w(N=64, K=64, bs=64, dq=256, codes=FAKE):
-    return _lib.Nf4Tensor(codes, FAKE, FAKE, N, K, bs, dq)
+def _w(N=64, K=64, bs=64, dq=256, codes=FAKE, code_type=_lib.QLORA_CODE_NF4):
+    return _lib.Nf4Tensor(codes, FAKE, FAKE, N, K, bs, dq, code_type)
 
 
 def test_quantize_rejects_bad_arguments_without_launching():
@@ -103,6 +134,13 @@ def test_quantize_rejects_bad_arguments_without_launching():
     assert call(bs=32) == _lib.QLORA_ERR_UNSUPPORTED
     assert call(dq=128) == _lib.QLORA_ERR_UNSUPPORTED
     assert call(W=FAKE + 4) == _lib.QLORA_ERR_INVALID
+    # the code-type variant: unknown types are rejected, the checks above apply
+    for ct, want in ((2, _lib.QLORA_ERR_UNSUPPORTED), (-1, _lib.QLORA_ERR_UNSUPPORTED)):
+        assert L.qlora_quantize(FAKE, 4, 128, ct, 64, 256, FAKE, FAKE, FAKE, None) == want
+    assert L.qlora_quantize(None, 4, 128, _lib.QLORA_CODE_FP4, 64, 256, FAKE, FAKE, FAKE,
+                            None) == _lib.QLORA_ERR_INVALID
+    assert L.qlora_quantize(FAKE, 4, 96, _lib.QLORA_CODE_FP4, 64, 256, FAKE, FAKE, FAKE,
+                            None) == _lib.QLORA_ERR_INVALID
 
 
 def test_linear_rejects_bad_arguments_without_launching():
@@ -120,6 +158,7 @@ def test_linear_rejects_bad_arguments_without_launching():
     assert fwd(w=_w(64, 100)) == _lib.QLORA_ERR_INVALID
     assert fwd(w=_w(60, 128)) == _lib.QLORA_ERR_INVALID
     assert fwd(w=_w(64, 128, bs=128)) == _lib.QLORA_ERR_UNSUPPORTED
+    assert fwd(w=_w(64, 128, code_type=5)) == _lib.QLORA_ERR_UNSUPPORTED
     assert fwd(w=_w(64, 128, codes=None)) == _lib.QLORA_ERR_INVALID
     assert fwd(nbytes=need - 1) == _lib.QLORA_ERR_WORKSPACE
     assert fwd(ws=None) == _lib.QLORA_ERR_INVALID
@@ -138,6 +177,10 @@ def test_linear_rejects_bad_arguments_without_launching():
 
     w = _w(64, 128)
     assert L.nf4_dequantize(ctypes.byref(w), None, None) == _lib.QLORA_ERR_INVALID
+    w = _w(64, 128, code_type=3)
+    assert L.nf4_dequantize(ctypes.byref(w), FAKE, None) == _lib.QLORA_ERR_UNSUPPORTED
+    assert L.qlora_linear_bwd(ctypes.byref(w), FAKE, FAKE, 32, FAKE, FAKE, None, 8, 1.0, None,
+                              FAKE, FAKE, FAKE, needb, None) == _lib.QLORA_ERR_UNSUPPORTED
 
 
 def test_status_strings():
