@@ -17,6 +17,14 @@ What the pages fix, and where:
 * The base is quantized once and dequantized to 16 bits on every forward and
   backward pass (blog section "Where the memory goes").
 
+k-bit NormalFloat (NF3, NF2): the ModuLoRA abstract ("ModuLoRA: Finetuning
+2-Bit LLMs on Consumer GPUs by Integrating with Modular Quantizers") finetunes
+through 2-, 3- and 4-bit weights with a backward pass that materializes the
+low-precision weight from whatever quantizer produced it.  Here the 2- and
+3-bit types are NormalFloat built the NF4 way with 2^k levels (see
+``nfk_levels_f64``), under the same blockwise absmax and double quantization;
+the codes are packed densely at k bits per weight (see ``pack_codes_k``).
+
 FP4, the other data type the capability page "Qlora 4 Bit Quantization With
 Nf4 Fp4 Data Types And Lora Adapters" names in its title (and the plain
 4-bit float NF4 is compared against in the blog section "NormalFloat, double
@@ -107,6 +115,43 @@ def nf4_levels() -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
+# k-bit NormalFloat
+# --------------------------------------------------------------------------
+
+def nfk_delta(k: int) -> float:
+    """Outermost probability of the k-bit type: the average of the centres
+    of the last bins of a (2^k - 1)-bin and a 2^k-bin grid on [0, 1], the
+    same offset as NF4's (k = 4 gives 1 - (1/30 + 1/32)/2)."""
+    n = 2 ** k
+    return 1.0 - 0.5 * (1.0 / (2 * (n - 1)) + 1.0 / (2 * n))
+
+
+def nfk_levels_f64(k: int) -> np.ndarray:
+    """The 2^k NormalFloat levels for k = 2, 3, 4 in fp64, ascending.
+
+    Reading (the pages give the construction only for 4 bits): an exact
+    zero, 2^(k-1) positive levels at probabilities evenly spaced from delta
+    down to (not including) 1/2, and 2^(k-1) - 1 negative levels mirrored
+    from evenly spaced probabilities on the same interval, all divided by
+    Phi^{-1}(delta) so that the outermost are -1 and +1.  For k = 4 this is
+    ``nf4_levels_f64``.
+    """
+    if k not in (2, 3, 4):
+        raise ValueError("k must be 2, 3 or 4")
+    d = nfk_delta(k)
+    half = 2 ** (k - 1)
+    pos = [normal_quantile(d - (d - 0.5) * i / half) for i in range(half)]
+    neg = [-normal_quantile(d - (d - 0.5) * j / (half - 1)) for j in range(half - 1)]
+    top = normal_quantile(d)
+    return np.array([v / top for v in sorted(neg + [0.0] + pos)], dtype=np.float64)
+
+
+def nfk_levels(k: int) -> np.ndarray:
+    """The k-bit NormalFloat levels rounded once to fp32."""
+    return nfk_levels_f64(k).astype(np.float32)
+
+
+# --------------------------------------------------------------------------
 # FP4 (E2M1) values
 # --------------------------------------------------------------------------
 
@@ -135,15 +180,26 @@ def fp4_values() -> np.ndarray:
     return fp4_values_f64().astype(np.float32)
 
 
-CODE_TYPES = ("nf4", "fp4")
+CODE_TYPES = ("nf4", "fp4", "nf3", "nf2")
+CODE_BITS = {"nf4": 4, "fp4": 4, "nf3": 3, "nf2": 2}
+
+
+def code_bits(code: str) -> int:
+    if code not in CODE_BITS:
+        raise ValueError(f"unknown code type {code!r}")
+    return CODE_BITS[code]
 
 
 def code_values(code: str = "nf4") -> np.ndarray:
-    """fp32 value of each of the 16 codes of a code type, in code order."""
+    """fp32 value of each of the 2^bits codes of a code type, in code order."""
     if code == "nf4":
         return nf4_levels()
     if code == "fp4":
         return fp4_values()
+    if code == "nf3":
+        return nfk_levels(3)
+    if code == "nf2":
+        return nfk_levels(2)
     raise ValueError(f"unknown code type {code!r}")
 
 
@@ -252,6 +308,56 @@ def unpack_codes(packed: np.ndarray) -> np.ndarray:
     return out
 
 
+def _kbit_positions(bits: int):
+    """For the 64 elements of a block: (word, bit) of each code bit, bit b of
+    the code of element e going to bit pos[b][e] of little-endian uint32
+    word word[b][e] of the block's 2 k words (k = bits).
+
+    Layout (chosen so that 8 consecutive codes unpack with a few shifts and
+    masks): a block is two halves of 32 elements, each half k words; write
+    element e = 32 h + 8 g + 2 i + p (g, i in 0..3, p in 0..1).  Code bits 0
+    and 1 go to bits 8 i + 2 g and 8 i + 2 g + 1 of word k h + p (the even
+    elements of a half in its first word, the odd ones in the second).  For
+    k = 3, code bit 2 goes to bit (8 i + 2 + 2 g + p) mod 32 of word 3 h + 2.
+    """
+    e = np.arange(64)
+    h, g, i, p = e >> 5, (e >> 3) & 3, (e >> 1) & 3, e & 1
+    word = [bits * h + p, bits * h + p]
+    pos = [8 * i + 2 * g, 8 * i + 2 * g + 1]
+    if bits == 3:
+        word.append(3 * h + 2)
+        pos.append((8 * i + 2 + 2 * g + p) % 32)
+    return word, pos
+
+
+def pack_codes_k(codes: np.ndarray, bits: int) -> np.ndarray:
+    """Pack codes of ``bits`` bits (4: ``pack_codes``; 3 or 2: the layout of
+    ``_kbit_positions``, 8 * bits bytes per 64-element block)."""
+    if bits == 4:
+        return pack_codes(codes)
+    c = np.ascontiguousarray(codes, dtype=np.uint32).reshape(-1, 64)
+    words = np.zeros((c.shape[0], 2 * bits), dtype=np.uint32)
+    wsel, pos = _kbit_positions(bits)
+    for b in range(bits):
+        bit = (c >> np.uint32(b)) & np.uint32(1)
+        for e in range(64):
+            words[:, wsel[b][e]] |= bit[:, e] << np.uint32(pos[b][e])
+    return words.astype("<u4").view(np.uint8).reshape(-1)
+
+
+def unpack_codes_k(packed: np.ndarray, bits: int) -> np.ndarray:
+    if bits == 4:
+        return unpack_codes(packed)
+    w = np.ascontiguousarray(packed, dtype=np.uint8).view("<u4").reshape(-1, 2 * bits)
+    out = np.zeros((w.shape[0], 64), dtype=np.uint8)
+    wsel, pos = _kbit_positions(bits)
+    for b in range(bits):
+        for e in range(64):
+            out[:, e] |= (((w[:, wsel[b][e]] >> np.uint32(pos[b][e])) & np.uint32(1))
+                          << np.uint32(b)).astype(np.uint8)
+    return out.reshape(-1)
+
+
 def double_quantize(c: np.ndarray, dq_blocksize: int = DQ_BLOCKSIZE):
     """Quantize the absmax constants to 8 bits under a coarser fp32 level.
 
@@ -290,7 +396,7 @@ def quantize(W: np.ndarray, blocksize: int = BLOCKSIZE, dq_blocksize: int = DQ_B
     c = block_absmax(W, blocksize)
     x = normalize(W, c, blocksize)
     codes = nearest_code(x, code_values(code))
-    packed = pack_codes(codes)
+    packed = pack_codes_k(codes, code_bits(code))
     q8, step = double_quantize(c, dq_blocksize)
     return packed, q8, step
 
@@ -306,7 +412,7 @@ def dequantize_f32(packed, q8, step, N, K, blocksize=BLOCKSIZE, dq_blocksize=DQ_
                    code="nf4") -> np.ndarray:
     """fl32(value[code] * c_hat_b) as fp32 [N, K], before the bf16 rounding."""
     levels = code_values(code)
-    codes = unpack_codes(packed)
+    codes = unpack_codes_k(packed, code_bits(code))
     chat = dequant_constants(q8, step, dq_blocksize)
     vals = levels[codes].reshape(-1, blocksize) * chat[:, None]
     return vals.astype(np.float32).reshape(N, K)
@@ -318,7 +424,8 @@ def dequantize(packed, q8, step, N, K, blocksize=BLOCKSIZE, dq_blocksize=DQ_BLOC
     return f32_to_bf16_bits(dequantize_f32(packed, q8, step, N, K, blocksize, dq_blocksize, code))
 
 
-def storage_bytes(N: int, K: int, blocksize=BLOCKSIZE, dq_blocksize=DQ_BLOCKSIZE) -> int:
+def storage_bytes(N: int, K: int, blocksize=BLOCKSIZE, dq_blocksize=DQ_BLOCKSIZE,
+                  code="nf4") -> int:
     """Bytes of the quantized state: packed codes + 8-bit constants + fp32 steps."""
     nb = N * K // blocksize
-    return N * K // 2 + nb + 4 * ((nb + dq_blocksize - 1) // dq_blocksize)
+    return N * K * code_bits(code) // 8 + nb + 4 * ((nb + dq_blocksize - 1) // dq_blocksize)

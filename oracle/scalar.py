@@ -53,6 +53,52 @@ def bf16_bits(x: float) -> int:
     return (lo >> 16) if ((lo >> 16) & 1) == 0 else ((hi >> 16) & 0xFFFF)
 
 
+def pack_kbit(codes, bits):
+    """Pack a flat list of codes (length a multiple of 64) into bytes.
+
+    bits = 4: element 2j in the low nibble of byte j.  bits = 3 or 2: per
+    64-element block, 2 * bits little-endian 32-bit words; element
+    e = 32 h + 8 g + 2 i + p puts code bits 0-1 at bit 8 i + 2 g of word
+    bits * h + p and, for 3 bits, code bit 2 at bit (8 i + 2 + 2 g + p) % 32
+    of word 3 h + 2.
+    """
+    if bits == 4:
+        return bytes(codes[2 * j] | (codes[2 * j + 1] << 4) for j in range(len(codes) // 2))
+    out = bytearray()
+    for b0 in range(0, len(codes), 64):
+        words = [0] * (2 * bits)
+        for e in range(64):
+            c = codes[b0 + e]
+            h, g, i, p = e // 32, (e // 8) % 4, (e // 2) % 4, e % 2
+            words[bits * h + p] |= (c & 3) << (8 * i + 2 * g)
+            if bits == 3:
+                words[3 * h + 2] |= ((c >> 2) & 1) << ((8 * i + 2 + 2 * g + p) % 32)
+        for w in words:
+            out += struct.pack("<I", w)
+    return bytes(out)
+
+
+def unpack_kbit(packed, bits, n):
+    """Inverse of pack_kbit for n codes."""
+    if bits == 4:
+        out = []
+        for byte in packed:
+            out += [byte & 0xF, byte >> 4]
+        return out[:n]
+    out = []
+    wb = 8 * bits  # bytes per block
+    for b0 in range(0, n, 64):
+        blk = packed[(b0 // 64) * wb:(b0 // 64 + 1) * wb]
+        words = list(struct.unpack("<%dI" % (2 * bits), blk))
+        for e in range(64):
+            h, g, i, p = e // 32, (e // 8) % 4, (e // 2) % 4, e % 2
+            c = (words[bits * h + p] >> (8 * i + 2 * g)) & 3
+            if bits == 3:
+                c |= ((words[3 * h + 2] >> ((8 * i + 2 + 2 * g + p) % 32)) & 1) << 2
+            out.append(c)
+    return out
+
+
 def quantize(W, levels, blocksize=64, dq_blocksize=256):
     """W: list of rows (lists of fp32-representable floats).  levels: the 16
     fp32-representable code values in code order (ascending for NF4; for
@@ -81,7 +127,8 @@ def quantize(W, levels, blocksize=64, dq_blocksize=256):
                 if bestd is None or d < bestd or (d == bestd and lv < levels[best]):
                     best, bestd = i, d
             codes.append(best)
-    packed = bytes(codes[2 * j] | (codes[2 * j + 1] << 4) for j in range(n // 2))
+    bits = {16: 4, 8: 3, 4: 2}[len(levels)]
+    packed = pack_kbit(codes, bits)
     q8, steps = [], []
     for g in range(0, nb, dq_blocksize):
         grp = c[g:g + dq_blocksize]
@@ -100,11 +147,11 @@ def quantize(W, levels, blocksize=64, dq_blocksize=256):
 
 def dequantize(packed, q8, steps, levels, blocksize=64, dq_blocksize=256):
     """Returns the bf16 bit patterns of W_hat, flat, row-major."""
+    bits = {16: 4, 8: 3, 4: 2}[len(levels)]
+    n = len(packed) * 8 // bits
     out = []
-    for j, byte in enumerate(packed):
-        for code in (byte & 0xF, byte >> 4):
-            e = len(out)
-            b = e // blocksize
-            chat = f32(float(q8[b]) * steps[b // dq_blocksize])
-            out.append(bf16_bits(f32(levels[code] * chat)))
+    for e, code in enumerate(unpack_kbit(packed, bits, n)):
+        b = e // blocksize
+        chat = f32(float(q8[b]) * steps[b // dq_blocksize])
+        out.append(bf16_bits(f32(levels[code] * chat)))
     return out
