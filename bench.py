@@ -250,8 +250,9 @@ def main():
     extra = {}
     if not args.no_extra:
         extra = run_extras(qn, L, ev, torch, dev, sp, d16)
-        extra["fp4"] = fp4_step(qn, L, torch, layers, M, r, s, sp, args.steps, args.warmup,
-                                flops_step)
+        for code in ("fp4", "nf3", "nf2"):
+            extra["code_types"][code]["fused_step"] = code_step(
+                qn, L, torch, layers, M, r, s, sp, args.steps, args.warmup, flops_step, code)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -282,12 +283,12 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def fp4_step(qn, L, torch, layers, M, r, s, sp, steps, warmup, flops_step):
+def code_step(qn, L, torch, layers, M, r, s, sp, steps, warmup, flops_step, code):
     """The same fused forward + backward step with the weights quantized to
-    the FP4 code type instead of NF4 (same kernels, other code table)."""
+    another code type (same kernels, other code table and width)."""
     from quantized_base_lora_nf4_amd._lib import check
-    fp4 = [qn.nf4_quantize(t["Wf32"], code="fp4") for t in layers]
-    sts = [w.struct() for w in fp4]
+    qw = [qn.nf4_quantize(t["Wf32"], code=code) for t in layers]
+    sts = [w.struct() for w in qw]
 
     def p(x):
         return x.data_ptr() if x is not None else None
@@ -296,10 +297,10 @@ def fp4_step(qn, L, torch, layers, M, r, s, sp, steps, warmup, flops_step):
         for t, st in zip(layers, sts):
             check(L.qlora_linear_fwd(ctypes.byref(st), p(t["X"]), M, p(t["A"]), p(t["B"]), r, s,
                                      p(t["Y"]), p(t["U"]), p(t["wsf"]), t["wsf"].numel(), sp),
-                  "fp4 fwd")
+                  f"{code} fwd")
             check(L.qlora_linear_bwd(ctypes.byref(st), p(t["X"]), p(t["dY"]), M, p(t["A"]),
                                      p(t["B"]), p(t["U"]), r, s, p(t["dX"]), p(t["dA"]),
-                                     p(t["dB"]), p(t["wsb"]), t["wsb"].numel(), sp), "fp4 bwd")
+                                     p(t["dB"]), p(t["wsb"]), t["wsb"].numel(), sp), f"{code} bwd")
     for _ in range(warmup):
         one()
     torch.cuda.synchronize()
@@ -311,9 +312,9 @@ def fp4_step(qn, L, torch, layers, M, r, s, sp, steps, warmup, flops_step):
     t1.record()
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / steps
-    del fp4
-    return {"code": "fp4 (E2M1 / 6)", "ms_per_step": round(ms, 4),
-            "TFLOP/s": round(flops_step / (ms * 1e-3) / 1e12, 2), "steps": steps}
+    del qw
+    return {"ms_per_step": round(ms, 4), "TFLOP/s": round(flops_step / (ms * 1e-3) / 1e12, 2),
+            "steps": steps}
 
 
 def run_extras(qn, L, ev, torch, dev, sp, d16):
@@ -322,7 +323,8 @@ def run_extras(qn, L, ev, torch, dev, sp, d16):
     from the 256 MB Infinity Cache."""
     from quantized_base_lora_nf4_amd._lib import check
     import workloads as wl_mod
-    res = {"gemv": [], "quantize": [], "copy": None}
+    res = {"gemv": [], "quantize": [], "copy": None,
+           "code_types": {c: {"gemv_M1": []} for c in ("fp4", "nf3", "nf2")}}
     # measured streaming reference next to the 8 TB/s spec: a plain 1 GiB
     # device copy (reads 1 GiB, writes 1 GiB; larger than the Infinity Cache)
     src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
@@ -372,16 +374,17 @@ def run_extras(qn, L, ev, torch, dev, sp, d16):
         for M in g.M:
             res["gemv"].append(_time_gemv(L, torch, ev, structs, inp, M, N, K, g, A, B, d16, dev,
                                           sp, wbytes, e0, e1))
-        if wi == 0:
-            # the FP4 code type on the same kernel, one token
+        # the other code types on the same kernel, one token; GB/s counts
+        # each type's own weight bytes
+        for code in ("fp4", "nf3", "nf2"):
             del copies, structs
             torch.cuda.empty_cache()
-            copies = [qn.nf4_quantize(W, code="fp4") for _ in range(ncopy)]
+            cb = qn.storage_bytes(N, K, code)
+            nc = max(3, int(np.ceil(768e6 / cb)))
+            copies = [qn.nf4_quantize(W, code=code) for _ in range(nc)]
             structs = [c.struct() for c in copies]
-            row = _time_gemv(L, torch, ev, structs, inp, 1, N, K, g, A, B, d16, dev, sp, wbytes,
-                             e0, e1)
-            row["code"] = "fp4"
-            res["gemv_fp4"] = [row]
+            res["code_types"][code]["gemv_M1"].append(
+                _time_gemv(L, torch, ev, structs, inp, 1, N, K, g, A, B, d16, dev, sp, cb, e0, e1))
         del copies, W
         torch.cuda.empty_cache()
     return res

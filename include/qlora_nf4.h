@@ -46,7 +46,23 @@
  *                   magnitudes {0, 1/2, 1, 3/2, 2, 3, 4, 6}, divided by 6
  *                   so the largest is 1, rounded once to fp32; code 8 is -0
  *                   and the quantizer writes code 0 for zero.
- *   Block scaling, double quantization and storage are the same for both.
+ *   QLORA_CODE_NF3, QLORA_CODE_NF2  k-bit NormalFloat, k = 3, 2 (the
+ *                   "ModuLoRA: Finetuning 2-Bit LLMs on Consumer GPUs by
+ *                   Integrating with Modular Quantizers" abstract finetunes
+ *                   through 2-, 3- and 4-bit weights): 2^k levels built as
+ *                   NF4's are (exact zero, 2^(k-1) positive and 2^(k-1)-1
+ *                   negative levels at evenly spaced normal probabilities
+ *                   up to delta_k = 1 - (1/(2(2^k-1)) + 1/2^(k+1))/2, over
+ *                   Phi^{-1}(delta_k)); ascending with the code.
+ *   Block scaling and double quantization are the same for all types.
+ *
+ * Code storage by width k (4 for NF4 and FP4): a 64-element block takes
+ * 8k bytes, two halves of 4k bytes (k little-endian 32-bit words) for
+ * elements 0..31 and 32..63.  k = 4: the layout above (element 2j of the
+ * block in the low nibble of byte j).  k = 3, 2: within a half, element
+ * 8g + 2i + p (g, i in 0..3, p in 0..1) keeps code bits 0-1 at bit 8i + 2g
+ * of word p and, for k = 3, code bit 2 at bit (8i + 2 + 2g + p) mod 32 of
+ * word 2.  `codes` then holds N*K*k/8 bytes.
  *
  * Conventions for every call:
  *   - bf16 tensors are passed as uint16_t bit patterns.
@@ -83,6 +99,8 @@ extern "C" {
 
 #define QLORA_CODE_NF4 0
 #define QLORA_CODE_FP4 1
+#define QLORA_CODE_NF3 2
+#define QLORA_CODE_NF2 3
 
 #define QLORA_NF4_BLOCKSIZE 64
 #define QLORA_NF4_DQ_BLOCKSIZE 256
@@ -90,15 +108,15 @@ extern "C" {
 
 /* The quantized frozen weight.  All pointers are device pointers. */
 typedef struct nf4_tensor_t {
-  const uint8_t* codes; /* [N*K/2]  */
+  const uint8_t* codes; /* [N*K*k/8], k = bits of code_type */
   const uint8_t* q8;    /* [N*K/64] */
   const float* step;    /* [ceil(N*K/16384)] */
   int64_t N;
   int64_t K;
   int32_t blocksize;    /* must be 64  */
   int32_t dq_blocksize; /* must be 256 */
-  int32_t code_type;    /* QLORA_CODE_NF4 or QLORA_CODE_FP4 (the type it was
-                           quantized with); others give QLORA_ERR_UNSUPPORTED */
+  int32_t code_type;    /* QLORA_CODE_* (the type it was quantized with);
+                           others give QLORA_ERR_UNSUPPORTED */
 } nf4_tensor_t;
 
 /* Text for a status code (static storage, never NULL). */
@@ -113,17 +131,22 @@ const char* qlora_status_str(int32_t status);
  * section "NormalFloat, double quantization, paged optimizers"). */
 void nf4_code_table(float* levels16, float* thresholds15);
 
-/* Host-side copy of the value of each of the 16 codes of `code_type` (in
- * code order, fp32) and of its decision thresholds: the fp32 midpoint of
- * each pair of consecutive distinct values, rounded toward -inf, ascending
- * (NF4: 15; FP4: 14, since +0 and -0 are one value, and thresholds15[14] is
- * set to 0).  Returns the number of thresholds, or QLORA_ERR_UNSUPPORTED for
- * an unknown code type.  Either pointer may be NULL; no device work. */
+/* Host-side copy of the value of each code of `code_type` (in code order,
+ * fp32; entries past 2^k are 0) and of its decision thresholds: the fp32
+ * midpoint of each pair of consecutive distinct values, rounded toward
+ * -inf, ascending (NF4: 15; FP4: 14, since +0 and -0 are one value; NF3: 7;
+ * NF2: 3; the rest of thresholds15 is set to 0).  Returns the number of
+ * thresholds, or QLORA_ERR_UNSUPPORTED for an unknown code type.  Either
+ * pointer may be NULL; no device work. */
 int32_t qlora_code_table(int32_t code_type, float* levels16, float* thresholds15);
 
 /* Bytes of the three NF4 arrays for an N x K weight (closed form:
  * N*K/2 + N*K/64 + 4*ceil(N*K/16384)); 0 for invalid sizes. */
 size_t nf4_storage_bytes(int64_t N, int64_t K);
+
+/* The same for any code type: N*K*k/8 + N*K/64 + 4*ceil(N*K/16384) with k
+ * its width in bits; 0 for invalid sizes or an unknown code type. */
+size_t qlora_storage_bytes(int32_t code_type, int64_t N, int64_t K);
 
 /* nf4_quantize -- blockwise NF4 quantization with double-quantized absmax
  * constants, once per frozen weight (blog section "NormalFloat, double
@@ -145,10 +168,11 @@ int32_t nf4_quantize(const float* W, int64_t N, int64_t K, int32_t blocksize,
                      int32_t dq_blocksize, uint8_t* codes, uint8_t* q8,
                      float* step, hipStream_t stream);
 
-/* qlora_quantize -- nf4_quantize for either code type: identical except that
+/* qlora_quantize -- nf4_quantize for any code type: identical except that
  * each element gets the code of the value of `code_type` nearest to
  * fl32(w / c_b) (ties to the lower value; zero, and an all-zero block, get
- * the code of zero: 7 for NF4, 0 for FP4).  An unknown code type gives
+ * the code of zero: 7 for NF4, 0 for FP4, 3 for NF3, 1 for NF2), stored at
+ * the type's width (codes [N*K*k/8]).  An unknown code type gives
  * QLORA_ERR_UNSUPPORTED.  nf4_quantize(...) is
  * qlora_quantize(..., QLORA_CODE_NF4, ...). */
 int32_t qlora_quantize(const float* W, int64_t N, int64_t K, int32_t code_type,

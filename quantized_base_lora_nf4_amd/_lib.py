@@ -18,6 +18,8 @@ QLORA_ERR_LAUNCH = -4
 
 QLORA_CODE_NF4 = 0
 QLORA_CODE_FP4 = 1
+QLORA_CODE_NF3 = 2
+QLORA_CODE_NF2 = 3
 
 # Every symbol the header declares.
 EXPORTS = (
@@ -25,6 +27,7 @@ EXPORTS = (
     "nf4_code_table",
     "qlora_code_table",
     "nf4_storage_bytes",
+    "qlora_storage_bytes",
     "nf4_quantize",
     "qlora_quantize",
     "nf4_dequantize",
@@ -77,6 +80,8 @@ def lib() -> ctypes.CDLL:
     L.qlora_code_table.argtypes = [i32, vp, vp]
     L.nf4_storage_bytes.restype = sz
     L.nf4_storage_bytes.argtypes = [i64, i64]
+    L.qlora_storage_bytes.restype = sz
+    L.qlora_storage_bytes.argtypes = [i32, i64, i64]
     L.nf4_quantize.restype = i32
     L.nf4_quantize.argtypes = [vp, i64, i64, i32, i32, vp, vp, vp, vp]
     L.qlora_quantize.restype = i32

@@ -71,7 +71,8 @@ bool nf4_ok(const nf4_tensor_t* w) {
 }
 
 inline bool code_ok(int32_t code_type) {
-  return code_type == QLORA_CODE_NF4 || code_type == QLORA_CODE_FP4;
+  return code_type == QLORA_CODE_NF4 || code_type == QLORA_CODE_FP4 ||
+         code_type == QLORA_CODE_NF3 || code_type == QLORA_CODE_NF2;
 }
 
 int32_t nf4_supported(const nf4_tensor_t* w) {
@@ -81,7 +82,8 @@ int32_t nf4_supported(const nf4_tensor_t* w) {
              : QLORA_ERR_UNSUPPORTED;
 }
 
-static_assert(CodeNF4::kId == QLORA_CODE_NF4 && CodeFP4::kId == QLORA_CODE_FP4,
+static_assert(CodeNF4::kId == QLORA_CODE_NF4 && CodeFP4::kId == QLORA_CODE_FP4 &&
+                  CodeNF3::kId == QLORA_CODE_NF3 && CodeNF2::kId == QLORA_CODE_NF2,
               "code type ids of the ABI and of the kernels agree");
 
 template <class CT>
@@ -128,9 +130,17 @@ void nf4_code_table(float* levels16, float* thresholds15) {
 }
 
 int32_t qlora_code_table(int32_t code_type, float* levels16, float* thresholds15) {
-  if (code_type == QLORA_CODE_NF4) return copy_table<CodeNF4>(levels16, thresholds15);
-  if (code_type == QLORA_CODE_FP4) return copy_table<CodeFP4>(levels16, thresholds15);
-  return QLORA_ERR_UNSUPPORTED;
+  if (!code_ok(code_type)) return QLORA_ERR_UNSUPPORTED;
+  return with_code(code_type, [&](auto ct) {
+    return copy_table<decltype(ct)>(levels16, thresholds15);
+  });
+}
+
+size_t qlora_storage_bytes(int32_t code_type, int64_t N, int64_t K) {
+  if (!code_ok(code_type) || N < 1 || K < 64 || (K % 64) != 0) return 0;
+  const int64_t nb = N * K / 64;
+  const int64_t bits = with_code(code_type, [](auto ct) { return decltype(ct)::kBits; });
+  return (size_t)(N * K / 8 * bits) + (size_t)nb + 4 * (size_t)((nb + 255) / 256);
 }
 
 size_t nf4_storage_bytes(int64_t N, int64_t K) {

@@ -118,15 +118,40 @@ struct Fp4Bits {
 };
 constexpr Fp4Bits kFp4Bits{};
 
+// k-bit NormalFloat for k = 3 and 2 (the ModuLoRA abstract finetunes through
+// 2-, 3- and 4-bit weights): 2^k levels built the NF4 way, with an exact
+// zero, 2^(k-1) positive and 2^(k-1) - 1 negative levels at evenly spaced
+// normal probabilities up to delta_k = 1 - (1/(2(2^k-1)) + 1/2^(k+1)) / 2,
+// divided by Phi^{-1}(delta_k) and rounded once to fp32 (bits from scipy's
+// ndtri; every value sits more than 5e-9 relative from an fp32 rounding
+// boundary).  The 16-entry tables are padded with +0 past 2^k codes.
+constexpr uint32_t kNf3Bits[16] = {0xbf800000u, 0xbf08f740u, 0xbe7cdb98u, 0x00000000u,
+                                   0x3e3bbcd2u, 0x3ec394b6u, 0x3f1f7bfeu, 0x3f800000u};
+constexpr uint32_t kNf2Bits[16] = {0xbf800000u, 0x00000000u, 0x3edf238fu, 0x3f800000u};
+
 // Each code type also gives the code for a threshold count in closed form
-// (checked against the table below).
+// (checked against the table below) and its width in bits.
 struct CodeNF4 {
   static constexpr int kId = 0;
+  static constexpr int kBits = 4;
   static constexpr CodeTable table = make_code_table(kLevelBits);
+  __host__ __device__ static constexpr uint32_t code_of_count(uint32_t n) { return n; }
+};
+struct CodeNF3 {
+  static constexpr int kId = 2;
+  static constexpr int kBits = 3;
+  static constexpr CodeTable table = make_code_table(kNf3Bits);
+  __host__ __device__ static constexpr uint32_t code_of_count(uint32_t n) { return n; }
+};
+struct CodeNF2 {
+  static constexpr int kId = 3;
+  static constexpr int kBits = 2;
+  static constexpr CodeTable table = make_code_table(kNf2Bits);
   __host__ __device__ static constexpr uint32_t code_of_count(uint32_t n) { return n; }
 };
 struct CodeFP4 {
   static constexpr int kId = 1;
+  static constexpr int kBits = 4;
   static constexpr CodeTable table = make_code_table(kFp4Bits.b);
   // counts 0..6 are -1 .. -1/12 (codes 15..9), 7 is zero (code 0), 8..14 are
   // 1/12 .. 1 (codes 1..7)
@@ -140,7 +165,15 @@ constexpr bool count_map_sound() {
     if (CT::code_of_count((uint32_t)n) != CT::table.dist_code[n]) return false;
   return true;
 }
-static_assert(count_map_sound<CodeNF4>() && count_map_sound<CodeFP4>(), "count -> code maps");
+static_assert(count_map_sound<CodeNF4>() && count_map_sound<CodeFP4>() &&
+                  count_map_sound<CodeNF3>() && count_map_sound<CodeNF2>(),
+              "count -> code maps");
+static_assert(CodeNF3::table.ndist == 8 && CodeNF3::table.zero_code == 3 &&
+                  code_table_sound(CodeNF3::table),
+              "NF3: 8 distinct levels, zero is code 3");
+static_assert(CodeNF2::table.ndist == 4 && CodeNF2::table.zero_code == 1 &&
+                  code_table_sound(CodeNF2::table),
+              "NF2: 4 distinct levels, zero is code 1");
 static_assert(CodeNF4::table.ndist == 16 && CodeNF4::table.zero_code == 7 &&
                   code_table_sound(CodeNF4::table),
               "NF4: 16 distinct levels, zero is code 7, thresholds are the midpoints rounded down");
@@ -151,6 +184,78 @@ static_assert(CodeFP4::table.ndist == 15 && CodeFP4::table.zero_code == 0 &&
 template <class CT>
 __host__ __device__ constexpr float code_value(int c) {
   return __builtin_bit_cast(float, CT::table.level[c]);
+}
+
+// Call f(CT{}) for the code type with this id (NF4 for an unknown id; the C
+// ABI rejects unknown ids before any launch).
+template <class F>
+__host__ auto with_code(int id, F&& f) {
+  switch (id) {
+    case CodeFP4::kId: return f(CodeFP4{});
+    case CodeNF3::kId: return f(CodeNF3{});
+    case CodeNF2::kId: return f(CodeNF2{});
+    default: return f(CodeNF4{});
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Packed codes.  A 64-element block takes 8 k bytes (k = bits per code), as
+// two halves of 4 k bytes (k little-endian words) for elements 0..31 and
+// 32..63.  4 bits: element 2j of the block in the low nibble of byte j.
+// 3 and 2 bits: within a half, element 8 g + 2 i + p (g, i in 0..3, p in
+// 0..1) has code bits 0-1 at bit 8 i + 2 g of word p and, for 3 bits, code
+// bit 2 at bit (8 i + 2 + 2 g + p) mod 32 of word 2.  Every kernel loads a
+// half's words and expands each group of eight codes into one word of eight
+// nibbles (element order), which is the 4-bit layout, just before its
+// table lookup.
+// ---------------------------------------------------------------------------
+template <int kBits>
+struct HalfRaw {
+  uint32_t w[kBits];
+};
+
+template <class CT>
+__host__ __device__ constexpr int64_t block_bytes() {
+  return 8 * CT::kBits;
+}
+template <class CT>
+__host__ __device__ constexpr int64_t half_bytes() {
+  return 4 * CT::kBits;
+}
+
+// The words of one half block at p (4-byte aligned; 16-byte aligned for
+// 4 bits, 8-byte aligned for 2 bits).
+template <class CT>
+__device__ __forceinline__ HalfRaw<CT::kBits> load_half(const uint8_t* p) {
+  HalfRaw<CT::kBits> r;
+  if constexpr (CT::kBits == 4) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+    r.w[0] = v[0]; r.w[1] = v[1]; r.w[2] = v[2]; r.w[3] = v[3];
+  } else if constexpr (CT::kBits == 2) {
+    const u32x2 v = *reinterpret_cast<const u32x2*>(p);
+    r.w[0] = v[0]; r.w[1] = v[1];
+  } else {
+    const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
+    r.w[0] = q[0]; r.w[1] = q[1]; r.w[2] = q[2];
+  }
+  return r;
+}
+
+// Codes 8 g .. 8 g + 7 of a half as eight nibbles (element 8 g + j in
+// nibble j).
+template <class CT>
+__device__ __forceinline__ uint32_t nibbles(const HalfRaw<CT::kBits>& r, int g) {
+  if constexpr (CT::kBits == 4) {
+    return r.w[g];
+  } else {
+    uint32_t e = (r.w[0] >> (2 * g)) & 0x03030303u;  // codes of elements 8 g + 2 i
+    uint32_t o = (r.w[1] >> (2 * g)) & 0x03030303u;  // codes of elements 8 g + 2 i + 1
+    if constexpr (CT::kBits == 3) {
+      e |= __builtin_amdgcn_alignbit(r.w[2], r.w[2], 2 * g) & 0x04040404u;
+      o |= __builtin_amdgcn_alignbit(r.w[2], r.w[2], 2 * g + 1) & 0x04040404u;
+    }
+    return e | (o << 4);
+  }
 }
 
 // ---------------------------------------------------------------------------

@@ -190,12 +190,14 @@ __global__ __launch_bounds__(64 * KW) void k_qgemv(GemvArgs p) {
   const int64_t d0 = T * wave / KW, d1 = T * (wave + 1) / KW;
   const bool odd_tail = (kblocks & 1) && wave == KW - 1;
 
+  // Lane quarter q reads half (q & 1) of block (q >> 1) of each double step.
   const uint8_t* crow[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     int64_t n = n0 + 16 * g + i16;
     if (n >= N) n = N - 1;  // computed and dropped
-    crow[g] = p.codes + n * (K >> 1) + 16 * q;
+    crow[g] = p.codes + n * kblocks * block_bytes<CT>() + (q >> 1) * block_bytes<CT>() +
+              (q & 1) * half_bytes<CT>();
   }
   // X fragment of word j: row i16, columns 64 (kb + (j >> 1)) + xo + 8 (j & 1).
   // Rows past M re-read row 0; their results are never stored.
@@ -209,7 +211,7 @@ __global__ __launch_bounds__(64 * KW) void k_qgemv(GemvArgs p) {
   // Raw loads of one double step (codes, X fragments).  Nothing is computed
   // from them at issue, so issuing never waits for a load.
   struct Slot {
-    u32x4 c[G];
+    HalfRaw<CT::kBits> c[G];
     u32x4 x[4];
   };
   Slot sl[PD];
@@ -221,10 +223,10 @@ __global__ __launch_bounds__(64 * KW) void k_qgemv(GemvArgs p) {
   auto issue = [&](Slot& S, int64_t d, bool tail) {
     if (d >= d1 && !tail) d = d1 - 1;
     const int64_t kb = 2 * d;
-    const int64_t off = (tail && q >= 2) ? kb * 32 - 32 : kb * 32;
+    const int64_t off = ((tail && q >= 2) ? kb - 1 : kb) * block_bytes<CT>();
     const int64_t kb2 = tail ? kb : kb + 1;
 #pragma unroll
-    for (int g = 0; g < G; ++g) S.c[g] = *reinterpret_cast<const u32x4*>(crow[g] + off);
+    for (int g = 0; g < G; ++g) S.c[g] = load_half<CT>(crow[g] + off);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       S.x[j] = *reinterpret_cast<const u32x4*>(xrow + 64 * ((j >> 1) ? kb2 : kb) + 8 * (j & 1));
@@ -238,7 +240,9 @@ __global__ __launch_bounds__(64 * KW) void k_qgemv(GemvArgs p) {
     const int64_t kb = 2 * d;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      u32x4 c = S.c[g];
+      u32x4 c;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) c[j] = nibbles<CT>(S.c[g], j);
       // lanes 0-31: (block kb words 0, 1 | words 2, 3) -> keep 0, 1, take the
       // other half's 0, 1 into 2, 3; lanes 32-63 the mirror image.
       const auto s02 = __builtin_amdgcn_permlane32_swap(c[0], c[2], false, false);
@@ -420,24 +424,27 @@ hipError_t launch_qgemv(const Nf4View& w, const uint16_t* X, int64_t M, const ui
   // 32 weight rows per workgroup, K split over its 8 waves
   constexpr int G = 2, KW = 8, PD = QN_GEMV_PD;
   static const hipError_t attr = [] {
-    // dynamic LDS above the default 64 KB needs the limit raised, once
-    const hipError_t a = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&k_qgemv<G, KW, PD, QN_GEMV_PERM, CodeNF4>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
-    const hipError_t b = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&k_qgemv<G, KW, PD, QN_GEMV_PERM, CodeFP4>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
-    return a != hipSuccess ? a : b;
+    // dynamic LDS above the default 64 KB needs the limit raised, once per
+    // instantiation
+    hipError_t r = hipSuccess;
+    for (int id = 0; id < 4; ++id) {
+      const hipError_t a = with_code(id, [](auto ct) {
+        return hipFuncSetAttribute(
+            reinterpret_cast<const void*>(&k_qgemv<G, KW, PD, QN_GEMV_PERM, decltype(ct)>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
+      });
+      if (r == hipSuccess) r = a;
+    }
+    return r;
   }();
   if (attr != hipSuccess) return attr;
   const size_t lds = 4 * (size_t)gemv_lds_words(G, KW, M, r, kblocks);
   const dim3 grid((unsigned)((w.N + 16 * G - 1) / (16 * G)));
-  if (w.code == CodeFP4::kId)
-    hipLaunchKernelGGL((k_qgemv<G, KW, PD, QN_GEMV_PERM, CodeFP4>), grid, dim3(64 * KW), lds,
+  with_code(w.code, [&](auto ct) {
+    hipLaunchKernelGGL((k_qgemv<G, KW, PD, QN_GEMV_PERM, decltype(ct)>), grid, dim3(64 * KW), lds,
                        stream, a);
-  else
-    hipLaunchKernelGGL((k_qgemv<G, KW, PD, QN_GEMV_PERM, CodeNF4>), grid, dim3(64 * KW), lds,
-                       stream, a);
+    return 0;
+  });
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (ev1) e = hipEventRecord(ev1, stream);

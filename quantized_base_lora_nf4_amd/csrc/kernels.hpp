@@ -18,7 +18,7 @@ struct Nf4View {
   const uint8_t* q8;
   const float* step;
   int64_t N, K;
-  int code;  // CodeNF4::kId or CodeFP4::kId
+  int code;  // kId of CodeNF4, CodeFP4, CodeNF3 or CodeNF2
 };
 
 // Y[M,N] = X[M,K] W^T + bf16(s U)[M,r] B[N,r]^T.  U has row stride ldu (a

@@ -1,5 +1,5 @@
-// 4-bit quantizer (NF4 or FP4 code table) with double-quantized absmax
-// constants, and the standalone dequantizer.
+// Block quantizer (NF4, FP4, NF3 or NF2 code table) with double-quantized
+// absmax constants, and the standalone dequantizer.
 //
 // Quantization follows "QLoRA: fine-tuning a 65B model on one GPU", section
 // "NormalFloat, double quantization, paged optimizers" (16 levels at normal
@@ -10,9 +10,11 @@
 // Layout: one workgroup per group of 256 consecutive 64-element blocks
 // (16384 fp32 = 64 KB of W).  Each wave walks 64 blocks, four at a time:
 // sixteen lanes share a block and each lane owns four consecutive elements,
-// so every load instruction reads 1 KB of contiguous W and every store writes
-// 128 contiguous code bytes.  The kernel is bound by HBM (4 B read and
-// 0.52 B written per weight).
+// so every load instruction reads 1 KB of contiguous W.  4-bit codes are
+// stored by every lane (128 contiguous bytes per instruction); 3- and 2-bit
+// codes are ORed into their half block's words across the eight lanes of
+// the half and stored by its first lane.  The kernel is bound by HBM (4 B
+// read and at most 0.52 B written per weight).
 #include "kernels.hpp"
 
 namespace qn {
@@ -62,8 +64,33 @@ __global__ __launch_bounds__(256) void k_nf4_quantize(const float* __restrict__ 
       } else {
         c0 = c1 = c2 = c3 = CT::table.zero_code;  // all-zero block: the zero level
       }
-      const uint16_t packed = (uint16_t)(c0 | (c1 << 4) | (c2 << 8) | (c3 << 12));
-      *reinterpret_cast<uint16_t*>(codes + b * 32 + sub * 2) = packed;
+      if constexpr (CT::kBits == 4) {
+        const uint16_t packed = (uint16_t)(c0 | (c1 << 4) | (c2 << 8) | (c3 << 12));
+        *reinterpret_cast<uint16_t*>(codes + b * 32 + sub * 2) = packed;
+      } else {
+        // elements 4 sub + t = 32 h + 8 g + 2 i + p of the block
+        const int h = sub >> 3, g = (sub >> 1) & 3, i0 = 2 * (sub & 1);
+        const uint32_t cc[4] = {c0, c1, c2, c3};
+        uint32_t wv[3] = {0u, 0u, 0u};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int i = i0 + (t >> 1), pp = t & 1;
+          wv[pp] |= (cc[t] & 3u) << (8 * i + 2 * g);
+          if (CT::kBits == 3) wv[2] |= ((cc[t] >> 2) & 1u) << ((8 * i + 2 + 2 * g + pp) & 31);
+        }
+#pragma unroll
+        for (int j = 0; j < CT::kBits; ++j) {
+          wv[j] |= __shfl_xor(wv[j], 1, 16);
+          wv[j] |= __shfl_xor(wv[j], 2, 16);
+          wv[j] |= __shfl_xor(wv[j], 4, 16);
+        }
+        if ((sub & 7) == 0) {
+          uint32_t* dst =
+              reinterpret_cast<uint32_t*>(codes + b * block_bytes<CT>() + h * half_bytes<CT>());
+#pragma unroll
+          for (int j = 0; j < CT::kBits; ++j) dst[j] = wv[j];
+        }
+      }
       if (sub == 0) cabs[bi] = m;
     }
   }
@@ -90,7 +117,7 @@ __global__ __launch_bounds__(256) void k_nf4_quantize(const float* __restrict__ 
 }
 
 // Standalone dequantizer: w = bf16_rne(value[code] * fl32(q8 * step)).
-// Each thread expands four code bytes (eight weights) into 16 bytes of bf16.
+// Each thread expands eight codes (eight weights) into 16 bytes of bf16.
 template <class CT>
 __global__ __launch_bounds__(256) void k_nf4_dequantize(const uint8_t* __restrict__ codes,
                                                         const uint8_t* __restrict__ q8,
@@ -101,8 +128,14 @@ __global__ __launch_bounds__(256) void k_nf4_dequantize(const uint8_t* __restric
   __syncthreads();
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n8;
        i += (int64_t)gridDim.x * blockDim.x) {
-    const uint32_t w = *reinterpret_cast<const uint32_t*>(codes + i * 4);
     const int64_t b = i >> 3;  // 8 groups of 8 weights per 64-element block
+    uint32_t w;
+    if constexpr (CT::kBits == 4) {
+      w = *reinterpret_cast<const uint32_t*>(codes + i * 4);
+    } else {
+      const int hh = (int)((i >> 2) & 1), g = (int)(i & 3);
+      w = nibbles<CT>(load_half<CT>(codes + b * block_bytes<CT>() + hh * half_bytes<CT>()), g);
+    }
     const float chat = (float)q8[b] * step[b >> 8];
     u32x4 o;
 #pragma unroll
@@ -118,13 +151,11 @@ __global__ __launch_bounds__(256) void k_nf4_dequantize(const uint8_t* __restric
 hipError_t launch_nf4_quantize(const float* W, int64_t nblocks, uint8_t* codes, uint8_t* q8,
                                float* step, int code, hipStream_t stream) {
   const int64_t ngroups = (nblocks + 255) / 256;
-  if (code == CodeFP4::kId)
-    hipLaunchKernelGGL(k_nf4_quantize<CodeFP4>, dim3((unsigned)ngroups), dim3(256), 0, stream, W,
-                       nblocks, codes, q8, step);
-  else
-    hipLaunchKernelGGL(k_nf4_quantize<CodeNF4>, dim3((unsigned)ngroups), dim3(256), 0, stream, W,
-                       nblocks, codes, q8, step);
-  return hipGetLastError();
+  return with_code(code, [&](auto ct) {
+    hipLaunchKernelGGL(k_nf4_quantize<decltype(ct)>, dim3((unsigned)ngroups), dim3(256), 0,
+                       stream, W, nblocks, codes, q8, step);
+    return hipGetLastError();
+  });
 }
 
 hipError_t launch_nf4_dequantize(const uint8_t* codes, const uint8_t* q8, const float* step,
@@ -132,13 +163,11 @@ hipError_t launch_nf4_dequantize(const uint8_t* codes, const uint8_t* q8, const 
   const int64_t n8 = nelem / 8;
   int64_t grid = (n8 + 255) / 256;
   if (grid > 65536) grid = 65536;
-  if (code == CodeFP4::kId)
-    hipLaunchKernelGGL(k_nf4_dequantize<CodeFP4>, dim3((unsigned)grid), dim3(256), 0, stream,
+  return with_code(code, [&](auto ct) {
+    hipLaunchKernelGGL(k_nf4_dequantize<decltype(ct)>, dim3((unsigned)grid), dim3(256), 0, stream,
                        codes, q8, step, n8, out);
-  else
-    hipLaunchKernelGGL(k_nf4_dequantize<CodeNF4>, dim3((unsigned)grid), dim3(256), 0, stream,
-                       codes, q8, step, n8, out);
-  return hipGetLastError();
+    return hipGetLastError();
+  });
 }
 
 }  // namespace qn

@@ -290,22 +290,24 @@ __device__ __forceinline__ void stage_rows_scaled(uint16_t* As, const uint16_t* 
 }
 
 // What one thread loads of the weights for one contraction step: the codes
-// (a whole or half block row), their 8-bit constant and group step.
-template <class C>
+// (a whole or half block row, as half-block words), their 8-bit constant
+// and group step.
+template <class C, class CT>
 struct StepRegs {
-  u32x4 c[C::WPT / 32];
+  HalfRaw<CT::kBits> c[C::WPT / 32];
   uint32_t q;   // 8-bit constant as loaded
   uint32_t qm;  // ~0, or 0 for weight rows past N (their values become 0)
   float st;
 };
 
 template <class C, class CT>
-__device__ __forceinline__ void dequant_codes(uint16_t* dst, const StepRegs<C>& r) {
+__device__ __forceinline__ void dequant_codes(uint16_t* dst, const StepRegs<C, CT>& r) {
   const LevelTable t = make_table<CT>((float)(r.q & r.qm) * r.st);
 #pragma unroll
   for (int h = 0; h < C::WPT / 32; ++h)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) *reinterpret_cast<u32x4*>(dst + 32 * h + 8 * q) = lookup8(r.c[h][q], t);
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<u32x4*>(dst + 32 * h + 8 * q) = lookup8(nibbles<CT>(r.c[h], q), t);
 }
 
 // One pipelined contraction step: the MFMAs on the current buffers (As, Bs)
@@ -318,7 +320,7 @@ __device__ __forceinline__ void dequant_codes(uint16_t* dst, const StepRegs<C>& 
 template <class C, bool kTransB, class CT>
 __device__ __forceinline__ void step_interleaved(const uint16_t* As, const uint16_t* Bs,
                                                  uint16_t* As_n, uint16_t* Bw_n,
-                                                 const StepRegs<C>& rn, int wm, int wn, int lane,
+                                                 const StepRegs<C, CT>& rn, int wm, int wn, int lane,
                                                  AccT<C>& acc) {
   constexpr int NW = C::WPT / 8;  // code words to expand
   (void)As_n;
@@ -331,7 +333,7 @@ __device__ __forceinline__ void step_interleaved(const uint16_t* As, const uint1
     mfma_frags(f[kk & 1], acc);
 #pragma unroll
     for (int w = kk * NW / 4; w < (kk + 1) * NW / 4; ++w)
-      *reinterpret_cast<u32x4*>(Bw_n + 8 * w) = lookup8(rn.c[w / 4][w % 4], t);
+      *reinterpret_cast<u32x4*>(Bw_n + 8 * w) = lookup8(nibbles<CT>(rn.c[w / 4], w % 4), t);
   }
 
 }
@@ -370,7 +372,8 @@ __global__ __launch_bounds__(C::NT, 1) void k_qgemm_fwd(FwdArgs p) {
   const int wrow = tid / PARTS, wpart = tid % PARTS;
   int64_t gn = n0 + wrow;
   if (gn >= N) gn = N - 1;
-  const uint8_t* wcodes = p.codes + gn * (K >> 1) + wpart * (C::WPT / 2);
+  const uint8_t* wcodes =
+      p.codes + gn * kblocks * block_bytes<CT>() + wpart * (C::WPT / 32) * half_bytes<CT>();
   const int64_t wblk0 = gn * kblocks;
 
   AccT<C> acc;
@@ -382,12 +385,12 @@ __global__ __launch_bounds__(C::NT, 1) void k_qgemm_fwd(FwdArgs p) {
   // into the other LDS buffer while the MFMAs of the current step run;
   // activations go straight from global memory into that buffer.  Steps
   // past the end reload the last step (harmless).
-  StepRegs<C> ra, rb;
-  auto load_w = [&](StepRegs<C>& r, int64_t kt) {
+  StepRegs<C, CT> ra, rb;
+  auto load_w = [&](StepRegs<C, CT>& r, int64_t kt) {
     if (kt >= kblocks) kt = kblocks - 1;
 #pragma unroll
     for (int h = 0; h < C::WPT / 32; ++h)
-      r.c[h] = *reinterpret_cast<const u32x4*>(wcodes + kt * 32 + 16 * h);
+      r.c[h] = load_half<CT>(wcodes + kt * block_bytes<CT>() + h * half_bytes<CT>());
     const int64_t blk = wblk0 + kt;
     r.q = p.q8[blk];
     r.qm = ~0u;
@@ -400,7 +403,7 @@ __global__ __launch_bounds__(C::NT, 1) void k_qgemm_fwd(FwdArgs p) {
   // (Measured: keeping the weight loads in flight across the barrier, as
   // the backward kernel does, is slower here; the forward step waits for
   // all of its loads.)
-  auto body = [&](StepRegs<C>& rnext, StepRegs<C>& rload, int64_t kt, int cur) {
+  auto body = [&](StepRegs<C, CT>& rnext, StepRegs<C, CT>& rload, int64_t kt, int cur) {
     const uint16_t* As = smem + cur * (C::TILE_A + C::TILE_BF);
     uint16_t* As_n = smem + (cur ^ 1) * (C::TILE_A + C::TILE_BF);
     load_x(As_n, kt + 1);
@@ -506,18 +509,19 @@ __global__ __launch_bounds__(C::NT, 1) void k_qgemm_bwd(BwdArgs p) {
 
   AccT<C> acc;
   zero_acc(acc);
-  StepRegs<C> ra, rb;
+  StepRegs<C, CT> ra, rb;
   // Rows past N get constant 0 (their dequantized values are +-0, so the
   // dY columns they meet add nothing); columns past K are computed from
   // clamped codes and dropped on store.  Every load is unconditional.
-  auto load_w = [&](StepRegs<C>& r, int64_t ns) {
+  auto load_w = [&](StepRegs<C, CT>& r, int64_t ns) {
     if (ns >= nsteps) ns = nsteps - 1;
     const int64_t n = ns * BK + wr;
     const bool nok = n < N;
     const int64_t nc = nok ? n : 0, kc = kvalid ? kcol : 0;
-    const uint8_t* src = p.codes + ((nc * K + kc) >> 1) + wh * (WPTB / 2);
+    const uint8_t* src = p.codes + (nc * kblocks + (kc >> 6)) * block_bytes<CT>() +
+                         wh * (WPTB / 32) * half_bytes<CT>();
 #pragma unroll
-    for (int h = 0; h < WPTB / 32; ++h) r.c[h] = *reinterpret_cast<const u32x4*>(src + 16 * h);
+    for (int h = 0; h < WPTB / 32; ++h) r.c[h] = load_half<CT>(src + h * half_bytes<CT>());
     const int64_t blk = nc * kblocks + (kc >> 6);
     r.q = p.q8[blk];
     r.qm = nok ? ~0u : 0u;
@@ -529,8 +533,10 @@ __global__ __launch_bounds__(C::NT, 1) void k_qgemm_bwd(BwdArgs p) {
     if (ns >= nsteps) ns = nsteps - 1;
     load_rows_lds<C, true>(As_dst, p.dY, N, m0, M, ns * BK, N, wave, lane);
   };
+  // (3-bit codes may take three dword loads per half: more loads after the
+  // tile loads only make the wait in step_barrier() stricter.)
   static_assert(WPTB / 32 + 2 == kWLoads, "weight loads per step");
-  auto body = [&](StepRegs<C>& rnext, StepRegs<C>& rload, int64_t ns, int cur) {
+  auto body = [&](StepRegs<C, CT>& rnext, StepRegs<C, CT>& rload, int64_t ns, int cur) {
     const uint16_t* As = smem + cur * (C::TILE_A + C::TILE_BB);
     uint16_t* As_n = smem + (cur ^ 1) * (C::TILE_A + C::TILE_BB);
     load_x(As_n, ns + 1);    // tile loads first ...
@@ -592,10 +598,10 @@ hipError_t launch_qgemm_fwd(const Nf4View& w, const uint16_t* X, int64_t M, cons
   using C = GemmCfg;
   FwdArgs a{X, w.codes, w.q8, w.step, U, ldu, B, r, s, Y, M, w.N, w.K};
   dim3 grid((unsigned)(((w.N + C::BN - 1) / C::BN) * ((M + C::BM - 1) / C::BM)));
-  if (w.code == CodeFP4::kId)
-    hipLaunchKernelGGL((k_qgemm_fwd<C, CodeFP4>), grid, dim3(C::NT), 0, stream, a);
-  else
-    hipLaunchKernelGGL((k_qgemm_fwd<C, CodeNF4>), grid, dim3(C::NT), 0, stream, a);
+  with_code(w.code, [&](auto ct) {
+    hipLaunchKernelGGL((k_qgemm_fwd<C, decltype(ct)>), grid, dim3(C::NT), 0, stream, a);
+    return 0;
+  });
   return hipGetLastError();
 }
 
@@ -605,10 +611,10 @@ hipError_t launch_qgemm_bwd(const Nf4View& w, const uint16_t* dY, int64_t M, con
   using C = GemmCfg;
   BwdArgs a{dY, w.codes, w.q8, w.step, dU, lddu, A, r, dX, M, w.N, w.K};
   dim3 grid((unsigned)(((w.K + C::BN - 1) / C::BN) * ((M + C::BM - 1) / C::BM)));
-  if (w.code == CodeFP4::kId)
-    hipLaunchKernelGGL((k_qgemm_bwd<C, CodeFP4>), grid, dim3(C::NT), 0, stream, a);
-  else
-    hipLaunchKernelGGL((k_qgemm_bwd<C, CodeNF4>), grid, dim3(C::NT), 0, stream, a);
+  with_code(w.code, [&](auto ct) {
+    hipLaunchKernelGGL((k_qgemm_bwd<C, decltype(ct)>), grid, dim3(C::NT), 0, stream, a);
+    return 0;
+  });
   return hipGetLastError();
 }
 

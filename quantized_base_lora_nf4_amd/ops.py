@@ -12,11 +12,14 @@ from typing import Optional, Tuple
 
 import torch
 
-from ._lib import QLORA_CODE_FP4, QLORA_CODE_NF4, Nf4Tensor, check, lib
+from ._lib import (QLORA_CODE_FP4, QLORA_CODE_NF2, QLORA_CODE_NF3, QLORA_CODE_NF4, Nf4Tensor,
+                   check, lib)
 
 BLOCKSIZE = 64
 DQ_BLOCKSIZE = 256
-CODE_TYPES = {"nf4": QLORA_CODE_NF4, "fp4": QLORA_CODE_FP4}
+CODE_TYPES = {"nf4": QLORA_CODE_NF4, "fp4": QLORA_CODE_FP4, "nf3": QLORA_CODE_NF3,
+              "nf2": QLORA_CODE_NF2}
+CODE_BITS = {"nf4": 4, "fp4": 4, "nf3": 3, "nf2": 2}
 
 
 def _code_id(code: str) -> int:
@@ -49,12 +52,12 @@ def _bf16_view(t: torch.Tensor) -> torch.Tensor:
 @dataclass
 class NF4Weight:
     """Device storage of one quantized frozen weight."""
-    codes: torch.Tensor   # uint8 [N*K/2]
+    codes: torch.Tensor   # uint8 [N*K*bits/8]
     q8: torch.Tensor      # uint8 [N*K/64]
     step: torch.Tensor    # float32 [ceil(N*K/16384)]
     N: int
     K: int
-    code: str = "nf4"     # the code table the codes index: "nf4" or "fp4"
+    code: str = "nf4"     # the code table the codes index: "nf4", "fp4", "nf3", "nf2"
 
     def struct(self) -> Nf4Tensor:
         return Nf4Tensor(_ptr(self.codes), _ptr(self.q8), _ptr(self.step), self.N, self.K,
@@ -65,25 +68,25 @@ class NF4Weight:
 
 
 def code_table(code: str = "nf4") -> Tuple[list, list]:
-    """The library's 16 code values (in code order) and its decision
-    thresholds (15 for NF4, 14 for FP4), fp32."""
+    """The library's code values (in code order, 2^bits of them) and its
+    decision thresholds (15 for NF4, 14 for FP4, 7 for NF3, 3 for NF2), fp32."""
     lv = (ctypes.c_float * 16)()
     th = (ctypes.c_float * 15)()
     n = lib().qlora_code_table(_code_id(code), ctypes.cast(lv, ctypes.c_void_p),
                                ctypes.cast(th, ctypes.c_void_p))
     check(min(n, 0), "qlora_code_table")
-    return list(lv), list(th)[:n]
+    return list(lv)[:2 ** CODE_BITS[code]], list(th)[:n]
 
 
-def storage_bytes(N: int, K: int) -> int:
-    return int(lib().nf4_storage_bytes(N, K))
+def storage_bytes(N: int, K: int, code: str = "nf4") -> int:
+    return int(lib().qlora_storage_bytes(_code_id(code), N, K))
 
 
 def alloc_nf4(N: int, K: int, device="cuda", code: str = "nf4") -> NF4Weight:
     nb = N * K // BLOCKSIZE
     ng = (nb + DQ_BLOCKSIZE - 1) // DQ_BLOCKSIZE
     return NF4Weight(
-        codes=torch.empty(N * K // 2, dtype=torch.uint8, device=device),
+        codes=torch.empty(N * K * CODE_BITS[code] // 8, dtype=torch.uint8, device=device),
         q8=torch.empty(nb, dtype=torch.uint8, device=device),
         step=torch.empty(ng, dtype=torch.float32, device=device),
         N=N, K=K, code=code)
@@ -91,14 +94,16 @@ def alloc_nf4(N: int, K: int, device="cuda", code: str = "nf4") -> NF4Weight:
 
 def nf4_quantize(W: torch.Tensor, out: Optional[NF4Weight] = None, stream=None,
                  code: str = "nf4") -> NF4Weight:
-    """Quantize an fp32 [N, K] device tensor to 4-bit codes (NF4 by default,
-    or FP4) with double-quantized constants."""
+    """Quantize an fp32 [N, K] device tensor to block codes (NF4 by default,
+    or FP4, NF3, NF2) with double-quantized constants."""
     if W.dtype != torch.float32 or W.dim() != 2:
         raise TypeError("W must be a 2-D float32 tensor")
     N, K = W.shape
     cid = _code_id(code)
     if out is None:
         out = alloc_nf4(N, K, W.device, code)
+    elif out.codes.numel() != N * K * CODE_BITS[code] // 8:
+        raise ValueError("out was allocated for another code width")
     else:
         out.code = code
     if cid == QLORA_CODE_NF4:

@@ -68,12 +68,13 @@ def test_threshold_rule_is_nearest_level_for_every_fp32_in_unit_interval():
         assert bad == 0, hex(first.value)
 
 
-@pytest.mark.parametrize("code", ["nf4", "fp4"])
+@pytest.mark.parametrize("code", ["nf4", "fp4", "nf3", "nf2"])
 def test_code_table_values_match_oracle(code):
     lv, th = qn.code_table(code)
     assert np.array_equal(np.array(lv, np.float32).view(np.uint32),
                           nf4.code_values(code).view(np.uint32))
-    assert len(th) == (15 if code == "nf4" else 14)
+    assert len(th) == {"nf4": 15, "fp4": 14, "nf3": 7, "nf2": 3}[code]
+    lv = lv + [0.0] * (16 - len(lv))   # the library pads its table with +0
     with tempfile.TemporaryDirectory() as d:
         so = os.path.join(d, "exh.so")
         src = os.path.join(ROOT, "tests", "csrc", "exhaustive_nearest.c")
@@ -101,8 +102,11 @@ def test_code_table_rejects_unknown_type():
 
 def test_storage_bytes_closed_form():
     for N, K in [(1, 64), (3, 1024), (1024, 1024), (22016, 8192), (5120, 13824)]:
-        assert qn.storage_bytes(N, K) == nf4.storage_bytes(N, K)
+        assert qn.lib().nf4_storage_bytes(N, K) == nf4.storage_bytes(N, K)
+        for code in ("nf4", "fp4", "nf3", "nf2"):
+            assert qn.storage_bytes(N, K, code) == nf4.storage_bytes(N, K, code=code)
     assert qn.storage_bytes(4, 65) == 0 and qn.storage_bytes(0, 64) == 0
+    assert qn.lib().qlora_storage_bytes(9, 64, 64) == 0
 
 
 def test_workspace_size_rules():
@@ -135,7 +139,7 @@ def test_quantize_rejects_bad_arguments_without_launching():
     assert call(dq=128) == _lib.QLORA_ERR_UNSUPPORTED
     assert call(W=FAKE + 4) == _lib.QLORA_ERR_INVALID
     # the code-type variant: unknown types are rejected, the checks above apply
-    for ct, want in ((2, _lib.QLORA_ERR_UNSUPPORTED), (-1, _lib.QLORA_ERR_UNSUPPORTED)):
+    for ct, want in ((4, _lib.QLORA_ERR_UNSUPPORTED), (-1, _lib.QLORA_ERR_UNSUPPORTED)):
         assert L.qlora_quantize(FAKE, 4, 128, ct, 64, 256, FAKE, FAKE, FAKE, None) == want
     assert L.qlora_quantize(None, 4, 128, _lib.QLORA_CODE_FP4, 64, 256, FAKE, FAKE, FAKE,
                             None) == _lib.QLORA_ERR_INVALID
@@ -177,7 +181,7 @@ def test_linear_rejects_bad_arguments_without_launching():
 
     w = _w(64, 128)
     assert L.nf4_dequantize(ctypes.byref(w), None, None) == _lib.QLORA_ERR_INVALID
-    w = _w(64, 128, code_type=3)
+    w = _w(64, 128, code_type=6)
     assert L.nf4_dequantize(ctypes.byref(w), FAKE, None) == _lib.QLORA_ERR_UNSUPPORTED
     assert L.qlora_linear_bwd(ctypes.byref(w), FAKE, FAKE, 32, FAKE, FAKE, None, 8, 1.0, None,
                               FAKE, FAKE, FAKE, needb, None) == _lib.QLORA_ERR_UNSUPPORTED
