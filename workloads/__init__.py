@@ -149,3 +149,33 @@ def draw_workload_weight(wl: Workload, wi: int, M: Optional[int] = None) -> Laye
     return draw_layer(spec.N, spec.K, M if M is not None else wl.M[0], wl.r, wl.s,
                       sigma=spec.sigma, heavy_frac=spec.heavy_frac, ab_sigma=wl.ab_sigma,
                       seed=wl.seed, index=wi, with_dy=not wl.fwd_only)
+
+
+@dataclass
+class LqInputs:
+    """Inputs of the low-rank plus quantized decomposition of one weight."""
+    W: np.ndarray       # fp32 [N, K]
+    Omega: np.ndarray   # fp32 [K, l], the random test matrix of the range finder
+    r: int
+    l: int
+
+
+def draw_lq_inputs(N: int, K: int, r: int, l: int, *, sigma: float = 0.02, rank0: Optional[int] = None,
+                   strength: float = 3.0, seed: int = 0, index: int = 0) -> LqInputs:
+    """W = sigma (G + P): G [N, K] i.i.d. N(0, 1), plus a planted component
+    P = strength (sqrt N + sqrt K) U0 V0^T of rank rank0 (default r), with
+    U0 [N, rank0] and V0 [K, rank0] i.i.d. N(0, 1) scaled by 1/sqrt(N) and
+    1/sqrt(K).  The planted singular values sit near strength times the edge
+    sqrt N + sqrt K of G's spectrum, which gives a pretrained-like matrix a
+    few dominant directions and a clear gap after them.  Omega [K, l] is
+    i.i.d. N(0, 1).  Draw order: G, U0, V0, Omega."""
+    rank0 = r if rank0 is None else rank0
+    rng = rng_for(seed, 1000 + index)
+    G = rng.standard_normal((N, K), dtype=np.float32)
+    U0 = rng.standard_normal((N, rank0)) / np.sqrt(N)
+    V0 = rng.standard_normal((K, rank0)) / np.sqrt(K)
+    P = (strength * (np.sqrt(N) + np.sqrt(K))) * (U0 @ V0.T)
+    W = (np.float64(sigma) * (G.astype(np.float64) + P)).astype(np.float32)
+    Omega = rng.standard_normal((K, l), dtype=np.float32)
+    return LqInputs(W=W, Omega=Omega, r=r, l=l)
+
