@@ -245,6 +245,51 @@ int32_t qlora_linear_bwd_ev(const nf4_tensor_t* w, const uint16_t* X,
                             void* ws, size_t ws_bytes, hipStream_t stream,
                             hipEvent_t ev_begin, hipEvent_t ev_end);
 
+/* ---- Low-rank plus quantized decomposition (adapter initialization) ----
+ *
+ * qlora_lq_init -- split a frozen weight into a quantized part Q and a
+ * rank-r part L1 L2 ("LQ-LoRA: Low-rank Plus Quantized Matrix Decomposition
+ * for Efficient Language Model Finetuning", abstract: an iterative
+ * algorithm; the quantized part stays fixed, the low-rank part is the
+ * trained adapter).  Alternating minimization of ||W - Q - L1 L2||_F:
+ *   L step: L1 L2 = rank-r approximation of W - Q, by randomized subspace
+ *           iteration from the caller's Gaussian test matrix `omega`
+ *           (power_iters rounds, each re-orthonormalized) and
+ *           Rayleigh-Ritz on its l-dimensional range;
+ *   Q step: Q = qlora_quantize(W - L1 L2) with `code_type`.
+ * `start` = QLORA_LQ_START_SVD begins with Q = 0 (the first L step fits W
+ * itself); QLORA_LQ_START_QUANTIZE begins with L = 0 (the first Q step is
+ * plain quantization).  One iteration is one L step and one Q step.
+ *
+ *   W       [N, K] fp32, device; K % 64 == 0
+ *   r, l    rank and subspace width: 1 <= r < l <= QLORA_LQ_MAX_L,
+ *           l % 16 == 0 (l - r extra directions improve the fit)
+ *   omega   [K, l] fp32, i.i.d. N(0, 1) drawn by the caller
+ *   iters   1..64;  power_iters 0..16
+ *   s       LoRA scale of the adapter outputs (nonzero)
+ *   codes, q8, step   out: Q, as qlora_quantize writes it
+ *   L1      [N, r] fp32 out;  L2t [K, r] fp32 out (L2 transposed);
+ *           L1 L2t^T is the low-rank part, the factors sharing each
+ *           singular value evenly (both carry its square root)
+ *   A       [r, K] bf16 out = bf16(L2);  B [N, r] bf16 out = bf16(L1 / s),
+ *           so that s B A ~ L1 L2 as the adapter of qlora_linear_fwd
+ *   ws      device workspace, 256-byte aligned, ws_bytes >=
+ *           qlora_lq_workspace_size(N, K, r, l) (about 4 N K bytes)
+ * The pair returned is the last Q step's Q with the L step before it
+ * (start SVD) or after it (start QUANTIZE).  Sums have a fixed order:
+ * results are reproducible.  The first call on a device raises the
+ * eigensolver kernel's dynamic LDS limit (process-wide, idempotent). */
+#define QLORA_LQ_MAX_L 96
+#define QLORA_LQ_START_SVD 0
+#define QLORA_LQ_START_QUANTIZE 1
+size_t qlora_lq_workspace_size(int64_t N, int64_t K, int32_t r, int32_t l);
+int32_t qlora_lq_init(const float* W, int64_t N, int64_t K, int32_t code_type,
+                      int32_t r, int32_t l, const float* omega, int32_t iters,
+                      int32_t power_iters, int32_t start, float s,
+                      uint8_t* codes, uint8_t* q8, float* step, uint16_t* A,
+                      uint16_t* B, float* L1, float* L2t, void* ws,
+                      size_t ws_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -36,6 +36,8 @@ EXPORTS = (
     "qlora_linear_bwd",
     "qlora_linear_fwd_ev",
     "qlora_linear_bwd_ev",
+    "qlora_lq_workspace_size",
+    "qlora_lq_init",
 )
 
 
@@ -100,6 +102,11 @@ def lib() -> ctypes.CDLL:
     L.qlora_linear_fwd_ev.argtypes = L.qlora_linear_fwd.argtypes + [vp, vp]
     L.qlora_linear_bwd_ev.restype = i32
     L.qlora_linear_bwd_ev.argtypes = L.qlora_linear_bwd.argtypes + [vp, vp]
+    L.qlora_lq_workspace_size.restype = sz
+    L.qlora_lq_workspace_size.argtypes = [i64, i64, i32, i32]
+    L.qlora_lq_init.restype = i32
+    L.qlora_lq_init.argtypes = [vp, i64, i64, i32, i32, i32, vp, i32, i32, i32, f32,
+                                vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     _lib = L
     return L
 

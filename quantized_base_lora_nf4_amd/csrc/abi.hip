@@ -313,3 +313,38 @@ int32_t qlora_linear_bwd_ev(const nf4_tensor_t* w, const uint16_t* X, const uint
 }
 
 }  // extern "C"
+
+extern "C" {
+
+size_t qlora_lq_workspace_size(int64_t N, int64_t K, int32_t r, int32_t l) {
+  if (N < 1 || K < 64 || (K % 64) != 0 || r < 1 || l <= r || l > QLORA_LQ_MAX_L || (l % 16) != 0 ||
+      N > ((int64_t)1 << 40) / K)
+    return 0;
+  return qn::lq_workspace_bytes(N, K, l);
+}
+
+int32_t qlora_lq_init(const float* W, int64_t N, int64_t K, int32_t code_type, int32_t r,
+                      int32_t l, const float* omega, int32_t iters, int32_t power_iters,
+                      int32_t start, float s, uint8_t* codes, uint8_t* q8, float* step,
+                      uint16_t* A, uint16_t* B, float* L1, float* L2t, void* ws, size_t ws_bytes,
+                      hipStream_t stream) {
+  if (!W || !omega || !codes || !q8 || !step || !A || !B || !L1 || !L2t || !ws)
+    return QLORA_ERR_INVALID;
+  const size_t need = qlora_lq_workspace_size(N, K, r, l);
+  if (need == 0 || iters < 1 || iters > 64 || power_iters < 0 || power_iters > 16 ||
+      (start != QLORA_LQ_START_SVD && start != QLORA_LQ_START_QUANTIZE) || !isfinite(s) ||
+      s == 0.0f)
+    return QLORA_ERR_INVALID;
+  if (!code_ok(code_type)) return QLORA_ERR_UNSUPPORTED;
+  if (!aligned16(W) || !aligned16(omega) || !aligned16(codes) || !aligned16(q8) ||
+      !aligned16(step) || !aligned16(A) || !aligned16(B) || !aligned16(L1) || !aligned16(L2t) ||
+      ((uintptr_t)ws & 255u) != 0)
+    return QLORA_ERR_INVALID;
+  if (ws_bytes < need) return QLORA_ERR_WORKSPACE;
+  const qn::LqArgs a{W, N, K, code_type, r, l, omega, iters, power_iters, start, s,
+                     codes, q8, step, A, B, L1, L2t, ws};
+  return launch_status(qn::launch_lq_init(a, stream));
+}
+
+}  // extern "C"
+

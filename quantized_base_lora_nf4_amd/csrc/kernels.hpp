@@ -78,4 +78,26 @@ SkinnyJob make_job(const SkinnyOp& op, float scale, uint16_t* out, int64_t o_si,
 // and, if any product has several contraction slices, one finish launch.
 hipError_t launch_skinny(const SkinnyJob* jobs, int njobs, hipStream_t stream);
 
+// ---- lq_init.hip: low-rank plus quantized decomposition of a weight ----
+struct LqArgs {
+  const float* W;      // [N, K]
+  int64_t N, K;
+  int code;            // code type id of the Q component
+  int r, l;            // rank, subspace width (r < l <= 96, l % 16 == 0)
+  const float* omega;  // [K, l] Gaussian test matrix
+  int iters, power_iters;
+  int start;           // 0: L step first (Q = 0), 1: Q step first (L = 0)
+  float s;             // LoRA scale of the adapter outputs
+  uint8_t* codes;
+  uint8_t* q8;
+  float* step;
+  uint16_t* A;         // [r, K] bf16
+  uint16_t* B;         // [N, r] bf16
+  float* L1;           // [N, r]
+  float* L2t;          // [K, r]
+  void* ws;            // lq_workspace_bytes(N, K, l) bytes, 256-byte aligned
+};
+size_t lq_workspace_bytes(int64_t N, int64_t K, int32_t l);
+hipError_t launch_lq_init(const LqArgs& a, hipStream_t stream);
+
 }  // namespace qn

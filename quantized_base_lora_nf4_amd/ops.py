@@ -180,6 +180,51 @@ def qlora_linear_bwd(w: NF4Weight, X: torch.Tensor, dY: torch.Tensor, A: torch.T
     return dX, dA, dB
 
 
+LQ_START = {"svd": 0, "quantize": 1}
+
+
+def lq_workspace_size(N: int, K: int, r: int, l: int) -> int:
+    return int(lib().qlora_lq_workspace_size(N, K, r, l))
+
+
+@dataclass
+class LqResult:
+    """Output of lq_init: the quantized part and the low-rank part."""
+    w: NF4Weight
+    A: torch.Tensor     # bf16 [r, K] = bf16(L2)
+    B: torch.Tensor     # bf16 [N, r] = bf16(L1 / s)
+    L1: torch.Tensor    # fp32 [N, r]
+    L2t: torch.Tensor   # fp32 [K, r]
+
+
+def lq_init(W: torch.Tensor, omega: torch.Tensor, r: int, iters: int = 2, power_iters: int = 2,
+            start: str = "svd", s: float = 1.0, code: str = "nf4",
+            ws: Optional[torch.Tensor] = None, stream=None) -> LqResult:
+    """Split the fp32 [N, K] weight W into a quantized part and a rank-r part
+    (alternating L and Q steps); omega is the fp32 [K, l] Gaussian test
+    matrix of the randomized range finder."""
+    if W.dtype != torch.float32 or W.dim() != 2 or omega.dtype != torch.float32:
+        raise TypeError("W and omega must be float32, W 2-D")
+    N, K = W.shape
+    l = omega.shape[1]
+    if omega.shape[0] != K:
+        raise ValueError("omega must be [K, l]")
+    dev = W.device
+    w = alloc_nf4(N, K, dev, code)
+    A = torch.empty(r, K, dtype=torch.bfloat16, device=dev)
+    B = torch.empty(N, r, dtype=torch.bfloat16, device=dev)
+    L1 = torch.empty(N, r, dtype=torch.float32, device=dev)
+    L2t = torch.empty(K, r, dtype=torch.float32, device=dev)
+    need = lq_workspace_size(N, K, r, l)
+    ws = _workspace(need, dev, ws)
+    st = lib().qlora_lq_init(_ptr(W), N, K, _code_id(code), r, l, _ptr(omega), iters, power_iters,
+                             LQ_START[start], float(s), _ptr(w.codes), _ptr(w.q8), _ptr(w.step),
+                             _ptr(A), _ptr(B), _ptr(L1), _ptr(L2t), _ptr(ws),
+                             ws.numel() * ws.element_size(), _stream(stream))
+    check(st, "qlora_lq_init")
+    return LqResult(w=w, A=A, B=B, L1=L1, L2t=L2t)
+
+
 class QLoRALinearFunction(torch.autograd.Function):
     """Autograd wrapper: gradients flow to X, A and B only (the NF4 base is frozen)."""
 
