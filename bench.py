@@ -48,6 +48,9 @@ def parse():
                          "counters) and exit")
     ap.add_argument("--cpu-rows", type=int, default=4096,
                     help="token rows of the workload the CPU oracle runs on")
+    ap.add_argument("--lq-only", action="store_true",
+                    help="only time the low-rank plus quantized initialization (the "
+                         "extra 'lq_init') and print it")
     return ap.parse_args()
 
 
@@ -111,6 +114,10 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.lq_only:
+        import quantized_base_lora_nf4_amd as qn
+        print(json.dumps({"lq_init": run_lq(qn, torch)}))
+        return
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
@@ -253,6 +260,7 @@ def main():
         for code in ("fp4", "nf3", "nf2"):
             extra["code_types"][code]["fused_step"] = code_step(
                 qn, L, torch, layers, M, r, s, sp, args.steps, args.warmup, flops_step, code)
+        extra["lq_init"] = run_lq(qn, torch)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -281,6 +289,48 @@ def main():
         "extra": extra,
     }
     print(json.dumps(out), flush=True)
+
+
+LQ_R, LQ_L, LQ_ITERS, LQ_POWER = 64, 80, 2, 2
+
+
+def run_lq(qn, torch, reps=5):
+    """Low-rank plus quantized initialization of the LLaMA-7B q_proj and
+    up_proj weights (planted-rank synthetic weights, rank 64, subspace 80,
+    2 iterations of 2 power rounds each, NF4): whole-call time, median of
+    `reps` calls after one warm-up."""
+    import workloads as wl_mod
+    out = []
+    for wi, (N, K) in enumerate(((4096, 4096), (11008, 4096))):
+        inp = wl_mod.draw_lq_inputs(N, K, LQ_R, LQ_L, seed=0, index=wi)
+        W = torch.from_numpy(inp.W).cuda()
+        Om = torch.from_numpy(inp.Omega).cuda()
+        ws = torch.empty(qn.lq_workspace_size(N, K, LQ_R, LQ_L), dtype=torch.uint8, device="cuda")
+        ts = []
+        for i in range(reps + 1):
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            qn.lq_init(W, Om, LQ_R, iters=LQ_ITERS, power_iters=LQ_POWER, start="svd", s=0.25,
+                       ws=ws)
+            e1.record()
+            torch.cuda.synchronize()
+            if i:
+                ts.append(e0.elapsed_time(e1))
+        ms = float(np.median(ts))
+        # E is streamed by 2 P + 2 products per L step (P power rounds), plus
+        # the residual (W in, R out) and the quantizer per Q step, plus the
+        # error pass (W and Q in, E out) from the second iteration on
+        e_reads = LQ_ITERS * (2 * LQ_POWER + 2)
+        flops = LQ_ITERS * (2 * LQ_POWER + 2) * 2.0 * N * K * LQ_L
+        out.append({"weight": f"{N}x{K}", "r": LQ_R, "l": LQ_L, "iters": LQ_ITERS,
+                    "power_iters": LQ_POWER, "ms": round(ms, 3),
+                    "products_TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 2),
+                    "E_passes": e_reads})
+        del W, Om, ws
+        torch.cuda.empty_cache()
+    return out
 
 
 def code_step(qn, L, torch, layers, M, r, s, sp, steps, warmup, flops_step, code):

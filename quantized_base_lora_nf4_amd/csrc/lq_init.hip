@@ -11,18 +11,24 @@
 //           the l-dimensional subspace;
 //   Q step  the block quantizer (nf4_quant.hip) on R = W - L1 L2.
 //
-// Kernels (all fp32 data, fp64 for the l x l Gram matrices and their
-// eigenvectors):
+// Kernels (all fp32 data, fp64 for the l x l Gram matrices, their Cholesky
+// factors and eigenvectors).  Orthonormal bases come from the Cholesky
+// factor of the Gram matrix (the oracle takes its eigenvectors instead:
+// both are bases of the same span, and L1 L2 depends on the spans only).
 //   k_lq_residual   R = W - L1 L2t^T                    (tiles, HBM + VALU)
 //   k_lq_error      E = W - W_hat(Q)                    (elementwise, HBM)
-//   k_lq_mul_ex     Y = E X      [N,K] x [K,l]          (E streamed once)
-//   k_lq_mul_ety    partial Z = E^T Y over row slices   (E streamed once)
+//   k_lq_mul        partial Y = E X or Z = E^T Y over contraction slices
+//                   (E streamed once per product)
 //   k_lq_reduce     sum of the slices, fixed order
 //   k_lq_gram       partial X^T X over row slices, fp64
-//   k_lq_eig        Jacobi eigenvectors of an l x l matrix, one workgroup
+//   k_lq_chol       Cholesky factor of a Gram matrix G = L L^T
+//   k_lq_trsm       X L^{-T} (orthonormal columns), one thread per row
+//   k_lq_eig        Jacobi eigenvectors of an l x l matrix (Ritz step)
 //   k_lq_mul_xm     Y = X M      [T,l] x [l,c]
 //   k_lq_adapter    A = bf16(L2), B = bf16(L1 / s)
 // No atomics: every sum has a fixed order, so results are reproducible.
+#include <type_traits>
+
 #include "kernels.hpp"
 
 namespace qn {
@@ -116,94 +122,115 @@ __global__ __launch_bounds__(256) void k_lq_error(const float* __restrict__ W,
 }
 
 // ---------------------------------------------------------------------------
-// Y[N,l] = E[N,K] X[K,l].  32 rows per workgroup; thread: rows ty, ty + 16,
-// columns cg + 16 m (m < l / 16).  K in chunks of 32 through LDS.
+// The two products with E: Y = E X ([N,K] x [K,l]) and Z = E^T Y
+// ([K,N] x [N,l]).  Both stream E once and share one inner loop: a
+// workgroup owns 64 rows of the output (rows of E for E X, columns of E for
+// E^T Y) and all l columns, for one slice of the contraction; thread
+// (rg, cg) accumulates output rows 4 rg .. 4 rg + 3 and columns
+// cg CP .. cg CP + CP - 1 (CP = l / 16).  Per 32-deep chunk the operands sit
+// in LDS as sa[kk][64] (the four rows of a thread are one 16-byte read) and
+// sb[kk][l]; the next chunk's global loads are issued before the current
+// chunk's products.  Slices write fp32 partials that k_lq_reduce sums in
+// slice order.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_lq_mul_ex(const float* __restrict__ E,
-                                                   const float* __restrict__ X, int64_t N,
-                                                   int64_t K, int l, float* __restrict__ Y) {
-  __shared__ float se[32 * 33];
-  __shared__ float sx[32 * kLqMaxL];
-  const int tid = threadIdx.x, cg = tid & 15, ty = tid >> 4;
-  const int64_t n0 = (int64_t)blockIdx.x * 32;
-  const int mc = l >> 4;
-  float acc[2][kLqMaxL / 16] = {};
-  for (int64_t k0 = 0; k0 < K; k0 += 32) {
+constexpr int kSA = 68;  // row stride of sa (floats)
+
+template <int CP>
+__device__ __forceinline__ void chunk_products(const float* sa, const float* sb, int l, int rg,
+                                               int cg, float (&acc)[4][6]) {
+#pragma unroll 8
+  for (int kk = 0; kk < 32; ++kk) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(sa + kk * kSA + 4 * rg);
+    float b[CP];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = tid + 256 * q, row = e >> 5, col = e & 31;
-      int64_t n = n0 + row;
-      if (n >= N) n = N - 1;
-      se[row * 33 + col] = E[n * K + k0 + col];
-    }
-    for (int e = tid; e < 32 * l; e += 256) sx[e] = X[k0 * l + e];
-    __syncthreads();
-#pragma unroll 4
-    for (int kk = 0; kk < 32; ++kk) {
-      const float e0 = se[ty * 33 + kk], e1 = se[(ty + 16) * 33 + kk];
+    for (int c = 0; c < CP; ++c) b[c] = sb[kk * l + cg * CP + c];
 #pragma unroll
-      for (int m = 0; m < kLqMaxL / 16; ++m) {
-        if (m < mc) {
-          const float x = sx[kk * l + cg + 16 * m];
-          acc[0][m] = fmaf(e0, x, acc[0][m]);
-          acc[1][m] = fmaf(e1, x, acc[1][m]);
-        }
-      }
-    }
-    __syncthreads();
-  }
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int64_t n = n0 + ty + 16 * h;
-    if (n >= N) continue;
-#pragma unroll
-    for (int m = 0; m < kLqMaxL / 16; ++m)
-      if (m < mc) Y[n * l + cg + 16 * m] = acc[h][m];
+      for (int c = 0; c < CP; ++c) acc[i][c] = fmaf(a[i], b[c], acc[i][c]);
   }
 }
 
-// ---------------------------------------------------------------------------
-// part[s][K][l] = sum over rows n of slice s of E[n][k] Y[n][j].  Workgroup:
-// 64 columns of E and one slice of rows; thread: column kk, output columns
-// jg + 4 m (m < l / 4).  Rows in chunks of 32 through LDS.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_lq_mul_ety(const float* __restrict__ E,
-                                                    const float* __restrict__ Y, int64_t N,
-                                                    int64_t K, int l, int64_t rows_per_slice,
-                                                    float* __restrict__ part) {
-  __shared__ float se[32 * 64];
-  __shared__ float sy[32 * kLqMaxL];
-  const int tid = threadIdx.x, kk = tid & 63, jg = tid >> 6;
-  const int64_t k0 = (int64_t)blockIdx.x * 64;
+// kTrans = false: part[s][N][l] of E X over K slice s (rows n0 .. n0 + 63).
+// kTrans = true:  part[s][K][l] of E^T Y over N slice s (columns k0 .. k0 + 63).
+template <bool kTrans, int CP>
+__global__ __launch_bounds__(256) void k_lq_mul(const float* __restrict__ E,
+                                                const float* __restrict__ Xin, int64_t N,
+                                                int64_t K, int64_t slice, float* __restrict__ part) {
+  __shared__ __attribute__((aligned(16))) float sa[32 * kSA];
+  __shared__ __attribute__((aligned(16))) float sb[32 * kLqMaxL];
+  constexpr int l = 16 * CP;
+  const int tid = threadIdx.x, rg = tid >> 4, cg = tid & 15;
+  const int64_t o0 = (int64_t)blockIdx.x * 64;          // first output row
   const int64_t s = blockIdx.y;
-  const int64_t nb = s * rows_per_slice;
-  const int64_t ne = nb + rows_per_slice < N ? nb + rows_per_slice : N;
-  const int mc = l >> 2;
-  float acc[kLqMaxL / 4] = {};
-  for (int64_t c0 = nb; c0 < ne; c0 += 32) {
-    const int rows = (int)(ne - c0 < 32 ? ne - c0 : 32);
+  const int64_t rows_out = kTrans ? K : N;
+  const int64_t ctot = kTrans ? N : K;                  // contraction length
+  const int64_t c0 = s * slice;
+  const int64_t c1 = c0 + slice < ctot ? c0 + slice : ctot;
+  float acc[4][6] = {};
+  // per chunk: 512 float4 of E, 8 CP float4 of the other operand per thread-row
+  f32x4 re[2], rx[3];
+  auto load = [&](int64_t cb) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int e = tid + 256 * q, row = e >> 6, col = e & 63;
-      se[e] = row < rows ? E[(c0 + row) * K + k0 + col] : 0.0f;
+    for (int q = 0; q < 2; ++q) {
+      const int idx = tid + 256 * q;
+      if (!kTrans) {  // E rows o0 + row, columns cb + 4 k4
+        const int row = idx >> 3, k4 = idx & 7;
+        int64_t n = o0 + row;
+        if (n >= N) n = N - 1;
+        re[q] = *reinterpret_cast<const f32x4*>(E + n * K + cb + 4 * k4);
+      } else {        // E rows cb + row (zero past the slice), columns o0 + 4 k4
+        const int row = idx >> 4, k4 = idx & 15;
+        re[q] = cb + row < c1 ? *reinterpret_cast<const f32x4*>(E + (cb + row) * K + o0 + 4 * k4)
+                              : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
     }
-    for (int e = tid; e < 32 * l; e += 256) {
-      const int row = e / l;
-      sy[e] = row < rows ? Y[c0 * l + e] : 0.0f;
-    }
-    __syncthreads();
-    for (int rr = 0; rr < rows; ++rr) {
-      const float ev = se[rr * 64 + kk];
 #pragma unroll
-      for (int m = 0; m < kLqMaxL / 4; ++m)
-        if (m < mc) acc[m] = fmaf(ev, sy[rr * l + jg + 4 * m], acc[m]);
+    for (int q = 0; q < 3; ++q) {
+      const int idx = tid + 256 * q;  // float4 index within the [32][l] chunk
+      if (idx < 8 * l) {
+        const int row = idx / (l / 4);
+        const bool in = kTrans ? cb + row < c1 : true;
+        rx[q] = in ? *reinterpret_cast<const f32x4*>(Xin + cb * l + 4 * idx)
+                   : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
     }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int idx = tid + 256 * q;
+      if (!kTrans) {  // transpose: sa[kk][row]
+        const int row = idx >> 3, k4 = idx & 7;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) sa[(4 * k4 + t) * kSA + row] = re[q][t];
+      } else {
+        const int row = idx >> 4, k4 = idx & 15;
+        *reinterpret_cast<f32x4*>(sa + row * kSA + 4 * k4) = re[q];
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      const int idx = tid + 256 * q;
+      if (idx < 8 * l) *reinterpret_cast<f32x4*>(sb + 4 * idx) = rx[q];
+    }
+  };
+  if (c0 < c1) load(c0);
+  for (int64_t cb = c0; cb < c1; cb += 32) {
+    __syncthreads();  // the previous chunk's reads are done
+    store();
     __syncthreads();
+    if (cb + 32 < c1) load(cb + 32);
+    chunk_products<CP>(sa, sb, l, rg, cg, acc);
   }
-  float* out = part + (s * K + k0 + kk) * l;
+  float* out = part + s * rows_out * l;
 #pragma unroll
-  for (int m = 0; m < kLqMaxL / 4; ++m)
-    if (m < mc) out[jg + 4 * m] = acc[m];
+  for (int i = 0; i < 4; ++i) {
+    const int64_t o = o0 + 4 * rg + i;
+    if (o >= rows_out) continue;
+#pragma unroll
+    for (int c = 0; c < CP; ++c) out[o * l + cg * CP + c] = acc[i][c];
+  }
 }
 
 // out[i] = sum_s part[s][i], s ascending.
@@ -265,14 +292,12 @@ __global__ __launch_bounds__(256) void k_lq_gram(const float* __restrict__ X, in
 // pair is rotated once.  A and V live in LDS.  The rotation of pair (p, q)
 // zeroes A[p][q] with t = tan(phi) the smaller root of
 // t^2 + 2 theta t - 1 = 0, theta = (A[q][q] - A[p][p]) / (2 A[p][q]).
-// Sweeps stop when the off-diagonal mass is below 1e-28 of the total (or
-// after 60 sweeps).  Eigenvalues are then sorted in descending order and:
-//   mode 0 (orthonormalizer)  M[a][b] = V[a][i_b] lambda_b^{-1/2}, l x l,
-//                             0 where lambda_b <= 1e-10 lambda_max;
-//   mode 1 (Ritz factors)     M[a][i] = V[a][i_i] lambda_i^{1/4} and
-//                             M[l r + a r + i] = V[a][i_i] lambda_i^{-1/4},
-//                             i < r (0 where lambda_i <= 0).
-// lam[i] receives the sorted eigenvalues.
+// Sweeps stop when the off-diagonal mass is below 1e-20 of the total (its
+// norm below 1e-10, far under the fp32 outputs' rounding) or after 60
+// sweeps.  Eigenvalues are then sorted in descending order
+// (lam[i]) and the Ritz factors written: M[a][i] = V[a][i_i] lambda_i^{1/4}
+// and M[l r + a r + i] = V[a][i_i] lambda_i^{-1/4} for i < r (0 where
+// lambda_i <= 0).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void jacobi_pair(int k, int t, int l, int& p, int& q) {
   const int m = l - 1;
@@ -290,35 +315,45 @@ __device__ __forceinline__ void jacobi_pair(int k, int t, int l, int& p, int& q)
   }
 }
 
-__global__ __launch_bounds__(256) void k_lq_eig(const double* __restrict__ G, int l, int r,
-                                                int mode, float* __restrict__ M,
-                                                double* __restrict__ lam) {
+constexpr int kEigThreads = 512;
+
+__global__ __launch_bounds__(kEigThreads) void k_lq_eig(const double* __restrict__ G, int l,
+                                                        int r, float* __restrict__ M,
+                                                        double* __restrict__ lam) {
   extern __shared__ double dsm[];
-  double* A = dsm;               // [l][l]
-  double* V = dsm + l * l;       // [l][l]
-  double* cs = V + l * l;        // [l / 2][2]
+  // A and V with an odd row stride S (doubles): a column walk (stride S)
+  // and a row walk (stride 1) both touch distinct LDS banks across a wave.
+  const int S = l | 1;
+  double* A = dsm;               // [l][S]
+  double* V = dsm + l * S;       // [l][S]
+  double* cs = V + l * S;        // [l / 2][2]
   int* pq = reinterpret_cast<int*>(cs + l);  // [l / 2][2]
-  __shared__ double red[256];
+  __shared__ double red[kEigThreads];
   __shared__ int order[kLqMaxL];
   __shared__ int done;
   const int tid = threadIdx.x;
-  const int ll = l * l, half = l / 2;
-  for (int e = tid; e < ll; e += 256) {
-    A[e] = G[e];
-    V[e] = (e / l == e % l) ? 1.0 : 0.0;
-  }
+  const int half = l / 2;
+  // thread layout of the rotation phases: pair group kg, 32-lane stripe jl
+  const int kg = tid >> 5, jl = tid & 31;
+  constexpr int KG = kEigThreads / 32;
+  for (int i = kg; i < l; i += KG)
+    for (int j = jl; j < l; j += 32) {
+      A[i * S + j] = G[i * l + j];
+      V[i * S + j] = (i == j) ? 1.0 : 0.0;
+    }
   __syncthreads();
   for (int sweep = 0; sweep < 60; ++sweep) {
     // convergence test: off-diagonal mass against the total
     double off = 0.0, tot = 0.0;
-    for (int e = tid; e < ll; e += 256) {
-      const double v = A[e] * A[e];
-      tot += v;
-      if (e / l != e % l) off += v;
-    }
+    for (int i = kg; i < l; i += KG)
+      for (int j = jl; j < l; j += 32) {
+        const double v = A[i * S + j] * A[i * S + j];
+        tot += v;
+        if (i != j) off += v;
+      }
     red[tid] = off;
     __syncthreads();
-    for (int w = 128; w > 0; w >>= 1) {
+    for (int w = kEigThreads / 2; w > 0; w >>= 1) {
       if (tid < w) red[tid] += red[tid + w];
       __syncthreads();
     }
@@ -326,21 +361,21 @@ __global__ __launch_bounds__(256) void k_lq_eig(const double* __restrict__ G, in
     __syncthreads();
     red[tid] = tot;
     __syncthreads();
-    for (int w = 128; w > 0; w >>= 1) {
+    for (int w = kEigThreads / 2; w > 0; w >>= 1) {
       if (tid < w) red[tid] += red[tid + w];
       __syncthreads();
     }
-    if (tid == 0) done = !(offs > 1e-28 * red[0]);
+    if (tid == 0) done = !(offs > 1e-20 * red[0]);
     __syncthreads();
     if (done) break;
     for (int t = 0; t < l - 1; ++t) {
       if (tid < half) {
         int p, q;
         jacobi_pair(tid, t, l, p, q);
-        const double apq = A[p * l + q];
+        const double apq = A[p * S + q];
         double c = 1.0, s = 0.0;
         if (apq != 0.0) {
-          const double theta = (A[q * l + q] - A[p * l + p]) / (2.0 * apq);
+          const double theta = (A[q * S + q] - A[p * S + p]) / (2.0 * apq);
           const double tt = (theta >= 0.0 ? 1.0 : -1.0) / (fabs(theta) + sqrt(theta * theta + 1.0));
           c = 1.0 / sqrt(tt * tt + 1.0);
           s = tt * c;
@@ -352,60 +387,143 @@ __global__ __launch_bounds__(256) void k_lq_eig(const double* __restrict__ G, in
       }
       __syncthreads();
       // rows p, q of every pair
-      for (int e = tid; e < half * l; e += 256) {
-        const int k = e / l, j = e - k * l;
+      for (int k = kg; k < half; k += KG) {
         const int p = pq[2 * k], q = pq[2 * k + 1];
         const double c = cs[2 * k], s = cs[2 * k + 1];
-        const double ap = A[p * l + j], aq = A[q * l + j];
-        A[p * l + j] = c * ap - s * aq;
-        A[q * l + j] = s * ap + c * aq;
+        for (int j = jl; j < l; j += 32) {
+          const double ap = A[p * S + j], aq = A[q * S + j];
+          A[p * S + j] = c * ap - s * aq;
+          A[q * S + j] = s * ap + c * aq;
+        }
       }
       __syncthreads();
       // columns p, q of every pair, in A and V
-      for (int e = tid; e < half * l; e += 256) {
-        const int k = e / l, i = e - k * l;
+      for (int k = kg; k < half; k += KG) {
         const int p = pq[2 * k], q = pq[2 * k + 1];
         const double c = cs[2 * k], s = cs[2 * k + 1];
-        const double ap = A[i * l + p], aq = A[i * l + q];
-        A[i * l + p] = c * ap - s * aq;
-        A[i * l + q] = s * ap + c * aq;
-        const double vp = V[i * l + p], vq = V[i * l + q];
-        V[i * l + p] = c * vp - s * vq;
-        V[i * l + q] = s * vp + c * vq;
+        for (int i = jl; i < l; i += 32) {
+          const double ap = A[i * S + p], aq = A[i * S + q];
+          A[i * S + p] = c * ap - s * aq;
+          A[i * S + q] = s * ap + c * aq;
+          const double vp = V[i * S + p], vq = V[i * S + q];
+          V[i * S + p] = c * vp - s * vq;
+          V[i * S + q] = s * vp + c * vq;
+        }
       }
       __syncthreads();
     }
   }
   // descending order of the eigenvalues (ties keep the lower index first)
   if (tid < l) {
-    const double me = A[tid * l + tid];
+    const double me = A[tid * S + tid];
     int rank = 0;
     for (int j = 0; j < l; ++j) {
-      const double o = A[j * l + j];
+      const double o = A[j * S + j];
       rank += (o > me || (o == me && j < tid)) ? 1 : 0;
     }
     order[rank] = tid;
   }
   __syncthreads();
-  if (tid < l) lam[tid] = A[order[tid] * l + order[tid]];
-  const double lmax = A[order[0] * l + order[0]];
-  if (mode == 0) {
-    for (int e = tid; e < ll; e += 256) {
-      const int a = e / l, b = e - a * l;
-      const double lb = A[order[b] * l + order[b]];
-      const double sc = lb > kDrop * lmax ? 1.0 / sqrt(lb) : 0.0;
-      M[e] = (float)(V[a * l + order[b]] * sc);
-    }
-  } else {
-    for (int e = tid; e < l * r; e += 256) {
-      const int a = e / r, i = e - a * r;
-      const double li = A[order[i] * l + order[i]];
-      const double q4 = li > 0.0 ? sqrt(sqrt(li)) : 0.0;
-      const double v = V[a * l + order[i]];
-      M[e] = (float)(v * q4);
-      M[l * r + e] = (float)(q4 > 0.0 ? v / q4 : 0.0);
-    }
+  if (tid < l) lam[tid] = A[order[tid] * S + order[tid]];
+  for (int e = tid; e < l * r; e += kEigThreads) {
+    const int a = e / r, i = e - a * r;
+    const double li = A[order[i] * S + order[i]];
+    const double q4 = li > 0.0 ? sqrt(sqrt(li)) : 0.0;
+    const double v = V[a * S + order[i]];
+    M[e] = (float)(v * q4);
+    M[l * r + e] = (float)(q4 > 0.0 ? v / q4 : 0.0);
   }
+}
+
+// ---------------------------------------------------------------------------
+// Cholesky factor of a Gram matrix G = X^T X (l x l, fp64): G = L L^T, so
+// that X L^{-T} has orthonormal columns spanning span(X).  One workgroup,
+// right-looking in LDS.  A pivot at or below 1e-10 times the largest
+// diagonal of G marks its column as dependent on the earlier ones: the
+// column is dropped (left out of the trailing update; its output column
+// will be 0), which keeps the other output columns orthonormal.  Writes L
+// as fp32 [l][l] (lower; 0 above) and invd[j] = 1 / L[j][j] (0 if dropped).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_lq_chol(const double* __restrict__ G, int l,
+                                                 float* __restrict__ Lout,
+                                                 float* __restrict__ invd) {
+  extern __shared__ double csm[];
+  const int S = l | 1;
+  double* Lm = csm;  // [l][S]
+  __shared__ double dmax;
+  const int tid = threadIdx.x, ti = tid >> 5, tk = tid & 31;
+  for (int i = ti; i < l; i += 8)
+    for (int j = tk; j < l; j += 32) Lm[i * S + j] = G[i * l + j];
+  __syncthreads();
+  if (tid == 0) {
+    double m = 0.0;
+    for (int j = 0; j < l; ++j) m = fmax(m, Lm[j * S + j]);
+    dmax = m;
+  }
+  __syncthreads();
+  const double tol = kDrop * dmax;
+  for (int j = 0; j < l; ++j) {
+    const double d = Lm[j * S + j];
+    const bool drop = !(d > tol);
+    const double piv = drop ? 1.0 : sqrt(d);
+    __syncthreads();  // every thread has read the pivot before it changes
+    if (tid == 0) {
+      Lm[j * S + j] = piv;
+      invd[j] = drop ? 0.0f : (float)(1.0 / piv);
+    }
+    for (int i = j + 1 + tid; i < l; i += 256) Lm[i * S + j] = drop ? 0.0 : Lm[i * S + j] / piv;
+    __syncthreads();
+    // trailing update of the lower triangle: A[i][k] -= L[i][j] L[k][j], j < k <= i
+    for (int i = j + 1 + ti; i < l; i += 8) {
+      const double lij = Lm[i * S + j];
+      for (int k = j + 1 + tk; k <= i; k += 32) Lm[i * S + k] -= lij * Lm[k * S + j];
+    }
+    __syncthreads();
+  }
+  for (int i = ti; i < l; i += 8)
+    for (int j = tk; j < l; j += 32) Lout[i * l + j] = j <= i ? (float)Lm[i * S + j] : 0.0f;
+}
+
+// out[t] = X[t] L^{-T}: row t of the output solves x L^T = X[t] by forward
+// substitution (x_j = (X[t][j] - sum_{k<j} x_k L[j][k]) invd[j]).  One
+// thread per row, the row in registers, L broadcast from LDS.
+template <int CP>
+__global__ __launch_bounds__(256) void k_lq_trsm(const float* __restrict__ X, int64_t T,
+                                                 const float* __restrict__ Lf,
+                                                 const float* __restrict__ invd,
+                                                 float* __restrict__ out) {
+  constexpr int l = 16 * CP;
+  __shared__ __attribute__((aligned(16))) float sl[l * l];
+  __shared__ float sd[l];
+  for (int e = threadIdx.x; e < l * l; e += 256) sl[e] = Lf[e];
+  if (threadIdx.x < l) sd[threadIdx.x] = invd[threadIdx.x];
+  __syncthreads();
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= T) return;
+  float x[l];
+#pragma unroll
+  for (int j = 0; j < l; j += 4) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(X + t * l + j);
+    x[j] = v[0]; x[j + 1] = v[1]; x[j + 2] = v[2]; x[j + 3] = v[3];
+  }
+#pragma unroll
+  for (int j = 0; j < l; ++j) {
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll
+    for (int k = 0; k + 4 <= j; k += 4) {
+      const f32x4 lv = *reinterpret_cast<const f32x4*>(sl + j * l + k);
+      a0 = fmaf(x[k], lv[0], a0);
+      a1 = fmaf(x[k + 1], lv[1], a1);
+      a2 = fmaf(x[k + 2], lv[2], a2);
+      a3 = fmaf(x[k + 3], lv[3], a3);
+    }
+#pragma unroll
+    for (int k = j & ~3; k < j; ++k) a0 = fmaf(x[k], sl[j * l + k], a0);
+    x[j] = (x[j] - ((a0 + a1) + (a2 + a3))) * sd[j];
+  }
+#pragma unroll
+  for (int j = 0; j < l; j += 4)
+    *reinterpret_cast<f32x4*>(out + t * l + j) = f32x4{x[j], x[j + 1], x[j + 2], x[j + 3]};
 }
 
 // ---------------------------------------------------------------------------
@@ -464,18 +582,36 @@ __global__ __launch_bounds__(256) void k_lq_adapter(const float* __restrict__ L1
 }
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// f(std::integral_constant<int, cp>) for cp = l / 16 in 1 .. 6
+template <class F>
+void with_cp(int cp, F&& f) {
+  switch (cp) {
+    case 1: f(std::integral_constant<int, 1>{}); break;
+    case 2: f(std::integral_constant<int, 2>{}); break;
+    case 3: f(std::integral_constant<int, 3>{}); break;
+    case 4: f(std::integral_constant<int, 4>{}); break;
+    case 5: f(std::integral_constant<int, 5>{}); break;
+    default: f(std::integral_constant<int, 6>{}); break;
+  }
+}
 inline size_t al(size_t v) { return (v + 255) / 256 * 256; }
 
-// Slices of the E^T Y product: enough workgroups to fill the chip.
-inline int64_t ety_slices(int64_t N, int64_t K) {
-  int64_t s = cdiv(512, K / 64);
-  const int64_t cap = cdiv(N, 32);
-  if (s > cap) s = cap;
-  return s < 1 ? 1 : s;
+// Contraction slices of the two E products (multiples of 32 long): enough
+// workgroups (64 output rows each) to fill the chip twice.
+inline int64_t mul_slice_len(int64_t rows_out, int64_t ctot) {
+  const int64_t tiles = cdiv(rows_out, 64);
+  int64_t ns = cdiv(512, tiles);
+  if (ns > cdiv(ctot, 256)) ns = cdiv(ctot, 256);  // at least 256 deep
+  if (ns < 1) ns = 1;
+  return cdiv(cdiv(ctot, ns), 32) * 32;
+}
+inline int64_t mul_slices(int64_t rows_out, int64_t ctot) {
+  return cdiv(ctot, mul_slice_len(rows_out, ctot));
 }
 inline int64_t gram_slices(int64_t T) {
-  int64_t s = cdiv(T, 256);
-  if (s > 128) s = 128;
+  int64_t s = cdiv(T, 32);
+  if (s > 512) s = 512;
   return s < 1 ? 1 : s;
 }
 
@@ -496,7 +632,8 @@ LqPlan plan(int64_t N, int64_t K, int l) {
   p.y2_off = take(4 * (size_t)N * l);
   p.z_off = take(4 * (size_t)K * l);
   p.z2_off = take(4 * (size_t)K * l);
-  p.part_off = take(4 * (size_t)ety_slices(N, K) * K * l);
+  const int64_t sx = mul_slices(N, K), sy = mul_slices(K, N);
+  p.part_off = take(4 * (size_t)(sx * N > sy * K ? sx * N : sy * K) * l);
   const int64_t gs = gram_slices(N > K ? N : K);
   p.partd_off = take(8 * (size_t)gs * l * l);
   p.g_off = take(8 * (size_t)l * l);
@@ -506,16 +643,23 @@ LqPlan plan(int64_t N, int64_t K, int l) {
   return p;
 }
 
-size_t eig_lds(int l) { return (size_t)(2 * l * l + l) * 8 + (size_t)l * 4; }
+size_t eig_lds(int l) { return (size_t)(2 * l * (l | 1) + l) * 8 + (size_t)l * 4; }
+size_t chol_lds(int l) { return (size_t)(l * (l | 1)) * 8; }
 
 }  // namespace
 
 size_t lq_workspace_bytes(int64_t N, int64_t K, int32_t l) { return plan(N, K, l).total; }
 
 hipError_t launch_lq_init(const LqArgs& a, hipStream_t stream) {
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&k_lq_eig), hipFuncAttributeMaxDynamicSharedMemorySize,
-      (int)eig_lds(kLqMaxL));
+  static const hipError_t attr = [] {
+    const hipError_t a = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_lq_eig),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             (int)eig_lds(kLqMaxL));
+    const hipError_t b = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_lq_chol),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             (int)chol_lds(kLqMaxL));
+    return a != hipSuccess ? a : b;
+  }();
   if (attr != hipSuccess) return attr;
   const int64_t N = a.N, K = a.K;
   const int l = a.l, r = a.r;
@@ -536,28 +680,38 @@ hipError_t launch_lq_init(const LqArgs& a, hipStream_t stream) {
   hipError_t e = hipSuccess;
   auto ok = [&]() { return (e = hipGetLastError()) == hipSuccess; };
 
-  auto mul_ex = [&](const float* E, const float* X, float* out) {
-    hipLaunchKernelGGL(k_lq_mul_ex, dim3((unsigned)cdiv(N, 32)), dim3(256), 0, stream, E, X, N,
-                       K, l, out);
-    return ok();
-  };
-  auto mul_ety = [&](const float* E, const float* Yin, float* out) {
-    const int64_t S = ety_slices(N, K), rps = cdiv(N, S);
-    hipLaunchKernelGGL(k_lq_mul_ety, dim3((unsigned)(K / 64), (unsigned)S), dim3(256), 0, stream,
-                       E, Yin, N, K, l, rps, part);
+  // one of the two E products into out, through the partial buffer
+  auto mul = [&](bool trans, const float* E, const float* X, float* out) {
+    const int64_t rows_out = trans ? K : N, ctot = trans ? N : K;
+    const int64_t len = mul_slice_len(rows_out, ctot), S = cdiv(ctot, len);
+    const dim3 grid((unsigned)cdiv(rows_out, 64), (unsigned)S);
+    const int cp = l / 16;
+    with_cp(cp, [&](auto cpc) {
+      constexpr int CP = decltype(cpc)::value;
+      if (trans)
+        hipLaunchKernelGGL((k_lq_mul<true, CP>), grid, dim3(256), 0, stream, E, X, N, K, len, part);
+      else
+        hipLaunchKernelGGL((k_lq_mul<false, CP>), grid, dim3(256), 0, stream, E, X, N, K, len, part);
+    });
     if (!ok()) return false;
-    hipLaunchKernelGGL(k_lq_reduce<float>, dim3((unsigned)cdiv(K * l, 256)), dim3(256), 0, stream,
-                       part, S, K * l, out);
+    hipLaunchKernelGGL(k_lq_reduce<float>, dim3((unsigned)cdiv(rows_out * l, 256)), dim3(256), 0,
+                       stream, part, S, rows_out * l, out);
     return ok();
   };
-  auto gram_eig = [&](const float* X, int64_t T, int mode) {
+  auto mul_ex = [&](const float* E, const float* X, float* out) { return mul(false, E, X, out); };
+  auto mul_ety = [&](const float* E, const float* Y, float* out) { return mul(true, E, Y, out); };
+  auto gram = [&](const float* X, int64_t T) {
     const int64_t S = gram_slices(T), rps = cdiv(T, S);
-    hipLaunchKernelGGL(k_lq_gram, dim3((unsigned)S), dim3(256), 0, stream, X, T, l, rps, partd);
+    hipLaunchKernelGGL(k_lq_gram, dim3((unsigned)cdiv(T, rps)), dim3(256), 0, stream, X, T, l, rps,
+                       partd);
     if (!ok()) return false;
     hipLaunchKernelGGL(k_lq_reduce<double>, dim3((unsigned)cdiv((int64_t)l * l, 256)), dim3(256), 0,
-                       stream, partd, S, (int64_t)l * l, G);
-    if (!ok()) return false;
-    hipLaunchKernelGGL(k_lq_eig, dim3(1), dim3(256), eig_lds(l), stream, G, l, r, mode, Mm, lam);
+                       stream, partd, cdiv(T, rps), (int64_t)l * l, G);
+    return ok();
+  };
+  auto ritz_factors = [&](const float* X, int64_t T) {
+    if (!gram(X, T)) return false;
+    hipLaunchKernelGGL(k_lq_eig, dim3(1), dim3(kEigThreads), eig_lds(l), stream, G, l, r, Mm, lam);
     return ok();
   };
   auto mul_xm = [&](const float* X, int64_t T, const float* M, int c, float* out) {
@@ -567,7 +721,16 @@ hipError_t launch_lq_init(const LqArgs& a, hipStream_t stream) {
   };
   // orthonormalize X [T][l] into out (a different buffer)
   auto orth = [&](const float* X, int64_t T, float* out) {
-    return gram_eig(X, T, 0) && mul_xm(X, T, Mm, l, out);
+    if (!gram(X, T)) return false;
+    float* invd = Mm + (size_t)l * l;
+    hipLaunchKernelGGL(k_lq_chol, dim3(1), dim3(256), chol_lds(l), stream, G, l, Mm, invd);
+    if (!ok()) return false;
+    with_cp(l / 16, [&](auto cpc) {
+      constexpr int CP = decltype(cpc)::value;
+      hipLaunchKernelGGL((k_lq_trsm<CP>), dim3((unsigned)cdiv(T, 256)), dim3(256), 0, stream, X, T,
+                         Mm, invd, out);
+    });
+    return ok();
   };
   // L step on E: L1 [N][r], L2t [K][r]
   auto l_step = [&](const float* E) {
@@ -580,7 +743,7 @@ hipError_t launch_lq_init(const LqArgs& a, hipStream_t stream) {
     }
     if (!orth(Y, N, Y2)) return false;         // Y2 = orth(Y)
     if (!mul_ety(E, Y2, Z)) return false;      // Z = E^T Y2 = B^T
-    if (!gram_eig(Z, K, 1)) return false;      // Ritz factors
+    if (!ritz_factors(Z, K)) return false;     // Ritz factors
     return mul_xm(Y2, N, Mm, r, a.L1) && mul_xm(Z, K, Mm + (size_t)l * r, r, a.L2t);
   };
   auto q_step = [&](const float* R) {

