@@ -96,6 +96,7 @@ extern "C" {
 #define QLORA_ERR_UNSUPPORTED (-2) /* block sizes other than 64 / 256, etc.  */
 #define QLORA_ERR_WORKSPACE (-3)   /* workspace smaller than required        */
 #define QLORA_ERR_LAUNCH (-4)      /* a HIP launch reported an error         */
+#define QLORA_ERR_INFEASIBLE (-5)  /* qlora_ilp_plan: no choice fits          */
 
 #define QLORA_CODE_NF4 0
 #define QLORA_CODE_FP4 1
@@ -289,6 +290,47 @@ int32_t qlora_lq_init(const float* W, int64_t N, int64_t K, int32_t code_type,
                       uint8_t* codes, uint8_t* q8, float* step, uint16_t* A,
                       uint16_t* B, float* L1, float* L2t, void* ws,
                       size_t ws_bytes, hipStream_t stream);
+
+/* ---- Quantization configuration per matrix under a memory budget ----
+ *
+ * The LQ-LoRA abstract ("LQ-LoRA: Low-rank Plus Quantized Matrix
+ * Decomposition for Efficient Language Model Finetuning") chooses each
+ * matrix's quantization parameters by an integer linear program so that the
+ * model meets an overall memory budget.  Here a configuration is a code type
+ * (QLORA_CODE_*; block size 64 with double quantization, what the layer
+ * takes), its memory the state bytes (qlora_storage_bytes) and its error on
+ * a matrix the squared Frobenius error of the quantized part.
+ *
+ * qlora_quant_error -- *sq_err = ||R - W_hat(R)||_F^2 in fp64, where
+ * R = W, or R = W - L1 L2t^T when L1 and L2t are given (the decomposition
+ * error of an LQ-LoRA initialization with that configuration), and W_hat(R)
+ * is R quantized with `code_type` and dequantized (as nf4_dequantize).
+ *   W      [N, K] fp32, device; K % 64 == 0
+ *   L1     [N, r] fp32, L2t [K, r] fp32, device, both NULL or both given;
+ *          1 <= r <= QLORA_LQ_MAX_L
+ *   sq_err one double, device (8-byte aligned), written on the stream
+ *   ws     device workspace, 256-byte aligned, ws_bytes >=
+ *          qlora_quant_error_workspace_size(N, K, code_type, L1 != NULL)
+ * The sum has a fixed order: the result is reproducible. */
+size_t qlora_quant_error_workspace_size(int64_t N, int64_t K, int32_t code_type,
+                                        int32_t with_lowrank);
+int32_t qlora_quant_error(const float* W, int64_t N, int64_t K,
+                          int32_t code_type, const float* L1, const float* L2t,
+                          int32_t r, double* sq_err, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
+
+/* qlora_ilp_plan -- host only, no device work.  Given, for M matrices and
+ * C configurations, the errors err[m*C + c] (finite) and the bytes
+ * bytes[m*C + c] (>= 0) (host arrays), choose one configuration per matrix
+ * minimizing the total error subject to total bytes <= budget.  Solved
+ * exactly (dynamic programming over the Pareto front of partial choices);
+ * errors are summed in matrix order, and ties go to fewer total bytes, then
+ * to the lexicographically smallest choice vector.  Writes choice[M] (host),
+ * *total_err and *total_bytes; returns QLORA_ERR_INFEASIBLE if no choice
+ * fits.  1 <= C <= 64. */
+int32_t qlora_ilp_plan(int32_t n_matrices, int32_t n_configs, const double* err,
+                       const int64_t* bytes, int64_t budget, int32_t* choice,
+                       double* total_err, int64_t* total_bytes);
 
 #ifdef __cplusplus
 }

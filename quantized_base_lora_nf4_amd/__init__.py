@@ -7,5 +7,6 @@ tensors into its calls (see :mod:`quantized_base_lora_nf4_amd.ops`).
 
 from ._lib import LIB_PATH, EXPORTS, QloraError, lib  # noqa: F401
 from .ops import (LqResult, NF4Weight, QLoRALinear, QLoRALinearFunction, alloc_nf4,  # noqa: F401
-                  code_table, lq_init, lq_workspace_size, nf4_dequantize, nf4_quantize,
-                  qlora_linear_bwd, qlora_linear_fwd, storage_bytes, workspace_size)
+                  code_table, ilp_plan, lq_init, lq_workspace_size, nf4_dequantize,
+                  nf4_quantize, qlora_linear_bwd, qlora_linear_fwd, quant_error, storage_bytes,
+                  workspace_size)

@@ -15,6 +15,7 @@ QLORA_ERR_INVALID = -1
 QLORA_ERR_UNSUPPORTED = -2
 QLORA_ERR_WORKSPACE = -3
 QLORA_ERR_LAUNCH = -4
+QLORA_ERR_INFEASIBLE = -5
 
 QLORA_CODE_NF4 = 0
 QLORA_CODE_FP4 = 1
@@ -38,6 +39,9 @@ EXPORTS = (
     "qlora_linear_bwd_ev",
     "qlora_lq_workspace_size",
     "qlora_lq_init",
+    "qlora_quant_error_workspace_size",
+    "qlora_quant_error",
+    "qlora_ilp_plan",
 )
 
 
@@ -107,6 +111,12 @@ def lib() -> ctypes.CDLL:
     L.qlora_lq_init.restype = i32
     L.qlora_lq_init.argtypes = [vp, i64, i64, i32, i32, i32, vp, i32, i32, i32, f32,
                                 vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.qlora_quant_error_workspace_size.restype = sz
+    L.qlora_quant_error_workspace_size.argtypes = [i64, i64, i32, i32]
+    L.qlora_quant_error.restype = i32
+    L.qlora_quant_error.argtypes = [vp, i64, i64, i32, vp, vp, i32, vp, vp, sz, vp]
+    L.qlora_ilp_plan.restype = i32
+    L.qlora_ilp_plan.argtypes = [i32, i32, vp, vp, i64, vp, vp, vp]
     _lib = L
     return L
 

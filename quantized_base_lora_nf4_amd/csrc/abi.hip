@@ -121,6 +121,7 @@ const char* qlora_status_str(int32_t status) {
       return "unsupported configuration (block sizes must be 64 and 256, code type NF4 or FP4)";
     case QLORA_ERR_WORKSPACE: return "workspace too small";
     case QLORA_ERR_LAUNCH: return "HIP launch error";
+    case QLORA_ERR_INFEASIBLE: return "no choice fits the budget";
     default: return "unknown status";
   }
 }
@@ -348,3 +349,42 @@ int32_t qlora_lq_init(const float* W, int64_t N, int64_t K, int32_t code_type, i
 
 }  // extern "C"
 
+extern "C" {
+
+size_t qlora_quant_error_workspace_size(int64_t N, int64_t K, int32_t code_type,
+                                        int32_t with_lowrank) {
+  if (!code_ok(code_type) || N < 1 || K < 64 || (K % 64) != 0 || N > ((int64_t)1 << 40) / K)
+    return 0;
+  const int bits = with_code(code_type, [](auto ct) { return decltype(ct)::kBits; });
+  return qn::quant_error_workspace_bytes(N, K, bits, with_lowrank != 0);
+}
+
+int32_t qlora_quant_error(const float* W, int64_t N, int64_t K, int32_t code_type,
+                          const float* L1, const float* L2t, int32_t r, double* sq_err, void* ws,
+                          size_t ws_bytes, hipStream_t stream) {
+  if (!W || !sq_err || !ws || ((L1 == nullptr) != (L2t == nullptr))) return QLORA_ERR_INVALID;
+  if (!code_ok(code_type)) return QLORA_ERR_UNSUPPORTED;
+  const size_t need = qlora_quant_error_workspace_size(N, K, code_type, L1 != nullptr);
+  if (need == 0) return QLORA_ERR_INVALID;
+  if (L1 && (r < 1 || r > QLORA_LQ_MAX_L || !aligned16(L1) || !aligned16(L2t)))
+    return QLORA_ERR_INVALID;
+  if (!aligned16(W) || ((uintptr_t)sq_err & 7u) != 0 || ((uintptr_t)ws & 255u) != 0)
+    return QLORA_ERR_INVALID;
+  if (ws_bytes < need) return QLORA_ERR_WORKSPACE;
+  return launch_status(qn::launch_quant_error(W, N, K, code_type, L1, L2t, r, sq_err, ws, stream));
+}
+
+int32_t qlora_ilp_plan(int32_t n_matrices, int32_t n_configs, const double* err,
+                       const int64_t* bytes, int64_t budget, int32_t* choice, double* total_err,
+                       int64_t* total_bytes) {
+  if (n_matrices < 1 || n_configs < 1 || n_configs > 64 || n_matrices > (1 << 20) || !err ||
+      !bytes || !choice || !total_err || !total_bytes || budget < 0)
+    return QLORA_ERR_INVALID;
+  for (int64_t i = 0; i < (int64_t)n_matrices * n_configs; ++i)
+    if (!isfinite(err[i]) || bytes[i] < 0) return QLORA_ERR_INVALID;
+  return qn::ilp_plan(n_matrices, n_configs, err, bytes, budget, choice, total_err, total_bytes)
+             ? QLORA_OK
+             : QLORA_ERR_INFEASIBLE;
+}
+
+}  // extern "C"

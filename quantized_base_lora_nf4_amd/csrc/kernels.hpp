@@ -99,5 +99,18 @@ struct LqArgs {
 };
 size_t lq_workspace_bytes(int64_t N, int64_t K, int32_t l);
 hipError_t launch_lq_init(const LqArgs& a, hipStream_t stream);
+// R = W - L1 L2t^T (fp32 [N, K]; L1 [N, r], L2t [K, r], r <= 96, K % 64 == 0)
+hipError_t launch_lq_residual(const float* W, const float* L1, const float* L2t, int64_t N,
+                              int64_t K, int r, float* R, hipStream_t stream);
+
+// ---- ilp.hip: configuration errors and the budget program ----
+size_t quant_error_workspace_bytes(int64_t N, int64_t K, int bits, bool lowrank);
+// *sq_err (device) = ||R - W_hat(R)||_F^2, R = W or W - L1 L2t^T (L1 non-null)
+hipError_t launch_quant_error(const float* W, int64_t N, int64_t K, int code, const float* L1,
+                              const float* L2t, int r, double* sq_err, void* ws,
+                              hipStream_t stream);
+// host: exact minimum-error choice within the budget; false if none fits
+bool ilp_plan(int M, int C, const double* err, const int64_t* bytes, int64_t budget,
+              int32_t* choice, double* total_err, int64_t* total_bytes);
 
 }  // namespace qn

@@ -650,6 +650,13 @@ size_t chol_lds(int l) { return (size_t)(l * (l | 1)) * 8; }
 
 size_t lq_workspace_bytes(int64_t N, int64_t K, int32_t l) { return plan(N, K, l).total; }
 
+hipError_t launch_lq_residual(const float* W, const float* L1, const float* L2t, int64_t N,
+                              int64_t K, int r, float* R, hipStream_t stream) {
+  hipLaunchKernelGGL(k_lq_residual, dim3((unsigned)(cdiv(N, 64) * (K / 64))), dim3(256), 0, stream,
+                     W, L1, L2t, N, K, r, R);
+  return hipGetLastError();
+}
+
 hipError_t launch_lq_init(const LqArgs& a, hipStream_t stream) {
   static const hipError_t attr = [] {
     const hipError_t a = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_lq_eig),

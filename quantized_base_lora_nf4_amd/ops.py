@@ -12,8 +12,8 @@ from typing import Optional, Tuple
 
 import torch
 
-from ._lib import (QLORA_CODE_FP4, QLORA_CODE_NF2, QLORA_CODE_NF3, QLORA_CODE_NF4, Nf4Tensor,
-                   check, lib)
+from ._lib import (QLORA_CODE_FP4, QLORA_CODE_NF2, QLORA_CODE_NF3, QLORA_CODE_NF4,
+                   QLORA_ERR_INFEASIBLE, Nf4Tensor, check, lib)
 
 BLOCKSIZE = 64
 DQ_BLOCKSIZE = 256
@@ -223,6 +223,47 @@ def lq_init(W: torch.Tensor, omega: torch.Tensor, r: int, iters: int = 2, power_
                              ws.numel() * ws.element_size(), _stream(stream))
     check(st, "qlora_lq_init")
     return LqResult(w=w, A=A, B=B, L1=L1, L2t=L2t)
+
+
+def quant_error(W: torch.Tensor, code: str = "nf4", L1: Optional[torch.Tensor] = None,
+                L2t: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """||R - W_hat(R)||_F^2 for one configuration, R = W or W - L1 L2t^T;
+    returns a one-element float64 device tensor (written on the stream)."""
+    if W.dtype != torch.float32 or W.dim() != 2:
+        raise TypeError("W must be a 2-D float32 tensor")
+    N, K = W.shape
+    r = 0 if L1 is None else L1.shape[1]
+    need = int(lib().qlora_quant_error_workspace_size(N, K, _code_id(code), int(L1 is not None)))
+    ws = _workspace(need, W.device, ws)
+    if out is None:
+        out = torch.empty(1, dtype=torch.float64, device=W.device)
+    st = lib().qlora_quant_error(_ptr(W), N, K, _code_id(code), _ptr(L1), _ptr(L2t), r,
+                                 _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
+                                 _stream(stream))
+    check(st, "qlora_quant_error")
+    return out
+
+
+def ilp_plan(err, nbytes, budget: int):
+    """Exact per-matrix configuration choice (host).  err, nbytes: [M][C]
+    array-likes.  Returns (choice list, total error, total bytes), or None
+    if nothing fits the budget."""
+    import numpy as np
+    e = np.ascontiguousarray(err, dtype=np.float64)
+    b = np.ascontiguousarray(nbytes, dtype=np.int64)
+    if e.ndim != 2 or e.shape != b.shape:
+        raise ValueError("err and nbytes must be [M][C] arrays of the same shape")
+    M, C = e.shape
+    choice = np.zeros(M, dtype=np.int32)
+    te = ctypes.c_double(0.0)
+    tb = ctypes.c_int64(0)
+    st = lib().qlora_ilp_plan(M, C, e.ctypes.data, b.ctypes.data, int(budget), choice.ctypes.data,
+                              ctypes.byref(te), ctypes.byref(tb))
+    if st == QLORA_ERR_INFEASIBLE:
+        return None
+    check(st, "qlora_ilp_plan")
+    return [int(c) for c in choice], te.value, tb.value
 
 
 class QLoRALinearFunction(torch.autograd.Function):

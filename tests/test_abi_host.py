@@ -187,7 +187,49 @@ def test_linear_rejects_bad_arguments_without_launching():
                               FAKE, FAKE, FAKE, needb, None) == _lib.QLORA_ERR_UNSUPPORTED
 
 
+@pytest.mark.parametrize("seed", range(12))
+def test_ilp_plan_matches_bruteforce(seed):
+    from oracle import ilp
+    rng = np.random.default_rng(seed)
+    M, C = int(rng.integers(1, 7)), int(rng.integers(1, 5))
+    err = rng.random((M, C)) * 10
+    if seed % 3 == 0:
+        err = np.round(err)                  # exact ties
+    nbytes = rng.integers(1, 50, (M, C))
+    lo, hi = int(nbytes.min(axis=1).sum()), int(nbytes.max(axis=1).sum())
+    for budget in (lo - 1, lo, (lo + hi) // 2, hi, hi + 5):
+        want = ilp.plan(err, nbytes, budget)
+        got = qn.ilp_plan(err, nbytes, budget)
+        if want is None:
+            assert got is None
+        else:
+            assert got is not None and tuple(got[0]) == tuple(want[0])
+            assert got[1] == want[1] and got[2] == want[2]
+
+
+def test_ilp_plan_rejects_bad_arguments():
+    L = qn.lib()
+    e = (ctypes.c_double * 4)(1, 2, 3, 4)
+    b = (ctypes.c_int64 * 4)(1, 2, 3, 4)
+    ch = (ctypes.c_int32 * 2)()
+    te, tb = ctypes.c_double(), ctypes.c_int64()
+    args = lambda **kw: dict(dict(M=2, C=2, e=e, b=b, budget=10), **kw)
+    def call(**kw):
+        a = args(**kw)
+        return L.qlora_ilp_plan(a["M"], a["C"], ctypes.cast(a["e"], ctypes.c_void_p) if a["e"] else None,
+                                ctypes.cast(a["b"], ctypes.c_void_p), a["budget"],
+                                ctypes.cast(ch, ctypes.c_void_p), ctypes.byref(te), ctypes.byref(tb))
+    assert call() == _lib.QLORA_OK
+    assert call(M=0) == _lib.QLORA_ERR_INVALID
+    assert call(C=65) == _lib.QLORA_ERR_INVALID
+    assert call(budget=-1) == _lib.QLORA_ERR_INVALID
+    assert call(e=None) == _lib.QLORA_ERR_INVALID
+    assert call(budget=3) == _lib.QLORA_ERR_INFEASIBLE
+    nan = (ctypes.c_double * 4)(1, float("nan"), 3, 4)
+    assert call(e=nan) == _lib.QLORA_ERR_INVALID
+
+
 def test_status_strings():
-    for st in (0, -1, -2, -3, -4):
+    for st in (0, -1, -2, -3, -4, -5):
         assert qn.lib().qlora_status_str(st)
     assert "workspace" in _lib.status_str(-3)
