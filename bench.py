@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--lq-only", action="store_true",
                     help="only time the low-rank plus quantized initialization (the "
                          "extra 'lq_init') and print it")
+    ap.add_argument("--ilp-only", action="store_true",
+                    help="only time the configuration error table and plans (the extra "
+                         "'ilp') and print it")
     return ap.parse_args()
 
 
@@ -114,9 +117,10 @@ def main():
         sys.exit(2)
 
     import torch
-    if args.lq_only:
+    if args.lq_only or args.ilp_only:
         import quantized_base_lora_nf4_amd as qn
-        print(json.dumps({"lq_init": run_lq(qn, torch)}))
+        print(json.dumps({"lq_init": run_lq(qn, torch)} if args.lq_only else
+                         {"ilp": run_ilp(qn, torch)}))
         return
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
@@ -261,6 +265,7 @@ def main():
             extra["code_types"][code]["fused_step"] = code_step(
                 qn, L, torch, layers, M, r, s, sp, args.steps, args.warmup, flops_step, code)
         extra["lq_init"] = run_lq(qn, torch)
+        extra["ilp"] = run_ilp(qn, torch)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -331,6 +336,57 @@ def run_lq(qn, torch, reps=5):
         del W, Om, ws
         torch.cuda.empty_cache()
     return out
+
+
+def run_ilp(qn, torch, reps=3):
+    """Error table of the LLaMA-13B block (7 matrices, 317M weights) for the
+    four code types, then plans at three average bit budgets.  Per table
+    call: the quantizer reads W and writes the state, the error pass reads W
+    and the state again."""
+    import workloads as wl_mod
+    configs = ("nf4", "fp4", "nf3", "nf2")
+    wl = wl_mod.LLAMA13B_BLOCK
+    Ws = [torch.from_numpy(wl_mod.draw_weight(sp, wl_mod.rng_for(wl.seed, 2000 + i))).cuda()
+          for i, sp in enumerate(wl.weights)]
+    need = max(int(qn.lib().qlora_quant_error_workspace_size(W.shape[0], W.shape[1], 0, 0))
+               for W in Ws)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    out = torch.empty(len(Ws) * len(configs), dtype=torch.float64, device="cuda")
+
+    def table():
+        for m, W in enumerate(Ws):
+            for c, code in enumerate(configs):
+                qn.quant_error(W, code, ws=ws, out=out[m * len(configs) + c:][:1])
+    table()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        table()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ms = float(np.median(ts))
+    err = out.cpu().numpy().reshape(len(Ws), len(configs))
+    nbytes = np.array([[qn.storage_bytes(W.shape[0], W.shape[1], c) for c in configs] for W in Ws])
+    nw = sum(W.numel() for W in Ws)
+    moved = sum(2 * 4 * W.numel() + 2 * int(nbytes[m][c]) for m, W in enumerate(Ws)
+                for c in range(len(configs)))
+    plans = []
+    for bits in (2.5, 3.0, 3.5):
+        t0 = time.perf_counter()
+        got = qn.ilp_plan(err, nbytes, int(nw * bits / 8))
+        dt = time.perf_counter() - t0
+        plans.append({"bits_per_weight": bits, "choice": [configs[c] for c in got[0]],
+                      "error_vs_all_nf4": round(got[1] / float(err[:, 0].sum()), 4),
+                      "plan_ms": round(dt * 1e3, 3)})
+    del Ws, ws
+    torch.cuda.empty_cache()
+    return {"matrices": len(wl.weights), "configs": list(configs), "weights": nw,
+            "table_ms": round(ms, 3), "table_GB/s": round(moved / (ms * 1e-3) / 1e9, 1),
+            "plans": plans}
 
 
 def code_step(qn, L, torch, layers, M, r, s, sp, steps, warmup, flops_step, code):

@@ -63,13 +63,20 @@ __global__ __launch_bounds__(256) void k_sq_error(const float* __restrict__ R,
   if (threadIdx.x == 0) part[blockIdx.x] = red[0];
 }
 
-// out = sum of the partials in index order.
-__global__ void k_sq_error_sum(const double* __restrict__ part, int n, double* __restrict__ out) {
-  if (threadIdx.x == 0 && blockIdx.x == 0) {
-    double s = 0.0;
-    for (int i = 0; i < n; ++i) s += part[i];
-    *out = s;
+// out = sum of the kErrBlocks partials: thread t adds partials 4 t .. 4 t + 3
+// in order, then a fixed tree in LDS (the same order on every call).
+__global__ __launch_bounds__(256) void k_sq_error_sum(const double* __restrict__ part,
+                                                      double* __restrict__ out) {
+  static_assert(kErrBlocks == 4 * 256, "four partials per thread");
+  __shared__ double red[256];
+  const int t = threadIdx.x;
+  red[t] = ((part[4 * t] + part[4 * t + 1]) + part[4 * t + 2]) + part[4 * t + 3];
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (t < w) red[t] += red[t + w];
+    __syncthreads();
   }
+  if (t == 0) *out = red[0];
 }
 
 inline size_t al(size_t v) { return (v + 255) / 256 * 256; }
@@ -128,7 +135,7 @@ hipError_t launch_quant_error(const float* W, int64_t N, int64_t K, int code, co
     return 0;
   });
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(k_sq_error_sum, dim3(1), dim3(64), 0, stream, part, kErrBlocks, sq_err);
+  hipLaunchKernelGGL(k_sq_error_sum, dim3(1), dim3(256), 0, stream, part, sq_err);
   return hipGetLastError();
 }
 
