@@ -29,6 +29,21 @@ __device__ __forceinline__ uint32_t quant_code(float x) {
   return CT::code_of_count(n);
 }
 
+// fl32(a / b) from r = fl32(1 / b): q = fl32(a r) is within an ulp or so;
+// the residual a - b q is exact through the fused multiply-add, and one
+// correction step rounds to the correctly rounded quotient (Markstein's
+// division refinement).  Used for blocks with b >= 2^-80 (no underflow in
+// the residual) and |a| <= b: there it is bit-identical to the IEEE
+// division for every quotient of magnitude 0.01 or more (a host test checks
+// this on random operands); a smaller quotient can be off by an ulp, which
+// cannot move it across a threshold (the smallest has magnitude 0.0398).
+__device__ __forceinline__ float div_refined(float a, float b, float r) {
+#pragma clang fp contract(off)
+  const float q = a * r;
+  const float e = __builtin_fmaf(-q, b, a);
+  return __builtin_fmaf(e, r, q);
+}
+
 template <class CT>
 __global__ __launch_bounds__(256) void k_nf4_quantize(const float* __restrict__ W,
                                                       int64_t nblocks,
@@ -55,8 +70,14 @@ __global__ __launch_bounds__(256) void k_nf4_quantize(const float* __restrict__ 
       m = fmaxf(m, __shfl_xor(m, 2, 16));
       m = fmaxf(m, __shfl_xor(m, 1, 16));
       uint32_t c0, c1, c2, c3;
-      if (m > 0.0f) {
-        // IEEE-correct fp32 division (the compiler's default for '/')
+      if (m >= 0x1p-80f) {
+        const float r = 1.0f / m;  // IEEE-correct fp32 division
+        c0 = quant_code<CT>(div_refined(v[0], m, r));
+        c1 = quant_code<CT>(div_refined(v[1], m, r));
+        c2 = quant_code<CT>(div_refined(v[2], m, r));
+        c3 = quant_code<CT>(div_refined(v[3], m, r));
+      } else if (m > 0.0f) {
+        // tiny block: IEEE-correct fp32 division (the compiler's default)
         c0 = quant_code<CT>(v[0] / m);
         c1 = quant_code<CT>(v[1] / m);
         c2 = quant_code<CT>(v[2] / m);

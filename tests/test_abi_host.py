@@ -100,6 +100,21 @@ def test_code_table_rejects_unknown_type():
         qn.code_table("int4")
 
 
+def test_quantizer_division_refinement_is_correctly_rounded():
+    with tempfile.TemporaryDirectory() as d:
+        so = os.path.join(d, "div.so")
+        src = os.path.join(ROOT, "tests", "csrc", "division_check.c")
+        subprocess.run(["gcc", "-O2", "-mfma", "-ffp-contract=off", "-shared", "-fPIC", src,
+                        "-o", so, "-lm"], check=True)
+        D = ctypes.CDLL(so)
+        D.division_mismatches.restype = ctypes.c_long
+        D.division_mismatches.argtypes = [ctypes.c_long, ctypes.c_uint64,
+                                          ctypes.POINTER(ctypes.c_uint32)]
+        first = (ctypes.c_uint32 * 2)()
+        bad = D.division_mismatches(40_000_000, 12345, first)
+        assert bad == 0, (hex(first[0]), hex(first[1]))
+
+
 def test_storage_bytes_closed_form():
     for N, K in [(1, 64), (3, 1024), (1024, 1024), (22016, 8192), (5120, 13824)]:
         assert qn.lib().nf4_storage_bytes(N, K) == nf4.storage_bytes(N, K)
