@@ -264,6 +264,7 @@ def main():
         for code in ("fp4", "nf3", "nf2"):
             extra["code_types"][code]["fused_step"] = code_step(
                 qn, L, torch, layers, M, r, s, sp, args.steps, args.warmup, flops_step, code)
+        extra["bf16_gemm_reference"] = run_gemm_reference(torch, layers, M, per_launch)
         extra["lq_init"] = run_lq(qn, torch)
         extra["ilp"] = run_ilp(qn, torch)
 
@@ -294,6 +295,41 @@ def main():
         "extra": extra,
     }
     print(json.dumps(out), flush=True)
+
+
+def run_gemm_reference(torch, layers, M, per_launch, reps=50):
+    """Context, not part of the path: a plain bf16 GEMM (torch.matmul, i.e.
+    the vendor BLAS) at the four shapes of the step (forward X W^T and
+    backward dY W per weight), random bf16 operands already in bf16, no
+    dequantization and no adapter, next to the fused kernels' median launch
+    times from the timed region."""
+    out = []
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+    for li, t in enumerate(layers):
+        N, K = t["spec"].N, t["spec"].K
+        for kind, (rows, cols, depth) in (("fwd", (M, N, K)), ("bwd", (M, K, N))):
+            a = torch.randn(rows, depth, device="cuda", dtype=torch.bfloat16, generator=g)
+            b = torch.randn(cols, depth, device="cuda", dtype=torch.bfloat16, generator=g)
+            for _ in range(5):
+                c = a @ b.t()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                c = a @ b.t()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) / reps * 1e3
+            ours = float(np.median(per_launch[kind][li]))
+            out.append({"shape_MxNxK": f"{rows}x{cols}x{depth}", "for": f"{kind} {t['spec'].name}",
+                        "bf16_blas_us": round(us, 1),
+                        "bf16_blas_TFLOP/s": round(2 * rows * cols * depth / us / 1e6, 1),
+                        "fused_nf4_lora_us": round(ours, 1)})
+            del a, b, c
+    torch.cuda.empty_cache()
+    return out
 
 
 LQ_R, LQ_L, LQ_ITERS, LQ_POWER = 64, 80, 2, 2

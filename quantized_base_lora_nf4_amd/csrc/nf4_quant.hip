@@ -19,13 +19,48 @@
 
 namespace qn {
 
+// The code of x in [-1, 1] is code_of_count(#{thresholds below x}).  The
+// count comes from a bucket table instead of one compare per threshold:
+// buckets split [-1, 1] by sign, binary exponent (2^-6 .. 2^0) and the top 4
+// mantissa bits, with one bucket per sign for |x| < 2^-6 (1 + 1/16).  A
+// bucket is at most 1/32 wide while consecutive thresholds of every code
+// type are at least 0.08 apart, so it holds at most one threshold: the
+// count is the bucket's base (thresholds below the whole bucket) plus
+// (x > the threshold inside it, +inf if none).  A host test checks this
+// against the direct count for every fp32 in [-1, 1].
+constexpr int kBuckets = 224;  // 2 signs x 7 exponents x 16
+
+// bucket[t] = {threshold inside (fp32 bits), base count}
 template <class CT>
-__device__ __forceinline__ uint32_t quant_code(float x) {
-  // number of thresholds strictly below x = nearest value, ties low
-  uint32_t n = 0;
-#pragma unroll
-  for (int i = 0; i < CT::table.ndist - 1; ++i)
-    n += (x > __builtin_bit_cast(float, CT::table.thr[i])) ? 1u : 0u;
+__device__ void build_buckets(uint2* bucket) {
+  for (int t = threadIdx.x; t < kBuckets; t += blockDim.x) {
+    const int sg = t / 112, ke = (t % 112) / 16, j = t % 16;
+    const float lo = (ke == 0 && j == 0) ? 0.0f : ldexpf(1.0f + j / 16.0f, ke - 6);
+    const float hi = ldexpf(1.0f + (j + 1) / 16.0f, ke - 6);
+    uint32_t base = 0;
+    float inside = __builtin_inff();
+    for (int i = 0; i < CT::table.ndist - 1; ++i) {
+      const float T = __builtin_bit_cast(float, CT::table.thr[i]);
+      if (sg == 0) {  // x in [lo, hi)
+        if (T < lo) ++base;
+        else if (T < hi) inside = T;
+      } else {        // x in (-hi, -lo]
+        if (T <= -hi) ++base;
+        else if (T <= -lo) inside = T;
+      }
+    }
+    bucket[t] = make_uint2(__builtin_bit_cast(uint32_t, inside), base);
+  }
+}
+
+template <class CT>
+__device__ __forceinline__ uint32_t quant_code(float x, const uint2* bucket) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const int e = (int)((u >> 23) & 0xffu);
+  const int sg = (int)(u >> 31);
+  const int key = e < 121 ? sg * 112 : sg * 112 + (e - 121) * 16 + (int)((u >> 19) & 15u);
+  const uint2 bk = bucket[key];
+  const uint32_t n = bk.y + (x > __builtin_bit_cast(float, bk.x) ? 1u : 0u);
   return CT::code_of_count(n);
 }
 
@@ -52,6 +87,9 @@ __global__ __launch_bounds__(256) void k_nf4_quantize(const float* __restrict__ 
                                                       float* __restrict__ step) {
   __shared__ float cabs[256];
   __shared__ float wmax[4];
+  __shared__ uint2 bucket[kBuckets];
+  build_buckets<CT>(bucket);
+  __syncthreads();
   const int64_t g = blockIdx.x;
   const int64_t b0 = g * 256;
   const int nb = (int)((nblocks - b0) < 256 ? (nblocks - b0) : 256);
@@ -72,16 +110,16 @@ __global__ __launch_bounds__(256) void k_nf4_quantize(const float* __restrict__ 
       uint32_t c0, c1, c2, c3;
       if (m >= 0x1p-80f) {
         const float r = 1.0f / m;  // IEEE-correct fp32 division
-        c0 = quant_code<CT>(div_refined(v[0], m, r));
-        c1 = quant_code<CT>(div_refined(v[1], m, r));
-        c2 = quant_code<CT>(div_refined(v[2], m, r));
-        c3 = quant_code<CT>(div_refined(v[3], m, r));
+        c0 = quant_code<CT>(div_refined(v[0], m, r), bucket);
+        c1 = quant_code<CT>(div_refined(v[1], m, r), bucket);
+        c2 = quant_code<CT>(div_refined(v[2], m, r), bucket);
+        c3 = quant_code<CT>(div_refined(v[3], m, r), bucket);
       } else if (m > 0.0f) {
         // tiny block: IEEE-correct fp32 division (the compiler's default)
-        c0 = quant_code<CT>(v[0] / m);
-        c1 = quant_code<CT>(v[1] / m);
-        c2 = quant_code<CT>(v[2] / m);
-        c3 = quant_code<CT>(v[3] / m);
+        c0 = quant_code<CT>(v[0] / m, bucket);
+        c1 = quant_code<CT>(v[1] / m, bucket);
+        c2 = quant_code<CT>(v[2] / m, bucket);
+        c3 = quant_code<CT>(v[3] / m, bucket);
       } else {
         c0 = c1 = c2 = c3 = CT::table.zero_code;  // all-zero block: the zero level
       }

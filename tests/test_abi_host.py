@@ -100,6 +100,24 @@ def test_code_table_rejects_unknown_type():
         qn.code_table("int4")
 
 
+@pytest.mark.parametrize("code", ["nf4", "fp4", "nf3", "nf2"])
+def test_quantizer_buckets_give_the_threshold_count(code):
+    _, th = qn.code_table(code)
+    with tempfile.TemporaryDirectory() as d:
+        so = os.path.join(d, "bk.so")
+        src = os.path.join(ROOT, "tests", "csrc", "bucket_check.c")
+        subprocess.run(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", src, "-o", so, "-lm"],
+                       check=True)
+        B = ctypes.CDLL(so)
+        B.bucket_mismatches.restype = ctypes.c_long
+        B.bucket_mismatches.argtypes = [ctypes.c_void_p, ctypes.c_int,
+                                        ctypes.POINTER(ctypes.c_uint32)]
+        T = (ctypes.c_float * len(th))(*th)
+        first = ctypes.c_uint32(0)
+        bad = B.bucket_mismatches(ctypes.cast(T, ctypes.c_void_p), len(th), ctypes.byref(first))
+        assert bad == 0, hex(first.value)
+
+
 def test_quantizer_division_refinement_is_correctly_rounded():
     with tempfile.TemporaryDirectory() as d:
         so = os.path.join(d, "div.so")
