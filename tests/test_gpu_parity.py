@@ -111,6 +111,10 @@ LSHAPES = [  # (M, N, K, r)
     (16, 1032, 1024, 16),
     (16, 8, 64, 3),
     (9, 2056, 4160, 64),
+    (300, 264, 512, 256),      # the largest rank: four LoRA steps, padded U
+    (4, 1024, 2048, 256),      # the largest rank on the few-token path
+    (130, 520, 576, 128),      # rank 128, ragged M and N
+    (2, 8, 64, 1),             # one block per weight row, smallest everything
 ]
 
 
