@@ -106,6 +106,9 @@ extern "C" {
 #define QLORA_NF4_BLOCKSIZE 64
 #define QLORA_NF4_DQ_BLOCKSIZE 256
 #define QLORA_MAX_RANK 256
+/* Largest N and K accepted by qlora_linear_fwd / qlora_linear_bwd (a 256-row
+ * tile of X or dY must span less than 2 GiB). */
+#define QLORA_LINEAR_MAX_NK (1 << 22)
 
 /* The quantized frozen weight.  All pointers are device pointers. */
 typedef struct nf4_tensor_t {
@@ -195,7 +198,8 @@ size_t qlora_workspace_size(int64_t M, int64_t N, int64_t K, int32_t r,
 /* qlora_linear_fwd -- Y = X W^T + s (X A^T) B^T with W dequantized on the
  * fly to bf16 (blog section "Where the memory goes").
  *
- *   w       quantized weight, N >= 1, N % 8 == 0, K % 64 == 0
+ *   w       quantized weight, N >= 1, N % 8 == 0, K % 64 == 0,
+ *           N, K <= QLORA_LINEAR_MAX_NK
  *   X       [M, K] bf16, M >= 1
  *   A       [r, K] bf16;  B [N, r] bf16;  1 <= r <= 256
  *   s       LoRA scale

@@ -35,8 +35,8 @@ struct BwdPlan {
 
 bool sizes_ok(int64_t M, int64_t N, int64_t K, int32_t r) {
   return M >= 1 && N >= 1 && K >= 64 && (K % 64) == 0 && (N % 8) == 0 && r >= 1 &&
-         r <= QLORA_MAX_RANK && M <= ((int64_t)1 << 31) && N <= ((int64_t)1 << 31) &&
-         K <= ((int64_t)1 << 31);
+         r <= QLORA_MAX_RANK && M <= ((int64_t)1 << 31) && N <= QLORA_LINEAR_MAX_NK &&
+         K <= QLORA_LINEAR_MAX_NK;
 }
 
 FwdPlan plan_fwd(int64_t M, int64_t N, int64_t K, int32_t r) {

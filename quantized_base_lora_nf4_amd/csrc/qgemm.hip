@@ -15,7 +15,7 @@
 // Tiling (both kernels): a 256 x 256 output tile per workgroup of 4 waves
 // (2 x 2), each wave owning 128 x 128 outputs as 4 x 4 MFMA 32x32x16 tiles
 // (256 fp32 accumulators per lane, held in AGPRs); 64-deep contraction steps;
-// both operand tiles double-buffered in LDS (147 KB) so that one barrier per
+// both operand tiles double-buffered in LDS (136 KiB) so that one barrier per
 // step separates filling the next buffer from the MFMAs on the current one.
 //
 // Dequantization: each thread owns one 64-weight block row per step.  It
@@ -131,10 +131,25 @@ __device__ __forceinline__ int a_off(int r, int c) { return r * 64 + ((c ^ ((r >
 // Each wave instruction fills 8 consecutive tile rows (1 KB); lane l writes
 // row 8 e + l / 8, slot l % 8, so it fetches the chunk that the swizzle puts
 // in that slot.
+//
+// The loads use the buffer form (buffer_load_dwordx4 ... lds) through a
+// resource whose base is the tile's first row.  With the global form the
+// compiler treats every later wait as if a flat access were pending and
+// drains all outstanding loads (vmcnt(0)) at the first use of any loaded
+// register; with the buffer form its waits count only the loads that are
+// actually needed, so the weight loads stay in flight across the step.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* src, int64_t ld,
+                                                            int64_t row0, int64_t rows) {
+  int64_t bytes = (rows - row0) * ld * 2;
+  if (bytes > 0x7fffffff) bytes = 0x7fffffff;
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(src + row0 * ld), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
 template <class C, bool kClampCols>
-__device__ __forceinline__ void load_rows_lds(uint16_t* As, const uint16_t* src, int64_t ld,
-                                              int64_t row0, int64_t rows, int64_t c0, int64_t cols,
-                                              int wave, int lane) {
+__device__ __forceinline__ void load_rows_lds(uint16_t* As, __amdgpu_buffer_rsrc_t rsrc,
+                                              int64_t ld, int64_t row0, int64_t rows, int64_t c0,
+                                              int64_t cols, int wave, int lane) {
 #pragma unroll
   for (int q = 0; q < C::XLD; ++q) {
     const int e = q * (C::NT / 64) + wave;  // 8-row group
@@ -144,9 +159,10 @@ __device__ __forceinline__ void load_rows_lds(uint16_t* As, const uint16_t* src,
     if (gr >= rows) gr = rows - 1;
     int64_t gc = c0 + c * 8;
     if (kClampCols && gc >= cols) gc = 0;
-    __builtin_amdgcn_global_load_lds((const void*)(src + gr * ld + gc),
-                                     (__attribute__((address_space(3))) void*)(As + 8 * e * 64),
-                                     16, 0, 0);
+    // < 2^31 bytes: ld is at most 2^22 (the C ABI rejects larger N and K)
+    const int voff = (int)(((gr - row0) * ld + gc) * 2);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rsrc, (__attribute__((address_space(3))) void*)(As + 8 * e * 64), 16, voff, 0, 0, 0);
   }
 }
 
@@ -357,7 +373,12 @@ struct FwdArgs {
 
 template <class C, class CT>
 __global__ __launch_bounds__(C::NT, 1) void k_qgemm_fwd(FwdArgs p) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[C::SMEM_F];
+  // One LDS object per buffer: the compiler's wait for a direct-to-LDS load
+  // then applies only to reads of the buffer that load writes.
+  __shared__ __attribute__((aligned(16))) uint16_t xs0[C::TILE_A];
+  __shared__ __attribute__((aligned(16))) uint16_t xs1[C::TILE_A];
+  __shared__ __attribute__((aligned(16))) uint16_t ws0[C::TILE_BF];
+  __shared__ __attribute__((aligned(16))) uint16_t ws1[C::TILE_BF];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / C::WN, wn = wave % C::WN;
   const int64_t M = p.M, N = p.N, K = p.K;
@@ -378,9 +399,6 @@ __global__ __launch_bounds__(C::NT, 1) void k_qgemm_fwd(FwdArgs p) {
 
   AccT<C> acc;
   zero_acc(acc);
-  // Two register sets of loads in flight: step t's loads are issued while
-  // the MFMAs of step t - 2 run, and turned into LDS tiles while those of
-  // step t - 1 run.  Steps past the end reload the last step (harmless).
   // Weights are loaded two steps ahead (two register sets) and dequantized
   // into the other LDS buffer while the MFMAs of the current step run;
   // activations go straight from global memory into that buffer.  Steps
@@ -396,29 +414,29 @@ __global__ __launch_bounds__(C::NT, 1) void k_qgemm_fwd(FwdArgs p) {
     r.qm = ~0u;
     r.st = p.step[blk >> 8];
   };
+  const __amdgpu_buffer_rsrc_t xrsrc = rows_rsrc(p.X, K, m0, M);
   auto load_x = [&](uint16_t* As_dst, int64_t kt) {
     if (kt >= kblocks) kt = kblocks - 1;
-    load_rows_lds<C, false>(As_dst, p.X, K, m0, M, kt * BK, K, wave, lane);  // K % 64 == 0
+    load_rows_lds<C, false>(As_dst, xrsrc, K, m0, M, kt * BK, K, wave, lane);  // K % 64 == 0
   };
-  // (Measured: keeping the weight loads in flight across the barrier, as
-  // the backward kernel does, is slower here; the forward step waits for
-  // all of its loads.)
   auto body = [&](StepRegs<C, CT>& rnext, StepRegs<C, CT>& rload, int64_t kt, int cur) {
-    const uint16_t* As = smem + cur * (C::TILE_A + C::TILE_BF);
-    uint16_t* As_n = smem + (cur ^ 1) * (C::TILE_A + C::TILE_BF);
-    load_x(As_n, kt + 1);
-    load_w(rload, kt + 2);
-    step_interleaved<C, false, CT>(As, As + C::TILE_A, As_n,
-                               As_n + C::TILE_A + wrow * LDA + wpart * C::WPT, rnext, wm, wn,
-                               lane, acc);
-    wait_vmem();
-    __syncthreads();
+    const uint16_t* As = cur ? xs1 : xs0;
+    const uint16_t* Bs = cur ? ws1 : ws0;
+    uint16_t* As_n = cur ? xs0 : xs1;
+    uint16_t* Bs_n = cur ? ws0 : ws1;
+    load_x(As_n, kt + 1);   // tile loads first ...
+    __builtin_amdgcn_sched_barrier(0);
+    load_w(rload, kt + 2);  // ... then the weight loads, which outlive the step
+    __builtin_amdgcn_sched_barrier(0);
+    step_interleaved<C, false, CT>(As, Bs, As_n, Bs_n + wrow * LDA + wpart * C::WPT, rnext, wm,
+                                   wn, lane, acc);
+    step_barrier();
   };
 
   load_w(ra, 0);
   load_w(rb, 1);
-  load_x(smem, 0);
-  dequant_codes<C, CT>(smem + C::TILE_A + wrow * LDA + wpart * C::WPT, ra);
+  load_x(xs0, 0);
+  dequant_codes<C, CT>(ws0 + wrow * LDA + wpart * C::WPT, ra);
   wait_vmem();
   __syncthreads();
   int64_t kt = 0;
@@ -427,15 +445,15 @@ __global__ __launch_bounds__(C::NT, 1) void k_qgemm_fwd(FwdArgs p) {
     body(ra, rb, kt + 1, 1);  // MFMA step kt+1 (buffer 1), stage kt+2 from ra, load kt+3 into rb
   }
   if (kt < kblocks) {  // odd number of steps: the last one is in buffer 0
-    mma_step<C, false>(smem, smem + C::TILE_A, wm, wn, lane, acc);
+    mma_step<C, false>(xs0, ws0, wm, wn, lane, acc);
     __syncthreads();
   }
 
   // LoRA: extra contraction over r with A-side bf16(s U) and B-side B.
   const bool bvec = (p.r & 7) == 0;
   for (int j0 = 0; j0 < p.r; j0 += 64) {
-    uint16_t* As = smem;
-    uint16_t* Bs = smem + C::TILE_A;
+    uint16_t* As = xs0;
+    uint16_t* Bs = ws0;
     stage_rows_scaled<C>(As, p.U, p.ldu, m0, M, j0, p.s, true, tid);
     for (int e = tid; e < C::BN * 8; e += C::NT) {
       const int row = e >> 3, c8 = e & 7;
@@ -485,7 +503,10 @@ struct BwdArgs {
 // k0..k0+BN-1, is dequantized into Bs[64][LDTB] in its natural layout.
 template <class C, class CT>
 __global__ __launch_bounds__(C::NT, 1) void k_qgemm_bwd(BwdArgs p) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[C::SMEM_B];
+  __shared__ __attribute__((aligned(16))) uint16_t xs0[C::TILE_A];
+  __shared__ __attribute__((aligned(16))) uint16_t xs1[C::TILE_A];
+  __shared__ __attribute__((aligned(16))) uint16_t ws0[C::TILE_BB];
+  __shared__ __attribute__((aligned(16))) uint16_t ws1[C::TILE_BB];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / C::WN, wn = wave % C::WN;
   const int64_t M = p.M, N = p.N, K = p.K;
@@ -529,30 +550,32 @@ __global__ __launch_bounds__(C::NT, 1) void k_qgemm_bwd(BwdArgs p) {
   };
   // dY tile of step ns straight into LDS; on a partial last step the chunks
   // past column N re-read column 0 and meet the zero rows above.
+  const __amdgpu_buffer_rsrc_t yrsrc = rows_rsrc(p.dY, N, m0, M);
   auto load_x = [&](uint16_t* As_dst, int64_t ns) {
     if (ns >= nsteps) ns = nsteps - 1;
-    load_rows_lds<C, true>(As_dst, p.dY, N, m0, M, ns * BK, N, wave, lane);
+    load_rows_lds<C, true>(As_dst, yrsrc, N, m0, M, ns * BK, N, wave, lane);
   };
   // (3-bit codes may take three dword loads per half: more loads after the
   // tile loads only make the wait in step_barrier() stricter.)
   static_assert(WPTB / 32 + 2 == kWLoads, "weight loads per step");
   auto body = [&](StepRegs<C, CT>& rnext, StepRegs<C, CT>& rload, int64_t ns, int cur) {
-    const uint16_t* As = smem + cur * (C::TILE_A + C::TILE_BB);
-    uint16_t* As_n = smem + (cur ^ 1) * (C::TILE_A + C::TILE_BB);
+    const uint16_t* As = cur ? xs1 : xs0;
+    const uint16_t* Bs = cur ? ws1 : ws0;
+    uint16_t* As_n = cur ? xs0 : xs1;
+    uint16_t* Bs_n = cur ? ws0 : ws1;
     load_x(As_n, ns + 1);    // tile loads first ...
     __builtin_amdgcn_sched_barrier(0);
     load_w(rload, ns + 2);   // ... then the weight loads, which outlive the step
     __builtin_amdgcn_sched_barrier(0);
-    step_interleaved<C, true, CT>(As, As + C::TILE_A, As_n,
-                              As_n + C::TILE_A + wr * C::LDTB + wb * C::BSTR + wh * WPTB, rnext,
-                              wm, wn, lane, acc);
+    step_interleaved<C, true, CT>(As, Bs, As_n, Bs_n + wr * C::LDTB + wb * C::BSTR + wh * WPTB,
+                                  rnext, wm, wn, lane, acc);
     step_barrier();
   };
 
   load_w(ra, 0);
   load_w(rb, 1);
-  load_x(smem, 0);
-  dequant_codes<C, CT>(smem + C::TILE_A + wr * C::LDTB + wb * C::BSTR + wh * WPTB, ra);
+  load_x(xs0, 0);
+  dequant_codes<C, CT>(ws0 + wr * C::LDTB + wb * C::BSTR + wh * WPTB, ra);
   wait_vmem();
   __syncthreads();
   int64_t ns = 0;
@@ -561,14 +584,14 @@ __global__ __launch_bounds__(C::NT, 1) void k_qgemm_bwd(BwdArgs p) {
     body(ra, rb, ns + 1, 1);
   }
   if (ns < nsteps) {
-    mma_step<C, true>(smem, smem + C::TILE_A, wm, wn, lane, acc);
+    mma_step<C, true>(xs0, ws0, wm, wn, lane, acc);
     __syncthreads();
   }
 
   // LoRA: dX += dU A, contraction over r.  A[j][k] is already [contraction][column].
   for (int j0 = 0; j0 < p.r; j0 += 64) {
-    uint16_t* As = smem;
-    uint16_t* Bs = smem + C::TILE_A;
+    uint16_t* As = xs0;
+    uint16_t* Bs = ws0;
     stage_rows_scaled<C>(As, p.dU, p.lddu, m0, M, j0, 1.0f, false, tid);
     for (int e = tid; e < 64 * (C::BN / 8); e += C::NT) {
       const int jr = e / (C::BN / 8), c8 = e % (C::BN / 8);  // adapter row j0 + jr
