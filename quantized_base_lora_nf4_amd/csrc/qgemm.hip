@@ -371,7 +371,11 @@ struct FwdArgs {
   int64_t M, N, K;
 };
 
-template <class C, class CT>
+// kQ4: K is a multiple of 256 (and q8 16-byte aligned, as the C ABI
+// requires), so the constants of four consecutive blocks of a weight row are
+// one aligned 32-bit word (and share one second-level step: 4 divides 256).  The row's constants are then
+// loaded once per four steps instead of a byte and a float per step.
+template <class C, class CT, bool kQ4>
 __global__ __launch_bounds__(C::NT, 1) void k_qgemm_fwd(FwdArgs p) {
   // One LDS object per buffer: the compiler's wait for a direct-to-LDS load
   // then applies only to reads of the buffer that load writes.
@@ -409,17 +413,34 @@ __global__ __launch_bounds__(C::NT, 1) void k_qgemm_fwd(FwdArgs p) {
 #pragma unroll
     for (int h = 0; h < C::WPT / 32; ++h)
       r.c[h] = load_half<CT>(wcodes + kt * block_bytes<CT>() + h * half_bytes<CT>());
-    const int64_t blk = wblk0 + kt;
-    r.q = p.q8[blk];
     r.qm = ~0u;
-    r.st = p.step[blk >> 8];
+    if constexpr (!kQ4) {
+      const int64_t blk = wblk0 + kt;
+      r.q = p.q8[blk];
+      r.st = p.step[blk >> 8];
+    }
+  };
+  // kQ4: group g of four steps (4g .. 4g+3) keeps its constants in register
+  // pair g % 2; group g + 1 is loaded when group g starts being expanded.
+  uint32_t q0 = 0, q1 = 0;
+  float s0 = 0.0f, s1 = 0.0f;
+  auto load_q4 = [&](uint32_t& q, float& st, int64_t g) {
+    if (g >= (kblocks >> 2)) g = (kblocks >> 2) - 1;
+    const int64_t blk = wblk0 + 4 * g;
+    q = *reinterpret_cast<const uint32_t*>(p.q8 + blk);
+    st = p.step[blk >> 8];
   };
   const __amdgpu_buffer_rsrc_t xrsrc = rows_rsrc(p.X, K, m0, M);
   auto load_x = [&](uint16_t* As_dst, int64_t kt) {
     if (kt >= kblocks) kt = kblocks - 1;
     load_rows_lds<C, false>(As_dst, xrsrc, K, m0, M, kt * BK, K, wave, lane);  // K % 64 == 0
   };
-  auto body = [&](StepRegs<C, CT>& rnext, StepRegs<C, CT>& rload, int64_t kt, int cur) {
+  // One step: MFMAs on buffer `cur` for step kt, step kt + 1 expanded into
+  // the other buffer.  kQ4: j = (kt + 1) % 4 is the position of step kt + 1
+  // in its group, whose constants are (qg, sg); j == 0 starts the group and
+  // loads the next one into (ql, sl).
+  auto body = [&](StepRegs<C, CT>& rnext, StepRegs<C, CT>& rload, int64_t kt, int cur, int j,
+                  uint32_t& qg, float& sg, uint32_t& ql, float& sl) {
     const uint16_t* As = cur ? xs1 : xs0;
     const uint16_t* Bs = cur ? ws1 : ws0;
     uint16_t* As_n = cur ? xs0 : xs1;
@@ -427,6 +448,11 @@ __global__ __launch_bounds__(C::NT, 1) void k_qgemm_fwd(FwdArgs p) {
     load_x(As_n, kt + 1);   // tile loads first ...
     __builtin_amdgcn_sched_barrier(0);
     load_w(rload, kt + 2);  // ... then the weight loads, which outlive the step
+    if constexpr (kQ4) {
+      if (j == 0) load_q4(ql, sl, ((kt + 1) >> 2) + 1);
+      rnext.q = (qg >> (8 * j)) & 0xffu;
+      rnext.st = sg;
+    }
     __builtin_amdgcn_sched_barrier(0);
     step_interleaved<C, false, CT>(As, Bs, As_n, Bs_n + wrow * LDA + wpart * C::WPT, rnext, wm,
                                    wn, lane, acc);
@@ -435,14 +461,41 @@ __global__ __launch_bounds__(C::NT, 1) void k_qgemm_fwd(FwdArgs p) {
 
   load_w(ra, 0);
   load_w(rb, 1);
+  if constexpr (kQ4) {
+    load_q4(q0, s0, 0);
+    load_q4(q1, s1, 1);
+    ra.q = q0 & 0xffu;
+    ra.st = s0;
+  }
   load_x(xs0, 0);
   dequant_codes<C, CT>(ws0 + wrow * LDA + wpart * C::WPT, ra);
   wait_vmem();
   __syncthreads();
   int64_t kt = 0;
-  for (; kt + 2 <= kblocks; kt += 2) {
-    body(rb, ra, kt, 0);      // MFMA step kt (buffer 0), stage kt+1 from rb, load kt+2 into ra
-    body(ra, rb, kt + 1, 1);  // MFMA step kt+1 (buffer 1), stage kt+2 from ra, load kt+3 into rb
+  if constexpr (kQ4) {  // kblocks % 4 == 0; groups 2i and 2i + 1 per iteration
+    for (; kt + 8 <= kblocks; kt += 8) {
+      body(rb, ra, kt, 0, 1, q0, s0, q1, s1);
+      body(ra, rb, kt + 1, 1, 2, q0, s0, q1, s1);
+      body(rb, ra, kt + 2, 0, 3, q0, s0, q1, s1);
+      body(ra, rb, kt + 3, 1, 0, q1, s1, q0, s0);
+      body(rb, ra, kt + 4, 0, 1, q1, s1, q0, s0);
+      body(ra, rb, kt + 5, 1, 2, q1, s1, q0, s0);
+      body(rb, ra, kt + 6, 0, 3, q1, s1, q0, s0);
+      body(ra, rb, kt + 7, 1, 0, q0, s0, q1, s1);
+    }
+    if (kt < kblocks) {  // one more group of four
+      body(rb, ra, kt, 0, 1, q0, s0, q1, s1);
+      body(ra, rb, kt + 1, 1, 2, q0, s0, q1, s1);
+      body(rb, ra, kt + 2, 0, 3, q0, s0, q1, s1);
+      body(ra, rb, kt + 3, 1, 0, q1, s1, q0, s0);
+      kt += 4;
+    }
+  } else {
+    for (; kt + 2 <= kblocks; kt += 2) {
+      // MFMA step kt (buffer 0), stage kt+1 from rb, load kt+2 into ra; then the converse
+      body(rb, ra, kt, 0, 0, q0, s0, q1, s1);
+      body(ra, rb, kt + 1, 1, 0, q0, s0, q1, s1);
+    }
   }
   if (kt < kblocks) {  // odd number of steps: the last one is in buffer 0
     mma_step<C, false>(xs0, ws0, wm, wn, lane, acc);
@@ -621,8 +674,12 @@ hipError_t launch_qgemm_fwd(const Nf4View& w, const uint16_t* X, int64_t M, cons
   using C = GemmCfg;
   FwdArgs a{X, w.codes, w.q8, w.step, U, ldu, B, r, s, Y, M, w.N, w.K};
   dim3 grid((unsigned)(((w.N + C::BN - 1) / C::BN) * ((M + C::BM - 1) / C::BM)));
+  const bool q4 = (w.K % 256) == 0;
   with_code(w.code, [&](auto ct) {
-    hipLaunchKernelGGL((k_qgemm_fwd<C, decltype(ct)>), grid, dim3(C::NT), 0, stream, a);
+    if (q4)
+      hipLaunchKernelGGL((k_qgemm_fwd<C, decltype(ct), true>), grid, dim3(C::NT), 0, stream, a);
+    else
+      hipLaunchKernelGGL((k_qgemm_fwd<C, decltype(ct), false>), grid, dim3(C::NT), 0, stream, a);
     return 0;
   });
   return hipGetLastError();

@@ -115,6 +115,8 @@ LSHAPES = [  # (M, N, K, r)
     (4, 1024, 2048, 256),      # the largest rank on the few-token path
     (130, 520, 576, 128),      # rank 128, ragged M and N
     (2, 8, 64, 1),             # one block per weight row, smallest everything
+    (260, 392, 768, 16),       # K % 256 == 0 with 12 steps: grouped constants plus a tail group
+    (33, 64, 256, 4),          # K = 256: the tail group alone
 ]
 
 
