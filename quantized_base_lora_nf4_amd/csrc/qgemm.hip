@@ -170,17 +170,22 @@ __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" 
 
 // End of a pipelined step: this wave's direct-to-LDS tile loads (issued
 // first in the step) and LDS writes are complete, then the workgroup
-// barrier.  The step's kWLoads weight loads (issued after the tile loads)
-// stay in flight into the next step, where they are consumed; vector memory
-// loads complete in issue order, so vmcnt(kWLoads) covers the tile loads.
+// barrier.  The step's weight loads (issued after the tile loads) stay in
+// flight into the next step, where they are consumed; vector memory loads
+// complete in issue order, so vmcnt(kAfter) covers the tile loads when the
+// step issued at least kAfter loads after them.
 // The wait is issued through the builtin (s_waitcnt simm16: vmcnt in bits
 // 3:0, expcnt 6:4, lgkmcnt 11:8) so that the compiler's own wait tracking
 // knows the tile loads are complete; the empty asm statements keep memory
 // operations from moving across it.
-constexpr int kWLoads = 3;  // codes (one 16-byte load), q8 byte, step
+// kAfter must not exceed the number of load instructions the step issued
+// after its tile loads (a smaller value only waits for more).
+constexpr int kWLoads = 3;  // codes (at least one load), q8 byte, step
+template <int kAfter = kWLoads>
 __device__ __forceinline__ void step_barrier() {
+  static_assert(kAfter >= 0 && kAfter <= 15, "vmcnt field");
   asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0x0070 | kWLoads);  // vmcnt(kWLoads) lgkmcnt(0)
+  __builtin_amdgcn_s_waitcnt(0x0070 | kAfter);  // vmcnt(kAfter) lgkmcnt(0)
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
@@ -456,7 +461,12 @@ __global__ __launch_bounds__(C::NT, 1) void k_qgemm_fwd(FwdArgs p) {
     __builtin_amdgcn_sched_barrier(0);
     step_interleaved<C, false, CT>(As, Bs, As_n, Bs_n + wrow * LDA + wpart * C::WPT, rnext, wm,
                                    wn, lane, acc);
-    step_barrier();
+    // loads after the tile loads: codes (>= 1), plus q8 and step unless kQ4
+    // (where a group start adds the word of constants and the step)
+    if (!kQ4 || j == 0)
+      step_barrier<kWLoads>();
+    else
+      step_barrier<1>();
   };
 
   load_w(ra, 0);
