@@ -443,9 +443,11 @@ __global__ __launch_bounds__(C::NT, 1) void k_qgemm_fwd(FwdArgs p) {
   // One step: MFMAs on buffer `cur` for step kt, step kt + 1 expanded into
   // the other buffer.  kQ4: j = (kt + 1) % 4 is the position of step kt + 1
   // in its group, whose constants are (qg, sg); j == 0 starts the group and
-  // loads the next one into (ql, sl).
+  // loads the next one into (ql, sl).  `last`: no later step consumes this
+  // step's weight loads, so the compiler may drop them and the barrier must
+  // wait for everything.
   auto body = [&](StepRegs<C, CT>& rnext, StepRegs<C, CT>& rload, int64_t kt, int cur, int j,
-                  uint32_t& qg, float& sg, uint32_t& ql, float& sl) {
+                  uint32_t& qg, float& sg, uint32_t& ql, float& sl, bool last) {
     const uint16_t* As = cur ? xs1 : xs0;
     const uint16_t* Bs = cur ? ws1 : ws0;
     uint16_t* As_n = cur ? xs0 : xs1;
@@ -463,7 +465,9 @@ __global__ __launch_bounds__(C::NT, 1) void k_qgemm_fwd(FwdArgs p) {
                                    wn, lane, acc);
     // loads after the tile loads: codes (>= 1), plus q8 and step unless kQ4
     // (where a group start adds the word of constants and the step)
-    if (!kQ4 || j == 0)
+    if (last)
+      step_barrier<0>();
+    else if (!kQ4 || j == 0)
       step_barrier<kWLoads>();
     else
       step_barrier<1>();
@@ -484,27 +488,27 @@ __global__ __launch_bounds__(C::NT, 1) void k_qgemm_fwd(FwdArgs p) {
   int64_t kt = 0;
   if constexpr (kQ4) {  // kblocks % 4 == 0; groups 2i and 2i + 1 per iteration
     for (; kt + 8 <= kblocks; kt += 8) {
-      body(rb, ra, kt, 0, 1, q0, s0, q1, s1);
-      body(ra, rb, kt + 1, 1, 2, q0, s0, q1, s1);
-      body(rb, ra, kt + 2, 0, 3, q0, s0, q1, s1);
-      body(ra, rb, kt + 3, 1, 0, q1, s1, q0, s0);
-      body(rb, ra, kt + 4, 0, 1, q1, s1, q0, s0);
-      body(ra, rb, kt + 5, 1, 2, q1, s1, q0, s0);
-      body(rb, ra, kt + 6, 0, 3, q1, s1, q0, s0);
-      body(ra, rb, kt + 7, 1, 0, q0, s0, q1, s1);
+      body(rb, ra, kt, 0, 1, q0, s0, q1, s1, false);
+      body(ra, rb, kt + 1, 1, 2, q0, s0, q1, s1, false);
+      body(rb, ra, kt + 2, 0, 3, q0, s0, q1, s1, false);
+      body(ra, rb, kt + 3, 1, 0, q1, s1, q0, s0, false);
+      body(rb, ra, kt + 4, 0, 1, q1, s1, q0, s0, false);
+      body(ra, rb, kt + 5, 1, 2, q1, s1, q0, s0, false);
+      body(rb, ra, kt + 6, 0, 3, q1, s1, q0, s0, false);
+      body(ra, rb, kt + 7, 1, 0, q0, s0, q1, s1, false);
     }
-    if (kt < kblocks) {  // one more group of four
-      body(rb, ra, kt, 0, 1, q0, s0, q1, s1);
-      body(ra, rb, kt + 1, 1, 2, q0, s0, q1, s1);
-      body(rb, ra, kt + 2, 0, 3, q0, s0, q1, s1);
-      body(ra, rb, kt + 3, 1, 0, q1, s1, q0, s0);
+    if (kt < kblocks) {  // one more group of four, the last steps
+      body(rb, ra, kt, 0, 1, q0, s0, q1, s1, false);
+      body(ra, rb, kt + 1, 1, 2, q0, s0, q1, s1, false);
+      body(rb, ra, kt + 2, 0, 3, q0, s0, q1, s1, false);
+      body(ra, rb, kt + 3, 1, 0, q1, s1, q0, s0, true);
       kt += 4;
     }
   } else {
     for (; kt + 2 <= kblocks; kt += 2) {
       // MFMA step kt (buffer 0), stage kt+1 from rb, load kt+2 into ra; then the converse
-      body(rb, ra, kt, 0, 0, q0, s0, q1, s1);
-      body(ra, rb, kt + 1, 1, 0, q0, s0, q1, s1);
+      body(rb, ra, kt, 0, 0, q0, s0, q1, s1, false);
+      body(ra, rb, kt + 1, 1, 0, q0, s0, q1, s1, false);
     }
   }
   if (kt < kblocks) {  // odd number of steps: the last one is in buffer 0
