@@ -75,22 +75,26 @@ __device__ __forceinline__ LevelTable make_table(float chat) {
 
 // Eight codes (one 32-bit word; element order = nibble order) -> four packed
 // bf16 pairs (element 2i in the low half of word i).
+//   a, b: the codes of elements 0..3 and 4..7 spread one per byte, in order;
+//   a byte select with selector c & 7 picks from the plane holding values
+//   0..7 or 8..15, and a mask (0xFF where c >= 8) chooses between the two.
+// The mask comes from v_perm's constant selectors on zero sources: selector
+// c + 5 is a byte of zeros (5..7), a zero sign (8..11), 0x00 (12) or 0xFF
+// (13 and above), so it is 0xFF exactly for c >= 8.
 __device__ __forceinline__ u32x4 lookup8(uint32_t w, const LevelTable& t) {
-  const uint32_t se = w & 0x07070707u;            // even elements, index bits 0..2
-  const uint32_t so = (w >> 4) & 0x07070707u;     // odd elements
-  // 0xFF in each byte whose index has bit 3 set (selector 13 -> 0xFF, 12 -> 0x00)
-  const uint32_t me = perm(0u, 0u, ((w >> 3) & 0x01010101u) | 0x0c0c0c0cu);
-  const uint32_t mo = perm(0u, 0u, ((w >> 7) & 0x01010101u) | 0x0c0c0c0cu);
-  const uint32_t le = (me & perm(t.lo[3], t.lo[2], se)) | (~me & perm(t.lo[1], t.lo[0], se));
-  const uint32_t he = (me & perm(t.hi[3], t.hi[2], se)) | (~me & perm(t.hi[1], t.hi[0], se));
-  const uint32_t lo = (mo & perm(t.lo[3], t.lo[2], so)) | (~mo & perm(t.lo[1], t.lo[0], so));
-  const uint32_t ho = (mo & perm(t.hi[3], t.hi[2], so)) | (~mo & perm(t.hi[1], t.hi[0], so));
-  const uint32_t t0 = perm(he, le, 0x05010400u);  // elements 0, 2
-  const uint32_t t1 = perm(he, le, 0x07030602u);  // elements 4, 6
-  const uint32_t u0 = perm(ho, lo, 0x05010400u);  // elements 1, 3
-  const uint32_t u1 = perm(ho, lo, 0x07030602u);  // elements 5, 7
-  return u32x4{perm(u0, t0, 0x05040100u), perm(u0, t0, 0x07060302u),
-               perm(u1, t1, 0x05040100u), perm(u1, t1, 0x07060302u)};
+  const uint32_t x = w & 0x0f0f0f0fu;          // elements 0, 2, 4, 6
+  const uint32_t y = (w >> 4) & 0x0f0f0f0fu;   // elements 1, 3, 5, 7
+  const uint32_t a = perm(y, x, 0x05010400u);  // elements 0, 1, 2, 3
+  const uint32_t b = perm(y, x, 0x07030602u);  // elements 4, 5, 6, 7
+  const uint32_t a7 = a & 0x07070707u, b7 = b & 0x07070707u;
+  const uint32_t ma = perm(0u, 0u, a + 0x05050505u);
+  const uint32_t mb = perm(0u, 0u, b + 0x05050505u);
+  const uint32_t la = (ma & perm(t.lo[3], t.lo[2], a7)) | (~ma & perm(t.lo[1], t.lo[0], a7));
+  const uint32_t ha = (ma & perm(t.hi[3], t.hi[2], a7)) | (~ma & perm(t.hi[1], t.hi[0], a7));
+  const uint32_t lb = (mb & perm(t.lo[3], t.lo[2], b7)) | (~mb & perm(t.lo[1], t.lo[0], b7));
+  const uint32_t hb = (mb & perm(t.hi[3], t.hi[2], b7)) | (~mb & perm(t.hi[1], t.hi[0], b7));
+  return u32x4{perm(ha, la, 0x05010400u), perm(ha, la, 0x07030602u),
+               perm(hb, lb, 0x05010400u), perm(hb, lb, 0x07030602u)};
 }
 
 
