@@ -199,7 +199,8 @@ size_t qlora_workspace_size(int64_t M, int64_t N, int64_t K, int32_t r,
  * fly to bf16 (blog section "Where the memory goes").
  *
  *   w       quantized weight, N >= 1, N % 8 == 0, K % 64 == 0,
- *           N, K <= QLORA_LINEAR_MAX_NK
+ *           N, K <= QLORA_LINEAR_MAX_NK, packed codes under 2 GiB
+ *           (N K bits / 8 < 2^31)
  *   X       [M, K] bf16, M >= 1
  *   A       [r, K] bf16;  B [N, r] bf16;  1 <= r <= 256
  *   s       LoRA scale

@@ -70,6 +70,13 @@ bool nf4_ok(const nf4_tensor_t* w) {
   return w && w->codes && w->q8 && w->step;
 }
 
+// The layer kernels address the packed codes with 32-bit buffer offsets.
+bool state_fits(const nf4_tensor_t* w) {
+  const int64_t bits =
+      with_code(w->code_type, [](auto ct) { return (int64_t)decltype(ct)::kBits; });
+  return w->N * w->K / 8 * bits < ((int64_t)1 << 31);
+}
+
 inline bool code_ok(int32_t code_type) {
   return code_type == QLORA_CODE_NF4 || code_type == QLORA_CODE_FP4 ||
          code_type == QLORA_CODE_NF3 || code_type == QLORA_CODE_NF2;
@@ -193,7 +200,7 @@ int32_t linear_fwd(const nf4_tensor_t* w, const uint16_t* X, int64_t M, const ui
   const int32_t sup = nf4_supported(w);
   if (sup != QLORA_OK) return sup;
   const int64_t N = w->N, K = w->K;
-  if (!sizes_ok(M, N, K, r) || !isfinite(s)) return QLORA_ERR_INVALID;
+  if (!sizes_ok(M, N, K, r) || !isfinite(s) || !state_fits(w)) return QLORA_ERR_INVALID;
   if (!aligned16(w->codes) || !aligned16(w->q8) || !aligned16(w->step) || !aligned16(X) ||
       !aligned16(A) || !aligned16(B) || !aligned16(Y) || !aligned16(ws) ||
       (U_out && !aligned16(U_out)))
@@ -229,7 +236,7 @@ int32_t linear_bwd(const nf4_tensor_t* w, const uint16_t* X, const uint16_t* dY,
   const int32_t sup = nf4_supported(w);
   if (sup != QLORA_OK) return sup;
   const int64_t N = w->N, K = w->K;
-  if (!sizes_ok(M, N, K, r) || !isfinite(s)) return QLORA_ERR_INVALID;
+  if (!sizes_ok(M, N, K, r) || !isfinite(s) || !state_fits(w)) return QLORA_ERR_INVALID;
   if (!aligned16(w->codes) || !aligned16(w->q8) || !aligned16(w->step) || !aligned16(X) ||
       !aligned16(dY) || !aligned16(A) || !aligned16(B) || !aligned16(dA) || !aligned16(dB) ||
       !aligned16(ws) || (U && !aligned16(U)) || (dX && !aligned16(dX)))

@@ -241,6 +241,33 @@ __device__ __forceinline__ HalfRaw<CT::kBits> load_half(const uint8_t* p) {
   return r;
 }
 
+// The same words through a buffer resource: byte offset voff (per lane)
+// plus soff (uniform).  Out-of-range words read as 0.
+template <class CT>
+__device__ __forceinline__ HalfRaw<CT::kBits> load_half(__amdgpu_buffer_rsrc_t rsrc, int voff,
+                                                        int soff) {
+  HalfRaw<CT::kBits> r;
+  if constexpr (CT::kBits == 4) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, soff, 0);
+    r.w[0] = v[0]; r.w[1] = v[1]; r.w[2] = v[2]; r.w[3] = v[3];
+  } else if constexpr (CT::kBits == 2) {
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rsrc, voff, soff, 0);
+    r.w[0] = v[0]; r.w[1] = v[1];
+  } else {
+    typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+    const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(rsrc, voff, soff, 0);
+    r.w[0] = v[0]; r.w[1] = v[1]; r.w[2] = v[2];
+  }
+  return r;
+}
+
+// A buffer resource over `bytes` bytes at p (the caller keeps bytes below
+// 2^31, so every offset fits the 32-bit offset fields).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t bytes_rsrc(const void* p, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
 // Codes 8 g .. 8 g + 7 of a half as eight nibbles (element 8 g + j in
 // nibble j).
 template <class CT>

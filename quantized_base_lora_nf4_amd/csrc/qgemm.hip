@@ -161,12 +161,20 @@ __device__ __forceinline__ void load_rows_lds(uint16_t* As, __amdgpu_buffer_rsrc
     const int c = (lane & 7) ^ ((r >> 1) & 7);
     int64_t gr = row0 + r;
     if (gr >= rows) gr = rows - 1;
-    int64_t gc = c0 + c * 8;
-    if (kClampCols && gc >= cols) gc = 0;
     // < 2^31 bytes: ld is at most 2^22 (the C ABI rejects larger N and K)
-    const int voff = (int)(((gr - row0) * ld + gc) * 2);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rsrc, (__attribute__((address_space(3))) void*)(As + 8 * e * 64), 16, voff, 0, 0, 0);
+    if constexpr (kClampCols) {
+      int64_t gc = c0 + c * 8;
+      if (gc >= cols) gc = 0;
+      const int voff = (int)(((gr - row0) * ld + gc) * 2);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsrc, (__attribute__((address_space(3))) void*)(As + 8 * e * 64), 16, voff, 0, 0, 0);
+    } else {
+      // the step's column offset is uniform: it goes in the scalar offset
+      const int voff = (int)(((gr - row0) * ld + c * 8) * 2);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsrc, (__attribute__((address_space(3))) void*)(As + 8 * e * 64), 16, voff,
+          (int)(c0 * 2), 0, 0);
+    }
   }
 }
 
@@ -321,13 +329,12 @@ template <class C, class CT>
 struct StepRegs {
   HalfRaw<CT::kBits> c[C::WPT / 32];
   uint32_t q;   // 8-bit constant as loaded
-  uint32_t qm;  // ~0, or 0 for weight rows past N (their values become 0)
   float st;
 };
 
 template <class C, class CT>
 __device__ __forceinline__ void dequant_codes(uint16_t* dst, const StepRegs<C, CT>& r) {
-  const LevelTable t = make_table<CT>((float)(r.q & r.qm) * r.st);
+  const LevelTable t = make_table<CT>((float)r.q * r.st);
 #pragma unroll
   for (int h = 0; h < C::WPT / 32; ++h)
 #pragma unroll
@@ -351,7 +358,7 @@ __device__ __forceinline__ void step_interleaved(const uint16_t* As, const uint1
   (void)As_n;
   Frags<C> f[2];
   read_frags<C, kTransB>(f[0], As, Bs, wm, wn, lane, 0);
-  const LevelTable t = make_table<CT>((float)(rn.q & rn.qm) * rn.st);
+  const LevelTable t = make_table<CT>((float)rn.q * rn.st);
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
     if (kk < 3) read_frags<C, kTransB>(f[(kk + 1) & 1], As, Bs, wm, wn, lane, kk + 1);
@@ -392,7 +399,8 @@ __global__ __launch_bounds__(C::NT, 1) void k_qgemm_fwd(FwdArgs p) {
   __shared__ __attribute__((aligned(16))) uint16_t xs1[C::TILE_A];
   __shared__ __attribute__((aligned(16))) uint16_t ws0[C::TILE_BF];
   __shared__ __attribute__((aligned(16))) uint16_t ws1[C::TILE_BF];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / C::WN, wn = wave % C::WN;
   const int64_t M = p.M, N = p.N, K = p.K;
   const int64_t tiles_n = (N + C::BN - 1) / C::BN;
@@ -406,8 +414,14 @@ __global__ __launch_bounds__(C::NT, 1) void k_qgemm_fwd(FwdArgs p) {
   const int wrow = tid / PARTS, wpart = tid % PARTS;
   int64_t gn = n0 + wrow;
   if (gn >= N) gn = N - 1;
-  const uint8_t* wcodes =
-      p.codes + gn * kblocks * block_bytes<CT>() + wpart * (C::WPT / 32) * half_bytes<CT>();
+  // Weight state through buffer resources (every offset below 2^31: the C
+  // ABI keeps the codes under 2 GiB): a per-thread offset plus the step's
+  // uniform offset, so the per-step address arithmetic is scalar.
+  const __amdgpu_buffer_rsrc_t crs = bytes_rsrc(p.codes, N * kblocks * block_bytes<CT>());
+  const __amdgpu_buffer_rsrc_t qrs = bytes_rsrc(p.q8, N * kblocks);
+  const __amdgpu_buffer_rsrc_t srs = bytes_rsrc(p.step, 4 * ((N * kblocks + 255) >> 8));
+  const int wvoff =
+      (int)(gn * kblocks * block_bytes<CT>() + wpart * (C::WPT / 32) * half_bytes<CT>());
   const int64_t wblk0 = gn * kblocks;
 
   AccT<C> acc;
@@ -421,12 +435,12 @@ __global__ __launch_bounds__(C::NT, 1) void k_qgemm_fwd(FwdArgs p) {
     if (kt >= kblocks) kt = kblocks - 1;
 #pragma unroll
     for (int h = 0; h < C::WPT / 32; ++h)
-      r.c[h] = load_half<CT>(wcodes + kt * block_bytes<CT>() + h * half_bytes<CT>());
-    r.qm = ~0u;
+      r.c[h] = load_half<CT>(crs, wvoff + h * (int)half_bytes<CT>(),
+                             (int)(kt * block_bytes<CT>()));
     if constexpr (!kQ4) {
-      const int64_t blk = wblk0 + kt;
-      r.q = p.q8[blk];
-      r.st = p.step[blk >> 8];
+      r.q = __builtin_amdgcn_raw_buffer_load_b8(qrs, (int)wblk0, (int)kt, 0);
+      r.st = __builtin_bit_cast(
+          float, __builtin_amdgcn_raw_buffer_load_b32(srs, (int)(((wblk0 + kt) >> 8) * 4), 0, 0));
     }
   };
   // kQ4: group g of four steps (4g .. 4g+3) keeps its constants in register
@@ -435,9 +449,9 @@ __global__ __launch_bounds__(C::NT, 1) void k_qgemm_fwd(FwdArgs p) {
   float s0 = 0.0f, s1 = 0.0f;
   auto load_q4 = [&](uint32_t& q, float& st, int64_t g) {
     if (g >= (kblocks >> 2)) g = (kblocks >> 2) - 1;
-    const int64_t blk = wblk0 + 4 * g;
-    q = *reinterpret_cast<const uint32_t*>(p.q8 + blk);
-    st = p.step[blk >> 8];
+    q = __builtin_amdgcn_raw_buffer_load_b32(qrs, (int)wblk0, (int)(4 * g), 0);
+    st = __builtin_bit_cast(
+        float, __builtin_amdgcn_raw_buffer_load_b32(srs, (int)(((wblk0 + 4 * g) >> 8) * 4), 0, 0));
   };
   const __amdgpu_buffer_rsrc_t xrsrc = rows_rsrc(p.X, K, m0, M);
   auto load_x = [&](uint16_t* As_dst, int64_t kt) {
@@ -578,7 +592,8 @@ __global__ __launch_bounds__(C::NT, 1) void k_qgemm_bwd(BwdArgs p) {
   __shared__ __attribute__((aligned(16))) uint16_t xs1[C::TILE_A];
   __shared__ __attribute__((aligned(16))) uint16_t ws0[C::TILE_BB];
   __shared__ __attribute__((aligned(16))) uint16_t ws1[C::TILE_BB];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / C::WN, wn = wave % C::WN;
   const int64_t M = p.M, N = p.N, K = p.K;
   const int64_t tiles_k = (K + C::BN - 1) / C::BN;
@@ -602,22 +617,30 @@ __global__ __launch_bounds__(C::NT, 1) void k_qgemm_bwd(BwdArgs p) {
   AccT<C> acc;
   zero_acc(acc);
   StepRegs<C, CT> ra, rb;
-  // Rows past N get constant 0 (their dequantized values are +-0, so the
-  // dY columns they meet add nothing); columns past K are computed from
-  // clamped codes and dropped on store.  Every load is unconditional.
+  // Weight state through buffer resources (offsets below 2^31 as in the
+  // forward): a per-thread offset for weight row wr and block column kb_own
+  // plus the step's uniform row offset.  Rows past N read past the end of
+  // the codes and constants, which buffer loads return as 0: their constant
+  // is 0 and their values +-0, so the dY columns they meet add nothing.
+  // Columns past K are computed from clamped codes and dropped on store.
+  // Every load is unconditional.
+  const int64_t rowb = kblocks * block_bytes<CT>();  // code bytes per weight row
+  const __amdgpu_buffer_rsrc_t crs = bytes_rsrc(p.codes, N * rowb);
+  const __amdgpu_buffer_rsrc_t qrs = bytes_rsrc(p.q8, N * kblocks);
+  const __amdgpu_buffer_rsrc_t srs = bytes_rsrc(p.step, 4 * ((N * kblocks + 255) >> 8));
+  const int64_t kb_own = (kvalid ? kcol : 0) >> 6;
+  const int64_t qown = wr * kblocks + kb_own;
+  const int cvoff =
+      (int)(wr * rowb + kb_own * block_bytes<CT>() + wh * (WPTB / 32) * half_bytes<CT>());
   auto load_w = [&](StepRegs<C, CT>& r, int64_t ns) {
     if (ns >= nsteps) ns = nsteps - 1;
-    const int64_t n = ns * BK + wr;
-    const bool nok = n < N;
-    const int64_t nc = nok ? n : 0, kc = kvalid ? kcol : 0;
-    const uint8_t* src = p.codes + (nc * kblocks + (kc >> 6)) * block_bytes<CT>() +
-                         wh * (WPTB / 32) * half_bytes<CT>();
+    const int64_t srow = ns * BK;  // first weight row of the step
 #pragma unroll
-    for (int h = 0; h < WPTB / 32; ++h) r.c[h] = load_half<CT>(src + h * half_bytes<CT>());
-    const int64_t blk = nc * kblocks + (kc >> 6);
-    r.q = p.q8[blk];
-    r.qm = nok ? ~0u : 0u;
-    r.st = p.step[blk >> 8];
+    for (int h = 0; h < WPTB / 32; ++h)
+      r.c[h] = load_half<CT>(crs, cvoff + h * (int)half_bytes<CT>(), (int)(srow * rowb));
+    r.q = __builtin_amdgcn_raw_buffer_load_b8(qrs, (int)qown, (int)(srow * kblocks), 0);
+    r.st = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                         srs, (int)(((srow * kblocks + qown) >> 8) * 4), 0, 0));
   };
   // dY tile of step ns straight into LDS; on a partial last step the chunks
   // past column N re-read column 0 and meet the zero rows above.
