@@ -120,11 +120,28 @@ __global__ __launch_bounds__(256) void k_lora_down_part(const uint16_t* __restri
   if (k1 > K) k1 = K;
   const uint16_t* xr = X + (mvalid ? i16 : 0) * K + 8 * q;
   const uint16_t* ar = A + (jvalid ? j : 0) * K + 8 * q;
+  const u32x4 zero = u32x4{0u, 0u, 0u, 0u};
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int64_t k = k0; k < k1; k += 32) {
-    const u32x4 xa = mvalid ? *reinterpret_cast<const u32x4*>(xr + k) : u32x4{0u, 0u, 0u, 0u};
-    const u32x4 aa = jvalid ? *reinterpret_cast<const u32x4*>(ar + k) : u32x4{0u, 0u, 0u, 0u};
-    acc = mfma16(as_bf16x8(xa), as_bf16x8(aa), acc);
+  // Batches of 8 steps: all 16 loads of a batch are issued (unconditionally:
+  // invalid rows re-read row 0 and are zeroed after) before the first use,
+  // so a batch costs one memory latency instead of eight.
+  constexpr int U = 8;
+  int64_t k = k0;
+  for (; k + 32 * U <= k1; k += 32 * U) {
+    u32x4 xa[U], aa[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      xa[u] = *reinterpret_cast<const u32x4*>(xr + k + 32 * u);
+      aa[u] = *reinterpret_cast<const u32x4*>(ar + k + 32 * u);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      acc = mfma16(as_bf16x8(mvalid ? xa[u] : zero), as_bf16x8(jvalid ? aa[u] : zero), acc);
+  }
+  for (; k < k1; k += 32) {
+    const u32x4 xa = *reinterpret_cast<const u32x4*>(xr + k);
+    const u32x4 aa = *reinterpret_cast<const u32x4*>(ar + k);
+    acc = mfma16(as_bf16x8(mvalid ? xa : zero), as_bf16x8(jvalid ? aa : zero), acc);
   }
   // D[m = 4 q + v][j]
   float* out = part + (int64_t)blockIdx.x * M * r;
