@@ -12,13 +12,15 @@
 //   Y  = [X | s U] [W | B]^T          (forward, contraction over K then r)
 //   dX = [dY | dU] [W ; A]            (backward, contraction over N then r)
 //
-// Tiling (both kernels): a 256 x 256 output tile per workgroup of 4 waves
-// (2 x 2), each wave owning 128 x 128 outputs as 4 x 4 MFMA 32x32x16 tiles
-// (256 fp32 accumulators per lane, held in AGPRs); 64-deep contraction steps;
-// both operand tiles double-buffered in LDS (136 KiB) so that one barrier per
-// step separates filling the next buffer from the MFMAs on the current one.
+// Tiling (both kernels, default configuration): a 256 x 256 output tile per
+// workgroup of 8 waves (2 x 4, two per SIMD), each wave owning 128 x 64
+// outputs as 4 x 2 MFMA 32x32x16 tiles (128 fp32 accumulators per lane);
+// 64-deep contraction steps; both operand tiles double-buffered in LDS
+// (136 KiB) so that one barrier per step separates filling the next buffer
+// from the MFMAs on the current one.
 //
-// Dequantization: each thread owns one 64-weight block row per step.  It
+// Dequantization: each thread owns half of a 64-weight block row per step
+// (a whole one with four waves).  It
 // builds that block's 16 possible bf16 values, bf16_rne(level[i] * c_hat),
 // once (16 multiplies), splits them into a low-byte and a high-byte plane of
 // 4 registers each, and then resolves every code with byte permutes
