@@ -18,6 +18,7 @@ Prints ONE JSON line (rank 0, N = 1).  FLOPs per weight and step:
 import argparse
 import ctypes
 import hashlib
+import re
 import json
 import os
 import sys
@@ -86,11 +87,19 @@ class HipEvents:
 
 
 def kernel_source_hash(names):
+    """Hash of the kernel sources' code: comments and blank lines are
+    removed first, so that editing a comment keeps the counters valid."""
     h = hashlib.sha256()
     for n in names:
-        with open(os.path.join(ROOT, "quantized_base_lora_nf4_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "quantized_base_lora_nf4_amd", "csrc", n)) as f:
+            h.update(strip_comments(f.read()).encode())
     return h.hexdigest()[:16]
+
+
+def strip_comments(src: str) -> str:
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    return "\n".join(l.rstrip() for l in src.splitlines() if l.strip())
 
 
 def load_traffic(kernel: str, workload: str, src_hash: str):
