@@ -201,6 +201,13 @@ def test_linear_rejects_bad_arguments_without_launching():
     assert fwd(ws=None) == _lib.QLORA_ERR_INVALID
     assert fwd(X=FAKE + 2) == _lib.QLORA_ERR_INVALID
     assert fwd(s=float("nan")) == _lib.QLORA_ERR_INVALID
+    # N or K above QLORA_LINEAR_MAX_NK, and packed codes of 2 GiB or more
+    # (the tile kernels use 32-bit offsets); the workspace size is not the
+    # reason for these rejections
+    big = 1 << 22
+    assert fwd(w=_w(2 * big, 128), nbytes=1 << 62) == _lib.QLORA_ERR_INVALID
+    assert fwd(w=_w(64, 2 * big), nbytes=1 << 62) == _lib.QLORA_ERR_INVALID
+    assert fwd(w=_w(big, 1024), nbytes=1 << 62) == _lib.QLORA_ERR_INVALID      # 2 GiB of codes
 
     needb = qn.workspace_size(32, 64, 128, 8, True)
 
