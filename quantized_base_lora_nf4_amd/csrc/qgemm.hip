@@ -30,6 +30,8 @@
 // Backward: the weight slice is written to LDS in its natural [n][k] layout
 // and read as the MFMA B operand with ds_read_b64_tr_b16, which hands each
 // lane 4 consecutive rows of one column.
+#include <type_traits>
+
 #include "kernels.hpp"
 
 namespace qn {
@@ -119,9 +121,13 @@ struct Cfg {
   static constexpr int SMEM_B = 2 * (TILE_A + TILE_BB);
   static constexpr int XCH = BM * 8 / NT;           // 16-byte activation chunks per thread
   static constexpr int XLD = BM / 8 / (NT / 64);    // direct-to-LDS loads per wave per step
-  static constexpr int WPT = BN * 64 / NT;          // forward weights dequantized per thread
+  // Threads that expand weights: one whole block row (64 weights) each per
+  // step, BN of them (the forward tile's BN rows; the backward slice's 64
+  // rows x BN / 64 blocks).  With 8 waves these are waves 0-3; the other
+  // four only run MFMAs, and each SIMD holds one wave of each kind.
+  static constexpr int NDQ = BN;
   static_assert(SMEM_F * 2 <= 160 * 1024 && SMEM_B * 2 <= 160 * 1024, "LDS budget");
-  static_assert(WPT == 64 || WPT == 32, "a thread dequantizes a whole or half block row");
+  static_assert(NDQ % 64 == 0 && NDQ <= NT, "whole waves expand weights");
 };
 
 // Activation tiles are [rows][64] bf16 with no padding; the eight 16-byte
@@ -324,52 +330,53 @@ __device__ __forceinline__ void stage_rows_scaled(uint16_t* As, const uint16_t* 
   }
 }
 
-// What one thread loads of the weights for one contraction step: the codes
-// (a whole or half block row, as half-block words), their 8-bit constant
+// What one expanding thread loads for one contraction step: the codes of
+// one whole block row (as two half-block word groups), its 8-bit constant
 // and group step.
-template <class C, class CT>
+template <class CT>
 struct StepRegs {
-  HalfRaw<CT::kBits> c[C::WPT / 32];
+  HalfRaw<CT::kBits> c[2];
   uint32_t q;   // 8-bit constant as loaded
   float st;
 };
 
-template <class C, class CT>
-__device__ __forceinline__ void dequant_codes(uint16_t* dst, const StepRegs<C, CT>& r) {
+template <class CT>
+__device__ __forceinline__ void dequant_block(uint16_t* dst, const StepRegs<CT>& r) {
   const LevelTable t = make_table<CT>((float)r.q * r.st);
 #pragma unroll
-  for (int h = 0; h < C::WPT / 32; ++h)
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      *reinterpret_cast<u32x4*>(dst + 32 * h + 8 * q) = lookup8(nibbles<CT>(r.c[h], q), t);
+  for (int w = 0; w < 8; ++w)
+    *reinterpret_cast<u32x4*>(dst + 8 * w) = lookup8(nibbles<CT>(r.c[w / 4], w % 4), t);
 }
 
 // One pipelined contraction step: the MFMAs on the current buffers (As, Bs)
-// while this thread writes its dequantized weights for the next step (codes
-// loaded two steps earlier, in rn) at Bw_n.  (The next activation tile is
-// already on its way into the other buffer by direct-to-LDS loads.)  The
-// four 16-deep sub-steps each read the next sub-step's fragments first, then
-// alternate their 16 MFMAs with the VALU work of expanding two code words,
-// then write those weight chunks.
-template <class C, bool kTransB, class CT>
+// and, in an expanding thread (kD), the dequantized block row for the next
+// step (codes loaded two steps earlier, in rn) written at Bw_n.  (The next
+// activation tile is already on its way into the other buffer by
+// direct-to-LDS loads.)  The four 16-deep sub-steps each read the next
+// sub-step's fragments first, then run their MFMAs and the VALU work of
+// expanding two code words, then write those weight chunks.  Expanding one
+// whole block row per thread builds each block's table once (two threads
+// on half rows built it twice), and pairing an expanding wave with an
+// MFMA-only wave on each SIMD lets one's lookups run beside the other's
+// MFMAs; measured 4-11 % faster than every wave expanding half rows.
+template <class C, bool kTransB, class CT, bool kD>
 __device__ __forceinline__ void step_interleaved(const uint16_t* As, const uint16_t* Bs,
-                                                 uint16_t* As_n, uint16_t* Bw_n,
-                                                 const StepRegs<C, CT>& rn, int wm, int wn, int lane,
-                                                 AccT<C>& acc) {
-  constexpr int NW = C::WPT / 8;  // code words to expand
-  (void)As_n;
+                                                 uint16_t* Bw_n, const StepRegs<CT>& rn, int wm,
+                                                 int wn, int lane, AccT<C>& acc) {
   Frags<C> f[2];
   read_frags<C, kTransB>(f[0], As, Bs, wm, wn, lane, 0);
-  const LevelTable t = make_table<CT>((float)rn.q * rn.st);
+  LevelTable t;
+  if constexpr (kD) t = make_table<CT>((float)rn.q * rn.st);
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
     if (kk < 3) read_frags<C, kTransB>(f[(kk + 1) & 1], As, Bs, wm, wn, lane, kk + 1);
     mfma_frags(f[kk & 1], acc);
+    if constexpr (kD) {
 #pragma unroll
-    for (int w = kk * NW / 4; w < (kk + 1) * NW / 4; ++w)
-      *reinterpret_cast<u32x4*>(Bw_n + 8 * w) = lookup8(nibbles<CT>(rn.c[w / 4], w % 4), t);
+      for (int w = 2 * kk; w < 2 * kk + 2; ++w)
+        *reinterpret_cast<u32x4*>(Bw_n + 8 * w) = lookup8(nibbles<CT>(rn.c[w / 4], w % 4), t);
+    }
   }
-
 }
 
 // ---------------------------------------------------------------------------
@@ -410,131 +417,141 @@ __global__ __launch_bounds__(C::NT, 1) void k_qgemm_fwd(FwdArgs p) {
   const int64_t m0 = (tile / tiles_n) * C::BM, n0 = (tile % tiles_n) * C::BN;
   const int64_t kblocks = K >> 6;
 
-  // This thread's weight row and part of the block (clamped; rows past N
-  // are computed and dropped).
-  constexpr int PARTS = 64 / C::WPT;
-  const int wrow = tid / PARTS, wpart = tid % PARTS;
-  int64_t gn = n0 + wrow;
-  if (gn >= N) gn = N - 1;
+  AccT<C> acc;
+  zero_acc(acc);
   // Weight state through buffer resources (every offset below 2^31: the C
   // ABI keeps the codes under 2 GiB): a per-thread offset plus the step's
   // uniform offset, so the per-step address arithmetic is scalar.
   const __amdgpu_buffer_rsrc_t crs = bytes_rsrc(p.codes, N * kblocks * block_bytes<CT>());
   const __amdgpu_buffer_rsrc_t qrs = bytes_rsrc(p.q8, N * kblocks);
   const __amdgpu_buffer_rsrc_t srs = bytes_rsrc(p.step, 4 * ((N * kblocks + 255) >> 8));
-  const int wvoff =
-      (int)(gn * kblocks * block_bytes<CT>() + wpart * (C::WPT / 32) * half_bytes<CT>());
-  const int64_t wblk0 = gn * kblocks;
-
-  AccT<C> acc;
-  zero_acc(acc);
-  // Weights are loaded two steps ahead (two register sets) and dequantized
-  // into the other LDS buffer while the MFMAs of the current step run;
-  // activations go straight from global memory into that buffer.  Steps
-  // past the end reload the last step (harmless).
-  StepRegs<C, CT> ra, rb;
-  auto load_w = [&](StepRegs<C, CT>& r, int64_t kt) {
-    if (kt >= kblocks) kt = kblocks - 1;
-#pragma unroll
-    for (int h = 0; h < C::WPT / 32; ++h)
-      r.c[h] = load_half<CT>(crs, wvoff + h * (int)half_bytes<CT>(),
-                             (int)(kt * block_bytes<CT>()));
-    if constexpr (!kQ4) {
-      r.q = __builtin_amdgcn_raw_buffer_load_b8(qrs, (int)wblk0, (int)kt, 0);
-      r.st = __builtin_bit_cast(
-          float, __builtin_amdgcn_raw_buffer_load_b32(srs, (int)(((wblk0 + kt) >> 8) * 4), 0, 0));
-    }
-  };
-  // kQ4: group g of four steps (4g .. 4g+3) keeps its constants in register
-  // pair g % 2; group g + 1 is loaded when group g starts being expanded.
-  uint32_t q0 = 0, q1 = 0;
-  float s0 = 0.0f, s1 = 0.0f;
-  auto load_q4 = [&](uint32_t& q, float& st, int64_t g) {
-    if (g >= (kblocks >> 2)) g = (kblocks >> 2) - 1;
-    q = __builtin_amdgcn_raw_buffer_load_b32(qrs, (int)wblk0, (int)(4 * g), 0);
-    st = __builtin_bit_cast(
-        float, __builtin_amdgcn_raw_buffer_load_b32(srs, (int)(((wblk0 + 4 * g) >> 8) * 4), 0, 0));
-  };
   const __amdgpu_buffer_rsrc_t xrsrc = rows_rsrc(p.X, K, m0, M);
   auto load_x = [&](uint16_t* As_dst, int64_t kt) {
     if (kt >= kblocks) kt = kblocks - 1;
     load_rows_lds<C, false>(As_dst, xrsrc, K, m0, M, kt * BK, K, wave, lane);  // K % 64 == 0
   };
-  // One step: MFMAs on buffer `cur` for step kt, step kt + 1 expanded into
-  // the other buffer.  kQ4: j = (kt + 1) % 4 is the position of step kt + 1
-  // in its group, whose constants are (qg, sg); j == 0 starts the group and
-  // loads the next one into (ql, sl).  `last`: no later step consumes this
-  // step's weight loads, so the compiler may drop them and the barrier must
-  // wait for everything.
-  auto body = [&](StepRegs<C, CT>& rnext, StepRegs<C, CT>& rload, int64_t kt, int cur, int j,
-                  uint32_t& qg, float& sg, uint32_t& ql, float& sl, bool last) {
-    const uint16_t* As = cur ? xs1 : xs0;
-    const uint16_t* Bs = cur ? ws1 : ws0;
-    uint16_t* As_n = cur ? xs0 : xs1;
-    uint16_t* Bs_n = cur ? ws0 : ws1;
-    load_x(As_n, kt + 1);   // tile loads first ...
-    __builtin_amdgcn_sched_barrier(0);
-    load_w(rload, kt + 2);  // ... then the weight loads, which outlive the step
-    if constexpr (kQ4) {
-      if (j == 0) load_q4(ql, sl, ((kt + 1) >> 2) + 1);
-      rnext.q = (qg >> (8 * j)) & 0xffu;
-      rnext.st = sg;
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    step_interleaved<C, false, CT>(As, Bs, As_n, Bs_n + wrow * LDA + wpart * C::WPT, rnext, wm,
-                                   wn, lane, acc);
-    // loads after the tile loads: codes (>= 1), plus q8 and step unless kQ4
-    // (where a group start adds the word of constants and the step)
-    if (last)
-      step_barrier<0>();
-    else if (!kQ4 || j == 0)
-      step_barrier<kWLoads>();
-    else
-      step_barrier<1>();
-  };
+  // The main loop, for an expanding thread (D: weight row tid of the tile,
+  // clamped; rows past N are computed and dropped) or an MFMA-only one.
+  // Both kinds pass the same barriers.
+  auto run = [&](auto kind) {
+    constexpr bool D = decltype(kind)::value;
+    const int wrow = tid;
+    int64_t gn = n0 + wrow;
+    if (gn >= N) gn = N - 1;
+    const int wvoff = (int)(gn * kblocks * block_bytes<CT>());
+    const int64_t wblk0 = gn * kblocks;
+    // Weights are loaded two steps ahead (two register sets) and expanded
+    // into the other LDS buffer while the MFMAs of the current step run;
+    // activations go straight from global memory into that buffer.  Steps
+    // past the end reload the last step (harmless).
+    StepRegs<CT> ra, rb;
+    auto load_w = [&](StepRegs<CT>& r, int64_t kt) {
+      if constexpr (D) {
+        if (kt >= kblocks) kt = kblocks - 1;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          r.c[h] = load_half<CT>(crs, wvoff + h * (int)half_bytes<CT>(),
+                                 (int)(kt * block_bytes<CT>()));
+        if constexpr (!kQ4) {
+          r.q = __builtin_amdgcn_raw_buffer_load_b8(qrs, (int)wblk0, (int)kt, 0);
+          r.st = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                               srs, (int)(((wblk0 + kt) >> 8) * 4), 0, 0));
+        }
+      }
+    };
+    // kQ4: group g of four steps (4g .. 4g+3) keeps its constants in
+    // register pair g % 2; group g + 1 is loaded when group g starts being
+    // expanded.
+    uint32_t q0 = 0, q1 = 0;
+    float s0 = 0.0f, s1 = 0.0f;
+    auto load_q4 = [&](uint32_t& q, float& st, int64_t g) {
+      if constexpr (D) {
+        if (g >= (kblocks >> 2)) g = (kblocks >> 2) - 1;
+        q = __builtin_amdgcn_raw_buffer_load_b32(qrs, (int)wblk0, (int)(4 * g), 0);
+        st = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                           srs, (int)(((wblk0 + 4 * g) >> 8) * 4), 0, 0));
+      }
+    };
+    // One step: MFMAs on buffer `cur` for step kt, step kt + 1 expanded
+    // into the other buffer.  kQ4: j = (kt + 1) % 4 is the position of step
+    // kt + 1 in its group, whose constants are (qg, sg); j == 0 starts the
+    // group and loads the next one into (ql, sl).  `last`: no later step
+    // consumes this step's weight loads, so the compiler may drop them and
+    // the barrier must wait for everything.
+    auto body = [&](StepRegs<CT>& rnext, StepRegs<CT>& rload, int64_t kt, int cur, int j,
+                    uint32_t& qg, float& sg, uint32_t& ql, float& sl, bool last) {
+      const uint16_t* As = cur ? xs1 : xs0;
+      const uint16_t* Bs = cur ? ws1 : ws0;
+      uint16_t* As_n = cur ? xs0 : xs1;
+      uint16_t* Bs_n = cur ? ws0 : ws1;
+      load_x(As_n, kt + 1);   // tile loads first ...
+      __builtin_amdgcn_sched_barrier(0);
+      load_w(rload, kt + 2);  // ... then the weight loads, which outlive the step
+      if constexpr (D && kQ4) {
+        if (j == 0) load_q4(ql, sl, ((kt + 1) >> 2) + 1);
+        rnext.q = (qg >> (8 * j)) & 0xffu;
+        rnext.st = sg;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      step_interleaved<C, false, CT, D>(As, Bs, Bs_n + wrow * LDA, rnext, wm, wn, lane, acc);
+      // loads after the tile loads: two code loads (>= 2 instructions),
+      // plus q8 and step unless kQ4 (where a group start adds the word of
+      // constants and the step); none in an MFMA-only thread
+      if (last || !D)
+        step_barrier<0>();
+      else if (!kQ4 || j == 0)
+        step_barrier<kWLoads>();
+      else
+        step_barrier<2>();
+    };
 
-  load_w(ra, 0);
-  load_w(rb, 1);
-  if constexpr (kQ4) {
-    load_q4(q0, s0, 0);
-    load_q4(q1, s1, 1);
-    ra.q = q0 & 0xffu;
-    ra.st = s0;
-  }
-  load_x(xs0, 0);
-  dequant_codes<C, CT>(ws0 + wrow * LDA + wpart * C::WPT, ra);
-  wait_vmem();
-  __syncthreads();
-  int64_t kt = 0;
-  if constexpr (kQ4) {  // kblocks % 4 == 0; groups 2i and 2i + 1 per iteration
-    for (; kt + 8 <= kblocks; kt += 8) {
-      body(rb, ra, kt, 0, 1, q0, s0, q1, s1, false);
-      body(ra, rb, kt + 1, 1, 2, q0, s0, q1, s1, false);
-      body(rb, ra, kt + 2, 0, 3, q0, s0, q1, s1, false);
-      body(ra, rb, kt + 3, 1, 0, q1, s1, q0, s0, false);
-      body(rb, ra, kt + 4, 0, 1, q1, s1, q0, s0, false);
-      body(ra, rb, kt + 5, 1, 2, q1, s1, q0, s0, false);
-      body(rb, ra, kt + 6, 0, 3, q1, s1, q0, s0, false);
-      body(ra, rb, kt + 7, 1, 0, q0, s0, q1, s1, false);
+    load_w(ra, 0);
+    load_w(rb, 1);
+    if constexpr (D && kQ4) {
+      load_q4(q0, s0, 0);
+      load_q4(q1, s1, 1);
+      ra.q = q0 & 0xffu;
+      ra.st = s0;
     }
-    if (kt < kblocks) {  // one more group of four, the last steps
-      body(rb, ra, kt, 0, 1, q0, s0, q1, s1, false);
-      body(ra, rb, kt + 1, 1, 2, q0, s0, q1, s1, false);
-      body(rb, ra, kt + 2, 0, 3, q0, s0, q1, s1, false);
-      body(ra, rb, kt + 3, 1, 0, q1, s1, q0, s0, true);
-      kt += 4;
-    }
-  } else {
-    for (; kt + 2 <= kblocks; kt += 2) {
-      // MFMA step kt (buffer 0), stage kt+1 from rb, load kt+2 into ra; then the converse
-      body(rb, ra, kt, 0, 0, q0, s0, q1, s1, false);
-      body(ra, rb, kt + 1, 1, 0, q0, s0, q1, s1, false);
-    }
-  }
-  if (kt < kblocks) {  // odd number of steps: the last one is in buffer 0
-    mma_step<C, false>(xs0, ws0, wm, wn, lane, acc);
+    load_x(xs0, 0);
+    if constexpr (D) dequant_block<CT>(ws0 + wrow * LDA, ra);
+    wait_vmem();
     __syncthreads();
-  }
+    int64_t kt = 0;
+    if constexpr (kQ4) {  // kblocks % 4 == 0; groups 2i and 2i + 1 per iteration
+      for (; kt + 8 <= kblocks; kt += 8) {
+        body(rb, ra, kt, 0, 1, q0, s0, q1, s1, false);
+        body(ra, rb, kt + 1, 1, 2, q0, s0, q1, s1, false);
+        body(rb, ra, kt + 2, 0, 3, q0, s0, q1, s1, false);
+        body(ra, rb, kt + 3, 1, 0, q1, s1, q0, s0, false);
+        body(rb, ra, kt + 4, 0, 1, q1, s1, q0, s0, false);
+        body(ra, rb, kt + 5, 1, 2, q1, s1, q0, s0, false);
+        body(rb, ra, kt + 6, 0, 3, q1, s1, q0, s0, false);
+        body(ra, rb, kt + 7, 1, 0, q0, s0, q1, s1, false);
+      }
+      if (kt < kblocks) {  // one more group of four, the last steps
+        body(rb, ra, kt, 0, 1, q0, s0, q1, s1, false);
+        body(ra, rb, kt + 1, 1, 2, q0, s0, q1, s1, false);
+        body(rb, ra, kt + 2, 0, 3, q0, s0, q1, s1, false);
+        body(ra, rb, kt + 3, 1, 0, q1, s1, q0, s0, true);
+        kt += 4;
+      }
+    } else {
+      for (; kt + 2 <= kblocks; kt += 2) {
+        // MFMA step kt (buffer 0), stage kt+1 from rb, load kt+2 into ra; then the converse
+        body(rb, ra, kt, 0, 0, q0, s0, q1, s1, false);
+        body(ra, rb, kt + 1, 1, 0, q0, s0, q1, s1, false);
+      }
+    }
+    if (kt < kblocks) {  // odd number of steps: the last one is in buffer 0
+      mma_step<C, false>(xs0, ws0, wm, wn, lane, acc);
+      __syncthreads();
+    }
+  };
+  if (tid < C::NDQ)  // whole waves
+    run(std::true_type{});
+  else
+    run(std::false_type{});
 
   // LoRA: extra contraction over r with A-side bf16(s U) and B-side B.
   const bool bvec = (p.r & 7) == 0;
@@ -604,21 +621,8 @@ __global__ __launch_bounds__(C::NT, 1) void k_qgemm_bwd(BwdArgs p) {
   const int64_t kblocks = K >> 6;
   const int64_t nsteps = (N + BK - 1) / BK;
 
-  // Weight slice work split: 64 rows x (BN / 64) blocks, each thread a whole
-  // or half block row.
-  constexpr int BPR = C::BN / 64;                 // blocks per slice row
-  constexpr int WPTB = 64 * C::BN / C::NT;        // weights per thread in the slice
-  static_assert(WPTB == 64 || WPTB == 32, "backward split");
-  constexpr int HP = 64 / WPTB;                   // threads per block row
-  const int wr = tid / (BPR * HP);
-  const int wb = (tid / HP) % BPR;
-  const int wh = tid % HP;
-  const int64_t kcol = k0 + wb * 64;
-  const bool kvalid = kcol < K;
-
   AccT<C> acc;
   zero_acc(acc);
-  StepRegs<C, CT> ra, rb;
   // Weight state through buffer resources (offsets below 2^31 as in the
   // forward): a per-thread offset for weight row wr and block column kb_own
   // plus the step's uniform row offset.  Rows past N read past the end of
@@ -630,20 +634,6 @@ __global__ __launch_bounds__(C::NT, 1) void k_qgemm_bwd(BwdArgs p) {
   const __amdgpu_buffer_rsrc_t crs = bytes_rsrc(p.codes, N * rowb);
   const __amdgpu_buffer_rsrc_t qrs = bytes_rsrc(p.q8, N * kblocks);
   const __amdgpu_buffer_rsrc_t srs = bytes_rsrc(p.step, 4 * ((N * kblocks + 255) >> 8));
-  const int64_t kb_own = (kvalid ? kcol : 0) >> 6;
-  const int64_t qown = wr * kblocks + kb_own;
-  const int cvoff =
-      (int)(wr * rowb + kb_own * block_bytes<CT>() + wh * (WPTB / 32) * half_bytes<CT>());
-  auto load_w = [&](StepRegs<C, CT>& r, int64_t ns) {
-    if (ns >= nsteps) ns = nsteps - 1;
-    const int64_t srow = ns * BK;  // first weight row of the step
-#pragma unroll
-    for (int h = 0; h < WPTB / 32; ++h)
-      r.c[h] = load_half<CT>(crs, cvoff + h * (int)half_bytes<CT>(), (int)(srow * rowb));
-    r.q = __builtin_amdgcn_raw_buffer_load_b8(qrs, (int)qown, (int)(srow * kblocks), 0);
-    r.st = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                         srs, (int)(((srow * kblocks + qown) >> 8) * 4), 0, 0));
-  };
   // dY tile of step ns straight into LDS; on a partial last step the chunks
   // past column N re-read column 0 and meet the zero rows above.
   const __amdgpu_buffer_rsrc_t yrsrc = rows_rsrc(p.dY, N, m0, M);
@@ -651,38 +641,69 @@ __global__ __launch_bounds__(C::NT, 1) void k_qgemm_bwd(BwdArgs p) {
     if (ns >= nsteps) ns = nsteps - 1;
     load_rows_lds<C, true>(As_dst, yrsrc, N, m0, M, ns * BK, N, wave, lane);
   };
-  // (3-bit codes may take three dword loads per half: more loads after the
-  // tile loads only make the wait in step_barrier() stricter.)
-  static_assert(WPTB / 32 + 2 == kWLoads, "weight loads per step");
-  auto body = [&](StepRegs<C, CT>& rnext, StepRegs<C, CT>& rload, int64_t ns, int cur) {
-    const uint16_t* As = cur ? xs1 : xs0;
-    const uint16_t* Bs = cur ? ws1 : ws0;
-    uint16_t* As_n = cur ? xs0 : xs1;
-    uint16_t* Bs_n = cur ? ws0 : ws1;
-    load_x(As_n, ns + 1);    // tile loads first ...
-    __builtin_amdgcn_sched_barrier(0);
-    load_w(rload, ns + 2);   // ... then the weight loads, which outlive the step
-    __builtin_amdgcn_sched_barrier(0);
-    step_interleaved<C, true, CT>(As, Bs, As_n, Bs_n + wr * C::LDTB + wb * C::BSTR + wh * WPTB,
-                                  rnext, wm, wn, lane, acc);
-    step_barrier();
-  };
+  // The main loop, for an expanding thread (D: weight slice row wr, block
+  // column wb of the step's 64 x BN slice) or an MFMA-only one.  Both
+  // kinds pass the same barriers.
+  auto run = [&](auto kind) {
+    constexpr bool D = decltype(kind)::value;
+    constexpr int BPR = C::BN / 64;  // blocks per slice row
+    const int wr = tid / BPR, wb = tid % BPR;
+    const int64_t kcol = k0 + wb * 64;
+    const int64_t kb_own = (kcol < K ? kcol : 0) >> 6;
+    const int64_t qown = wr * kblocks + kb_own;
+    const int cvoff = (int)(wr * rowb + kb_own * block_bytes<CT>());
+    StepRegs<CT> ra, rb;
+    auto load_w = [&](StepRegs<CT>& r, int64_t ns) {
+      if constexpr (D) {
+        if (ns >= nsteps) ns = nsteps - 1;
+        const int64_t srow = ns * BK;  // first weight row of the step
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          r.c[h] = load_half<CT>(crs, cvoff + h * (int)half_bytes<CT>(), (int)(srow * rowb));
+        r.q = __builtin_amdgcn_raw_buffer_load_b8(qrs, (int)qown, (int)(srow * kblocks), 0);
+        r.st = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                             srs, (int)(((srow * kblocks + qown) >> 8) * 4), 0, 0));
+      }
+    };
+    auto body = [&](StepRegs<CT>& rnext, StepRegs<CT>& rload, int64_t ns, int cur) {
+      const uint16_t* As = cur ? xs1 : xs0;
+      const uint16_t* Bs = cur ? ws1 : ws0;
+      uint16_t* As_n = cur ? xs0 : xs1;
+      uint16_t* Bs_n = cur ? ws0 : ws1;
+      load_x(As_n, ns + 1);    // tile loads first ...
+      __builtin_amdgcn_sched_barrier(0);
+      load_w(rload, ns + 2);   // ... then the weight loads, which outlive the step
+      __builtin_amdgcn_sched_barrier(0);
+      step_interleaved<C, true, CT, D>(As, Bs, Bs_n + wr * C::LDTB + wb * C::BSTR, rnext, wm,
+                                       wn, lane, acc);
+      // two code loads, q8 and step after the tile loads (>= kWLoads); none
+      // in an MFMA-only thread
+      if constexpr (D)
+        step_barrier<kWLoads>();
+      else
+        step_barrier<0>();
+    };
 
-  load_w(ra, 0);
-  load_w(rb, 1);
-  load_x(xs0, 0);
-  dequant_codes<C, CT>(ws0 + wr * C::LDTB + wb * C::BSTR + wh * WPTB, ra);
-  wait_vmem();
-  __syncthreads();
-  int64_t ns = 0;
-  for (; ns + 2 <= nsteps; ns += 2) {
-    body(rb, ra, ns, 0);
-    body(ra, rb, ns + 1, 1);
-  }
-  if (ns < nsteps) {
-    mma_step<C, true>(xs0, ws0, wm, wn, lane, acc);
+    load_w(ra, 0);
+    load_w(rb, 1);
+    load_x(xs0, 0);
+    if constexpr (D) dequant_block<CT>(ws0 + wr * C::LDTB + wb * C::BSTR, ra);
+    wait_vmem();
     __syncthreads();
-  }
+    int64_t ns = 0;
+    for (; ns + 2 <= nsteps; ns += 2) {
+      body(rb, ra, ns, 0);
+      body(ra, rb, ns + 1, 1);
+    }
+    if (ns < nsteps) {
+      mma_step<C, true>(xs0, ws0, wm, wn, lane, acc);
+      __syncthreads();
+    }
+  };
+  if (tid < C::NDQ)  // whole waves
+    run(std::true_type{});
+  else
+    run(std::false_type{});
 
   // LoRA: dX += dU A, contraction over r.  A[j][k] is already [contraction][column].
   for (int j0 = 0; j0 < p.r; j0 += 64) {
