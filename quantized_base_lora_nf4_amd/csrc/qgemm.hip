@@ -586,6 +586,10 @@ __global__ __launch_bounds__(C::NT, 1) void k_qgemm_fwd(FwdArgs p) {
   store_tile<C>(p.Y, N, m0, n0, M, N, wm, wn, lane, acc);
 }
 
+// A per-thread buffer offset past every buffer this file reads (each under
+// 2^31 bytes): such a load returns 0 without touching memory.
+constexpr int kOutOfRange = INT32_MIN;
+
 // ---------------------------------------------------------------------------
 // Backward (dX)
 // ---------------------------------------------------------------------------
@@ -625,11 +629,12 @@ __global__ __launch_bounds__(C::NT, 1) void k_qgemm_bwd(BwdArgs p) {
   zero_acc(acc);
   // Weight state through buffer resources (offsets below 2^31 as in the
   // forward): a per-thread offset for weight row wr and block column kb_own
-  // plus the step's uniform row offset.  Rows past N read past the end of
-  // the codes and constants, which buffer loads return as 0: their constant
-  // is 0 and their values +-0, so the dY columns they meet add nothing.
-  // Columns past K are computed from clamped codes and dropped on store.
-  // Every load is unconditional.
+  // plus the step's uniform row offset.  A row past N (partial last step)
+  // takes the per-thread offset 2^31, past every buffer's end whether or
+  // not the range check counts the uniform offset: its loads return 0, so
+  // its constant is 0 and its values +-0, and the dY columns it meets add
+  // nothing.  Columns past K are computed from clamped codes and dropped
+  // on store.  Every load is issued unconditionally.
   const int64_t rowb = kblocks * block_bytes<CT>();  // code bytes per weight row
   const __amdgpu_buffer_rsrc_t crs = bytes_rsrc(p.codes, N * rowb);
   const __amdgpu_buffer_rsrc_t qrs = bytes_rsrc(p.q8, N * kblocks);
@@ -657,12 +662,16 @@ __global__ __launch_bounds__(C::NT, 1) void k_qgemm_bwd(BwdArgs p) {
       if constexpr (D) {
         if (ns >= nsteps) ns = nsteps - 1;
         const int64_t srow = ns * BK;  // first weight row of the step
+        const bool in = srow + wr < N;
 #pragma unroll
         for (int h = 0; h < 2; ++h)
-          r.c[h] = load_half<CT>(crs, cvoff + h * (int)half_bytes<CT>(), (int)(srow * rowb));
-        r.q = __builtin_amdgcn_raw_buffer_load_b8(qrs, (int)qown, (int)(srow * kblocks), 0);
-        r.st = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                             srs, (int)(((srow * kblocks + qown) >> 8) * 4), 0, 0));
+          r.c[h] = load_half<CT>(crs, in ? cvoff + h * (int)half_bytes<CT>() : kOutOfRange,
+                                 (int)(srow * rowb));
+        r.q = __builtin_amdgcn_raw_buffer_load_b8(qrs, in ? (int)qown : kOutOfRange,
+                                                  (int)(srow * kblocks), 0);
+        r.st = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(
+                       srs, in ? (int)(((srow * kblocks + qown) >> 8) * 4) : kOutOfRange, 0, 0));
       }
     };
     auto body = [&](StepRegs<CT>& rnext, StepRegs<CT>& rload, int64_t ns, int cur) {

@@ -159,6 +159,42 @@ def test_layer_parity(shape):
     assert_close("dB", got["dB"], dB)
 
 
+def _poisoned_copy(w, rows=64):
+    """The same weight state at the start of larger buffers whose bytes past
+    the end hold garbage (codes 0xFF, constants 255, steps NaN), `rows`
+    weight rows' worth of each.  A kernel that reads any of it for a row past
+    N puts NaN or huge values into its results."""
+    kb = w.K // 64
+    def pad(t, extra, fill):
+        big = torch.full((t.numel() + extra,), fill, dtype=t.dtype, device=t.device)
+        big[:t.numel()].copy_(t)
+        return big[:t.numel()]
+    return qn.NF4Weight(codes=pad(w.codes, rows * w.codes.numel() // w.N, 0xFF),
+                        q8=pad(w.q8, rows * kb, 0xFF),
+                        step=pad(w.step, rows * kb // 256 + 2, float("nan")),
+                        N=w.N, K=w.K, code=w.code)
+
+
+@pytest.mark.parametrize("shape", [(300, 136, 192, 8), (260, 392, 768, 16), (130, 520, 576, 128),
+                                   (16, 1032, 1024, 16)])
+def test_layer_reads_nothing_past_the_weight(shape):
+    """N not a multiple of 64: the backward's last contraction step covers
+    weight rows past N, which must contribute exactly zero without reading
+    memory past the weight's buffers (garbage is planted there)."""
+    M, N, K, r = shape
+    say(f"[poisoned tail] M={M} N={N} K={K} r={r}")
+    inp = _layer(M, N, K, r, seed=5)
+    w = _poisoned_copy(gpu_quantize(inp.W))
+    got = _gpu_fwd_bwd(inp, w)
+    Wh = oracle_what(inp.W)
+    X, A, B, dY = f32(inp.X), f32(inp.A), f32(inp.B), f32(inp.dY)
+    assert_close("Y", got["Y"], linear.forward(X, Wh, A, B, inp.s))
+    dX, dA, dB = linear.backward(X, dY, Wh, A, B, inp.s)
+    assert_close("dX", got["dX"], dX)
+    assert_close("dA", got["dA"], dA)
+    assert_close("dB", got["dB"], dB)
+
+
 @pytest.mark.parametrize("shape", [(300, 136, 192, 8), (4, 1024, 2048, 16), (257, 512, 512, 64)])
 def test_lora_terms_in_isolation(shape):
     """W = 0 leaves only the adapter: Y = s U B^T, dX = s dY B A.  The LoRA
