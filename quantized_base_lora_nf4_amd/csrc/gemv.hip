@@ -426,6 +426,38 @@ size_t gemv_workspace_bytes(int64_t M, int32_t r, int64_t K) {
   return (size_t)gemv_lora_slices(K) * M * r * sizeof(float);
 }
 
+#ifndef QN_GEMV_G7
+#define QN_GEMV_G7 1
+#endif
+
+template <int G>
+hipError_t launch_qgemv_g(const GemvArgs& a, int code, hipStream_t stream) {
+  constexpr int KW = 8, PD = QN_GEMV_PD;
+  static const hipError_t attr = [] {
+    // dynamic LDS above the default 64 KB needs the limit raised, once per
+    // instantiation
+    hipError_t r = hipSuccess;
+    for (int id = 0; id < 4; ++id) {
+      const hipError_t e = with_code(id, [](auto ct) {
+        return hipFuncSetAttribute(
+            reinterpret_cast<const void*>(&k_qgemv<G, KW, PD, QN_GEMV_PERM, decltype(ct)>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
+      });
+      if (r == hipSuccess) r = e;
+    }
+    return r;
+  }();
+  if (attr != hipSuccess) return attr;
+  const size_t lds = 4 * (size_t)gemv_lds_words(G, KW, a.M, a.r, a.K / 64);
+  const dim3 grid((unsigned)((a.N + 16 * G - 1) / (16 * G)));
+  with_code(code, [&](auto ct) {
+    hipLaunchKernelGGL((k_qgemv<G, KW, PD, QN_GEMV_PERM, decltype(ct)>), grid, dim3(64 * KW), lds,
+                       stream, a);
+    return 0;
+  });
+  return hipGetLastError();
+}
+
 hipError_t launch_qgemv(const Nf4View& w, const uint16_t* X, int64_t M, const uint16_t* A,
                         const uint16_t* B, int32_t r, float s, uint16_t* Y, uint16_t* U_out,
                         float* upart, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
@@ -438,31 +470,20 @@ hipError_t launch_qgemv(const Nf4View& w, const uint16_t* X, int64_t M, const ui
   if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
   const GemvArgs a{w.codes, w.q8, w.step, X, M, w.N, w.K, upart, (int32_t)gu.x, B, r, s, Y, U_out};
   const int64_t kblocks = w.K / 64;
-  // 32 weight rows per workgroup, K split over its 8 waves
-  constexpr int G = 2, KW = 8, PD = QN_GEMV_PD;
-  static const hipError_t attr = [] {
-    // dynamic LDS above the default 64 KB needs the limit raised, once per
-    // instantiation
-    hipError_t r = hipSuccess;
-    for (int id = 0; id < 4; ++id) {
-      const hipError_t a = with_code(id, [](auto ct) {
-        return hipFuncSetAttribute(
-            reinterpret_cast<const void*>(&k_qgemv<G, KW, PD, QN_GEMV_PERM, decltype(ct)>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
-      });
-      if (r == hipSuccess) r = a;
-    }
-    return r;
+  // 16 G weight rows per workgroup, K split over its 8 waves.  G = 2, or 7
+  // when the 16-row groups make exactly one workgroup of 7 per CU (a
+  // 28672-row weight on 256 CUs), so that no CU gets more rows than another.
+  static const int cus = [] {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    return n;
   }();
-  if (attr != hipSuccess) return attr;
-  const size_t lds = 4 * (size_t)gemv_lds_words(G, KW, M, r, kblocks);
-  const dim3 grid((unsigned)((w.N + 16 * G - 1) / (16 * G)));
-  with_code(w.code, [&](auto ct) {
-    hipLaunchKernelGGL((k_qgemv<G, KW, PD, QN_GEMV_PERM, decltype(ct)>), grid, dim3(64 * KW), lds,
-                       stream, a);
-    return 0;
-  });
-  e = hipGetLastError();
+  const int64_t groups = (w.N + 15) / 16;
+  const bool g7 = QN_GEMV_G7 && cus > 0 && groups % (7 * (int64_t)cus) == 0 &&
+                  4 * gemv_lds_words(7, 8, M, r, kblocks) <= 96 * 1024;
+  e = g7 ? launch_qgemv_g<7>(a, w.code, stream) : launch_qgemv_g<2>(a, w.code, stream);
   if (e != hipSuccess) return e;
   if (ev1) e = hipEventRecord(ev1, stream);
   return e;

@@ -117,6 +117,11 @@ LSHAPES = [  # (M, N, K, r)
     (2, 8, 64, 1),             # one block per weight row, smallest everything
     (260, 392, 768, 16),       # K % 256 == 0 with 12 steps: grouped constants plus a tail group
     (33, 64, 256, 4),          # K = 256: the tail group alone
+    # 28672 rows = 7 x 16 rows per CU on a 256-CU device: the few-token
+    # forward takes workgroups of 7 row groups there
+    (3, 28672, 64, 4),         # one block per row: the odd tail step alone
+    (16, 28672, 192, 16),      # three blocks: one double step and the tail
+    (7, 28672, 576, 8),
 ]
 
 
