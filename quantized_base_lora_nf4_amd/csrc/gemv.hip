@@ -470,9 +470,15 @@ hipError_t launch_qgemv(const Nf4View& w, const uint16_t* X, int64_t M, const ui
   if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
   const GemvArgs a{w.codes, w.q8, w.step, X, M, w.N, w.K, upart, (int32_t)gu.x, B, r, s, Y, U_out};
   const int64_t kblocks = w.K / 64;
-  // 16 G weight rows per workgroup, K split over its 8 waves.  G = 2, or 7
-  // when the 16-row groups make exactly one workgroup of 7 per CU (a
-  // 28672-row weight on 256 CUs), so that no CU gets more rows than another.
+  // 16 G weight rows per workgroup, K split over its 8 waves.
+  //  - G = 7 when the 16-row groups make exactly one workgroup of 7 per CU
+  //    (a 28672-row weight on 256 CUs): no CU gets more rows than another,
+  //    and each CU loads the X fragments once.
+  //  - G = 1 for one or two tokens when G = 2 would leave at most one
+  //    workgroup (8 waves) per CU: twice the waves keep more loads in
+  //    flight.  With more tokens the X fragments, loaded once per
+  //    workgroup, cost more than that gains.
+  //  - G = 2 otherwise.
   static const int cus = [] {
     int dev = 0, n = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
@@ -483,7 +489,10 @@ hipError_t launch_qgemv(const Nf4View& w, const uint16_t* X, int64_t M, const ui
   const int64_t groups = (w.N + 15) / 16;
   const bool g7 = QN_GEMV_G7 && cus > 0 && groups % (7 * (int64_t)cus) == 0 &&
                   4 * gemv_lds_words(7, 8, M, r, kblocks) <= 96 * 1024;
-  e = g7 ? launch_qgemv_g<7>(a, w.code, stream) : launch_qgemv_g<2>(a, w.code, stream);
+  const bool g1 = !g7 && M <= 2 && cus > 0 && groups <= 2 * (int64_t)cus;
+  e = g7   ? launch_qgemv_g<7>(a, w.code, stream)
+      : g1 ? launch_qgemv_g<1>(a, w.code, stream)
+           : launch_qgemv_g<2>(a, w.code, stream);
   if (e != hipSuccess) return e;
   if (ev1) e = hipEventRecord(ev1, stream);
   return e;

@@ -122,6 +122,7 @@ LSHAPES = [  # (M, N, K, r)
     (3, 28672, 64, 4),         # one block per row: the odd tail step alone
     (16, 28672, 192, 16),      # three blocks: one double step and the tail
     (7, 28672, 576, 8),
+    (2, 1000, 1088, 8),        # two tokens: one row group per workgroup, ragged rows, odd block count
 ]
 
 
