@@ -209,7 +209,9 @@ size_t qlora_workspace_size(int64_t M, int64_t N, int64_t K, int32_t r,
  *           qlora_linear_bwd can take back instead of recomputing it
  *   ws      device workspace of ws_bytes >= qlora_workspace_size(M,N,K,r,0)
  * Accumulation is fp32.  M <= 16 takes a bandwidth-bound path that
- * streams the packed weight once; larger M takes an MFMA tile path.
+ * streams the packed weight once (when its per-workgroup tables fit in
+ * LDS: K up to about 32000 at M = 16, r = 256); larger M, or
+ * larger K, takes the MFMA tile path.  Both meet the same tolerance.
  */
 int32_t qlora_linear_fwd(const nf4_tensor_t* w, const uint16_t* X, int64_t M,
                          const uint16_t* A, const uint16_t* B, int32_t r,

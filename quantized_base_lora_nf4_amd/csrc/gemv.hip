@@ -410,7 +410,7 @@ __global__ __launch_bounds__(64 * KW) void k_qgemv(GemvArgs p) {
 }  // namespace
 
 bool gemv_fits(int64_t M, int32_t r, int64_t K) {
-  // the workgroup's LDS within 96 KB (K up to about 24000 at rank 256)
+  // the workgroup's LDS within 96 KB (K up to about 32000 at 16 tokens and rank 256)
   return M <= kGemvMaxM && 4 * gemv_lds_words(2, 8, M, r, K / 64) <= 96 * 1024;
 }
 

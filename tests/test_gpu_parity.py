@@ -123,6 +123,7 @@ LSHAPES = [  # (M, N, K, r)
     (16, 28672, 192, 16),      # three blocks: one double step and the tail
     (7, 28672, 576, 8),
     (2, 1000, 1088, 8),        # two tokens: one row group per workgroup, ragged rows, odd block count
+    (3, 64, 41024, 4),         # few tokens, K past the few-token kernel's LDS tables: tile path
 ]
 
 
