@@ -6,10 +6,9 @@
 // Dequantize-on-the-fly as in "QLoRA: fine-tuning a 65B model on one GPU",
 // section "Where the memory goes".  A memory-bound stream leaves only a few
 // lane operations per weight, so the codes are expanded to *unscaled* bf16
-// levels (a 256-entry byte table in LDS, or byte permutes over the level
-// table held in registers), the MFMA sums one 64-element block at a time,
-// and the block constant fl32(q8 * step) multiplies that block's fp32
-// partial sum.  The result differs from using the bf16-rounded dequantized
+// levels (a 256-entry byte table in LDS, one lookup per code byte), the
+// MFMA sums one 64-element block at a time, and the block constant
+// fl32(q8 * step) multiplies that block's fp32 partial sum.  The result differs from using the bf16-rounded dequantized
 // weight only by the bf16 rounding of the levels (relative 2^-9 per weight);
 // accumulation is fp32.
 //
@@ -34,62 +33,6 @@
 namespace qn {
 
 namespace {
-
-// bf16 bits of an fp32 value (round to nearest even; finite input)
-constexpr uint32_t bf16_rne_bits(uint32_t f) { return (f + 0x7fffu + ((f >> 16) & 1u)) >> 16; }
-
-__device__ __forceinline__ uint32_t perm(uint32_t s0, uint32_t s1, uint32_t sel) {
-  return __builtin_amdgcn_perm(s0, s1, sel);
-}
-
-// Byte planes of the 16 unscaled bf16 code values: lo[q] byte e = low byte
-// of the value of code 4 q + e, hi[q] byte e = high byte.
-struct UnscaledPlanes {
-  uint32_t lo[4], hi[4];
-};
-template <class CT>
-constexpr UnscaledPlanes make_planes() {
-  UnscaledPlanes p{};
-  for (int q = 0; q < 4; ++q) {
-    uint32_t lo = 0, hi = 0;
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t b = bf16_rne_bits(CT::table.level[4 * q + e]);
-      lo |= (b & 0xffu) << (8 * e);
-      hi |= ((b >> 8) & 0xffu) << (8 * e);
-    }
-    p.lo[q] = lo;
-    p.hi[q] = hi;
-  }
-  return p;
-}
-template <class CT>
-struct Planes {
-  static constexpr UnscaledPlanes v = make_planes<CT>();
-};
-
-// Eight codes (nibble order) -> four packed bf16 level pairs, by permutes.
-template <class CT>
-__device__ __forceinline__ u32x4 levels8_perm(uint32_t w) {
-  constexpr UnscaledPlanes kPlanes = Planes<CT>::v;
-  const uint32_t se = w & 0x07070707u;
-  const uint32_t so = (w >> 4) & 0x07070707u;
-  const uint32_t me = perm(0u, 0u, ((w >> 3) & 0x01010101u) | 0x0c0c0c0cu);
-  const uint32_t mo = perm(0u, 0u, ((w >> 7) & 0x01010101u) | 0x0c0c0c0cu);
-  const uint32_t le = (me & perm(kPlanes.lo[3], kPlanes.lo[2], se)) |
-                      (~me & perm(kPlanes.lo[1], kPlanes.lo[0], se));
-  const uint32_t he = (me & perm(kPlanes.hi[3], kPlanes.hi[2], se)) |
-                      (~me & perm(kPlanes.hi[1], kPlanes.hi[0], se));
-  const uint32_t lo = (mo & perm(kPlanes.lo[3], kPlanes.lo[2], so)) |
-                      (~mo & perm(kPlanes.lo[1], kPlanes.lo[0], so));
-  const uint32_t ho = (mo & perm(kPlanes.hi[3], kPlanes.hi[2], so)) |
-                      (~mo & perm(kPlanes.hi[1], kPlanes.hi[0], so));
-  const uint32_t t0 = perm(he, le, 0x05010400u);
-  const uint32_t t1 = perm(he, le, 0x07030602u);
-  const uint32_t u0 = perm(ho, lo, 0x05010400u);
-  const uint32_t u1 = perm(ho, lo, 0x07030602u);
-  return u32x4{perm(u0, t0, 0x05040100u), perm(u0, t0, 0x07060302u), perm(u1, t1, 0x05040100u),
-               perm(u1, t1, 0x07060302u)};
-}
 
 // Eight codes -> four packed bf16 level pairs, by a byte-indexed LDS table.
 // The table is replicated 16 times, entry b of copy l at word 16 b + l, and
@@ -167,9 +110,6 @@ struct GemvArgs {
   uint16_t* U_out;  // nullable, bf16 [M][r]
 };
 
-#ifndef QN_GEMV_PERM
-#define QN_GEMV_PERM false
-#endif
 #ifndef QN_GEMV_PD
 #define QN_GEMV_PD 3
 #endif
@@ -185,7 +125,7 @@ __host__ __device__ constexpr int64_t gemv_lds_words(int G, int KW, int64_t M, i
   return kLutWords + M * r + (chat > red ? chat : red);
 }
 
-template <int G, int KW, int PD, bool kPerm, class CT>
+template <int G, int KW, int PD, class CT>
 __global__ __launch_bounds__(64 * KW) void k_qgemv(GemvArgs p) {
   constexpr int NT = 64 * KW;
   extern __shared__ float lds[];
@@ -270,14 +210,8 @@ __global__ __launch_bounds__(64 * KW) void k_qgemv(GemvArgs p) {
       c[3] = s13[1];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        u32x4 w0, w1;
-        if (kPerm) {
-          w0 = levels8_perm<CT>(c[2 * h]);
-          w1 = levels8_perm<CT>(c[2 * h + 1]);
-        } else {
-          w0 = levels8_lut(c[2 * h], lut + i16);
-          w1 = levels8_lut(c[2 * h + 1], lut + i16);
-        }
+        const u32x4 w0 = levels8_lut(c[2 * h], lut + i16);
+        const u32x4 w1 = levels8_lut(c[2 * h + 1], lut + i16);
         f32x4 pb = mfma16(as_bf16x8(S.x[2 * h]), as_bf16x8(w0), f32x4{0.f, 0.f, 0.f, 0.f});
         pb = mfma16(as_bf16x8(S.x[2 * h + 1]), as_bf16x8(w1), pb);
         const float chat = (h && tail) ? 0.0f : crow_t[g][kb + h];
@@ -296,11 +230,9 @@ __global__ __launch_bounds__(64 * KW) void k_qgemv(GemvArgs p) {
   // constants fl32(q8 * step) of rows n0 .. n0 + 16 G - 1, and the U sums of
   // the partial slices written by the previous launch on this stream.  All
   // of a thread's loads are issued before any is used (one latency).
-  if (!kPerm) {
-    for (int e = tid; e < kLutWords; e += NT) {
-      const int b = e >> 4;  // copy e % 16 of entry b
-      lut[e] = pack_bf16x2(code_value<CT>(b & 15), code_value<CT>(b >> 4));
-    }
+  for (int e = tid; e < kLutWords; e += NT) {
+    const int b = e >> 4;  // copy e % 16 of entry b
+    lut[e] = pack_bf16x2(code_value<CT>(b & 15), code_value<CT>(b >> 4));
   }
   {
     // The workgroup's constants are the contiguous q8 range starting at
@@ -426,10 +358,6 @@ size_t gemv_workspace_bytes(int64_t M, int32_t r, int64_t K) {
   return (size_t)gemv_lora_slices(K) * M * r * sizeof(float);
 }
 
-#ifndef QN_GEMV_G7
-#define QN_GEMV_G7 1
-#endif
-
 template <int G>
 hipError_t launch_qgemv_g(const GemvArgs& a, int code, hipStream_t stream) {
   constexpr int KW = 8, PD = QN_GEMV_PD;
@@ -440,7 +368,7 @@ hipError_t launch_qgemv_g(const GemvArgs& a, int code, hipStream_t stream) {
     for (int id = 0; id < 4; ++id) {
       const hipError_t e = with_code(id, [](auto ct) {
         return hipFuncSetAttribute(
-            reinterpret_cast<const void*>(&k_qgemv<G, KW, PD, QN_GEMV_PERM, decltype(ct)>),
+            reinterpret_cast<const void*>(&k_qgemv<G, KW, PD, decltype(ct)>),
             hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
       });
       if (r == hipSuccess) r = e;
@@ -451,7 +379,7 @@ hipError_t launch_qgemv_g(const GemvArgs& a, int code, hipStream_t stream) {
   const size_t lds = 4 * (size_t)gemv_lds_words(G, KW, a.M, a.r, a.K / 64);
   const dim3 grid((unsigned)((a.N + 16 * G - 1) / (16 * G)));
   with_code(code, [&](auto ct) {
-    hipLaunchKernelGGL((k_qgemv<G, KW, PD, QN_GEMV_PERM, decltype(ct)>), grid, dim3(64 * KW), lds,
+    hipLaunchKernelGGL((k_qgemv<G, KW, PD, decltype(ct)>), grid, dim3(64 * KW), lds,
                        stream, a);
     return 0;
   });
@@ -487,7 +415,7 @@ hipError_t launch_qgemv(const Nf4View& w, const uint16_t* X, int64_t M, const ui
     return n;
   }();
   const int64_t groups = (w.N + 15) / 16;
-  const bool g7 = QN_GEMV_G7 && cus > 0 && groups % (7 * (int64_t)cus) == 0 &&
+  const bool g7 = cus > 0 && groups % (7 * (int64_t)cus) == 0 &&
                   4 * gemv_lds_words(7, 8, M, r, kblocks) <= 96 * 1024;
   const bool g1 = !g7 && M <= 2 && cus > 0 && groups <= 2 * (int64_t)cus;
   e = g7   ? launch_qgemv_g<7>(a, w.code, stream)
