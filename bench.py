@@ -588,6 +588,10 @@ def qn_ws(L, M, N, K, r):
     return int(L.qlora_workspace_size(M, N, K, r, 0))
 
 
+CPU_BASELINE_MIN_S = 10.0
+CPU_BASELINE_MAX_PASSES = 20
+
+
 def cpu_baseline(host_inputs, wl, rows):
     """The CPU oracle, as it stands, on a bounded sample of the same workload:
     dequantize every weight from its (oracle-made) NF4 state, then fp64
@@ -600,18 +604,24 @@ def cpu_baseline(host_inputs, wl, rows):
         states.append((nf4.quantize(inp.W), spec))
     cores = len(os.sched_getaffinity(0))
     flops = 0.0
+    passes = 0
     t0 = time.perf_counter()
-    for inp, (st, spec) in zip(host_inputs, states):
-        N, K = spec.N, spec.K
-        Wh = nf4.bf16_bits_to_f32(nf4.dequantize(*st, N, K))
-        X = nf4.bf16_bits_to_f32(inp.X[:rows])
-        dY = nf4.bf16_bits_to_f32(inp.dY[:rows])
-        A = nf4.bf16_bits_to_f32(inp.A)
-        B = nf4.bf16_bits_to_f32(inp.B)
-        linear.forward(X, Wh, A, B, wl.s)
-        linear.backward(X, dY, Wh, A, B, wl.s)
-        flops += 4.0 * rows * N * K + 6.0 * rows * wl.r * (N + K)
-    dt = time.perf_counter() - t0
+    # whole passes over the sample until at least MIN_S seconds of CPU work
+    while True:
+        for inp, (st, spec) in zip(host_inputs, states):
+            N, K = spec.N, spec.K
+            Wh = nf4.bf16_bits_to_f32(nf4.dequantize(*st, N, K))
+            X = nf4.bf16_bits_to_f32(inp.X[:rows])
+            dY = nf4.bf16_bits_to_f32(inp.dY[:rows])
+            A = nf4.bf16_bits_to_f32(inp.A)
+            B = nf4.bf16_bits_to_f32(inp.B)
+            linear.forward(X, Wh, A, B, wl.s)
+            linear.backward(X, dY, Wh, A, B, wl.s)
+            flops += 4.0 * rows * N * K + 6.0 * rows * wl.r * (N + K)
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt >= CPU_BASELINE_MIN_S or passes >= CPU_BASELINE_MAX_PASSES:
+            break
     try:
         from threadpoolctl import threadpool_info
         info = [d for d in threadpool_info() if d.get("user_api") == "blas"]
@@ -622,9 +632,9 @@ def cpu_baseline(host_inputs, wl, rows):
     return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle",
             "sample": (f"{wl.name}: all {len(wl.weights)} weights, first {rows} of {wl.M[0]} "
-                       f"token rows; oracle dequantize + fp64 forward + backward "
-                       f"({dt:.1f} s, numpy BLAS {blas}, {threads} threads of {cores} "
-                       f"host cores)"),
+                       f"token rows; oracle dequantize + fp64 forward + backward, "
+                       f"{passes} passes ({dt:.1f} s, numpy BLAS {blas}, {threads} threads "
+                       f"of {cores} host cores)"),
             "seconds": round(dt, 2)}
 
 
