@@ -112,7 +112,8 @@ def test_identity_input_returns_dequantized_weight(code, M):
 
 @pytest.mark.parametrize("code", CODES)
 @pytest.mark.parametrize("shape", [(256, 1024, 1024, 8), (300, 136, 192, 8), (513, 520, 1088, 72),
-                                   (1, 1024, 2048, 16), (16, 1032, 1024, 16), (9, 2056, 4160, 64)])
+                                   (1, 1024, 2048, 16), (16, 1032, 1024, 16), (9, 2056, 4160, 64),
+                                   (4, 28672, 192, 8)])
 def test_layer_parity(code, shape):
     M, N, K, r = shape
     say(f"[{code} layer] M={M} N={N} K={K} r={r}")
