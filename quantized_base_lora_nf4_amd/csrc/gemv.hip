@@ -8,9 +8,9 @@
 // lane operations per weight, so the codes are expanded to *unscaled* bf16
 // levels (a 256-entry byte table in LDS, one lookup per code byte), the
 // MFMA sums one 64-element block at a time, and the block constant
-// fl32(q8 * step) multiplies that block's fp32 partial sum.  The result differs from using the bf16-rounded dequantized
-// weight only by the bf16 rounding of the levels (relative 2^-9 per weight);
-// accumulation is fp32.
+// fl32(q8 * step) multiplies that block's fp32 partial sum.  The result
+// differs from using the bf16-rounded dequantized weight only by the bf16
+// rounding of the levels (relative 2^-9 per weight); accumulation is fp32.
 //
 // Two launches per call:
 //  1. k_lora_down_part: fp32 partial sums of U = X A^T over S slices of K.
