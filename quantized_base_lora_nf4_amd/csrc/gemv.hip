@@ -276,16 +276,19 @@ __global__ __launch_bounds__(64 * KW) void k_qgemv(GemvArgs p) {
   }
   {
     const int64_t ur = (int64_t)M * p.r;
-    constexpr int kMaxSlices = 8;
+    // slices in order, eight loads in flight at a time
+    constexpr int kBatch = 8;
     for (int64_t e = tid; e < ur; e += NT) {
-      float v[kMaxSlices];
-#pragma unroll
-      for (int sp = 0; sp < kMaxSlices; ++sp)
-        v[sp] = p.upart[(int64_t)(sp < p.us ? sp : 0) * ur + e];
       float u = 0.0f;
+      for (int sp0 = 0; sp0 < p.us; sp0 += kBatch) {
+        float v[kBatch];
 #pragma unroll
-      for (int sp = 0; sp < kMaxSlices; ++sp)
-        if (sp < p.us) u += v[sp];
+        for (int i = 0; i < kBatch; ++i)
+          v[i] = p.upart[(int64_t)(sp0 + i < p.us ? sp0 + i : sp0) * ur + e];
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i)
+          if (sp0 + i < p.us) u += v[i];
+      }
       ush[e] = u;
     }
   }
@@ -346,16 +349,19 @@ bool gemv_fits(int64_t M, int32_t r, int64_t K) {
   return M <= kGemvMaxM && 4 * gemv_lds_words(2, 8, M, r, K / 64) <= 96 * 1024;
 }
 
-int gemv_lora_slices(int64_t K) {
-  // slices of at least 1024 columns, at most 8 of them (k_qgemv sums them)
-  int64_t s = K / 1024;
-  if (s > 8) s = 8;
+int gemv_lora_slices(int64_t M, int32_t r, int64_t K) {
+  // Slices of at least 256 columns (one batch of loads per wave), at most
+  // 32, and at most 8192 partial values in all: k_qgemv's prologue sums
+  // them, M r values per slice.
+  int64_t s = K / 256;
+  if (s > 32) s = 32;
+  while (s > 1 && s * M * r > 8192) s /= 2;
   if (s < 1) s = 1;
   return (int)s;
 }
 
 size_t gemv_workspace_bytes(int64_t M, int32_t r, int64_t K) {
-  return (size_t)gemv_lora_slices(K) * M * r * sizeof(float);
+  return (size_t)gemv_lora_slices(M, r, K) * M * r * sizeof(float);
 }
 
 template <int G>
@@ -389,7 +395,7 @@ hipError_t launch_qgemv_g(const GemvArgs& a, int code, hipStream_t stream) {
 hipError_t launch_qgemv(const Nf4View& w, const uint16_t* X, int64_t M, const uint16_t* A,
                         const uint16_t* B, int32_t r, float s, uint16_t* Y, uint16_t* U_out,
                         float* upart, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
-  const int us = gemv_lora_slices(w.K);
+  const int us = gemv_lora_slices(M, r, w.K);
   const int64_t slice = (w.K / us + 31) / 32 * 32;
   dim3 gu((unsigned)((w.K + slice - 1) / slice), (unsigned)((r + 63) / 64));
   hipLaunchKernelGGL(k_lora_down_part, gu, dim3(256), 0, stream, X, M, A, r, w.K, slice, upart);
