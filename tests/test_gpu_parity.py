@@ -166,6 +166,28 @@ def test_layer_parity(shape):
     assert_close("dB", got["dB"], dB)
 
 
+@pytest.mark.parametrize("shape", [(3, 8, 1 << 22, 2),     # K = QLORA_LINEAR_MAX_NK: 8 MB rows
+                                   (2, 1 << 22, 64, 1)])   # N = QLORA_LINEAR_MAX_NK
+def test_layer_parity_at_the_largest_N_and_K(shape):
+    """The largest N and K the layer calls accept: every 32-bit offset the
+    kernels form (a 256-row tile of 8 MB rows spans just under 2 GiB) and
+    the tile path a few tokens take when K is past the few-token kernel's
+    tables."""
+    M, N, K, r = shape
+    say(f"[layer max] M={M} N={N} K={K} r={r}")
+    inp = _layer(M, N, K, r)
+    w = gpu_quantize(inp.W)
+    got = _gpu_fwd_bwd(inp, w)
+    Wh = oracle_what(inp.W)
+    X, A, B, dY = f32(inp.X), f32(inp.A), f32(inp.B), f32(inp.dY)
+    assert_close("Y", got["Y"], linear.forward(X, Wh, A, B, inp.s))
+    assert_close("U", got["U"], linear.lora_down(X, A))
+    dX, dA, dB = linear.backward(X, dY, Wh, A, B, inp.s)
+    assert_close("dX", got["dX"], dX)
+    assert_close("dA", got["dA"], dA)
+    assert_close("dB", got["dB"], dB)
+
+
 def _poisoned_copy(w, rows=64):
     """The same weight state at the start of larger buffers whose bytes past
     the end hold garbage (codes 0xFF, constants 255, steps NaN), `rows`
