@@ -124,6 +124,8 @@ LSHAPES = [  # (M, N, K, r)
     (7, 28672, 576, 8),
     (2, 1000, 1088, 8),        # two tokens: one row group per workgroup, ragged rows, odd block count
     (3, 64, 41024, 4),         # few tokens, K past the few-token kernel's LDS tables: tile path
+    (70000, 136, 192, 8),      # 274 row tiles (ragged, not a multiple of 8): the XCD tile order's
+                               # remainder, and 70000-long contractions for dA and dB
 ]
 
 
