@@ -273,11 +273,30 @@ def test_backward_without_dx_and_without_saved_u():
     assert_close("dB", f32(host_u16(dB)), rdB)
 
 
-def test_layer_is_deterministic():
-    inp = _layer(300, 520, 1088, 16)
+@pytest.mark.parametrize("shape", [(300, 520, 1088, 16),   # tile path
+                                   (4, 28672, 192, 8),     # few tokens, 7 row groups per workgroup
+                                   (1, 1024, 2048, 16)])   # few tokens, 1 row group per workgroup
+def test_layer_is_deterministic(shape):
+    inp = _layer(*shape)
     w = gpu_quantize(inp.W)
     a = _gpu_fwd_bwd(inp, w)
     b = _gpu_fwd_bwd(inp, w)
+    for k in a:
+        assert np.array_equal(a[k].view(np.uint32), b[k].view(np.uint32)), k
+
+
+@pytest.mark.parametrize("shape", [(300, 520, 1088, 16), (4, 1024, 2048, 16)])
+def test_layer_on_a_side_stream_matches_the_default_stream(shape):
+    """Every launch goes to the stream the caller passes (here torch's
+    current stream inside a stream context): bit-identical results."""
+    inp = _layer(*shape)
+    w = gpu_quantize(inp.W)
+    a = _gpu_fwd_bwd(inp, w)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        b = _gpu_fwd_bwd(inp, w)
+    torch.cuda.synchronize()
     for k in a:
         assert np.array_equal(a[k].view(np.uint32), b[k].view(np.uint32)), k
 
