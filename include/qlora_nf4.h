@@ -75,8 +75,12 @@
  *     global state: calls are reentrant and thread-safe.  Calls that share
  *     a workspace must be ordered (same stream).
  *   - Every call validates its arguments before launching anything and
- *     returns a status code (QLORA_OK or a negative error, see below); on
- *     error nothing has been enqueued and no output has been touched.
+ *     returns a status code (QLORA_OK or a negative error, see below).  On
+ *     an argument error (QLORA_ERR_INVALID, _UNSUPPORTED, _WORKSPACE)
+ *     nothing has been enqueued and no output has been touched.
+ *     QLORA_ERR_LAUNCH means a launch failed after the arguments were
+ *     accepted: launches of the same call made before it stay enqueued, and
+ *     the outputs are undefined.
  *   - Results are deterministic: the same inputs give bit-identical outputs.
  */
 #ifndef QLORA_NF4_H_

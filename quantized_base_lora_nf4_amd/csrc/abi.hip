@@ -125,7 +125,7 @@ const char* qlora_status_str(int32_t status) {
     case QLORA_OK: return "ok";
     case QLORA_ERR_INVALID: return "invalid argument (null pointer, size or alignment)";
     case QLORA_ERR_UNSUPPORTED:
-      return "unsupported configuration (block sizes must be 64 and 256, code type NF4 or FP4)";
+      return "unsupported configuration (block size, double-quantization block size or code type)";
     case QLORA_ERR_WORKSPACE: return "workspace too small";
     case QLORA_ERR_LAUNCH: return "HIP launch error";
     case QLORA_ERR_INFEASIBLE: return "no choice fits the budget";
@@ -193,18 +193,27 @@ inline hipError_t record(hipEvent_t ev, hipStream_t stream) {
   return ev ? hipEventRecord(ev, stream) : hipSuccess;
 }
 
+// Every check of the forward call's arguments except the workspace.
+int32_t check_fwd(const nf4_tensor_t* w, const uint16_t* X, int64_t M, const uint16_t* A,
+                  const uint16_t* B, int32_t r, float s, const uint16_t* Y,
+                  const uint16_t* U_out) {
+  if (!nf4_ok(w) || !X || !A || !B || !Y) return QLORA_ERR_INVALID;
+  const int32_t sup = nf4_supported(w);
+  if (sup != QLORA_OK) return sup;
+  if (!sizes_ok(M, w->N, w->K, r) || !isfinite(s) || !state_fits(w)) return QLORA_ERR_INVALID;
+  if (!aligned16(w->codes) || !aligned16(w->q8) || !aligned16(w->step) || !aligned16(X) ||
+      !aligned16(A) || !aligned16(B) || !aligned16(Y) || (U_out && !aligned16(U_out)))
+    return QLORA_ERR_INVALID;
+  return QLORA_OK;
+}
+
 int32_t linear_fwd(const nf4_tensor_t* w, const uint16_t* X, int64_t M, const uint16_t* A,
                    const uint16_t* B, int32_t r, float s, uint16_t* Y, uint16_t* U_out, void* ws,
                    size_t ws_bytes, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
-  if (!nf4_ok(w) || !X || !A || !B || !Y || !ws) return QLORA_ERR_INVALID;
-  const int32_t sup = nf4_supported(w);
-  if (sup != QLORA_OK) return sup;
+  const int32_t chk = check_fwd(w, X, M, A, B, r, s, Y, U_out);
+  if (chk != QLORA_OK) return chk;
+  if (!ws || !aligned16(ws)) return QLORA_ERR_INVALID;
   const int64_t N = w->N, K = w->K;
-  if (!sizes_ok(M, N, K, r) || !isfinite(s) || !state_fits(w)) return QLORA_ERR_INVALID;
-  if (!aligned16(w->codes) || !aligned16(w->q8) || !aligned16(w->step) || !aligned16(X) ||
-      !aligned16(A) || !aligned16(B) || !aligned16(Y) || !aligned16(ws) ||
-      (U_out && !aligned16(U_out)))
-    return QLORA_ERR_INVALID;
   const FwdPlan pl = plan_fwd(M, N, K, r);
   if (ws_bytes < pl.total) return QLORA_ERR_WORKSPACE;
 

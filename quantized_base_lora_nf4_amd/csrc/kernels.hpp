@@ -6,7 +6,7 @@
 
 namespace qn {
 
-// ---- nf4_quant.hip ----  (code: CodeNF4::kId or CodeFP4::kId)
+// ---- nf4_quant.hip ----  (code: kId of CodeNF4, CodeFP4, CodeNF3 or CodeNF2)
 hipError_t launch_nf4_quantize(const float* W, int64_t nblocks, uint8_t* codes, uint8_t* q8,
                                float* step, int code, hipStream_t stream);
 hipError_t launch_nf4_dequantize(const uint8_t* codes, const uint8_t* q8, const float* step,
@@ -35,7 +35,7 @@ hipError_t launch_qgemm_bwd(const Nf4View& w, const uint16_t* dY, int64_t M, con
 // ---- gemv.hip: bandwidth-bound forward for M <= 16 ----
 constexpr int kGemvMaxM = 16;
 // Whether launch_qgemv takes these sizes (its per-workgroup table of block
-// constants must fit in LDS: K up to about 24000 at rank 256).
+// constants must fit in LDS: K up to about 32000 at 16 tokens and rank 256).
 bool gemv_fits(int64_t M, int32_t r, int64_t K);
 // Workspace of launch_qgemv: fp32 partial sums of U = X A^T.
 size_t gemv_workspace_bytes(int64_t M, int32_t r, int64_t K);

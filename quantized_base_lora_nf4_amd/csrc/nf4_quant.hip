@@ -64,14 +64,16 @@ __device__ __forceinline__ uint32_t quant_code(float x, const uint2* bucket) {
   return CT::code_of_count(n);
 }
 
-// fl32(a / b) from r = fl32(1 / b): q = fl32(a r) is within an ulp or so;
-// the residual a - b q is exact through the fused multiply-add, and one
-// correction step rounds to the correctly rounded quotient (Markstein's
-// division refinement).  Used for blocks with b >= 2^-80 (no underflow in
-// the residual) and |a| <= b: there it is bit-identical to the IEEE
-// division for every quotient of magnitude 0.01 or more (a host test checks
-// this on random operands); a smaller quotient can be off by an ulp, which
-// cannot move it across a threshold (the smallest has magnitude 0.0398).
+// fl32(a / b) from r = fl32(1 / b): q = fl32(a r) is within two ulps of
+// a / b, the residual e = a - b q comes out of the fused multiply-add with at
+// most a 2^-24 relative error, and one correction step q + e r lands within
+// one ulp of the IEEE quotient (a division refinement in Markstein's form).
+// Used for blocks with 2^-60 <= b <= 2^126 and |a| <= b, where every
+// intermediate near a threshold is a normal number: the outcome then depends
+// only on the mantissas, and a host test checks every divisor mantissa with
+// every dividend whose quotient lies within 4 ulps of any threshold of any
+// code type: the refined quotient is the IEEE one there, so every code is
+// the one the IEEE quotient gives.  Other blocks take the IEEE division.
 __device__ __forceinline__ float div_refined(float a, float b, float r) {
 #pragma clang fp contract(off)
   const float q = a * r;
@@ -108,14 +110,14 @@ __global__ __launch_bounds__(256) void k_nf4_quantize(const float* __restrict__ 
       m = fmaxf(m, __shfl_xor(m, 2, 16));
       m = fmaxf(m, __shfl_xor(m, 1, 16));
       uint32_t c0, c1, c2, c3;
-      if (m >= 0x1p-80f) {
+      if (m >= 0x1p-60f && m <= 0x1p126f) {
         const float r = 1.0f / m;  // IEEE-correct fp32 division
         c0 = quant_code<CT>(div_refined(v[0], m, r), bucket);
         c1 = quant_code<CT>(div_refined(v[1], m, r), bucket);
         c2 = quant_code<CT>(div_refined(v[2], m, r), bucket);
         c3 = quant_code<CT>(div_refined(v[3], m, r), bucket);
       } else if (m > 0.0f) {
-        // tiny block: IEEE-correct fp32 division (the compiler's default)
+        // tiny or huge block: IEEE-correct fp32 division (the compiler's default)
         c0 = quant_code<CT>(v[0] / m, bucket);
         c1 = quant_code<CT>(v[1] / m, bucket);
         c2 = quant_code<CT>(v[2] / m, bucket);

@@ -130,28 +130,92 @@ def workspace_size(M: int, N: int, K: int, r: int, for_bwd: bool) -> int:
     return int(lib().qlora_workspace_size(M, N, K, r, 1 if for_bwd else 0))
 
 
+def _stream_obj(stream):
+    """The torch stream the kernels run on (a torch stream, a raw HIP stream
+    handle, or None for the current stream)."""
+    if stream is None:
+        return torch.cuda.current_stream()
+    if hasattr(stream, "cuda_stream"):
+        return stream
+    return torch.cuda.ExternalStream(int(stream))
+
+
+def _check_tensors(items, device) -> None:
+    """Shapes and dtypes, then devices and layout, of the tensors handed to a
+    layer call: (name, tensor or None, expected shape, 16-bit?) tuples.  The
+    C ABI sees bare pointers, so this is where a wrong shape or a tensor on
+    another device is caught, before any launch."""
+    for name, t, shape, sixteen in items:
+        if t is None:
+            continue
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch tensor")
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+        if sixteen and t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+            raise TypeError(f"{name} must be bf16 (or its 16-bit view), got {t.dtype}")
+    for name, t, _, _ in items:
+        if t is None:
+            continue
+        if not t.is_cuda or t.device != device:
+            raise ValueError(f"{name} is on {t.device}, expected {device}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+
+
+def _check_weight(w: NF4Weight) -> torch.device:
+    if w.code not in CODE_TYPES:
+        raise ValueError(f"unknown code type {w.code!r}")
+    if w.codes.dtype != torch.uint8 or w.q8.dtype != torch.uint8 or w.step.dtype != torch.float32:
+        raise TypeError("codes and q8 must be uint8, step float32")
+    if w.codes.numel() != w.N * w.K * CODE_BITS[w.code] // 8:
+        raise ValueError("codes do not match the weight's shape and code width")
+    if w.q8.numel() != w.N * w.K // BLOCKSIZE or w.step.numel() != -(-w.q8.numel() // DQ_BLOCKSIZE):
+        raise ValueError("q8 / step do not match the weight's shape")
+    return w.codes.device
+
+
+def _check_fwd(w: NF4Weight, X, A, B, Y, U_out, extra=()) -> Tuple[int, int, torch.device]:
+    dev = _check_weight(w)
+    if X.dim() != 2 or A.dim() != 2:
+        raise ValueError("X and A must be 2-D")
+    M, r = X.shape[0], A.shape[0]
+    _check_tensors([("codes", w.codes, w.codes.shape, False), ("q8", w.q8, w.q8.shape, False),
+                    ("step", w.step, w.step.shape, False),
+                    ("X", X, (M, w.K), True), ("A", A, (r, w.K), True), ("B", B, (w.N, r), True),
+                    ("Y", Y, (M, w.N), True), ("U", U_out, (M, r), True),
+                    *[(n, t, shp(M, r), True) for n, t, shp in extra]], dev)
+    return M, r, dev
+
+
 def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> torch.Tensor:
-    if ws is not None and ws.numel() * ws.element_size() >= nbytes:
-        return ws
+    if ws is not None:
+        if not ws.is_cuda or ws.device != device or not ws.is_contiguous():
+            raise ValueError("ws must be a contiguous tensor on the layer's GPU")
+        if ws.numel() * ws.element_size() >= nbytes:
+            return ws
     return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
 
 
 def qlora_linear_fwd(w: NF4Weight, X: torch.Tensor, A: torch.Tensor, B: torch.Tensor, s: float,
                      Y: Optional[torch.Tensor] = None, U_out: Optional[torch.Tensor] = None,
                      ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """Y = X W^T + s (X A^T) B^T.  X [M, K], A [r, K], B [N, r] bf16."""
-    M = X.shape[0]
-    r = A.shape[0]
-    if Y is None:
-        Y = torch.empty(M, w.N, dtype=torch.bfloat16, device=X.device)
-    nbytes = workspace_size(M, w.N, w.K, r, False)
-    ws = _workspace(nbytes, X.device, ws)
+    """Y = X W^T + s (X A^T) B^T.  X [M, K], A [r, K], B [N, r] bf16.
+
+    Buffers allocated here (Y, the workspace) are allocated on the stream the
+    kernels run on, so the caching allocator does not hand them to other
+    streams while those kernels may still use them."""
+    M, r, dev = _check_fwd(w, X, A, B, Y, U_out)
+    st = _stream_obj(stream)
+    with torch.cuda.stream(st):
+        if Y is None:
+            Y = torch.empty(M, w.N, dtype=torch.bfloat16, device=dev)
+        ws = _workspace(workspace_size(M, w.N, w.K, r, False), dev, ws)
     s_ = w.struct()
-    st = lib().qlora_linear_fwd(ctypes.byref(s_), _ptr(_bf16_view(X)), M, _ptr(_bf16_view(A)),
-                                _ptr(_bf16_view(B)), r, float(s), _ptr(_bf16_view(Y)),
-                                _ptr(U_out), _ptr(ws), ws.numel() * ws.element_size(),
-                                _stream(stream))
-    check(st, "qlora_linear_fwd")
+    rc = lib().qlora_linear_fwd(ctypes.byref(s_), _ptr(X), M, _ptr(A), _ptr(B), r, float(s),
+                                _ptr(Y), _ptr(U_out), _ptr(ws), ws.numel() * ws.element_size(),
+                                st.cuda_stream)
+    check(rc, "qlora_linear_fwd")
     return Y
 
 
@@ -159,24 +223,28 @@ def qlora_linear_bwd(w: NF4Weight, X: torch.Tensor, dY: torch.Tensor, A: torch.T
                      B: torch.Tensor, s: float, U: Optional[torch.Tensor] = None,
                      need_dX: bool = True, out: Optional[tuple] = None,
                      ws: Optional[torch.Tensor] = None, stream=None):
-    """Returns (dX or None, dA, dB), all bf16."""
-    M = X.shape[0]
-    r = A.shape[0]
-    dev = X.device
-    if out is None:
-        dX = torch.empty(M, w.K, dtype=torch.bfloat16, device=dev) if need_dX else None
-        dA = torch.empty(r, w.K, dtype=torch.bfloat16, device=dev)
-        dB = torch.empty(w.N, r, dtype=torch.bfloat16, device=dev)
-    else:
+    """Returns (dX or None, dA, dB), all bf16.  Buffers allocated here are
+    allocated on the stream the kernels run on."""
+    extra = [("dY", dY, lambda M, r: (M, w.N))]
+    if out is not None:
         dX, dA, dB = out
-    nbytes = workspace_size(M, w.N, w.K, r, True)
-    ws = _workspace(nbytes, dev, ws)
+        if dA is None or dB is None:
+            raise ValueError("dA and dB outputs are required")
+        extra += [("dX", dX, lambda M, r: (M, w.K)), ("dA", dA, lambda M, r: (r, w.K)),
+                  ("dB", dB, lambda M, r: (w.N, r))]
+    M, r, dev = _check_fwd(w, X, A, B, None, U, extra=extra)
+    st = _stream_obj(stream)
+    with torch.cuda.stream(st):
+        if out is None:
+            dX = torch.empty(M, w.K, dtype=torch.bfloat16, device=dev) if need_dX else None
+            dA = torch.empty(r, w.K, dtype=torch.bfloat16, device=dev)
+            dB = torch.empty(w.N, r, dtype=torch.bfloat16, device=dev)
+        ws = _workspace(workspace_size(M, w.N, w.K, r, True), dev, ws)
     s_ = w.struct()
-    st = lib().qlora_linear_bwd(ctypes.byref(s_), _ptr(_bf16_view(X)), _ptr(_bf16_view(dY)), M,
-                                _ptr(_bf16_view(A)), _ptr(_bf16_view(B)), _ptr(U), r, float(s),
-                                _ptr(dX), _ptr(dA), _ptr(dB), _ptr(ws),
-                                ws.numel() * ws.element_size(), _stream(stream))
-    check(st, "qlora_linear_bwd")
+    rc = lib().qlora_linear_bwd(ctypes.byref(s_), _ptr(X), _ptr(dY), M, _ptr(A), _ptr(B), _ptr(U),
+                                r, float(s), _ptr(dX), _ptr(dA), _ptr(dB), _ptr(ws),
+                                ws.numel() * ws.element_size(), st.cuda_stream)
+    check(rc, "qlora_linear_bwd")
     return dX, dA, dB
 
 

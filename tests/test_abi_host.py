@@ -133,6 +133,32 @@ def test_quantizer_division_refinement_is_correctly_rounded():
         assert bad == 0, (hex(first[0]), hex(first[1]))
 
 
+def test_quantizer_division_refinement_near_every_threshold_is_exact():
+    """Complete check (tests/csrc/division_exhaustive.c explains why it is
+    complete): for every divisor mantissa and every dividend whose quotient
+    lies within 4 ulps of a threshold of any code type, the refined quotient
+    equals the IEEE quotient bit for bit."""
+    ths = sorted({abs(t) for c in ("nf4", "fp4", "nf3", "nf2") for t in qn.code_table(c)[1]})
+    with tempfile.TemporaryDirectory() as d:
+        so = os.path.join(d, "divx.so")
+        src = os.path.join(ROOT, "tests", "csrc", "division_exhaustive.c")
+        subprocess.run(["gcc", "-O2", "-mfma", "-ffp-contract=off", "-fopenmp", "-shared", "-fPIC",
+                        src, "-o", so, "-lm"], check=True)
+        D = ctypes.CDLL(so)
+        D.division_exhaustive.restype = ctypes.c_long
+        D.division_exhaustive.argtypes = [ctypes.c_void_p, ctypes.c_int,
+                                          ctypes.POINTER(ctypes.c_uint32),
+                                          ctypes.POINTER(ctypes.c_long)]
+        T = (ctypes.c_float * len(ths))(*ths)
+        first = (ctypes.c_uint32 * 2)()
+        n = ctypes.c_long(0)
+        bad = D.division_exhaustive(ctypes.cast(T, ctypes.c_void_p), len(ths), first,
+                                    ctypes.byref(n))
+        assert bad == 0, (hex(first[0]), hex(first[1]))
+        # about nine dividends per divisor mantissa and threshold
+        assert n.value > 8 * (1 << 23) * len(ths)
+
+
 def test_storage_bytes_closed_form():
     for N, K in [(1, 64), (3, 1024), (1024, 1024), (22016, 8192), (5120, 13824)]:
         assert qn.lib().nf4_storage_bytes(N, K) == nf4.storage_bytes(N, K)

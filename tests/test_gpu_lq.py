@@ -151,3 +151,36 @@ def test_lq_full_size_q_proj():
     cmis = np.mean(nf4.unpack_codes(codes) != nf4.unpack_codes(oc))
     say(f"[lq] full size: L rel {e_l:.2e} objective {obj:.6g} vs {oobj:.6g} code mismatch {cmis:.1e}")
     assert e_l <= 1e-3 and abs(obj - oobj) <= 1e-3 * oobj and cmis <= 1e-3
+
+
+def test_lq_rank_deficient_weight():
+    """W of exact rank 4 (up to its fp32 rounding) with l = 32: the sampled
+    range has 4 real directions, and the orthonormalization must drop the
+    other 28.  The GPU drops a Cholesky pivot below 1e-10 of the largest
+    diagonal of the Gram matrix, the oracle an eigenvalue below 1e-10 of the
+    largest: different rules that must keep the same span here.  Both
+    low-rank parts then reproduce W to fp32 rounding, and W - L is rounding
+    noise, so the codes of Q are not compared; the objective is (about 1e-6
+    of ||W||)."""
+    N, K, r, l = 300, 640, 12, 32
+    rng = np.random.default_rng(21)
+    W = ((rng.standard_normal((N, 4)) @ rng.standard_normal((4, K))) * 0.01).astype(np.float32)
+    Om = rng.standard_normal((K, l)).astype(np.float32)
+
+    class Inp:
+        pass
+    inp = Inp()
+    inp.W, inp.Omega, inp.r, inp.l = W, Om, r, l
+    res = _run(inp, 1, 2, "svd", "nf4")
+    (codes, q8, step), L1, L2t = _host(res)
+    assert np.all(np.isfinite(L1)) and np.all(np.isfinite(L2t))
+    (oc, oq, os_), oL1, oL2t = lq.decompose(W, Om, r, 1, 2)
+    L, oL = L1 @ L2t.T, oL1 @ oL2t.T
+    Wd = W.astype(np.float64)
+    say(f"[lq] rank 4: |L-W|/|W| {_rel(L, Wd):.2e}  |oL-W|/|W| {_rel(oL, Wd):.2e}  "
+        f"|L-oL|/|oL| {_rel(L, oL):.2e}")
+    assert _rel(oL, Wd) <= 1e-6
+    assert _rel(L, Wd) <= 1e-5 and _rel(L, oL) <= 1e-5
+    obj = lq.objective(W, (codes, q8, step), L1, L2t)
+    assert obj <= 1e-5 * np.linalg.norm(Wd)
+    _check_adapter(res, 0.25)

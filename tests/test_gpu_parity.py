@@ -49,6 +49,11 @@ def _special_weights():
         tie += [lo, np.nextafter(lo, np.float32(np.inf))]
     tie += [1.0, -1.0]
     out["transition_points"] = np.array([tie + tie[::-1]] * 2, np.float32) * np.float32(0.5)
+    # the same values in blocks whose absmax sits at and past the ends of the
+    # quantizer's refined-division range (2^-60 .. 2^126): IEEE division there
+    tp = np.array([tie + tie[::-1]], np.float64)
+    out["transition_points_scaled"] = np.concatenate(
+        [tp * 2.0 ** e for e in (126, 127, -60, -61, -75, -100)]).astype(np.float32)
     row = np.tile(nf4.nf4_levels() * np.float32(2.0 ** -5), 4)
     out["levels_in_order"] = row[None, :].astype(np.float32)
     w = np.zeros((1, 64 * 4), np.float32)
@@ -318,3 +323,49 @@ def test_autograd_function_matches_direct_calls():
     assert_close("dX", X.grad.float().cpu().numpy(), dX)
     assert_close("dA", lay.A.grad.float().cpu().numpy(), dA)
     assert_close("dB", lay.B.grad.float().cpu().numpy(), dB)
+
+
+def test_quantizer_reproduces_the_stored_tiny_fixture():
+    """tests/golden/nf4_tiny_2x128.txt (written by the oracle's script):
+    codes, constants, step and dequantized bits of a hand-built 2x128 weight
+    with a zero, a sine ramp, periodic 5x spikes and one -0.25 outlier."""
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "nf4_tiny_2x128.txt")
+    rows = {l.split(" ", 1)[0]: l.split()[1:] for l in open(path) if not l.startswith("#")}
+    W = np.array([int(t, 16) for t in rows["W"]], np.uint32).view(np.float32).reshape(2, 128)
+    w = gpu_quantize(W)
+    codes, q8, step = nf4_host(w)
+    assert codes.tobytes().hex() == rows["codes"][0]
+    assert q8.tobytes().hex() == rows["q8"][0]
+    assert ["%08x" % v for v in step.view(np.uint32)] == rows["step"]
+    deq = host_u16(qn.nf4_dequantize(w))
+    assert ["%04x" % v for v in deq.reshape(-1)] == rows["deq"]
+
+
+def test_explicit_stream_argument_allocates_on_that_stream():
+    """stream= a side stream (not the current one): the binding allocates Y,
+    the gradients and the workspace on that stream, so memory that the
+    current stream allocates and fills right after the calls, before any
+    synchronization, cannot alias buffers the side stream's kernels still
+    use.  Results are bit-identical to the default-stream run."""
+    inp = _layer(300, 520, 1088, 16)
+    w = gpu_quantize(inp.W)
+    ref = _gpu_fwd_bwd(inp, w)
+    X, A, B, dY = dev_u16(inp.X), dev_u16(inp.A), dev_u16(inp.B), dev_u16(inp.dY)
+    M, r = inp.X.shape[0], inp.A.shape[0]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    U = torch.empty(M, r, dtype=torch.int16, device="cuda")
+    U.record_stream(side)
+    Y = qn.qlora_linear_fwd(w, X, A, B, inp.s, U_out=U, stream=side)
+    dX, dA, dB = qn.qlora_linear_bwd(w, X, dY, A, B, inp.s, U=U, stream=side)
+    # the current stream takes and overwrites memory of the same sizes now
+    junk = [torch.full((n,), -1, dtype=torch.uint8, device="cuda")
+            for n in (qn.workspace_size(M, w.N, w.K, r, True), Y.numel() * 2, dX.numel() * 2,
+                      dA.numel() * 2, dB.numel() * 2)]
+    torch.cuda.synchronize()
+    del junk
+    got = {"Y": f32(host_u16(Y)), "U": f32(host_u16(U)), "dX": f32(host_u16(dX)),
+           "dA": f32(host_u16(dA)), "dB": f32(host_u16(dB))}
+    for k in ref:
+        assert np.array_equal(ref[k].view(np.uint32), got[k].view(np.uint32)), k

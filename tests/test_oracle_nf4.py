@@ -305,3 +305,37 @@ def test_quantizer_output_sizes():
     assert packed.size == 3 * 8192 // 2 and q8.size == 3 * 8192 // 64
     assert step.size == math.ceil(3 * 8192 / 64 / 256)
     assert packed.size + q8.size + 4 * step.size == nf4.storage_bytes(3, 8192)
+
+
+def _tiny_fixture():
+    path = __file__.replace("test_oracle_nf4.py", "golden/nf4_tiny_2x128.txt")
+    rows = {}
+    for line in open(path):
+        if line.startswith("#"):
+            continue
+        key, rest = line.split(" ", 1)
+        rows[key] = rest.split()
+    W = np.array([int(t, 16) for t in rows["W"]], np.uint32).view(np.float32).reshape(2, 128)
+    codes = np.frombuffer(bytes.fromhex(rows["codes"][0]), np.uint8)
+    q8 = np.frombuffer(bytes.fromhex(rows["q8"][0]), np.uint8)
+    step = np.array([int(t, 16) for t in rows["step"]], np.uint32)
+    deq = np.array([int(t, 16) for t in rows["deq"]], np.uint16).reshape(2, 128)
+    return W, codes, q8, step, deq
+
+
+def test_tiny_fixture_is_reproduced_by_the_scalar_quantizer():
+    """The stored 2x128 fixture (written by the vectorized oracle) against the
+    element-by-element pure-Python quantizer and dequantizer: two independent
+    codings of the same definition agree bit for bit."""
+    W, codes, q8, step, deq = _tiny_fixture()
+    sc, sq, ss = scalar.quantize(W.tolist(), [float(v) for v in LEVELS])
+    assert bytes(sc) == codes.tobytes()
+    assert list(sq) == q8.tolist()
+    assert [scalar.f32_bits(v) for v in ss] == step.tolist()
+    sd = scalar.dequantize(sc, sq, ss, [float(v) for v in LEVELS])
+    assert list(sd) == deq.reshape(-1).tolist()
+    # and the vectorized oracle as it stands today
+    pc, pq, ps = nf4.quantize(W)
+    assert np.array_equal(pc, codes) and np.array_equal(pq, q8)
+    assert np.array_equal(ps.view(np.uint32), step)
+    assert np.array_equal(nf4.dequantize(pc, pq, ps, 2, 128), deq)
