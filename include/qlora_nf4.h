@@ -71,9 +71,10 @@
  *     from a caller-provided device workspace sized by
  *     qlora_workspace_size().  Pointers must be 16-byte aligned.
  *   - Work is enqueued on `stream` (0 = the null stream) and is
- *     asynchronous; no call synchronizes.  The library keeps no mutable
- *     global state: calls are reentrant and thread-safe.  Calls that share
- *     a workspace must be ordered (same stream).
+ *     asynchronous; no call synchronizes.  Apart from the fixed scratch
+ *     array of qlora_linear_fwd_noalloc (below), the library keeps no
+ *     mutable global state: calls are reentrant and thread-safe.  Calls that
+ *     share a workspace must be ordered (same stream).
  *   - Every call validates its arguments before launching anything and
  *     returns a status code (QLORA_OK or a negative error, see below).  On
  *     an argument error (QLORA_ERR_INVALID, _UNSUPPORTED, _WORKSPACE)
@@ -256,6 +257,26 @@ int32_t qlora_linear_bwd_ev(const nf4_tensor_t* w, const uint16_t* X,
                             float s, uint16_t* dX, uint16_t* dA, uint16_t* dB,
                             void* ws, size_t ws_bytes, hipStream_t stream,
                             hipEvent_t ev_begin, hipEvent_t ev_end);
+
+/* qlora_linear_fwd_noalloc -- for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): qlora_linear_fwd with the same arguments except the
+ * workspace, and the same result bit for bit.  Its scratch (U and the fp32
+ * partial sums) is a fixed device array of QLORA_NOALLOC_SCRATCH_BYTES that
+ * the library holds on every device it runs on until the process ends; the
+ * call allocates nothing (no hipMalloc, hipFree or allocating library
+ * routine).  Sizes whose workspace (qlora_workspace_size(M, N, K, r, 0))
+ * exceeds the array give QLORA_ERR_WORKSPACE before any launch.  Every call
+ * on one device shares that device's array and leaves its contents behind;
+ * calls that overlap on one device (two host threads, or two streams not
+ * ordered by events) race on it and give undefined results.  The caller
+ * still owns X, A, B, Y and U_out. */
+#define QLORA_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int32_t qlora_linear_fwd_noalloc(const nf4_tensor_t* w, const uint16_t* X,
+                                 int64_t M, const uint16_t* A,
+                                 const uint16_t* B, int32_t r, float s,
+                                 uint16_t* Y, uint16_t* U_out,
+                                 hipStream_t stream);
 
 /* ---- Low-rank plus quantized decomposition (adapter initialization) ----
  *

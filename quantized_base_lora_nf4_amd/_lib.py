@@ -22,6 +22,9 @@ QLORA_CODE_FP4 = 1
 QLORA_CODE_NF3 = 2
 QLORA_CODE_NF2 = 3
 
+# Size of the fixed device scratch of qlora_linear_fwd_noalloc
+QLORA_NOALLOC_SCRATCH_BYTES = 16 << 20
+
 # Every symbol the header declares.
 EXPORTS = (
     "qlora_status_str",
@@ -37,6 +40,7 @@ EXPORTS = (
     "qlora_linear_bwd",
     "qlora_linear_fwd_ev",
     "qlora_linear_bwd_ev",
+    "qlora_linear_fwd_noalloc",
     "qlora_lq_workspace_size",
     "qlora_lq_init",
     "qlora_quant_error_workspace_size",
@@ -106,6 +110,9 @@ def lib() -> ctypes.CDLL:
     L.qlora_linear_fwd_ev.argtypes = L.qlora_linear_fwd.argtypes + [vp, vp]
     L.qlora_linear_bwd_ev.restype = i32
     L.qlora_linear_bwd_ev.argtypes = L.qlora_linear_bwd.argtypes + [vp, vp]
+    L.qlora_linear_fwd_noalloc.restype = i32
+    L.qlora_linear_fwd_noalloc.argtypes = [ctypes.POINTER(Nf4Tensor), vp, i64, vp, vp, i32, f32,
+                                           vp, vp, vp]
     L.qlora_lq_workspace_size.restype = sz
     L.qlora_lq_workspace_size.argtypes = [i64, i64, i32, i32]
     L.qlora_lq_init.restype = i32

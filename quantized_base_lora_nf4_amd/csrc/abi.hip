@@ -6,6 +6,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "kernels.hpp"
 
@@ -330,6 +331,53 @@ int32_t qlora_linear_bwd_ev(const nf4_tensor_t* w, const uint16_t* X, const uint
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Forward pass without a caller workspace: the scratch is this file's fixed
+// device array.  Host code never passes the array's name to a kernel (on the
+// host it is only a stand-in for the symbol); it passes the device address
+// that hipGetSymbolAddress returns, fetched once per device with that device
+// current and cached per device.
+// ---------------------------------------------------------------------------
+namespace {
+
+__device__ __align__(256) unsigned char scratch[QLORA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int32_t scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return QLORA_ERR_LAUNCH;
+  if (dev < 0 || dev >= kMaxDevices) return QLORA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return QLORA_ERR_LAUNCH;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return QLORA_OK;
+}
+
+}  // namespace
+
+extern "C" int32_t qlora_linear_fwd_noalloc(const nf4_tensor_t* w, const uint16_t* X, int64_t M,
+                                            const uint16_t* A, const uint16_t* B, int32_t r,
+                                            float s, uint16_t* Y, uint16_t* U_out,
+                                            hipStream_t stream) {
+  // Argument errors first, as qlora_linear_fwd reports them, so that nothing
+  // else (not even the symbol lookup) happens for a rejected call.
+  const int32_t chk = check_fwd(w, X, M, A, B, r, s, Y, U_out);
+  if (chk != QLORA_OK) return chk;
+  if (plan_fwd(M, w->N, w->K, r).total > QLORA_NOALLOC_SCRATCH_BYTES) return QLORA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  const int32_t st = scratch_address(&ws);
+  if (st != QLORA_OK) return st;
+  return linear_fwd(w, X, M, A, B, r, s, Y, U_out, ws, QLORA_NOALLOC_SCRATCH_BYTES, stream,
+                    nullptr, nullptr);
+}
 
 extern "C" {
 

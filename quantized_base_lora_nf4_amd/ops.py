@@ -219,6 +219,20 @@ def qlora_linear_fwd(w: NF4Weight, X: torch.Tensor, A: torch.Tensor, B: torch.Te
     return Y
 
 
+def qlora_linear_fwd_noalloc(w: NF4Weight, X: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+                             s: float, Y: torch.Tensor, U_out: Optional[torch.Tensor] = None,
+                             stream=None) -> torch.Tensor:
+    """qlora_linear_fwd without a workspace: the library's fixed device
+    scratch is used and nothing is allocated (Y is the caller's)."""
+    M, r, dev = _check_fwd(w, X, A, B, Y, U_out)
+    s_ = w.struct()
+    rc = lib().qlora_linear_fwd_noalloc(ctypes.byref(s_), _ptr(X), M, _ptr(A), _ptr(B), r,
+                                        float(s), _ptr(Y), _ptr(U_out),
+                                        _stream_obj(stream).cuda_stream)
+    check(rc, "qlora_linear_fwd_noalloc")
+    return Y
+
+
 def qlora_linear_bwd(w: NF4Weight, X: torch.Tensor, dY: torch.Tensor, A: torch.Tensor,
                      B: torch.Tensor, s: float, U: Optional[torch.Tensor] = None,
                      need_dX: bool = True, out: Optional[tuple] = None,

@@ -253,6 +253,33 @@ def test_linear_rejects_bad_arguments_without_launching():
                               FAKE, FAKE, FAKE, needb, None) == _lib.QLORA_ERR_UNSUPPORTED
 
 
+def test_noalloc_forward_rejects_bad_arguments_and_oversized_calls_without_launching():
+    """The forward without a workspace checks its arguments as the plain
+    forward does, and rejects sizes whose workspace exceeds its fixed scratch
+    (QLORA_ERR_WORKSPACE) before it touches a device."""
+    L = qn.lib()
+
+    def fwd(w=None, X=FAKE, M=32, r=8, s=1.0, Y=FAKE):
+        w = w or _w(64, 128)
+        return L.qlora_linear_fwd_noalloc(ctypes.byref(w), X, M, FAKE, FAKE, r, s, Y, None, None)
+    assert fwd(X=None) == _lib.QLORA_ERR_INVALID
+    assert fwd(Y=None) == _lib.QLORA_ERR_INVALID
+    assert fwd(M=0) == _lib.QLORA_ERR_INVALID
+    assert fwd(r=300) == _lib.QLORA_ERR_INVALID
+    assert fwd(X=FAKE + 2) == _lib.QLORA_ERR_INVALID
+    assert fwd(s=float("inf")) == _lib.QLORA_ERR_INVALID
+    assert fwd(w=_w(64, 128, bs=128)) == _lib.QLORA_ERR_UNSUPPORTED
+    # the largest token count whose workspace fits the scratch, and one past it
+    N, K, r = 64, 128, 256
+    cap = _lib.QLORA_NOALLOC_SCRATCH_BYTES
+    lo, hi = 1, 1 << 20
+    while hi - lo > 1:
+        mid = (lo + hi) // 2
+        lo, hi = (mid, hi) if qn.workspace_size(mid, N, K, r, False) <= cap else (lo, mid)
+    assert qn.workspace_size(lo, N, K, r, False) <= cap < qn.workspace_size(hi, N, K, r, False)
+    assert fwd(w=_w(N, K), M=hi, r=r) == _lib.QLORA_ERR_WORKSPACE
+
+
 @pytest.mark.parametrize("seed", range(12))
 def test_ilp_plan_matches_bruteforce(seed):
     from oracle import ilp

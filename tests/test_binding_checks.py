@@ -47,6 +47,14 @@ def test_forward_rejects_host_tensors():
         qn.qlora_linear_fwd(_weight(), _bf(M, K), _bf(R, K), _bf(N, R), 2.0, Y=_bf(M, N))
 
 
+def test_noalloc_forward_rejects_host_tensors_and_shapes():
+    with pytest.raises(ValueError, match="Y has shape"):
+        qn.qlora_linear_fwd_noalloc(_weight(), _bf(M, K), _bf(R, K), _bf(N, R), 2.0,
+                                    Y=_bf(M, N + 8))
+    with pytest.raises(ValueError, match="is on cpu"):
+        qn.qlora_linear_fwd_noalloc(_weight(), _bf(M, K), _bf(R, K), _bf(N, R), 2.0, Y=_bf(M, N))
+
+
 @pytest.mark.parametrize("bad", ["dY", "dX", "dA", "dB"])
 def test_backward_rejects_a_wrong_shape(bad):
     out = {"dX": _bf(M, K), "dA": _bf(R, K), "dB": _bf(N, R)}
