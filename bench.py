@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--ilp-only", action="store_true",
                     help="only time the configuration error table and plans (the extra "
                          "'ilp') and print it")
+    ap.add_argument("--gemv-only", action="store_true",
+                    help="only time the few-token forward and the quantizer (the extras "
+                         "'gemv', 'quantize', 'code_types') and print them")
     return ap.parse_args()
 
 
@@ -70,6 +73,7 @@ class HipEvents:
                                                 ctypes.c_void_p]
         self.rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
         self.rt.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.rt.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
 
     def create(self):
         e = ctypes.c_void_p()
@@ -131,6 +135,17 @@ def main():
         print(json.dumps({"lq_init": run_lq(qn, torch)} if args.lq_only else
                          {"ilp": run_ilp(qn, torch)}))
         return
+    if args.gemv_only:
+        import quantized_base_lora_nf4_amd as qn
+        qn.lib()
+        ev = HipEvents()
+        dev = "cuda"
+
+        def d16(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+        print(json.dumps(run_extras(qn, qn.lib(), ev, torch, dev,
+                                    torch.cuda.current_stream().cuda_stream, d16)))
+        return
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
@@ -140,142 +155,47 @@ def main():
         print(json.dumps({"copy_bytes": 1 << 30, "launches": 4}))
         return
     import quantized_base_lora_nf4_amd as qn
-    from quantized_base_lora_nf4_amd._lib import check
     import workloads as wl_mod
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     qn.lib()
     wl = {w.name: w for w in wl_mod.WORKLOADS}[args.workload]
     assert not wl.fwd_only, "the headline workload is forward + backward"
-    M, r, s = wl.M[0], wl.r, wl.s
     dev = "cuda"
-    stream = torch.cuda.current_stream()
-    sp = stream.cuda_stream
+    sp = torch.cuda.current_stream().cuda_stream
     L = qn.lib()
     ev = HipEvents()
 
     def d16(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
 
-    # ---- inputs (seeded, host-generated, then resident in HBM) ----
-    layers = []
-    host_inputs = []
-    for wi, spec in enumerate(wl.weights):
-        inp = wl_mod.draw_workload_weight(wl, wi)
-        host_inputs.append(inp)
-        W = torch.from_numpy(inp.W).to(dev)
-        w = qn.nf4_quantize(W)
-        N, K = spec.N, spec.K
-        t = dict(spec=spec, w=w, Wf32=W, X=d16(inp.X), dY=d16(inp.dY), A=d16(inp.A), B=d16(inp.B),
-                 U=torch.empty(M, r, dtype=torch.int16, device=dev),
-                 Y=torch.empty(M, N, dtype=torch.int16, device=dev),
-                 dX=torch.empty(M, K, dtype=torch.int16, device=dev),
-                 dA=torch.empty(r, K, dtype=torch.int16, device=dev),
-                 dB=torch.empty(N, r, dtype=torch.int16, device=dev))
-        t["wsf"] = torch.empty(qn.workspace_size(M, N, K, r, False), dtype=torch.uint8, device=dev)
-        t["wsb"] = torch.empty(qn.workspace_size(M, N, K, r, True), dtype=torch.uint8, device=dev)
-        t["st"] = w.struct()
-        # one set of 4 events per timed step: begin/end of the dominant
-        # forward kernel and of the dominant backward kernel
-        t["ev"] = [[ev.create() for _ in range(4)] for _ in range(args.steps)]
-        layers.append(t)
-    torch.cuda.synchronize()
-
-    def p(x):
-        return x.data_ptr() if x is not None else None
-
-    def step(i):
-        for t in layers:
-            timed = i is not None and i % args.events_every == 0
-            e = t["ev"][i] if timed else [None] * 4
-            check(L.qlora_linear_fwd_ev(ctypes.byref(t["st"]), p(t["X"]), M, p(t["A"]), p(t["B"]), r,
-                                        s, p(t["Y"]), p(t["U"]), p(t["wsf"]), t["wsf"].numel(), sp,
-                                        e[0], e[1]), "fwd")
-            check(L.qlora_linear_bwd_ev(ctypes.byref(t["st"]), p(t["X"]), p(t["dY"]), M, p(t["A"]),
-                                        p(t["B"]), p(t["U"]), r, s, p(t["dX"]), p(t["dA"]),
-                                        p(t["dB"]), p(t["wsb"]), t["wsb"].numel(), sp, e[2], e[3]),
-                  "bwd")
-
-    for _ in range(args.warmup):
-        step(None)
-    torch.cuda.synchronize()
-
-    # ---- timed region: exactly `steps` steps, kernel events recorded live ----
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t0.record()
-    for i in range(args.steps):
-        step(i)
-    t1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_total = t0.elapsed_time(t1)
-    ms_step = ms_total / args.steps
-
-    kt = {"fwd": [0.0, 0], "bwd": [0.0, 0]}  # summed kernel time (ms), launches
-    per_launch = {"fwd": [], "bwd": []}      # per layer and step (us)
-    for t in layers:
-        lf, lb = [], []
-        for i, e in enumerate(t["ev"]):
-            if i % args.events_every:
-                continue
-            f_ms, b_ms = ev.elapsed_ms(e[0], e[1]), ev.elapsed_ms(e[2], e[3])
-            kt["fwd"][0] += f_ms
-            kt["fwd"][1] += 1
-            kt["bwd"][0] += b_ms
-            kt["bwd"][1] += 1
-            lf.append(f_ms * 1e3)
-            lb.append(b_ms * 1e3)
-        per_launch["fwd"].append(lf)
-        per_launch["bwd"].append(lb)
-
-    flops_step = 0.0
-    flops_fwd_kernel = 0.0
-    flops_bwd_kernel = 0.0
-    for t in layers:
-        N, K = t["spec"].N, t["spec"].K
-        flops_step += 4.0 * M * N * K + 6.0 * M * r * (N + K)
-        flops_fwd_kernel += 2.0 * M * N * (K + r)      # X W^T + (sU) B^T
-        flops_bwd_kernel += 2.0 * M * K * (N + r)      # dY W + dU A
-    tflops = flops_step / (ms_step * 1e-3) / 1e12
-
-    fwd_ms = kt["fwd"][0] / max(1, kt["fwd"][1]) * len(layers)   # per step
-    bwd_ms = kt["bwd"][0] / max(1, kt["bwd"][1]) * len(layers)
-    fwd_tf = flops_fwd_kernel / (fwd_ms * 1e-3) / 1e12
-    bwd_tf = flops_bwd_kernel / (bwd_ms * 1e-3) / 1e12
-    # dominant kernel = the one with the larger share of the step
-    if bwd_ms >= fwd_ms:
-        dom, dom_tf, dom_us = "k_qgemm_bwd", bwd_tf, bwd_ms / len(layers) * 1e3
-    else:
-        dom, dom_tf, dom_us = "k_qgemm_fwd", fwd_tf, fwd_ms / len(layers) * 1e3
+    # ---- headline: the fused step on rotated weight copies (cold Infinity
+    # Cache), inputs resident in HBM; kernel events recorded live ----
+    fx = FusedWorkload(qn, torch, ev, wl, d16, dev, rotate=True)
+    head = fx.run(args.steps, args.warmup, args.events_every, sp)
+    M, r = wl.M[0], wl.r
     src_hash = kernel_source_hash(["qgemm.hip", "common.hpp"])
-    roofline = {
-        "bound": "mfma", "kernel": dom, "achieved": round(dom_tf, 1),
-        "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-        "frac": round(dom_tf / MFMA_BF16_PEAK_TFLOPS, 4),
-        "traffic": load_traffic(dom, wl.name, src_hash),
-        "avg_launch_us": round(dom_us, 1),
-        "other": {"k_qgemm_fwd": {"TFLOP/s": round(fwd_tf, 1), "ms_per_step": round(fwd_ms, 4)},
-                  "k_qgemm_bwd": {"TFLOP/s": round(bwd_tf, 1), "ms_per_step": round(bwd_ms, 4)},
-                  "launch_us_p10_p50_p90": {
-                      f"{kn} {t['spec'].name}": [round(float(np.percentile(v, q)), 1)
-                                                for q in (10, 50, 90)]
-                      for kn, key in (("k_qgemm_fwd", "fwd"), ("k_qgemm_bwd", "bwd"))
-                      for t, v in zip(layers, per_launch[key])},
-                  "events_on_every_nth_step": args.events_every},
-    }
+    roofline = dict(head["roofline"])
+    roofline["traffic"] = load_traffic(roofline["kernel"], wl.name, src_hash)
 
     extra = {}
     if not args.no_extra:
-        extra = run_extras(qn, L, ev, torch, dev, sp, d16)
+        # the same step without rotation (weights may be served from the
+        # Infinity Cache), labeled as such
+        extra["warm_step"] = fx.run(args.steps, args.warmup, 0, sp, rotate=False)["summary"]
+        extra["workloads"] = run_workloads(qn, torch, ev, d16, dev, sp, args)
+        extra.update(run_extras(qn, L, ev, torch, dev, sp, d16))
         for code in ("fp4", "nf3", "nf2"):
             extra["code_types"][code]["fused_step"] = code_step(
-                qn, L, torch, layers, M, r, s, sp, args.steps, args.warmup, flops_step, code)
-        extra["bf16_gemm_reference"] = run_gemm_reference(torch, layers, M, per_launch)
+                qn, L, torch, fx.layers, M, r, wl.s, sp, args.steps, args.warmup,
+                head["flops_step"], code)
+        extra["bf16_gemm_reference"] = run_gemm_reference(torch, fx.layers, M,
+                                                          head["per_launch"])
         extra["lq_init"] = run_lq(qn, torch)
         extra["ilp"] = run_ilp(qn, torch)
+    host_inputs = fx.host_inputs
+    del fx
+    torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -283,12 +203,12 @@ def main():
 
     out = {
         "metric": "fused NF4+LoRA linear fwd+bwd TFLOP/s (% bf16 MFMA peak); GEMV GB/s",
-        "value": round(tflops, 2),
+        "value": head["summary"]["TFLOP/s"],
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
+        "ms_per_step": head["summary"]["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -297,13 +217,219 @@ def main():
         "config": {"workload": wl.name, "tokens": M, "r": r, "alpha": wl.alpha,
                    "weights": [f"{w_.name} {w_.N}x{w_.K}" for w_ in wl.weights],
                    "nf4": "blocksize 64, double-quant 256 (8-bit constants, fp32 steps)",
-                   "pct_bf16_mfma_peak": round(100 * tflops / MFMA_BF16_PEAK_TFLOPS, 2),
-                   "wall_s_timed": round(wall, 4)},
+                   "pct_bf16_mfma_peak": head["summary"]["pct_bf16_mfma_peak"],
+                   "weight_copies_rotated": head["summary"]["weight_copies_rotated"],
+                   "wall_s_timed": head["summary"]["wall_s_timed"]},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "extra": extra,
     }
     print(json.dumps(out), flush=True)
+
+
+ROTATE_BYTES = 512e6   # rotated weight state per workload: twice the 256 MB Infinity Cache
+MAX_COPIES = 64
+
+
+class FusedWorkload:
+    """One forward + backward workload: seeded host inputs, device inputs
+    and outputs, and `copies` quantized copies of each weight (rotated step
+    by step so that no step's weights are served from the Infinity Cache;
+    at most MAX_COPIES, so a tiny workload stays warm)."""
+
+    def __init__(self, qn, torch, ev, wl, d16, dev, rotate=True, keep_host=True):
+        import workloads as wl_mod
+        self.qn, self.torch, self.ev, self.wl = qn, torch, ev, wl
+        M, r = wl.M[0], wl.r
+        self.layers = []
+        self.host_inputs = []
+        state = sum(qn.storage_bytes(sp_.N, sp_.K) for sp_ in wl.weights)
+        self.copies = int(min(MAX_COPIES, max(1, np.ceil(ROTATE_BYTES / state)))) if rotate else 1
+        for wi, spec in enumerate(wl.weights):
+            inp = wl_mod.draw_workload_weight(wl, wi)
+            if keep_host:
+                self.host_inputs.append(inp)
+            W = torch.from_numpy(inp.W).to(dev)
+            ws = [qn.nf4_quantize(W) for _ in range(self.copies)]
+            N, K = spec.N, spec.K
+            t = dict(spec=spec, w=ws[0], ws_all=ws, Wf32=W, X=d16(inp.X), dY=d16(inp.dY),
+                     A=d16(inp.A), B=d16(inp.B),
+                     U=torch.empty(M, r, dtype=torch.int16, device=dev),
+                     Y=torch.empty(M, N, dtype=torch.int16, device=dev),
+                     dX=torch.empty(M, K, dtype=torch.int16, device=dev),
+                     dA=torch.empty(r, K, dtype=torch.int16, device=dev),
+                     dB=torch.empty(N, r, dtype=torch.int16, device=dev))
+            t["wsf"] = torch.empty(qn.workspace_size(M, N, K, r, False), dtype=torch.uint8,
+                                   device=dev)
+            t["wsb"] = torch.empty(qn.workspace_size(M, N, K, r, True), dtype=torch.uint8,
+                                   device=dev)
+            t["st"] = [w.struct() for w in ws]
+            self.layers.append(t)
+        torch.cuda.synchronize()
+
+    def flops(self):
+        M, r = self.wl.M[0], self.wl.r
+        step = fwd = bwd = 0.0
+        for t in self.layers:
+            N, K = t["spec"].N, t["spec"].K
+            step += 4.0 * M * N * K + 6.0 * M * r * (N + K)
+            fwd += 2.0 * M * N * (K + r)      # X W^T + (sU) B^T
+            bwd += 2.0 * M * K * (N + r)      # dY W + dU A
+        return step, fwd, bwd
+
+    def run(self, steps, warmup, events_every, sp, rotate=True):
+        """Times exactly `steps` steps after `warmup` untimed ones.  With
+        events_every > 0 the dominant kernels of every n-th timed step are
+        bracketed by events recorded on the launch stream."""
+        from quantized_base_lora_nf4_amd._lib import check
+        torch, L, ev = self.torch, self.qn.lib(), self.ev
+        M, r, s = self.wl.M[0], self.wl.r, self.wl.s
+        copies = self.copies if rotate else 1
+        nev = steps if events_every else 0
+        evs = [[[ev.create() for _ in range(4)] for _ in range(nev)] for _ in self.layers]
+
+        def p(x):
+            return x.data_ptr() if x is not None else None
+
+        def step(i, k):
+            for li, t in enumerate(self.layers):
+                timed = i is not None and events_every and i % events_every == 0
+                e = evs[li][i] if timed else [None] * 4
+                st = t["st"][k % copies]
+                check(L.qlora_linear_fwd_ev(ctypes.byref(st), p(t["X"]), M, p(t["A"]), p(t["B"]),
+                                            r, s, p(t["Y"]), p(t["U"]), p(t["wsf"]),
+                                            t["wsf"].numel(), sp, e[0], e[1]), "fwd")
+                check(L.qlora_linear_bwd_ev(ctypes.byref(st), p(t["X"]), p(t["dY"]), M, p(t["A"]),
+                                            p(t["B"]), p(t["U"]), r, s, p(t["dX"]), p(t["dA"]),
+                                            p(t["dB"]), p(t["wsb"]), t["wsb"].numel(), sp, e[2],
+                                            e[3]), "bwd")
+
+        for k in range(warmup):
+            step(None, k)
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        t0.record()
+        for i in range(steps):
+            step(i, warmup + i)
+        t1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        ms_step = t0.elapsed_time(t1) / steps
+        flops_step, flops_fwd, flops_bwd = self.flops()
+        tflops = flops_step / (ms_step * 1e-3) / 1e12
+        summary = {"ms_per_step": round(ms_step, 4), "TFLOP/s": round(tflops, 2),
+                   "pct_bf16_mfma_peak": round(100 * tflops / MFMA_BF16_PEAK_TFLOPS, 2),
+                   "steps": steps, "weight_copies_rotated": copies,
+                   "wall_s_timed": round(wall, 4)}
+        out = {"summary": summary, "flops_step": flops_step}
+        if not events_every:
+            return out
+        kt = {"fwd": [0.0, 0], "bwd": [0.0, 0]}
+        per_launch = {"fwd": [], "bwd": []}
+        for li, t in enumerate(self.layers):
+            lf, lb = [], []
+            for i, e in enumerate(evs[li]):
+                if i % events_every:
+                    continue
+                f_ms, b_ms = ev.elapsed_ms(e[0], e[1]), ev.elapsed_ms(e[2], e[3])
+                kt["fwd"][0] += f_ms
+                kt["fwd"][1] += 1
+                kt["bwd"][0] += b_ms
+                kt["bwd"][1] += 1
+                lf.append(f_ms * 1e3)
+                lb.append(b_ms * 1e3)
+            per_launch["fwd"].append(lf)
+            per_launch["bwd"].append(lb)
+        for row in evs:
+            for e4 in row:
+                for e in e4:
+                    ev.destroy(e)
+        nl = len(self.layers)
+        fwd_ms = kt["fwd"][0] / max(1, kt["fwd"][1]) * nl   # per step
+        bwd_ms = kt["bwd"][0] / max(1, kt["bwd"][1]) * nl
+        fwd_tf = flops_fwd / (fwd_ms * 1e-3) / 1e12
+        bwd_tf = flops_bwd / (bwd_ms * 1e-3) / 1e12
+        if bwd_ms >= fwd_ms:   # the dominant kernel: the larger share of the step
+            dom, dom_tf, dom_us = "k_qgemm_bwd", bwd_tf, bwd_ms / nl * 1e3
+        else:
+            dom, dom_tf, dom_us = "k_qgemm_fwd", fwd_tf, fwd_ms / nl * 1e3
+        out["per_launch"] = per_launch
+        out["roofline"] = {
+            "bound": "mfma", "kernel": dom, "achieved": round(dom_tf, 1),
+            "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(dom_tf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+            "avg_launch_us": round(dom_us, 1),
+            "other": {"k_qgemm_fwd": {"TFLOP/s": round(fwd_tf, 1), "ms_per_step": round(fwd_ms, 4)},
+                      "k_qgemm_bwd": {"TFLOP/s": round(bwd_tf, 1), "ms_per_step": round(bwd_ms, 4)},
+                      "lora_and_other_ms_per_step": round(ms_step - fwd_ms - bwd_ms, 4),
+                      "launch_us_p10_p50_p90": {
+                          f"{kn} {t['spec'].name}": [round(float(np.percentile(v, q)), 1)
+                                                    for q in (10, 50, 90)]
+                          for kn, key in (("k_qgemm_fwd", "fwd"), ("k_qgemm_bwd", "bwd"))
+                          for t, v in zip(self.layers, per_launch[key])},
+                      "events_on_every_nth_step": events_every},
+        }
+        return out
+
+
+# The other forward + backward workloads, reported under extra.workloads:
+# (name, timed steps, warmup steps, CPU sample: weight rows, token rows).
+EXTRA_WORKLOADS = (("single_1024x1024_M256_r8", 50, 10, 1024, 256),
+                   ("llama65b_mlp_M4096_r64", 10, 3, 512, 256),
+                   ("llama13b_block_M2048_r64", 20, 5, 1024, 256))
+
+
+def run_workloads(qn, torch, ev, d16, dev, sp, args):
+    """Every other forward + backward workload at full size, on rotated
+    weight copies: step time and TFLOP/s, the dominant kernel's roofline,
+    and the CPU oracle on a bounded sample (the first weight rows and token
+    rows of every weight).  The LLaMA-13B block also times its one-time
+    quantization of all seven weights."""
+    import workloads as wl_mod
+    out = {}
+    for name, steps, warmup, wrows, trows in EXTRA_WORKLOADS:
+        wl = {w.name: w for w in wl_mod.WORKLOADS}[name]
+        fx = FusedWorkload(qn, torch, ev, wl, d16, dev, rotate=True)
+        res = fx.run(steps, warmup, 2, sp)
+        entry = dict(res["summary"])
+        entry["roofline"] = res["roofline"]
+        if name == "llama13b_block_M2048_r64":
+            entry["quantize_all_weights"] = time_quantize_all(qn, torch, fx)
+        host = fx.host_inputs
+        del fx, res
+        torch.cuda.empty_cache()
+        if not args.no_cpu_baseline:
+            entry["cpu_baseline"] = cpu_baseline_sample(host, wl, wrows, trows)
+        del host
+        out[name] = entry
+    return out
+
+
+def time_quantize_all(qn, torch, fx, reps=5):
+    """One-time quantization of every weight of the workload (fp32 W
+    resident in HBM, 1.3 GB for the LLaMA-13B block, more than the Infinity
+    Cache): median of `reps` passes over all weights, after one warm-up."""
+    ts = []
+    for i in range(reps + 1):
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for t in fx.layers:
+            qn.nf4_quantize(t["Wf32"], out=t["ws_all"][i % len(t["ws_all"])])
+        e1.record()
+        torch.cuda.synchronize()
+        if i:
+            ts.append(e0.elapsed_time(e1))
+    ms = float(np.median(ts))
+    nbytes = sum(4 * t["spec"].N * t["spec"].K + qn.storage_bytes(t["spec"].N, t["spec"].K)
+                 for t in fx.layers)
+    return {"weights": len(fx.layers), "ms": round(ms, 3), "bytes_read_plus_written": nbytes,
+            "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
 
 
 def run_gemm_reference(torch, layers, M, per_launch, reps=50):
@@ -496,6 +622,8 @@ def run_extras(qn, L, ev, torch, dev, sp, d16):
     del src, dst
     torch.cuda.empty_cache()
     g = wl_mod.SKINNY_GEMV
+    res["hbm_read_ceiling"] = hbm_read_ceiling(
+        qn, torch, ev, sp, [qn.storage_bytes(sp_.N, sp_.K) for sp_ in g.weights])
     e0, e1, a0, a1 = ev.create(), ev.create(), ev.create(), ev.create()
     for wi, spec in enumerate(g.weights):
         N, K = spec.N, spec.K
@@ -543,22 +671,30 @@ def run_extras(qn, L, ev, torch, dev, sp, d16):
 
 def _time_gemv(L, torch, ev, structs, inp, M, N, K, g, A, B, d16, dev, sp, wbytes, e0, e1):
     """Few-token forward on rotated weight copies: the weight-streaming
-    kernel alone (events around its launch) and the whole call."""
+    kernel alone and the whole call.  Calls are issued back to back; each
+    call's weight-streaming kernel is bracketed by its own pair of events
+    (recorded on the launch stream), so a pair measures the kernel without
+    the idle-to-busy dispatch a synchronized single call would add."""
     from quantized_base_lora_nf4_amd._lib import check
     ncopy = len(structs)
     X = d16(inp.X[:M])
     Y = torch.empty(M, N, dtype=torch.int16, device=dev)
     ws = torch.empty(qn_ws(L, M, N, K, g.r), dtype=torch.uint8, device=dev)
     it, warm = 60, 6
-    kern = []
+    pairs = [(ev.create(), ev.create()) for _ in range(it)]
     for i in range(it + warm):
         st = structs[i % ncopy]
+        a, b = pairs[i - warm] if i >= warm else (None, None)
         check(L.qlora_linear_fwd_ev(ctypes.byref(st), X.data_ptr(), M, A.data_ptr(),
                                     B.data_ptr(), g.r, g.s, Y.data_ptr(), None,
-                                    ws.data_ptr(), ws.numel(), sp, e0, e1), "gemv")
-        torch.cuda.synchronize()
-        if i >= warm:
-            kern.append(ev.elapsed_ms(e0, e1))
+                                    ws.data_ptr(), ws.numel(), sp, a, b), "gemv")
+        if i == warm - 1:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    kern = [ev.elapsed_ms(a, b) for a, b in pairs]
+    for a, b in pairs:
+        ev.destroy(a)
+        ev.destroy(b)
     # whole call (all launches) on the stream
     for i in range(it + warm):
         st = structs[i % ncopy]
@@ -574,6 +710,8 @@ def _time_gemv(L, torch, ev, structs, inp, M, N, K, g, A, B, d16, dev, sp, wbyte
     torch.cuda.synchronize()
     call_ms = c0.elapsed_time(c1) / it
     k_ms = float(np.median(kern))
+    k_avg = float(np.mean(kern))
+    gbs = wbytes / (k_avg * 1e-3) / 1e9
     return {
         "weight": f"{N}x{K}", "M": M, "r": g.r,
         "kernel_us": round(k_ms * 1e3, 2),
@@ -581,7 +719,47 @@ def _time_gemv(L, torch, ev, structs, inp, M, N, K, g, A, B, d16, dev, sp, wbyte
         "kernel_frac_hbm": round(wbytes / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "call_us": round(call_ms * 1e3, 2),
         "call_GB/s": round(wbytes / (call_ms * 1e-3) / 1e9, 1),
-        "weight_bytes": wbytes, "copies_rotated": ncopy}
+        "weight_bytes": wbytes, "copies_rotated": ncopy,
+        "roofline": {"bound": "hbm", "kernel": "k_qgemv", "achieved": round(gbs, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBPS, 4), "avg_launch_us": round(k_avg * 1e3, 2)}}
+
+
+def hbm_read_ceiling(qn, torch, ev, sp, sizes, reps=40):
+    """The measured HBM read ceiling next to the 8 TB/s spec: a read-only
+    stream (qlora_stream_read) over buffers of the few-token weight
+    streams' sizes, rotated over copies that together exceed the Infinity
+    Cache three times; launches back to back, each between its own events."""
+    from quantized_base_lora_nf4_amd._lib import QLORA_STREAM_GRID, check
+    L = qn.lib()
+    out = []
+    sink = torch.empty(QLORA_STREAM_GRID, dtype=torch.int32, device="cuda")
+    for nbytes in sizes:
+        nb = (int(nbytes) + 15) // 16 * 16
+        ncopy = max(3, int(np.ceil(768e6 / nb)))
+        bufs = [torch.full((nb,), 1, dtype=torch.uint8, device="cuda") for _ in range(ncopy)]
+        pairs = [(ev.create(), ev.create()) for _ in range(reps)]
+        for i in range(reps + 4):
+            a, b = pairs[i - 4] if i >= 4 else (None, None)
+            if a is not None:
+                assert ev.rt.hipEventRecord(a, ctypes.c_void_p(sp)) == 0
+            check(L.qlora_stream_read(bufs[i % ncopy].data_ptr(), nb, sink.data_ptr(), sp),
+                  "stream_read")
+            if b is not None:
+                assert ev.rt.hipEventRecord(b, ctypes.c_void_p(sp)) == 0
+        torch.cuda.synchronize()
+        ts = [ev.elapsed_ms(a, b) for a, b in pairs]
+        for a, b in pairs:
+            ev.destroy(a)
+            ev.destroy(b)
+        ms = float(np.median(ts))
+        out.append({"bytes": nb, "us": round(ms * 1e3, 2),
+                    "GB/s": round(nb / (ms * 1e-3) / 1e9, 1),
+                    "frac_hbm": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                    "copies_rotated": ncopy})
+        del bufs
+        torch.cuda.empty_cache()
+    return out
 
 
 def qn_ws(L, M, N, K, r):
@@ -590,6 +768,53 @@ def qn_ws(L, M, N, K, r):
 
 CPU_BASELINE_MIN_S = 10.0
 CPU_BASELINE_MAX_PASSES = 20
+
+
+CPU_SAMPLE_MIN_S = 3.0
+
+
+def cpu_baseline_sample(host_inputs, wl, wrows, trows):
+    """The CPU oracle, as it stands, on a bounded sample of a workload: for
+    every weight its first `wrows` rows (quantized by the oracle, untimed)
+    and the first `trows` token rows; timed: dequantize + fp64 forward +
+    backward (the backward's dA and dX over the sampled weight rows)."""
+    from oracle import linear, nf4
+    states = []
+    for inp in host_inputs:
+        Wr = np.ascontiguousarray(inp.W[:wrows])
+        states.append((nf4.quantize(Wr), Wr.shape))
+    cores = len(os.sched_getaffinity(0))
+    flops, passes = 0.0, 0
+    t0 = time.perf_counter()
+    while True:
+        for inp, (st, (N, K)) in zip(host_inputs, states):
+            Wh = nf4.bf16_bits_to_f32(nf4.dequantize(*st, N, K))
+            X = nf4.bf16_bits_to_f32(inp.X[:trows])
+            dY = nf4.bf16_bits_to_f32(inp.dY[:trows, :N])
+            A = nf4.bf16_bits_to_f32(inp.A)
+            B = nf4.bf16_bits_to_f32(inp.B[:N])
+            linear.forward(X, Wh, A, B, wl.s)
+            linear.backward(X, dY, Wh, A, B, wl.s)
+            flops += 4.0 * trows * N * K + 6.0 * trows * wl.r * (N + K)
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt >= CPU_SAMPLE_MIN_S or passes >= CPU_BASELINE_MAX_PASSES:
+            break
+    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": blas_threads(cores),
+            "kind": "oracle",
+            "sample": (f"{wl.name}: first {wrows} rows of each of the {len(host_inputs)} weights, "
+                       f"first {trows} of {wl.M[0]} token rows; oracle dequantize + fp64 forward "
+                       f"+ backward, {passes} passes ({dt:.1f} s)"),
+            "seconds": round(dt, 2)}
+
+
+def blas_threads(cores):
+    try:
+        from threadpoolctl import threadpool_info
+        info = [d for d in threadpool_info() if d.get("user_api") == "blas"]
+        return max([d.get("num_threads", 0) for d in info] + [1])
+    except Exception:  # pragma: no cover
+        return cores
 
 
 def cpu_baseline(host_inputs, wl, rows):

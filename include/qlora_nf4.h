@@ -278,6 +278,17 @@ int32_t qlora_linear_fwd_noalloc(const nf4_tensor_t* w, const uint16_t* X,
                                  uint16_t* Y, uint16_t* U_out,
                                  hipStream_t stream);
 
+/* Measurement helper (not part of the layer): a read-only stream over
+ * `bytes` bytes of device memory at src (16-byte aligned, bytes a multiple
+ * of 16), the HBM read ceiling the few-token forward's weight stream is
+ * compared with.  Every 16-byte word is read once; each of the
+ * QLORA_STREAM_GRID workgroups writes one uint32 to sink[0 ..
+ * QLORA_STREAM_GRID - 1] (a device buffer the caller owns).  Errors as for
+ * the other calls; nothing is allocated. */
+#define QLORA_STREAM_GRID 1024
+int32_t qlora_stream_read(const void* src, size_t bytes, uint32_t* sink,
+                          hipStream_t stream);
+
 /* ---- Low-rank plus quantized decomposition (adapter initialization) ----
  *
  * qlora_lq_init -- split a frozen weight into a quantized part Q and a
@@ -310,8 +321,8 @@ int32_t qlora_linear_fwd_noalloc(const nf4_tensor_t* w, const uint16_t* X,
  *           qlora_lq_workspace_size(N, K, r, l) (about 4 N K bytes)
  * The pair returned is the last Q step's Q with the L step before it
  * (start SVD) or after it (start QUANTIZE).  Sums have a fixed order:
- * results are reproducible.  The first call on a device raises the
- * eigensolver kernel's dynamic LDS limit (process-wide, idempotent). */
+ * results are reproducible.  Every call raises the dynamic LDS limit of the
+ * two one-workgroup solver kernels (idempotent). */
 #define QLORA_LQ_MAX_L 96
 #define QLORA_LQ_START_SVD 0
 #define QLORA_LQ_START_QUANTIZE 1

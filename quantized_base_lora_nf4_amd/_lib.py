@@ -24,6 +24,8 @@ QLORA_CODE_NF2 = 3
 
 # Size of the fixed device scratch of qlora_linear_fwd_noalloc
 QLORA_NOALLOC_SCRATCH_BYTES = 16 << 20
+# Workgroups (and sink words) of qlora_stream_read
+QLORA_STREAM_GRID = 1024
 
 # Every symbol the header declares.
 EXPORTS = (
@@ -41,6 +43,7 @@ EXPORTS = (
     "qlora_linear_fwd_ev",
     "qlora_linear_bwd_ev",
     "qlora_linear_fwd_noalloc",
+    "qlora_stream_read",
     "qlora_lq_workspace_size",
     "qlora_lq_init",
     "qlora_quant_error_workspace_size",
@@ -113,6 +116,8 @@ def lib() -> ctypes.CDLL:
     L.qlora_linear_fwd_noalloc.restype = i32
     L.qlora_linear_fwd_noalloc.argtypes = [ctypes.POINTER(Nf4Tensor), vp, i64, vp, vp, i32, f32,
                                            vp, vp, vp]
+    L.qlora_stream_read.restype = i32
+    L.qlora_stream_read.argtypes = [vp, sz, vp, vp]
     L.qlora_lq_workspace_size.restype = sz
     L.qlora_lq_workspace_size.argtypes = [i64, i64, i32, i32]
     L.qlora_lq_init.restype = i32

@@ -379,6 +379,14 @@ extern "C" int32_t qlora_linear_fwd_noalloc(const nf4_tensor_t* w, const uint16_
                     nullptr, nullptr);
 }
 
+extern "C" int32_t qlora_stream_read(const void* src, size_t bytes, uint32_t* sink,
+                                     hipStream_t stream) {
+  if (!src || !sink || bytes == 0 || (bytes % 16) != 0 || !aligned16(src) ||
+      ((uintptr_t)sink & 3u) != 0)
+    return QLORA_ERR_INVALID;
+  return launch_status(qn::launch_stream_read(src, bytes, sink, QLORA_STREAM_GRID, stream));
+}
+
 extern "C" {
 
 size_t qlora_lq_workspace_size(int64_t N, int64_t K, int32_t r, int32_t l) {

@@ -367,29 +367,18 @@ size_t gemv_workspace_bytes(int64_t M, int32_t r, int64_t K) {
 template <int G>
 hipError_t launch_qgemv_g(const GemvArgs& a, int code, hipStream_t stream) {
   constexpr int KW = 8, PD = QN_GEMV_PD;
-  static const hipError_t attr = [] {
-    // dynamic LDS above the default 64 KB needs the limit raised, once per
-    // instantiation
-    hipError_t r = hipSuccess;
-    for (int id = 0; id < 4; ++id) {
-      const hipError_t e = with_code(id, [](auto ct) {
-        return hipFuncSetAttribute(
-            reinterpret_cast<const void*>(&k_qgemv<G, KW, PD, decltype(ct)>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
-      });
-      if (r == hipSuccess) r = e;
-    }
-    return r;
-  }();
-  if (attr != hipSuccess) return attr;
   const size_t lds = 4 * (size_t)gemv_lds_words(G, KW, a.M, a.r, a.K / 64);
   const dim3 grid((unsigned)((a.N + 16 * G - 1) / (16 * G)));
-  with_code(code, [&](auto ct) {
-    hipLaunchKernelGGL((k_qgemv<G, KW, PD, decltype(ct)>), grid, dim3(64 * KW), lds,
-                       stream, a);
-    return 0;
+  return with_code(code, [&](auto ct) {
+    const void* fn = reinterpret_cast<const void*>(&k_qgemv<G, KW, PD, decltype(ct)>);
+    // dynamic LDS above the default 64 KB needs the limit raised; the call is
+    // cheap and idempotent, and made for the device the launch goes to
+    // (a per-process cache would only cover the first device)
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_qgemv<G, KW, PD, decltype(ct)>), grid, dim3(64 * KW), lds, stream, a);
+    return hipGetLastError();
   });
-  return hipGetLastError();
 }
 
 hipError_t launch_qgemv(const Nf4View& w, const uint16_t* X, int64_t M, const uint16_t* A,
@@ -413,13 +402,11 @@ hipError_t launch_qgemv(const Nf4View& w, const uint16_t* X, int64_t M, const ui
   //    flight.  With more tokens the X fragments, loaded once per
   //    workgroup, cost more than that gains.
   //  - G = 2 otherwise.
-  static const int cus = [] {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      return 0;
-    return n;
-  }();
+  // compute units of the current device, the one the launch goes to
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 0;
   const int64_t groups = (w.N + 15) / 16;
   const bool g7 = cus > 0 && groups % (7 * (int64_t)cus) == 0 &&
                   4 * gemv_lds_words(7, 8, M, r, kblocks) <= 96 * 1024;

@@ -103,6 +103,12 @@ hipError_t launch_lq_init(const LqArgs& a, hipStream_t stream);
 hipError_t launch_lq_residual(const float* W, const float* L1, const float* L2t, int64_t N,
                               int64_t K, int r, float* R, hipStream_t stream);
 
+// ---- stream.hip: read-only HBM stream (measurement helper) ----
+// Reads bytes / 16 16-byte words of src with `grid` workgroups of 256
+// lanes; writes one word per workgroup to sink[0 .. grid - 1].
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int grid,
+                              hipStream_t stream);
+
 // ---- ilp.hip: configuration errors and the budget program ----
 size_t quant_error_workspace_bytes(int64_t N, int64_t K, int bits, bool lowrank);
 // *sq_err (device) = ||R - W_hat(R)||_F^2, R = W or W - L1 L2t^T (L1 non-null)

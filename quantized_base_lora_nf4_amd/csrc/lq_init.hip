@@ -658,15 +658,15 @@ hipError_t launch_lq_residual(const float* W, const float* L1, const float* L2t,
 }
 
 hipError_t launch_lq_init(const LqArgs& a, hipStream_t stream) {
-  static const hipError_t attr = [] {
-    const hipError_t a = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_lq_eig),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             (int)eig_lds(kLqMaxL));
-    const hipError_t b = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_lq_chol),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             (int)chol_lds(kLqMaxL));
-    return a != hipSuccess ? a : b;
-  }();
+  // The two one-workgroup solvers use more than the default 64 KB of
+  // dynamic LDS; the limit is raised on every call (cheap, idempotent), so
+  // that it holds for whichever device is current.
+  hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_lq_eig),
+                                        hipFuncAttributeMaxDynamicSharedMemorySize,
+                                        (int)eig_lds(kLqMaxL));
+  if (attr == hipSuccess)
+    attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_lq_chol),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)chol_lds(kLqMaxL));
   if (attr != hipSuccess) return attr;
   const int64_t N = a.N, K = a.K;
   const int l = a.l, r = a.r;
