@@ -9,9 +9,11 @@ matrix so that the model meets an overall memory budget.
 Readings taken (listed in the design notes):
 
 * A configuration is a code type of the block quantizer (NF4, FP4, NF3,
-  NF2) at block size 64 with double-quantized constants, the block size the
-  layer's kernels take; its memory is the bytes of the stored state
-  (codes + 8-bit constants + fp32 steps).
+  NF2) and a block size (64, 128 or 256 consecutive elements of the
+  row-major weight share one absmax constant), with the constants double
+  quantized in groups of 256 blocks as at block size 64; the codes are
+  packed in 64-element units whatever the block size.  Its memory is the
+  bytes of the stored state (codes + 8-bit constants + fp32 steps).
 * The error of matrix m under configuration c is the squared Frobenius
   error of its quantized part: ||R - W_hat_c(R)||_F^2 with R = W (plain
   QLoRA) or R = fl32(W - L1 L2^T) when a low-rank part is given (then it is
@@ -28,7 +30,10 @@ import numpy as np
 
 from . import nf4
 
-CONFIGS = ("nf4", "fp4", "nf3", "nf2")
+CODES = ("nf4", "fp4", "nf3", "nf2")
+BLOCKSIZES = (64, 128, 256)
+# every (code type, block size) pair, code type major
+CONFIGS = tuple((c, b) for c in CODES for b in BLOCKSIZES)
 
 
 def residual(W, L1=None, L2t=None) -> np.ndarray:
@@ -38,18 +43,19 @@ def residual(W, L1=None, L2t=None) -> np.ndarray:
             ).astype(np.float32)
 
 
-def quant_error(R, code: str) -> float:
+def quant_error(R, code: str, blocksize: int = nf4.BLOCKSIZE) -> float:
     """||R - W_hat(R)||_F^2 in fp64 for one configuration."""
     R = np.asarray(R, np.float32)
     N, K = R.shape
-    packed, q8, step = nf4.quantize(R, code=code)
-    what = nf4.bf16_bits_to_f32(nf4.dequantize(packed, q8, step, N, K, code=code))
+    packed, q8, step = nf4.quantize(R, blocksize=blocksize, code=code)
+    what = nf4.bf16_bits_to_f32(nf4.dequantize(packed, q8, step, N, K, blocksize=blocksize,
+                                               code=code))
     d = R.astype(np.float64) - what.astype(np.float64)
     return float(np.sum(d * d))
 
 
-def state_bytes(N: int, K: int, code: str) -> int:
-    return nf4.storage_bytes(N, K, code=code)
+def state_bytes(N: int, K: int, code: str, blocksize: int = nf4.BLOCKSIZE) -> int:
+    return nf4.storage_bytes(N, K, blocksize=blocksize, code=code)
 
 
 def plan(err, nbytes, budget: int):

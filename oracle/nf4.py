@@ -387,12 +387,16 @@ def double_quantize(c: np.ndarray, dq_blocksize: int = DQ_BLOCKSIZE):
 
 def quantize(W: np.ndarray, blocksize: int = BLOCKSIZE, dq_blocksize: int = DQ_BLOCKSIZE,
              code: str = "nf4"):
-    """Full 4-bit (NF4 by default, or FP4) + double-quant encoding of W
-    [N, K] fp32.
+    """Block quantization (NF4 by default, or FP4, NF3, NF2) + double-quant
+    encoding of W [N, K] fp32, one absmax constant per `blocksize`
+    consecutive elements (a multiple of 64 dividing K).
 
-    Returns (codes uint8 [N*K/2], q8 uint8 [N*K/64], step fp32
-    [ceil(N*K/64/256)]).
+    Returns (packed codes uint8 [N*K*bits/8], packed in 64-element units
+    whatever the block size; q8 uint8 [N*K/blocksize]; step fp32
+    [ceil(N*K/blocksize/dq_blocksize)]).
     """
+    if blocksize % 64:
+        raise ValueError("the block size must be a multiple of 64")
     c = block_absmax(W, blocksize)
     x = normalize(W, c, blocksize)
     codes = nearest_code(x, code_values(code))

@@ -42,7 +42,7 @@ def _gpu_err(W, code, L1=None, L2t=None):
 SHAPES = [(1, 64), (7, 192), (300, 1024), (1024, 4160)]
 
 
-@pytest.mark.parametrize("code", ilp.CONFIGS)
+@pytest.mark.parametrize("code", ilp.CODES)
 @pytest.mark.parametrize("shape", SHAPES)
 def test_quant_error_matches_oracle(code, shape):
     W = draw_weight(WeightSpec("w", *shape, 0.02, heavy_frac=0.01), rng_for(40, shape[0]))
@@ -74,9 +74,9 @@ def test_plan_from_gpu_errors_matches_oracle():
              WeightSpec("c", 128, 2048, 0.01), WeightSpec("d", 384, 768, 0.03, heavy_frac=0.02),
              WeightSpec("e", 640, 256, 0.02), WeightSpec("f", 200, 1280, 0.02)]
     Ws = [draw_weight(sp, rng_for(42, i)) for i, sp in enumerate(specs)]
-    err_g = np.array([[_gpu_err(W, c) for c in ilp.CONFIGS] for W in Ws])
-    err_o = np.array([[ilp.quant_error(W, c) for c in ilp.CONFIGS] for W in Ws])
-    nbytes = np.array([[qn.storage_bytes(*W.shape, c) for c in ilp.CONFIGS] for W in Ws])
+    err_g = np.array([[_gpu_err(W, c) for c in ilp.CODES] for W in Ws])
+    err_o = np.array([[ilp.quant_error(W, c) for c in ilp.CODES] for W in Ws])
+    nbytes = np.array([[qn.storage_bytes(*W.shape, c) for c in ilp.CODES] for W in Ws])
     assert np.all(np.abs(err_g - err_o) <= 1e-12 * err_o)
     total_w = sum(W.size for W in Ws)
     for bits in (2.3, 3.0, 3.6, 4.2):
