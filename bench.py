@@ -189,6 +189,10 @@ def main():
             extra["code_types"][code]["fused_step"] = code_step(
                 qn, L, torch, fx.layers, M, r, wl.s, sp, args.steps, args.warmup,
                 head["flops_step"], code)
+        extra["block_sizes"] = {
+            f"nf4/{bs}": code_step(qn, L, torch, fx.layers, M, r, wl.s, sp, args.steps,
+                                   args.warmup, head["flops_step"], "nf4", bs)
+            for bs in (128, 256)}
         extra["bf16_gemm_reference"] = run_gemm_reference(torch, fx.layers, M,
                                                           head["per_launch"])
         extra["lq_init"] = run_lq(qn, torch)
@@ -510,24 +514,24 @@ def run_lq(qn, torch, reps=5):
 
 
 def run_ilp(qn, torch, reps=3):
-    """Error table of the LLaMA-13B block (7 matrices, 317M weights) for the
-    four code types, then plans at three average bit budgets.  Per table
-    call: the quantizer reads W and writes the state, the error pass reads W
-    and the state again."""
+    """Error table of the LLaMA-13B block (7 matrices, 317M weights) for
+    every configuration (four code types x block sizes 64, 128, 256), then
+    plans at four average bit budgets.  Per table call: the quantizer reads
+    W and writes the state, the error pass reads W and the state again."""
     import workloads as wl_mod
-    configs = ("nf4", "fp4", "nf3", "nf2")
+    configs = tuple((c, b) for c in ("nf4", "fp4", "nf3", "nf2") for b in (64, 128, 256))
     wl = wl_mod.LLAMA13B_BLOCK
     Ws = [torch.from_numpy(wl_mod.draw_weight(sp, wl_mod.rng_for(wl.seed, 2000 + i))).cuda()
           for i, sp in enumerate(wl.weights)]
-    need = max(int(qn.lib().qlora_quant_error_workspace_size(W.shape[0], W.shape[1], 0, 0))
+    need = max(int(qn.lib().qlora_config_error_workspace_size(W.shape[0], W.shape[1], 0, 64, 0))
                for W in Ws)
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
     out = torch.empty(len(Ws) * len(configs), dtype=torch.float64, device="cuda")
 
     def table():
         for m, W in enumerate(Ws):
-            for c, code in enumerate(configs):
-                qn.quant_error(W, code, ws=ws, out=out[m * len(configs) + c:][:1])
+            for c, (code, bs) in enumerate(configs):
+                qn.quant_error(W, code, ws=ws, out=out[m * len(configs) + c:][:1], blocksize=bs)
     table()
     torch.cuda.synchronize()
     ts = []
@@ -541,30 +545,33 @@ def run_ilp(qn, torch, reps=3):
         ts.append(e0.elapsed_time(e1))
     ms = float(np.median(ts))
     err = out.cpu().numpy().reshape(len(Ws), len(configs))
-    nbytes = np.array([[qn.storage_bytes(W.shape[0], W.shape[1], c) for c in configs] for W in Ws])
+    nbytes = np.array([[qn.storage_bytes(W.shape[0], W.shape[1], c, b) for c, b in configs]
+                       for W in Ws])
     nw = sum(W.numel() for W in Ws)
     moved = sum(2 * 4 * W.numel() + 2 * int(nbytes[m][c]) for m, W in enumerate(Ws)
                 for c in range(len(configs)))
     plans = []
-    for bits in (2.5, 3.0, 3.5):
+    for bits in (2.3, 2.7, 3.2, 3.7):
         t0 = time.perf_counter()
         got = qn.ilp_plan(err, nbytes, int(nw * bits / 8))
         dt = time.perf_counter() - t0
-        plans.append({"bits_per_weight": bits, "choice": [configs[c] for c in got[0]],
-                      "error_vs_all_nf4": round(got[1] / float(err[:, 0].sum()), 4),
+        plans.append({"bits_per_weight": bits,
+                      "choice": [f"{configs[c][0]}/{configs[c][1]}" for c in got[0]],
+                      "error_vs_all_nf4_64": round(got[1] / float(err[:, 0].sum()), 4),
                       "plan_ms": round(dt * 1e3, 3)})
     del Ws, ws
     torch.cuda.empty_cache()
-    return {"matrices": len(wl.weights), "configs": list(configs), "weights": nw,
-            "table_ms": round(ms, 3), "table_GB/s": round(moved / (ms * 1e-3) / 1e9, 1),
-            "plans": plans}
+    return {"matrices": len(wl.weights), "configs": [f"{c}/{b}" for c, b in configs],
+            "weights": nw, "table_ms": round(ms, 3),
+            "table_GB/s": round(moved / (ms * 1e-3) / 1e9, 1), "plans": plans}
 
 
-def code_step(qn, L, torch, layers, M, r, s, sp, steps, warmup, flops_step, code):
+def code_step(qn, L, torch, layers, M, r, s, sp, steps, warmup, flops_step, code, blocksize=64):
     """The same fused forward + backward step with the weights quantized to
-    another code type (same kernels, other code table and width)."""
+    another code type or block size (same kernels, other code table, code
+    width or constant indexing)."""
     from quantized_base_lora_nf4_amd._lib import check
-    qw = [qn.nf4_quantize(t["Wf32"], code=code) for t in layers]
+    qw = [qn.nf4_quantize(t["Wf32"], code=code, blocksize=blocksize) for t in layers]
     sts = [w.struct() for w in qw]
 
     def p(x):

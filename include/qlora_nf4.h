@@ -27,11 +27,13 @@
  *   Backward: dU = s dY B;  dX = dY W + dU A;  dA = dU^T X;  dB = s dY^T (X A^T)
  *   where W is the dequantized weight; there is no gradient for W.
  *
- * NF4 storage of W (the "nf4 tensor"):
+ * NF4 storage of W (the "nf4 tensor"), block size B = 64 by default (128
+ * and 256 are offered too: the LQ-LoRA abstract's integer program chooses
+ * the block size per matrix):
  *   codes [N*K/2] uint8  two 4-bit level indices per byte, element 2j of the
  *                        row-major flattening in the low nibble of byte j
- *   q8    [N*K/64] uint8 8-bit absmax constant of each 64-element block
- *   step  [ceil(N*K/64/256)] fp32  per group of 256 consecutive blocks:
+ *   q8    [N*K/B] uint8  8-bit absmax constant of each B-element block
+ *   step  [ceil(N*K/B/256)] fp32  per group of 256 consecutive blocks:
  *                        the group's largest absmax divided by 255
  *   Dequantized weight: w = bf16_rne(level[code] * (q8 * step)), both
  *   products rounded to fp32.
@@ -118,11 +120,13 @@ extern "C" {
 /* The quantized frozen weight.  All pointers are device pointers. */
 typedef struct nf4_tensor_t {
   const uint8_t* codes; /* [N*K*k/8], k = bits of code_type */
-  const uint8_t* q8;    /* [N*K/64] */
-  const float* step;    /* [ceil(N*K/16384)] */
+  const uint8_t* q8;    /* [N*K/blocksize] */
+  const float* step;    /* [ceil(N*K/blocksize/256)] */
   int64_t N;
   int64_t K;
-  int32_t blocksize;    /* must be 64  */
+  int32_t blocksize;    /* 64, 128 or 256, dividing K (others give
+                           QLORA_ERR_UNSUPPORTED; K not a multiple of it,
+                           QLORA_ERR_INVALID) */
   int32_t dq_blocksize; /* must be 256 */
   int32_t code_type;    /* QLORA_CODE_* (the type it was quantized with);
                            others give QLORA_ERR_UNSUPPORTED */
@@ -149,6 +153,12 @@ void nf4_code_table(float* levels16, float* thresholds15);
  * pointer may be NULL; no device work. */
 int32_t qlora_code_table(int32_t code_type, float* levels16, float* thresholds15);
 
+/* Bytes of the three arrays of one configuration (code type, block size 64,
+ * 128 or 256) for an N x K weight: N*K*k/8 + N*K/B + 4*ceil(N*K/B/256), k
+ * the code width and B the block size; 0 for invalid sizes, an unknown code
+ * type or an unsupported block size. */
+size_t qlora_config_bytes(int32_t code_type, int32_t blocksize, int64_t N, int64_t K);
+
 /* Bytes of the three NF4 arrays for an N x K weight (closed form:
  * N*K/2 + N*K/64 + 4*ceil(N*K/16384)); 0 for invalid sizes. */
 size_t nf4_storage_bytes(int64_t N, int64_t K);
@@ -165,7 +175,9 @@ size_t qlora_storage_bytes(int32_t code_type, int64_t N, int64_t K);
  *
  *   W      [N, K] fp32, device.  Must be finite.
  *   N, K   N >= 1, K >= 64, K % 64 == 0.
- *   blocksize, dq_blocksize   must be 64 and 256.
+ *   blocksize, dq_blocksize   64, 128 or 256 (dividing K), and 256; codes
+ *          are packed in 64-element units whatever the block size, q8 has
+ *          N*K/blocksize bytes and step ceil(N*K/blocksize/256) floats.
  *   codes  [N*K/2] out;  q8 [N*K/64] out;  step [ceil(N*K/16384)] out.
  * Per block b of 64 consecutive elements: c_b = max|w|; each element gets
  * the level nearest to fl32(w / c_b) (ties to the lower level; an all-zero
@@ -340,9 +352,10 @@ int32_t qlora_lq_init(const float* W, int64_t N, int64_t K, int32_t code_type,
  * Decomposition for Efficient Language Model Finetuning") chooses each
  * matrix's quantization parameters by an integer linear program so that the
  * model meets an overall memory budget.  Here a configuration is a code type
- * (QLORA_CODE_*; block size 64 with double quantization, what the layer
- * takes), its memory the state bytes (qlora_storage_bytes) and its error on
- * a matrix the squared Frobenius error of the quantized part.
+ * (QLORA_CODE_*) and a block size (64, 128 or 256, with double
+ * quantization; the layer takes all of them), its memory the state bytes
+ * (qlora_config_bytes) and its error on a matrix the squared Frobenius
+ * error of the quantized part.
  *
  * qlora_quant_error -- *sq_err = ||R - W_hat(R)||_F^2 in fp64, where
  * R = W, or R = W - L1 L2t^T when L1 and L2t are given (the decomposition
@@ -361,6 +374,19 @@ int32_t qlora_quant_error(const float* W, int64_t N, int64_t K,
                           int32_t code_type, const float* L1, const float* L2t,
                           int32_t r, double* sq_err, void* ws, size_t ws_bytes,
                           hipStream_t stream);
+
+/* qlora_config_error -- qlora_quant_error for any configuration: code type
+ * and block size (64, 128 or 256, dividing K; the abstract's "bit-width,
+ * block size"); qlora_quant_error is this call at block size 64.  The
+ * workspace is sized by qlora_config_error_workspace_size. */
+size_t qlora_config_error_workspace_size(int64_t N, int64_t K,
+                                         int32_t code_type, int32_t blocksize,
+                                         int32_t with_lowrank);
+int32_t qlora_config_error(const float* W, int64_t N, int64_t K,
+                           int32_t code_type, int32_t blocksize,
+                           const float* L1, const float* L2t, int32_t r,
+                           double* sq_err, void* ws, size_t ws_bytes,
+                           hipStream_t stream);
 
 /* qlora_ilp_plan -- host only, no device work.  Given, for M matrices and
  * C configurations, the errors err[m*C + c] (finite) and the bytes

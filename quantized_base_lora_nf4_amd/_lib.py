@@ -49,6 +49,9 @@ EXPORTS = (
     "qlora_quant_error_workspace_size",
     "qlora_quant_error",
     "qlora_ilp_plan",
+    "qlora_config_bytes",
+    "qlora_config_error_workspace_size",
+    "qlora_config_error",
 )
 
 
@@ -127,6 +130,12 @@ def lib() -> ctypes.CDLL:
     L.qlora_quant_error_workspace_size.argtypes = [i64, i64, i32, i32]
     L.qlora_quant_error.restype = i32
     L.qlora_quant_error.argtypes = [vp, i64, i64, i32, vp, vp, i32, vp, vp, sz, vp]
+    L.qlora_config_bytes.restype = sz
+    L.qlora_config_bytes.argtypes = [i32, i32, i64, i64]
+    L.qlora_config_error_workspace_size.restype = sz
+    L.qlora_config_error_workspace_size.argtypes = [i64, i64, i32, i32, i32]
+    L.qlora_config_error.restype = i32
+    L.qlora_config_error.argtypes = [vp, i64, i64, i32, i32, vp, vp, i32, vp, vp, sz, vp]
     L.qlora_ilp_plan.restype = i32
     L.qlora_ilp_plan.argtypes = [i32, i32, vp, vp, i64, vp, vp, vp]
     _lib = L

@@ -83,11 +83,32 @@ inline bool code_ok(int32_t code_type) {
          code_type == QLORA_CODE_NF3 || code_type == QLORA_CODE_NF2;
 }
 
+// Block sizes 64, 128, 256 as 64 << shift; -1 for others.
+inline int bshift_of(int32_t blocksize) {
+  return blocksize == 64 ? 0 : blocksize == 128 ? 1 : blocksize == 256 ? 2 : -1;
+}
+
+// Configuration of a quantized weight: a supported block size, DQ block
+// size and code type (else QLORA_ERR_UNSUPPORTED), and K a multiple of the
+// block size (else QLORA_ERR_INVALID).
 int32_t nf4_supported(const nf4_tensor_t* w) {
-  return (w->blocksize == QLORA_NF4_BLOCKSIZE && w->dq_blocksize == QLORA_NF4_DQ_BLOCKSIZE &&
-          code_ok(w->code_type))
-             ? QLORA_OK
-             : QLORA_ERR_UNSUPPORTED;
+  if (bshift_of(w->blocksize) < 0 || w->dq_blocksize != QLORA_NF4_DQ_BLOCKSIZE ||
+      !code_ok(w->code_type))
+    return QLORA_ERR_UNSUPPORTED;
+  return (w->K % w->blocksize) == 0 ? QLORA_OK : QLORA_ERR_INVALID;
+}
+
+inline Nf4View view_of(const nf4_tensor_t* w) {
+  return Nf4View{w->codes, w->q8, w->step, w->N, w->K, w->code_type, bshift_of(w->blocksize)};
+}
+
+size_t config_bytes(int32_t code_type, int32_t blocksize, int64_t N, int64_t K) {
+  if (!code_ok(code_type) || bshift_of(blocksize) < 0 || N < 1 || K < 64 || (K % 64) != 0 ||
+      (K % blocksize) != 0)
+    return 0;
+  const int64_t nb = N * K / blocksize;
+  const int64_t bits = with_code(code_type, [](auto ct) { return decltype(ct)::kBits; });
+  return (size_t)(N * K / 8 * bits) + (size_t)nb + 4 * (size_t)((nb + 255) / 256);
 }
 
 static_assert(CodeNF4::kId == QLORA_CODE_NF4 && CodeFP4::kId == QLORA_CODE_FP4 &&
@@ -109,12 +130,14 @@ int32_t quantize(const float* W, int64_t N, int64_t K, int32_t code_type, int32_
                  hipStream_t stream) {
   if (!W || !codes || !q8 || !step) return QLORA_ERR_INVALID;
   if (N < 1 || K < 64 || (K % 64) != 0 || N > ((int64_t)1 << 40) / K) return QLORA_ERR_INVALID;
-  if (blocksize != QLORA_NF4_BLOCKSIZE || dq_blocksize != QLORA_NF4_DQ_BLOCKSIZE ||
-      !code_ok(code_type))
+  const int bs = bshift_of(blocksize);
+  if (bs < 0 || dq_blocksize != QLORA_NF4_DQ_BLOCKSIZE || !code_ok(code_type))
     return QLORA_ERR_UNSUPPORTED;
+  if ((K % blocksize) != 0) return QLORA_ERR_INVALID;
   if (!aligned16(W) || !aligned16(codes) || !aligned16(q8) || !aligned16(step))
     return QLORA_ERR_INVALID;
-  return launch_status(launch_nf4_quantize(W, N * K / 64, codes, q8, step, code_type, stream));
+  return launch_status(
+      launch_nf4_quantize(W, N * K / blocksize, codes, q8, step, code_type, bs, stream));
 }
 
 }  // namespace
@@ -146,10 +169,11 @@ int32_t qlora_code_table(int32_t code_type, float* levels16, float* thresholds15
 }
 
 size_t qlora_storage_bytes(int32_t code_type, int64_t N, int64_t K) {
-  if (!code_ok(code_type) || N < 1 || K < 64 || (K % 64) != 0) return 0;
-  const int64_t nb = N * K / 64;
-  const int64_t bits = with_code(code_type, [](auto ct) { return decltype(ct)::kBits; });
-  return (size_t)(N * K / 8 * bits) + (size_t)nb + 4 * (size_t)((nb + 255) / 256);
+  return config_bytes(code_type, QLORA_NF4_BLOCKSIZE, N, K);
+}
+
+size_t qlora_config_bytes(int32_t code_type, int32_t blocksize, int64_t N, int64_t K) {
+  return config_bytes(code_type, blocksize, N, K);
 }
 
 size_t nf4_storage_bytes(int64_t N, int64_t K) {
@@ -177,8 +201,8 @@ int32_t nf4_dequantize(const nf4_tensor_t* w, uint16_t* W_bf16, hipStream_t stre
   if (sup != QLORA_OK) return sup;
   if (!aligned16(w->codes) || !aligned16(w->q8) || !aligned16(w->step) || !aligned16(W_bf16))
     return QLORA_ERR_INVALID;
-  return launch_status(
-      launch_nf4_dequantize(w->codes, w->q8, w->step, w->N * w->K, W_bf16, w->code_type, stream));
+  return launch_status(launch_nf4_dequantize(w->codes, w->q8, w->step, w->N * w->K, W_bf16,
+                                             w->code_type, bshift_of(w->blocksize), stream));
 }
 
 size_t qlora_workspace_size(int64_t M, int64_t N, int64_t K, int32_t r, int32_t for_bwd) {
@@ -221,7 +245,7 @@ int32_t linear_fwd(const nf4_tensor_t* w, const uint16_t* X, int64_t M, const ui
   char* base = static_cast<char*>(ws);
   uint16_t* ws_u = reinterpret_cast<uint16_t*>(base + pl.u_off);
   float* part = reinterpret_cast<float*>(base + pl.part_off);
-  const Nf4View v{w->codes, w->q8, w->step, N, K, w->code_type};
+  const Nf4View v = view_of(w);
   const int64_t rp = rank_pad(r);
 
   if (gemv_fits(M, r, K))
@@ -288,7 +312,7 @@ int32_t linear_bwd(const nf4_tensor_t* w, const uint16_t* X, const uint16_t* dY,
 
   // dX = dY W + dU A
   if (dX) {
-    const Nf4View v{w->codes, w->q8, w->step, N, K, w->code_type};
+    const Nf4View v = view_of(w);
     if (record(ev0, stream) != hipSuccess) return QLORA_ERR_LAUNCH;
     e = launch_qgemm_bwd(v, dY, M, ws_du, rp, A, r, dX, stream);
     if (e != hipSuccess || record(ev1, stream) != hipSuccess) return QLORA_ERR_LAUNCH;
@@ -423,27 +447,42 @@ int32_t qlora_lq_init(const float* W, int64_t N, int64_t K, int32_t code_type, i
 
 extern "C" {
 
-size_t qlora_quant_error_workspace_size(int64_t N, int64_t K, int32_t code_type,
-                                        int32_t with_lowrank) {
-  if (!code_ok(code_type) || N < 1 || K < 64 || (K % 64) != 0 || N > ((int64_t)1 << 40) / K)
+size_t qlora_config_error_workspace_size(int64_t N, int64_t K, int32_t code_type,
+                                         int32_t blocksize, int32_t with_lowrank) {
+  if (!code_ok(code_type) || bshift_of(blocksize) < 0 || N < 1 || K < 64 || (K % 64) != 0 ||
+      (K % blocksize) != 0 || N > ((int64_t)1 << 40) / K)
     return 0;
   const int bits = with_code(code_type, [](auto ct) { return decltype(ct)::kBits; });
-  return qn::quant_error_workspace_bytes(N, K, bits, with_lowrank != 0);
+  return qn::quant_error_workspace_bytes(N, K, bits, bshift_of(blocksize), with_lowrank != 0);
 }
 
-int32_t qlora_quant_error(const float* W, int64_t N, int64_t K, int32_t code_type,
-                          const float* L1, const float* L2t, int32_t r, double* sq_err, void* ws,
-                          size_t ws_bytes, hipStream_t stream) {
+size_t qlora_quant_error_workspace_size(int64_t N, int64_t K, int32_t code_type,
+                                        int32_t with_lowrank) {
+  return qlora_config_error_workspace_size(N, K, code_type, QLORA_NF4_BLOCKSIZE, with_lowrank);
+}
+
+int32_t qlora_config_error(const float* W, int64_t N, int64_t K, int32_t code_type,
+                           int32_t blocksize, const float* L1, const float* L2t, int32_t r,
+                           double* sq_err, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!W || !sq_err || !ws || ((L1 == nullptr) != (L2t == nullptr))) return QLORA_ERR_INVALID;
-  if (!code_ok(code_type)) return QLORA_ERR_UNSUPPORTED;
-  const size_t need = qlora_quant_error_workspace_size(N, K, code_type, L1 != nullptr);
+  if (!code_ok(code_type) || bshift_of(blocksize) < 0) return QLORA_ERR_UNSUPPORTED;
+  const size_t need =
+      qlora_config_error_workspace_size(N, K, code_type, blocksize, L1 != nullptr);
   if (need == 0) return QLORA_ERR_INVALID;
   if (L1 && (r < 1 || r > QLORA_LQ_MAX_L || !aligned16(L1) || !aligned16(L2t)))
     return QLORA_ERR_INVALID;
   if (!aligned16(W) || ((uintptr_t)sq_err & 7u) != 0 || ((uintptr_t)ws & 255u) != 0)
     return QLORA_ERR_INVALID;
   if (ws_bytes < need) return QLORA_ERR_WORKSPACE;
-  return launch_status(qn::launch_quant_error(W, N, K, code_type, L1, L2t, r, sq_err, ws, stream));
+  return launch_status(qn::launch_quant_error(W, N, K, code_type, bshift_of(blocksize), L1, L2t,
+                                              r, sq_err, ws, stream));
+}
+
+int32_t qlora_quant_error(const float* W, int64_t N, int64_t K, int32_t code_type,
+                          const float* L1, const float* L2t, int32_t r, double* sq_err, void* ws,
+                          size_t ws_bytes, hipStream_t stream) {
+  return qlora_config_error(W, N, K, code_type, QLORA_NF4_BLOCKSIZE, L1, L2t, r, sq_err, ws,
+                            ws_bytes, stream);
 }
 
 int32_t qlora_ilp_plan(int32_t n_matrices, int32_t n_configs, const double* err,

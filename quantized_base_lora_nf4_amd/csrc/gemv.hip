@@ -108,6 +108,7 @@ struct GemvArgs {
   float s;
   uint16_t* Y;
   uint16_t* U_out;  // nullable, bf16 [M][r]
+  int bshift;       // block size 64 << bshift
 };
 
 #ifndef QN_GEMV_PD
@@ -234,7 +235,18 @@ __global__ __launch_bounds__(64 * KW) void k_qgemv(GemvArgs p) {
     const int b = e >> 4;  // copy e % 16 of entry b
     lut[e] = pack_bf16x2(code_value<CT>(b & 15), code_value<CT>(b >> 4));
   }
-  {
+  if (p.bshift > 0) {
+    // blocks of 64 << bshift: each 64-element block takes the constant of
+    // the block it lies in (rows past N take the last row's)
+    const int bs = p.bshift;
+    const int64_t cblocks = kblocks >> bs;
+    for (int64_t e = tid; e < 16 * G * kblocks; e += NT) {
+      const int64_t row = e / kblocks, kb = e - row * kblocks;
+      const int64_t n = n0 + row < N ? n0 + row : N - 1;
+      const int64_t ci = n * cblocks + (kb >> bs);
+      chat_t[row * kbs + kb] = (float)p.q8[ci] * p.step[ci >> 8];
+    }
+  } else {
     // The workgroup's constants are the contiguous q8 range starting at
     // n0 kblocks (a multiple of 16 bytes), 16 G kblocks bytes long; rows
     // past N read clamped bytes (their results are dropped).
@@ -391,7 +403,8 @@ hipError_t launch_qgemv(const Nf4View& w, const uint16_t* X, int64_t M, const ui
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
-  const GemvArgs a{w.codes, w.q8, w.step, X, M, w.N, w.K, upart, (int32_t)gu.x, B, r, s, Y, U_out};
+  const GemvArgs a{w.codes, w.q8, w.step, X,     M, w.N, w.K,  upart, (int32_t)gu.x,
+                   B,       r,    s,      Y, U_out, w.bshift};
   const int64_t kblocks = w.K / 64;
   // 16 G weight rows per workgroup, K split over its 8 waves.
   //  - G = 7 when the 16-row groups make exactly one workgroup of 7 per CU

@@ -26,7 +26,7 @@ __global__ __launch_bounds__(256) void k_sq_error(const float* __restrict__ R,
                                                   const uint8_t* __restrict__ codes,
                                                   const uint8_t* __restrict__ q8,
                                                   const float* __restrict__ step, int64_t n8,
-                                                  double* __restrict__ part) {
+                                                  int bshift, double* __restrict__ part) {
   __shared__ float lv[16];
   __shared__ double red[256];
   if (threadIdx.x < 16) lv[threadIdx.x] = code_value<CT>(threadIdx.x);
@@ -42,7 +42,8 @@ __global__ __launch_bounds__(256) void k_sq_error(const float* __restrict__ R,
       w = nibbles<CT>(load_half<CT>(codes + b * block_bytes<CT>() + ((i >> 2) & 1) * half_bytes<CT>()),
                       (int)(i & 3));
     }
-    const float chat = (float)q8[b] * step[b >> 8];
+    const int64_t cb = b >> bshift;  // the block of 64 << bshift elements
+    const float chat = (float)q8[cb] * step[cb >> 8];
     const f32x4 r0 = *reinterpret_cast<const f32x4*>(R + i * 8);
     const f32x4 r1 = *reinterpret_cast<const f32x4*>(R + i * 8 + 4);
 #pragma unroll
@@ -85,7 +86,7 @@ struct ErrPlan {
   size_t r_off, codes_off, q8_off, step_off, part_off, total;
 };
 
-ErrPlan err_plan(int64_t N, int64_t K, int bits, bool lowrank) {
+ErrPlan err_plan(int64_t N, int64_t K, int bits, int bshift, bool lowrank) {
   ErrPlan p{};
   size_t o = 0;
   auto take = [&](size_t b) {
@@ -93,7 +94,7 @@ ErrPlan err_plan(int64_t N, int64_t K, int bits, bool lowrank) {
     o += al(b);
     return at;
   };
-  const int64_t nb = N * K / 64;
+  const int64_t nb = N * K / (64 << bshift);
   p.r_off = lowrank ? take(4 * (size_t)N * K) : 0;
   p.codes_off = take((size_t)(N * K / 8 * bits));
   p.q8_off = take((size_t)nb);
@@ -105,16 +106,16 @@ ErrPlan err_plan(int64_t N, int64_t K, int bits, bool lowrank) {
 
 }  // namespace
 
-size_t quant_error_workspace_bytes(int64_t N, int64_t K, int bits, bool lowrank) {
-  return err_plan(N, K, bits, lowrank).total;
+size_t quant_error_workspace_bytes(int64_t N, int64_t K, int bits, int bshift, bool lowrank) {
+  return err_plan(N, K, bits, bshift, lowrank).total;
 }
 
-hipError_t launch_quant_error(const float* W, int64_t N, int64_t K, int code, const float* L1,
-                              const float* L2t, int r, double* sq_err, void* ws,
+hipError_t launch_quant_error(const float* W, int64_t N, int64_t K, int code, int bshift,
+                              const float* L1, const float* L2t, int r, double* sq_err, void* ws,
                               hipStream_t stream) {
   const int bits = with_code(code, [](auto ct) { return decltype(ct)::kBits; });
   const bool lowrank = L1 != nullptr;
-  const ErrPlan pl = err_plan(N, K, bits, lowrank);
+  const ErrPlan pl = err_plan(N, K, bits, bshift, lowrank);
   char* base = static_cast<char*>(ws);
   const float* R = W;
   if (lowrank) {
@@ -127,11 +128,12 @@ hipError_t launch_quant_error(const float* W, int64_t N, int64_t K, int code, co
   uint8_t* q8 = reinterpret_cast<uint8_t*>(base + pl.q8_off);
   float* step = reinterpret_cast<float*>(base + pl.step_off);
   double* part = reinterpret_cast<double*>(base + pl.part_off);
-  hipError_t e = launch_nf4_quantize(R, N * K / 64, codes, q8, step, code, stream);
+  hipError_t e =
+      launch_nf4_quantize(R, N * K / (64 << bshift), codes, q8, step, code, bshift, stream);
   if (e != hipSuccess) return e;
   with_code(code, [&](auto ct) {
     hipLaunchKernelGGL(k_sq_error<decltype(ct)>, dim3(kErrBlocks), dim3(256), 0, stream, R, codes,
-                       q8, step, N * K / 8, part);
+                       q8, step, N * K / 8, bshift, part);
     return 0;
   });
   if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -7,10 +7,13 @@
 namespace qn {
 
 // ---- nf4_quant.hip ----  (code: kId of CodeNF4, CodeFP4, CodeNF3 or CodeNF2)
+// Blocks of 64 << bshift elements (bshift 0, 1, 2: block size 64, 128, 256);
+// nblocks counts those blocks.
 hipError_t launch_nf4_quantize(const float* W, int64_t nblocks, uint8_t* codes, uint8_t* q8,
-                               float* step, int code, hipStream_t stream);
+                               float* step, int code, int bshift, hipStream_t stream);
 hipError_t launch_nf4_dequantize(const uint8_t* codes, const uint8_t* q8, const float* step,
-                                 int64_t nelem, uint16_t* out, int code, hipStream_t stream);
+                                 int64_t nelem, uint16_t* out, int code, int bshift,
+                                 hipStream_t stream);
 
 // ---- qgemm.hip: MFMA tile kernels with the NF4 dequantization in the prologue ----
 struct Nf4View {
@@ -18,7 +21,8 @@ struct Nf4View {
   const uint8_t* q8;
   const float* step;
   int64_t N, K;
-  int code;  // kId of CodeNF4, CodeFP4, CodeNF3 or CodeNF2
+  int code;    // kId of CodeNF4, CodeFP4, CodeNF3 or CodeNF2
+  int bshift;  // block size 64 << bshift (K is a multiple of it)
 };
 
 // Y[M,N] = X[M,K] W^T + bf16(s U)[M,r] B[N,r]^T.  U has row stride ldu (a
@@ -110,10 +114,10 @@ hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int
                               hipStream_t stream);
 
 // ---- ilp.hip: configuration errors and the budget program ----
-size_t quant_error_workspace_bytes(int64_t N, int64_t K, int bits, bool lowrank);
+size_t quant_error_workspace_bytes(int64_t N, int64_t K, int bits, int bshift, bool lowrank);
 // *sq_err (device) = ||R - W_hat(R)||_F^2, R = W or W - L1 L2t^T (L1 non-null)
-hipError_t launch_quant_error(const float* W, int64_t N, int64_t K, int code, const float* L1,
-                              const float* L2t, int r, double* sq_err, void* ws,
+hipError_t launch_quant_error(const float* W, int64_t N, int64_t K, int code, int bshift,
+                              const float* L1, const float* L2t, int r, double* sq_err, void* ws,
                               hipStream_t stream);
 // host: exact minimum-error choice within the budget; false if none fits
 bool ilp_plan(int M, int C, const double* err, const int64_t* bytes, int64_t budget,

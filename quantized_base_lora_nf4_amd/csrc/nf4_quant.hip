@@ -7,10 +7,12 @@
 // coarser level) and the capability page "Qlora 4 Bit Quantization With Nf4
 // Fp4 Data Types And Lora Adapters", NF4 entry (block-wise absmax scaling).
 //
-// Layout: one workgroup per group of 256 consecutive 64-element blocks
-// (16384 fp32 = 64 KB of W).  Each wave walks 64 blocks, four at a time:
-// sixteen lanes share a block and each lane owns four consecutive elements,
-// so every load instruction reads 1 KB of contiguous W.  4-bit codes are
+// Layout: one workgroup per group of 256 consecutive blocks (blocks of 64,
+// 128 or 256 elements: 64, 128 or 256 KB of W).  Each wave walks a quarter
+// of the group, 256 elements per load instruction (1 KB of contiguous W):
+// each lane owns four consecutive elements, and the 16, 32 or 64 lanes of a
+// block reduce its absmax by butterfly shuffles.  Codes are packed in
+// 64-element units whatever the block size.  4-bit codes are
 // stored by every lane (128 contiguous bytes per instruction); 3- and 2-bit
 // codes are ORed into their half block's words across the eight lanes of
 // the half and stored by its first lane.  The kernel is bound by HBM (4 B
@@ -81,34 +83,39 @@ __device__ __forceinline__ float div_refined(float a, float b, float r) {
   return __builtin_fmaf(e, r, q);
 }
 
-template <class CT>
+// Block size 64 << BS (BS = 0, 1, 2: 64, 128, 256 elements per constant).
+template <class CT, int BS>
 __global__ __launch_bounds__(256) void k_nf4_quantize(const float* __restrict__ W,
                                                       int64_t nblocks,
                                                       uint8_t* __restrict__ codes,
                                                       uint8_t* __restrict__ q8,
                                                       float* __restrict__ step) {
+  constexpr int kLanesPerBlock = 16 << BS;  // four elements per lane
   __shared__ float cabs[256];
   __shared__ float wmax[4];
   __shared__ uint2 bucket[kBuckets];
   build_buckets<CT>(bucket);
   __syncthreads();
   const int64_t g = blockIdx.x;
-  const int64_t b0 = g * 256;
+  const int64_t b0 = g * 256;  // first block of the group
   const int nb = (int)((nblocks - b0) < 256 ? (nblocks - b0) : 256);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int sub = lane & 15;  // lane within the block: elements 4*sub .. 4*sub+3
+  const int sub = lane & 15;  // lane within its 64-element unit: elements 4*sub .. 4*sub+3
 
-  for (int it = 0; it < 16; ++it) {
-    const int bi = wave * 64 + it * 4 + (lane >> 4);  // block within the group
+  // Each wave walks a quarter of the group, 256 elements (a 64-lane
+  // instruction of 16 bytes each) per iteration.
+  for (int it = 0; it < (16 << BS); ++it) {
+    const int64_t e0 = (((int64_t)wave << (4 + BS)) + it) * 256 + 4 * lane;  // element in group
+    const int bi = (int)(e0 >> (6 + BS));                                    // block in group
     if (bi < nb) {
-      const int64_t b = b0 + bi;
-      const f32x4 v = *reinterpret_cast<const f32x4*>(W + b * 64 + sub * 4);
+      const int64_t e = (b0 << (6 + BS)) + e0;  // element index in W
+      const int64_t u = e >> 6;                 // its 64-element packing unit
+      const f32x4 v = *reinterpret_cast<const f32x4*>(W + e);
       float m = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
-      m = fmaxf(m, __shfl_xor(m, 8, 16));
-      m = fmaxf(m, __shfl_xor(m, 4, 16));
-      m = fmaxf(m, __shfl_xor(m, 2, 16));
-      m = fmaxf(m, __shfl_xor(m, 1, 16));
+#pragma unroll
+      for (int off = kLanesPerBlock / 2; off >= 1; off >>= 1)
+        m = fmaxf(m, __shfl_xor(m, off, kLanesPerBlock));
       uint32_t c0, c1, c2, c3;
       if (m >= 0x1p-60f && m <= 0x1p126f) {
         const float r = 1.0f / m;  // IEEE-correct fp32 division
@@ -127,9 +134,9 @@ __global__ __launch_bounds__(256) void k_nf4_quantize(const float* __restrict__ 
       }
       if constexpr (CT::kBits == 4) {
         const uint16_t packed = (uint16_t)(c0 | (c1 << 4) | (c2 << 8) | (c3 << 12));
-        *reinterpret_cast<uint16_t*>(codes + b * 32 + sub * 2) = packed;
+        *reinterpret_cast<uint16_t*>(codes + u * 32 + sub * 2) = packed;
       } else {
-        // elements 4 sub + t = 32 h + 8 g + 2 i + p of the block
+        // elements 4 sub + t = 32 h + 8 g + 2 i + p of the unit
         const int h = sub >> 3, g = (sub >> 1) & 3, i0 = 2 * (sub & 1);
         const uint32_t cc[4] = {c0, c1, c2, c3};
         uint32_t wv[3] = {0u, 0u, 0u};
@@ -147,12 +154,12 @@ __global__ __launch_bounds__(256) void k_nf4_quantize(const float* __restrict__ 
         }
         if ((sub & 7) == 0) {
           uint32_t* dst =
-              reinterpret_cast<uint32_t*>(codes + b * block_bytes<CT>() + h * half_bytes<CT>());
+              reinterpret_cast<uint32_t*>(codes + u * block_bytes<CT>() + h * half_bytes<CT>());
 #pragma unroll
           for (int j = 0; j < CT::kBits; ++j) dst[j] = wv[j];
         }
       }
-      if (sub == 0) cabs[bi] = m;
+      if ((lane & (kLanesPerBlock - 1)) == 0) cabs[bi] = m;
     }
   }
   __syncthreads();
@@ -183,7 +190,8 @@ template <class CT>
 __global__ __launch_bounds__(256) void k_nf4_dequantize(const uint8_t* __restrict__ codes,
                                                         const uint8_t* __restrict__ q8,
                                                         const float* __restrict__ step,
-                                                        int64_t n8, uint16_t* __restrict__ out) {
+                                                        int64_t n8, int bshift,
+                                                        uint16_t* __restrict__ out) {
   __shared__ float lv[16];
   if (threadIdx.x < 16) lv[threadIdx.x] = code_value<CT>(threadIdx.x);
   __syncthreads();
@@ -197,7 +205,8 @@ __global__ __launch_bounds__(256) void k_nf4_dequantize(const uint8_t* __restric
       const int hh = (int)((i >> 2) & 1), g = (int)(i & 3);
       w = nibbles<CT>(load_half<CT>(codes + b * block_bytes<CT>() + hh * half_bytes<CT>()), g);
     }
-    const float chat = (float)q8[b] * step[b >> 8];
+    const int64_t cb = b >> bshift;  // the block of 64 << bshift elements
+    const float chat = (float)q8[cb] * step[cb >> 8];
     u32x4 o;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -210,23 +219,32 @@ __global__ __launch_bounds__(256) void k_nf4_dequantize(const uint8_t* __restric
 }
 
 hipError_t launch_nf4_quantize(const float* W, int64_t nblocks, uint8_t* codes, uint8_t* q8,
-                               float* step, int code, hipStream_t stream) {
+                               float* step, int code, int bshift, hipStream_t stream) {
   const int64_t ngroups = (nblocks + 255) / 256;
   return with_code(code, [&](auto ct) {
-    hipLaunchKernelGGL(k_nf4_quantize<decltype(ct)>, dim3((unsigned)ngroups), dim3(256), 0,
-                       stream, W, nblocks, codes, q8, step);
+    using CT = decltype(ct);
+    if (bshift == 2)
+      hipLaunchKernelGGL((k_nf4_quantize<CT, 2>), dim3((unsigned)ngroups), dim3(256), 0, stream, W,
+                         nblocks, codes, q8, step);
+    else if (bshift == 1)
+      hipLaunchKernelGGL((k_nf4_quantize<CT, 1>), dim3((unsigned)ngroups), dim3(256), 0, stream, W,
+                         nblocks, codes, q8, step);
+    else
+      hipLaunchKernelGGL((k_nf4_quantize<CT, 0>), dim3((unsigned)ngroups), dim3(256), 0, stream, W,
+                         nblocks, codes, q8, step);
     return hipGetLastError();
   });
 }
 
 hipError_t launch_nf4_dequantize(const uint8_t* codes, const uint8_t* q8, const float* step,
-                                 int64_t nelem, uint16_t* out, int code, hipStream_t stream) {
+                                 int64_t nelem, uint16_t* out, int code, int bshift,
+                                 hipStream_t stream) {
   const int64_t n8 = nelem / 8;
   int64_t grid = (n8 + 255) / 256;
   if (grid > 65536) grid = 65536;
   return with_code(code, [&](auto ct) {
     hipLaunchKernelGGL(k_nf4_dequantize<decltype(ct)>, dim3((unsigned)grid), dim3(256), 0, stream,
-                       codes, q8, step, n8, out);
+                       codes, q8, step, n8, bshift, out);
     return hipGetLastError();
   });
 }

@@ -400,8 +400,11 @@ struct FwdArgs {
 // requires), so the constants of four consecutive blocks of a weight row are
 // one aligned 32-bit word (and share one second-level step: 4 divides 256).  The row's constants are then
 // loaded once per four steps instead of a byte and a float per step.
-template <class C, class CT, bool kQ4>
+// BS: block size 64 << BS (one 8-bit constant per 64 << BS weights of a row;
+// kQ4 only with BS = 0).
+template <class C, class CT, bool kQ4, int BS>
 __global__ __launch_bounds__(C::NT, 1) void k_qgemm_fwd(FwdArgs p) {
+  static_assert(!kQ4 || BS == 0, "grouped constants need 64-element blocks");
   // One LDS object per buffer: the compiler's wait for a direct-to-LDS load
   // then applies only to reads of the buffer that load writes.
   __shared__ __attribute__((aligned(16))) uint16_t xs0[C::TILE_A];
@@ -423,8 +426,9 @@ __global__ __launch_bounds__(C::NT, 1) void k_qgemm_fwd(FwdArgs p) {
   // ABI keeps the codes under 2 GiB): a per-thread offset plus the step's
   // uniform offset, so the per-step address arithmetic is scalar.
   const __amdgpu_buffer_rsrc_t crs = bytes_rsrc(p.codes, N * kblocks * block_bytes<CT>());
-  const __amdgpu_buffer_rsrc_t qrs = bytes_rsrc(p.q8, N * kblocks);
-  const __amdgpu_buffer_rsrc_t srs = bytes_rsrc(p.step, 4 * ((N * kblocks + 255) >> 8));
+  const int64_t cblocks = kblocks >> BS;  // constants per weight row
+  const __amdgpu_buffer_rsrc_t qrs = bytes_rsrc(p.q8, N * cblocks);
+  const __amdgpu_buffer_rsrc_t srs = bytes_rsrc(p.step, 4 * ((N * cblocks + 255) >> 8));
   const __amdgpu_buffer_rsrc_t xrsrc = rows_rsrc(p.X, K, m0, M);
   auto load_x = [&](uint16_t* As_dst, int64_t kt) {
     if (kt >= kblocks) kt = kblocks - 1;
@@ -439,7 +443,7 @@ __global__ __launch_bounds__(C::NT, 1) void k_qgemm_fwd(FwdArgs p) {
     int64_t gn = n0 + wrow;
     if (gn >= N) gn = N - 1;
     const int wvoff = (int)(gn * kblocks * block_bytes<CT>());
-    const int64_t wblk0 = gn * kblocks;
+    const int64_t wblk0 = gn * cblocks;  // the row's first constant
     // Weights are loaded two steps ahead (two register sets) and expanded
     // into the other LDS buffer while the MFMAs of the current step run;
     // activations go straight from global memory into that buffer.  Steps
@@ -453,9 +457,10 @@ __global__ __launch_bounds__(C::NT, 1) void k_qgemm_fwd(FwdArgs p) {
           r.c[h] = load_half<CT>(crs, wvoff + h * (int)half_bytes<CT>(),
                                  (int)(kt * block_bytes<CT>()));
         if constexpr (!kQ4) {
-          r.q = __builtin_amdgcn_raw_buffer_load_b8(qrs, (int)wblk0, (int)kt, 0);
+          // step kt lies in the row's constant kt >> BS
+          r.q = __builtin_amdgcn_raw_buffer_load_b8(qrs, (int)wblk0, (int)(kt >> BS), 0);
           r.st = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                               srs, (int)(((wblk0 + kt) >> 8) * 4), 0, 0));
+                                               srs, (int)(((wblk0 + (kt >> BS)) >> 8) * 4), 0, 0));
         }
       }
     };
@@ -609,7 +614,8 @@ struct BwdArgs {
 // Output tile BM tokens x BN input features; contraction over the weight's
 // rows in steps of 64.  The step's weight slice, rows n..n+63 and columns
 // k0..k0+BN-1, is dequantized into Bs[64][LDTB] in its natural layout.
-template <class C, class CT>
+// BS: block size 64 << BS, as in the forward kernel.
+template <class C, class CT, int BS>
 __global__ __launch_bounds__(C::NT, 1) void k_qgemm_bwd(BwdArgs p) {
   __shared__ __attribute__((aligned(16))) uint16_t xs0[C::TILE_A];
   __shared__ __attribute__((aligned(16))) uint16_t xs1[C::TILE_A];
@@ -637,8 +643,9 @@ __global__ __launch_bounds__(C::NT, 1) void k_qgemm_bwd(BwdArgs p) {
   // on store.  Every load is issued unconditionally.
   const int64_t rowb = kblocks * block_bytes<CT>();  // code bytes per weight row
   const __amdgpu_buffer_rsrc_t crs = bytes_rsrc(p.codes, N * rowb);
-  const __amdgpu_buffer_rsrc_t qrs = bytes_rsrc(p.q8, N * kblocks);
-  const __amdgpu_buffer_rsrc_t srs = bytes_rsrc(p.step, 4 * ((N * kblocks + 255) >> 8));
+  const int64_t cblocks = kblocks >> BS;  // constants per weight row
+  const __amdgpu_buffer_rsrc_t qrs = bytes_rsrc(p.q8, N * cblocks);
+  const __amdgpu_buffer_rsrc_t srs = bytes_rsrc(p.step, 4 * ((N * cblocks + 255) >> 8));
   // dY tile of step ns straight into LDS; on a partial last step the chunks
   // past column N re-read column 0 and meet the zero rows above.
   const __amdgpu_buffer_rsrc_t yrsrc = rows_rsrc(p.dY, N, m0, M);
@@ -655,7 +662,7 @@ __global__ __launch_bounds__(C::NT, 1) void k_qgemm_bwd(BwdArgs p) {
     const int wr = tid / BPR, wb = tid % BPR;
     const int64_t kcol = k0 + wb * 64;
     const int64_t kb_own = (kcol < K ? kcol : 0) >> 6;
-    const int64_t qown = wr * kblocks + kb_own;
+    const int64_t qown = wr * cblocks + (kb_own >> BS);  // this thread's constant, row wr
     const int cvoff = (int)(wr * rowb + kb_own * block_bytes<CT>());
     StepRegs<CT> ra, rb;
     auto load_w = [&](StepRegs<CT>& r, int64_t ns) {
@@ -668,10 +675,10 @@ __global__ __launch_bounds__(C::NT, 1) void k_qgemm_bwd(BwdArgs p) {
           r.c[h] = load_half<CT>(crs, in ? cvoff + h * (int)half_bytes<CT>() : kOutOfRange,
                                  (int)(srow * rowb));
         r.q = __builtin_amdgcn_raw_buffer_load_b8(qrs, in ? (int)qown : kOutOfRange,
-                                                  (int)(srow * kblocks), 0);
+                                                  (int)(srow * cblocks), 0);
         r.st = __builtin_bit_cast(
             float, __builtin_amdgcn_raw_buffer_load_b32(
-                       srs, in ? (int)(((srow * kblocks + qown) >> 8) * 4) : kOutOfRange, 0, 0));
+                       srs, in ? (int)(((srow * cblocks + qown) >> 8) * 4) : kOutOfRange, 0, 0));
       }
     };
     auto body = [&](StepRegs<CT>& rnext, StepRegs<CT>& rload, int64_t ns, int cur) {
@@ -747,12 +754,17 @@ hipError_t launch_qgemm_fwd(const Nf4View& w, const uint16_t* X, int64_t M, cons
   using C = GemmCfg;
   FwdArgs a{X, w.codes, w.q8, w.step, U, ldu, B, r, s, Y, M, w.N, w.K};
   dim3 grid((unsigned)(((w.N + C::BN - 1) / C::BN) * ((M + C::BM - 1) / C::BM)));
-  const bool q4 = (w.K % 256) == 0;
+  const bool q4 = (w.K % 256) == 0 && w.bshift == 0;
   with_code(w.code, [&](auto ct) {
+    using CT = decltype(ct);
     if (q4)
-      hipLaunchKernelGGL((k_qgemm_fwd<C, decltype(ct), true>), grid, dim3(C::NT), 0, stream, a);
+      hipLaunchKernelGGL((k_qgemm_fwd<C, CT, true, 0>), grid, dim3(C::NT), 0, stream, a);
+    else if (w.bshift == 2)
+      hipLaunchKernelGGL((k_qgemm_fwd<C, CT, false, 2>), grid, dim3(C::NT), 0, stream, a);
+    else if (w.bshift == 1)
+      hipLaunchKernelGGL((k_qgemm_fwd<C, CT, false, 1>), grid, dim3(C::NT), 0, stream, a);
     else
-      hipLaunchKernelGGL((k_qgemm_fwd<C, decltype(ct), false>), grid, dim3(C::NT), 0, stream, a);
+      hipLaunchKernelGGL((k_qgemm_fwd<C, CT, false, 0>), grid, dim3(C::NT), 0, stream, a);
     return 0;
   });
   return hipGetLastError();
@@ -765,7 +777,13 @@ hipError_t launch_qgemm_bwd(const Nf4View& w, const uint16_t* dY, int64_t M, con
   BwdArgs a{dY, w.codes, w.q8, w.step, dU, lddu, A, r, dX, M, w.N, w.K};
   dim3 grid((unsigned)(((w.K + C::BN - 1) / C::BN) * ((M + C::BM - 1) / C::BM)));
   with_code(w.code, [&](auto ct) {
-    hipLaunchKernelGGL((k_qgemm_bwd<C, decltype(ct)>), grid, dim3(C::NT), 0, stream, a);
+    using CT = decltype(ct);
+    if (w.bshift == 2)
+      hipLaunchKernelGGL((k_qgemm_bwd<C, CT, 2>), grid, dim3(C::NT), 0, stream, a);
+    else if (w.bshift == 1)
+      hipLaunchKernelGGL((k_qgemm_bwd<C, CT, 1>), grid, dim3(C::NT), 0, stream, a);
+    else
+      hipLaunchKernelGGL((k_qgemm_bwd<C, CT, 0>), grid, dim3(C::NT), 0, stream, a);
     return 0;
   });
   return hipGetLastError();

@@ -58,10 +58,11 @@ class NF4Weight:
     N: int
     K: int
     code: str = "nf4"     # the code table the codes index: "nf4", "fp4", "nf3", "nf2"
+    blocksize: int = BLOCKSIZE  # elements per 8-bit constant: 64, 128 or 256
 
     def struct(self) -> Nf4Tensor:
         return Nf4Tensor(_ptr(self.codes), _ptr(self.q8), _ptr(self.step), self.N, self.K,
-                         BLOCKSIZE, DQ_BLOCKSIZE, _code_id(self.code))
+                         self.blocksize, DQ_BLOCKSIZE, _code_id(self.code))
 
     def nbytes(self) -> int:
         return self.codes.numel() + self.q8.numel() + 4 * self.step.numel()
@@ -78,39 +79,49 @@ def code_table(code: str = "nf4") -> Tuple[list, list]:
     return list(lv)[:2 ** CODE_BITS[code]], list(th)[:n]
 
 
-def storage_bytes(N: int, K: int, code: str = "nf4") -> int:
-    return int(lib().qlora_storage_bytes(_code_id(code), N, K))
+BLOCKSIZES = (64, 128, 256)
 
 
-def alloc_nf4(N: int, K: int, device="cuda", code: str = "nf4") -> NF4Weight:
-    nb = N * K // BLOCKSIZE
+def storage_bytes(N: int, K: int, code: str = "nf4", blocksize: int = BLOCKSIZE) -> int:
+    """Bytes of the quantized state of one configuration (0 if unsupported)."""
+    return int(lib().qlora_config_bytes(_code_id(code), blocksize, N, K))
+
+
+def alloc_nf4(N: int, K: int, device="cuda", code: str = "nf4",
+              blocksize: int = BLOCKSIZE) -> NF4Weight:
+    if blocksize not in BLOCKSIZES or K % blocksize:
+        raise ValueError(f"block size must be one of {BLOCKSIZES} and divide K")
+    nb = N * K // blocksize
     ng = (nb + DQ_BLOCKSIZE - 1) // DQ_BLOCKSIZE
     return NF4Weight(
         codes=torch.empty(N * K * CODE_BITS[code] // 8, dtype=torch.uint8, device=device),
         q8=torch.empty(nb, dtype=torch.uint8, device=device),
         step=torch.empty(ng, dtype=torch.float32, device=device),
-        N=N, K=K, code=code)
+        N=N, K=K, code=code, blocksize=blocksize)
 
 
 def nf4_quantize(W: torch.Tensor, out: Optional[NF4Weight] = None, stream=None,
-                 code: str = "nf4") -> NF4Weight:
+                 code: str = "nf4", blocksize: int = BLOCKSIZE) -> NF4Weight:
     """Quantize an fp32 [N, K] device tensor to block codes (NF4 by default,
-    or FP4, NF3, NF2) with double-quantized constants."""
+    or FP4, NF3, NF2) with double-quantized constants, one per `blocksize`
+    elements (64, 128 or 256)."""
     if W.dtype != torch.float32 or W.dim() != 2:
         raise TypeError("W must be a 2-D float32 tensor")
     N, K = W.shape
     cid = _code_id(code)
     if out is None:
-        out = alloc_nf4(N, K, W.device, code)
-    elif out.codes.numel() != N * K * CODE_BITS[code] // 8:
-        raise ValueError("out was allocated for another code width")
+        out = alloc_nf4(N, K, W.device, code, blocksize)
+    elif (out.codes.numel() != N * K * CODE_BITS[code] // 8 or
+          out.q8.numel() != N * K // blocksize):
+        raise ValueError("out was allocated for another code width or block size")
     else:
         out.code = code
+        out.blocksize = blocksize
     if cid == QLORA_CODE_NF4:
-        st = lib().nf4_quantize(_ptr(W), N, K, BLOCKSIZE, DQ_BLOCKSIZE, _ptr(out.codes),
+        st = lib().nf4_quantize(_ptr(W), N, K, blocksize, DQ_BLOCKSIZE, _ptr(out.codes),
                                 _ptr(out.q8), _ptr(out.step), _stream(stream))
     else:
-        st = lib().qlora_quantize(_ptr(W), N, K, cid, BLOCKSIZE, DQ_BLOCKSIZE, _ptr(out.codes),
+        st = lib().qlora_quantize(_ptr(W), N, K, cid, blocksize, DQ_BLOCKSIZE, _ptr(out.codes),
                                   _ptr(out.q8), _ptr(out.step), _stream(stream))
     check(st, "nf4_quantize")
     return out
@@ -170,7 +181,9 @@ def _check_weight(w: NF4Weight) -> torch.device:
         raise TypeError("codes and q8 must be uint8, step float32")
     if w.codes.numel() != w.N * w.K * CODE_BITS[w.code] // 8:
         raise ValueError("codes do not match the weight's shape and code width")
-    if w.q8.numel() != w.N * w.K // BLOCKSIZE or w.step.numel() != -(-w.q8.numel() // DQ_BLOCKSIZE):
+    if w.blocksize not in BLOCKSIZES:
+        raise ValueError(f"block size must be one of {BLOCKSIZES}")
+    if w.q8.numel() != w.N * w.K // w.blocksize or w.step.numel() != -(-w.q8.numel() // DQ_BLOCKSIZE):
         raise ValueError("q8 / step do not match the weight's shape")
     return w.codes.device
 
@@ -309,21 +322,24 @@ def lq_init(W: torch.Tensor, omega: torch.Tensor, r: int, iters: int = 2, power_
 
 def quant_error(W: torch.Tensor, code: str = "nf4", L1: Optional[torch.Tensor] = None,
                 L2t: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
-                out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """||R - W_hat(R)||_F^2 for one configuration, R = W or W - L1 L2t^T;
-    returns a one-element float64 device tensor (written on the stream)."""
+                out: Optional[torch.Tensor] = None, stream=None,
+                blocksize: int = BLOCKSIZE) -> torch.Tensor:
+    """||R - W_hat(R)||_F^2 for one configuration (code type, block size),
+    R = W or W - L1 L2t^T; returns a one-element float64 device tensor
+    (written on the stream)."""
     if W.dtype != torch.float32 or W.dim() != 2:
         raise TypeError("W must be a 2-D float32 tensor")
     N, K = W.shape
     r = 0 if L1 is None else L1.shape[1]
-    need = int(lib().qlora_quant_error_workspace_size(N, K, _code_id(code), int(L1 is not None)))
+    need = int(lib().qlora_config_error_workspace_size(N, K, _code_id(code), blocksize,
+                                                       int(L1 is not None)))
     ws = _workspace(need, W.device, ws)
     if out is None:
         out = torch.empty(1, dtype=torch.float64, device=W.device)
-    st = lib().qlora_quant_error(_ptr(W), N, K, _code_id(code), _ptr(L1), _ptr(L2t), r,
-                                 _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
-                                 _stream(stream))
-    check(st, "qlora_quant_error")
+    st = lib().qlora_config_error(_ptr(W), N, K, _code_id(code), blocksize, _ptr(L1), _ptr(L2t),
+                                  r, _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
+                                  _stream(stream))
+    check(st, "qlora_config_error")
     return out
 
 

@@ -37,9 +37,9 @@ def f32(b: np.ndarray) -> np.ndarray:
     return nf4.bf16_bits_to_f32(b)
 
 
-def gpu_quantize(W: np.ndarray, code: str = "nf4"):
+def gpu_quantize(W: np.ndarray, code: str = "nf4", blocksize: int = 64):
     Wd = torch.from_numpy(np.ascontiguousarray(W, dtype=np.float32)).cuda()
-    w = qn.nf4_quantize(Wd, code=code)
+    w = qn.nf4_quantize(Wd, code=code, blocksize=blocksize)
     torch.cuda.synchronize()
     return w
 
@@ -76,7 +76,7 @@ def assert_close(name: str, got: np.ndarray, ref: np.ndarray, tol: float = TOL,
     return e
 
 
-def oracle_what(W: np.ndarray, code: str = "nf4") -> np.ndarray:
+def oracle_what(W: np.ndarray, code: str = "nf4", blocksize: int = 64) -> np.ndarray:
     """Oracle-side quantize + dequantize, as fp32 values of the bf16 W_hat."""
-    packed, q8, step = nf4.quantize(W, code=code)
-    return f32(nf4.dequantize(packed, q8, step, *W.shape, code=code))
+    packed, q8, step = nf4.quantize(W, blocksize=blocksize, code=code)
+    return f32(nf4.dequantize(packed, q8, step, *W.shape, blocksize=blocksize, code=code))

@@ -220,7 +220,8 @@ def test_linear_rejects_bad_arguments_without_launching():
     assert fwd(r=300) == _lib.QLORA_ERR_INVALID
     assert fwd(w=_w(64, 100)) == _lib.QLORA_ERR_INVALID
     assert fwd(w=_w(60, 128)) == _lib.QLORA_ERR_INVALID
-    assert fwd(w=_w(64, 128, bs=128)) == _lib.QLORA_ERR_UNSUPPORTED
+    assert fwd(w=_w(64, 128, bs=96)) == _lib.QLORA_ERR_UNSUPPORTED
+    assert fwd(w=_w(64, 192, bs=128)) == _lib.QLORA_ERR_INVALID   # K not a multiple of it
     assert fwd(w=_w(64, 128, code_type=5)) == _lib.QLORA_ERR_UNSUPPORTED
     assert fwd(w=_w(64, 128, codes=None)) == _lib.QLORA_ERR_INVALID
     assert fwd(nbytes=need - 1) == _lib.QLORA_ERR_WORKSPACE
@@ -268,7 +269,8 @@ def test_noalloc_forward_rejects_bad_arguments_and_oversized_calls_without_launc
     assert fwd(r=300) == _lib.QLORA_ERR_INVALID
     assert fwd(X=FAKE + 2) == _lib.QLORA_ERR_INVALID
     assert fwd(s=float("inf")) == _lib.QLORA_ERR_INVALID
-    assert fwd(w=_w(64, 128, bs=128)) == _lib.QLORA_ERR_UNSUPPORTED
+    assert fwd(w=_w(64, 128, bs=96)) == _lib.QLORA_ERR_UNSUPPORTED
+    assert fwd(w=_w(64, 192, bs=128)) == _lib.QLORA_ERR_INVALID   # K not a multiple of it
     # the largest token count whose workspace fits the scratch, and one past it
     N, K, r = 64, 128, 256
     cap = _lib.QLORA_NOALLOC_SCRATCH_BYTES
