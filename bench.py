@@ -189,6 +189,11 @@ def main():
             extra["code_types"][code]["fused_step"] = code_step(
                 qn, L, torch, fx.layers, M, r, wl.s, sp, args.steps, args.warmup,
                 head["flops_step"], code)
+        import workloads as wl_mod
+        book = wl_mod.draw_codebook(wl_mod.rng_for(77, 0), 4, "plain")
+        extra["code_types"]["user4"] = {"fused_step": code_step(
+            qn, L, torch, fx.layers, M, r, wl.s, sp, args.steps, args.warmup,
+            head["flops_step"], "user4", levels=book)}
         extra["block_sizes"] = {
             f"nf4/{bs}": code_step(qn, L, torch, fx.layers, M, r, wl.s, sp, args.steps,
                                    args.warmup, head["flops_step"], "nf4", bs)
@@ -566,12 +571,14 @@ def run_ilp(qn, torch, reps=3):
             "table_GB/s": round(moved / (ms * 1e-3) / 1e9, 1), "plans": plans}
 
 
-def code_step(qn, L, torch, layers, M, r, s, sp, steps, warmup, flops_step, code, blocksize=64):
+def code_step(qn, L, torch, layers, M, r, s, sp, steps, warmup, flops_step, code, blocksize=64,
+              levels=None):
     """The same fused forward + backward step with the weights quantized to
-    another code type or block size (same kernels, other code table, code
-    width or constant indexing)."""
+    another code type, a caller's codebook or another block size (same
+    kernels, other code table, code width or constant indexing)."""
     from quantized_base_lora_nf4_amd._lib import check
-    qw = [qn.nf4_quantize(t["Wf32"], code=code, blocksize=blocksize) for t in layers]
+    qw = [qn.nf4_quantize(t["Wf32"], code=code, blocksize=blocksize, levels=levels)
+          for t in layers]
     sts = [w.struct() for w in qw]
 
     def p(x):

@@ -56,6 +56,21 @@
  *                   negative levels at evenly spaced normal probabilities
  *                   up to delta_k = 1 - (1/(2(2^k-1)) + 1/2^(k+1))/2, over
  *                   Phi^{-1}(delta_k)); ascending with the code.
+ *   QLORA_CODE_USER4, QLORA_CODE_USER3, QLORA_CODE_USER2  a caller's
+ *                   codebook of 2^k values, k = 4, 3, 2 (the ModuLoRA
+ *                   abstract materializes the low-precision weight from a
+ *                   black-box quantizer: the kernels only need the values
+ *                   behind the codes).  The values, fp32 in code order, are
+ *                   passed in nf4_tensor_t.levels (and to
+ *                   qlora_quantize_user); each must be finite with
+ *                   |v| <= 1, and either 0 or |v| >= 2^-20 (so that every
+ *                   midpoint of two values is exact in fp64); any order,
+ *                   repeats allowed.  Quantizer: the nearest value, ties to
+ *                   the lower value, of equal values the lowest code; an
+ *                   all-zero block takes the code of the value nearest to 0.
+ *                   Accepted by the quantizer, the dequantizer and the
+ *                   layer; not by qlora_lq_init and the configuration-error
+ *                   calls (QLORA_ERR_UNSUPPORTED).
  *   Block scaling and double quantization are the same for all types.
  *
  * Code storage by width k (4 for NF4 and FP4): a 64-element block takes
@@ -109,6 +124,11 @@ extern "C" {
 #define QLORA_CODE_FP4 1
 #define QLORA_CODE_NF3 2
 #define QLORA_CODE_NF2 3
+#define QLORA_CODE_USER4 4
+#define QLORA_CODE_USER3 5
+#define QLORA_CODE_USER2 6
+/* Smallest magnitude of a nonzero value of a caller's codebook: 2^-20. */
+#define QLORA_USER_MIN_MAGNITUDE (1.0f / 1048576.0f)
 
 #define QLORA_NF4_BLOCKSIZE 64
 #define QLORA_NF4_DQ_BLOCKSIZE 256
@@ -130,6 +150,11 @@ typedef struct nf4_tensor_t {
   int32_t dq_blocksize; /* must be 256 */
   int32_t code_type;    /* QLORA_CODE_* (the type it was quantized with);
                            others give QLORA_ERR_UNSUPPORTED */
+  const float* levels;  /* QLORA_CODE_USER*: HOST pointer to the 2^k code
+                           values (code order), read during each call that
+                           takes the tensor and not kept; NULL or values
+                           outside the contract give QLORA_ERR_INVALID.
+                           Ignored for the built-in code types. */
 } nf4_tensor_t;
 
 /* Text for a status code (static storage, never NULL). */
@@ -152,6 +177,16 @@ void nf4_code_table(float* levels16, float* thresholds15);
  * thresholds, or QLORA_ERR_UNSUPPORTED for an unknown code type.  Either
  * pointer may be NULL; no device work. */
 int32_t qlora_code_table(int32_t code_type, float* levels16, float* thresholds15);
+
+/* Host-side check of a caller's codebook for QLORA_CODE_USER* and the
+ * decision thresholds the quantizer derives from it (as qlora_code_table
+ * gives them for the built-in types: the fp32 midpoint of each pair of
+ * consecutive distinct values, rounded toward -inf, ascending; the rest of
+ * thresholds15 is set to 0).  levels: 2^k fp32 values (host).  Returns the
+ * number of thresholds, QLORA_ERR_UNSUPPORTED for a code type that is not a
+ * user type, or QLORA_ERR_INVALID for NULL levels or values outside the
+ * contract.  thresholds15 may be NULL; no device work. */
+int32_t qlora_user_table(int32_t code_type, const float* levels, float* thresholds15);
 
 /* Bytes of the three arrays of one configuration (code type, block size 64,
  * 128 or 256) for an N x K weight: N*K*k/8 + N*K/B + 4*ceil(N*K/B/256), k
@@ -194,11 +229,22 @@ int32_t nf4_quantize(const float* W, int64_t N, int64_t K, int32_t blocksize,
  * fl32(w / c_b) (ties to the lower value; zero, and an all-zero block, get
  * the code of zero: 7 for NF4, 0 for FP4, 3 for NF3, 1 for NF2), stored at
  * the type's width (codes [N*K*k/8]).  An unknown code type gives
- * QLORA_ERR_UNSUPPORTED.  nf4_quantize(...) is
+ * QLORA_ERR_UNSUPPORTED, a user code type QLORA_ERR_INVALID (it needs its
+ * values: qlora_quantize_user).  nf4_quantize(...) is
  * qlora_quantize(..., QLORA_CODE_NF4, ...). */
 int32_t qlora_quantize(const float* W, int64_t N, int64_t K, int32_t code_type,
                        int32_t blocksize, int32_t dq_blocksize, uint8_t* codes,
                        uint8_t* q8, float* step, hipStream_t stream);
+
+/* qlora_quantize_user -- qlora_quantize with a caller's codebook:
+ * code_type QLORA_CODE_USER4, _USER3 or _USER2 and `levels` (host, 2^k
+ * fp32 values in code order, read during the call) under the contract and
+ * quantizer rule above.  The division w / c_b is the IEEE-correct one for
+ * every block.  A built-in code type gives QLORA_ERR_UNSUPPORTED (use
+ * qlora_quantize); bad levels, QLORA_ERR_INVALID. */
+int32_t qlora_quantize_user(const float* W, int64_t N, int64_t K, int32_t code_type,
+                            const float* levels, int32_t blocksize, int32_t dq_blocksize,
+                            uint8_t* codes, uint8_t* q8, float* step, hipStream_t stream);
 
 /* nf4_dequantize -- materialize the bf16 weight [N, K] from its quantized
  * state, with the code table of w->code_type (for checking and interop; the

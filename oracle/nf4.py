@@ -33,6 +33,13 @@ double quantization and storage; only the 16 values behind the codes differ.
 The pages give no bit layout for it; it is read as the E2M1 format (see
 ``fp4_values``).
 
+A caller's codebook ("user4", "user3", "user2"): the ModuLoRA abstract's
+backward materializes the weight from a black-box quantizer, so the kernels
+must work with whatever 2^k values stand behind the codes.  The oracle
+quantizes to such a codebook by its definition, the nearest value with ties
+to the lower value (``nearest_code_exact``), under the same block scaling,
+double quantization and storage.
+
 Readings taken where the pages are silent (each is listed in the design
 notes): level offset delta = 1 - (1/30 + 1/32)/2 with 7 negative levels, an
 exact zero and 8 positive levels; blocks of 64 consecutive row-major
@@ -181,7 +188,9 @@ def fp4_values() -> np.ndarray:
 
 
 CODE_TYPES = ("nf4", "fp4", "nf3", "nf2")
-CODE_BITS = {"nf4": 4, "fp4": 4, "nf3": 3, "nf2": 2}
+USER_CODES = ("user4", "user3", "user2")
+CODE_BITS = {"nf4": 4, "fp4": 4, "nf3": 3, "nf2": 2, "user4": 4, "user3": 3, "user2": 2}
+USER_MIN_MAGNITUDE = 2.0 ** -20
 
 
 def code_bits(code: str) -> int:
@@ -190,8 +199,27 @@ def code_bits(code: str) -> int:
     return CODE_BITS[code]
 
 
-def code_values(code: str = "nf4") -> np.ndarray:
-    """fp32 value of each of the 2^bits codes of a code type, in code order."""
+def user_values(code: str, levels) -> np.ndarray:
+    """A caller's codebook as fp32, checked against the contract: 2^bits
+    finite values with |v| <= 1 and v = 0 or |v| >= 2^-20.  Under it the sum
+    of two values is exact in fp64 (their bits span at most 45 places), so
+    every midpoint is exact."""
+    f = np.asarray(levels, dtype=np.float64).astype(np.float32)  # rounded to fp32
+    if f.shape != (2 ** code_bits(code),):
+        raise ValueError(f"{code} takes {2 ** code_bits(code)} values")
+    if not np.all(np.isfinite(f)):
+        raise ValueError("codebook values must be finite")
+    a = np.abs(f.astype(np.float64))
+    if np.any(a > 1.0) or np.any((a != 0) & (a < USER_MIN_MAGNITUDE)):
+        raise ValueError("codebook values need |v| <= 1 and v = 0 or |v| >= 2^-20")
+    return f
+
+
+def code_values(code: str = "nf4", levels=None) -> np.ndarray:
+    """fp32 value of each of the 2^bits codes of a code type, in code order
+    (for a user code type, the caller's ``levels``)."""
+    if code in USER_CODES:
+        return user_values(code, levels)
     if code == "nf4":
         return nf4_levels()
     if code == "fp4":
@@ -272,6 +300,23 @@ def nearest_code(x: np.ndarray, values_f32: np.ndarray) -> np.ndarray:
     v = np.asarray(values_f32, dtype=np.float32)
     order = np.lexsort((np.arange(v.size), v.astype(np.float64)))
     return order[nearest_level(x, v[order])].astype(np.uint8)
+
+
+def nearest_code_exact(x: np.ndarray, values_f32: np.ndarray) -> np.ndarray:
+    """Code whose value is nearest to each fp32 x, ties to the lower value,
+    of equal values the lowest code, decided without any rounded distance:
+    x is nearer to the upper of two consecutive distinct values exactly when
+    x > their midpoint, and both x and the midpoint (for values under the
+    user-codebook contract) are exact in fp64.  So the nearest value is the
+    number of midpoints below x, counted in the ascending list."""
+    v = np.asarray(values_f32, dtype=np.float32)
+    dist = np.unique(v.astype(np.float64))           # ascending, -0 and +0 once
+    codes_of = np.array([int(np.flatnonzero(v.astype(np.float64) == d)[0]) for d in dist],
+                        dtype=np.uint8)               # lowest code of each value
+    mid = (dist[:-1] + dist[1:]) / 2.0
+    assert np.array_equal(mid * 2.0 - dist[:-1], dist[1:]), "midpoints must be exact"
+    n = np.searchsorted(mid, np.asarray(x, np.float32).astype(np.float64), side="left")
+    return codes_of[n]
 
 
 def block_absmax(W: np.ndarray, blocksize: int = BLOCKSIZE) -> np.ndarray:
@@ -386,10 +431,11 @@ def double_quantize(c: np.ndarray, dq_blocksize: int = DQ_BLOCKSIZE):
 
 
 def quantize(W: np.ndarray, blocksize: int = BLOCKSIZE, dq_blocksize: int = DQ_BLOCKSIZE,
-             code: str = "nf4"):
-    """Block quantization (NF4 by default, or FP4, NF3, NF2) + double-quant
-    encoding of W [N, K] fp32, one absmax constant per `blocksize`
-    consecutive elements (a multiple of 64 dividing K).
+             code: str = "nf4", levels=None):
+    """Block quantization (NF4 by default, or FP4, NF3, NF2, or a caller's
+    codebook ``levels`` for the user code types) + double-quant encoding of
+    W [N, K] fp32, one absmax constant per `blocksize` consecutive elements
+    (a multiple of 64 dividing K).
 
     Returns (packed codes uint8 [N*K*bits/8], packed in 64-element units
     whatever the block size; q8 uint8 [N*K/blocksize]; step fp32
@@ -399,7 +445,10 @@ def quantize(W: np.ndarray, blocksize: int = BLOCKSIZE, dq_blocksize: int = DQ_B
         raise ValueError("the block size must be a multiple of 64")
     c = block_absmax(W, blocksize)
     x = normalize(W, c, blocksize)
-    codes = nearest_code(x, code_values(code))
+    if code in USER_CODES:
+        codes = nearest_code_exact(x, code_values(code, levels))
+    else:
+        codes = nearest_code(x, code_values(code))
     packed = pack_codes_k(codes, code_bits(code))
     q8, step = double_quantize(c, dq_blocksize)
     return packed, q8, step
@@ -413,9 +462,9 @@ def dequant_constants(q8: np.ndarray, step: np.ndarray, dq_blocksize: int = DQ_B
 
 
 def dequantize_f32(packed, q8, step, N, K, blocksize=BLOCKSIZE, dq_blocksize=DQ_BLOCKSIZE,
-                   code="nf4") -> np.ndarray:
+                   code="nf4", levels=None) -> np.ndarray:
     """fl32(value[code] * c_hat_b) as fp32 [N, K], before the bf16 rounding."""
-    levels = code_values(code)
+    levels = code_values(code, levels)
     codes = unpack_codes_k(packed, code_bits(code))
     chat = dequant_constants(q8, step, dq_blocksize)
     vals = levels[codes].reshape(-1, blocksize) * chat[:, None]
@@ -423,9 +472,10 @@ def dequantize_f32(packed, q8, step, N, K, blocksize=BLOCKSIZE, dq_blocksize=DQ_
 
 
 def dequantize(packed, q8, step, N, K, blocksize=BLOCKSIZE, dq_blocksize=DQ_BLOCKSIZE,
-               code="nf4") -> np.ndarray:
+               code="nf4", levels=None) -> np.ndarray:
     """The dequantized weight W_hat as bf16 bit patterns [N, K] (uint16)."""
-    return f32_to_bf16_bits(dequantize_f32(packed, q8, step, N, K, blocksize, dq_blocksize, code))
+    return f32_to_bf16_bits(dequantize_f32(packed, q8, step, N, K, blocksize, dq_blocksize, code,
+                                           levels))
 
 
 def storage_bytes(N: int, K: int, blocksize=BLOCKSIZE, dq_blocksize=DQ_BLOCKSIZE,

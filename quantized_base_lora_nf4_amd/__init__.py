@@ -9,4 +9,4 @@ from ._lib import LIB_PATH, EXPORTS, QloraError, lib  # noqa: F401
 from .ops import (LqResult, NF4Weight, QLoRALinear, QLoRALinearFunction, alloc_nf4,  # noqa: F401
                   code_table, ilp_plan, lq_init, lq_workspace_size, nf4_dequantize,
                   nf4_quantize, qlora_linear_bwd, qlora_linear_fwd, qlora_linear_fwd_noalloc,
-                  quant_error, storage_bytes, workspace_size)
+                  quant_error, storage_bytes, user_table, workspace_size, USER_CODES)

@@ -21,6 +21,10 @@ QLORA_CODE_NF4 = 0
 QLORA_CODE_FP4 = 1
 QLORA_CODE_NF3 = 2
 QLORA_CODE_NF2 = 3
+QLORA_CODE_USER4 = 4
+QLORA_CODE_USER3 = 5
+QLORA_CODE_USER2 = 6
+QLORA_USER_MIN_MAGNITUDE = 2.0 ** -20
 
 # Size of the fixed device scratch of qlora_linear_fwd_noalloc
 QLORA_NOALLOC_SCRATCH_BYTES = 16 << 20
@@ -36,6 +40,8 @@ EXPORTS = (
     "qlora_storage_bytes",
     "nf4_quantize",
     "qlora_quantize",
+    "qlora_quantize_user",
+    "qlora_user_table",
     "nf4_dequantize",
     "qlora_workspace_size",
     "qlora_linear_fwd",
@@ -66,6 +72,7 @@ class Nf4Tensor(ctypes.Structure):
         ("blocksize", ctypes.c_int32),
         ("dq_blocksize", ctypes.c_int32),
         ("code_type", ctypes.c_int32),
+        ("levels", ctypes.c_void_p),
     ]
 
 
@@ -102,6 +109,10 @@ def lib() -> ctypes.CDLL:
     L.nf4_quantize.argtypes = [vp, i64, i64, i32, i32, vp, vp, vp, vp]
     L.qlora_quantize.restype = i32
     L.qlora_quantize.argtypes = [vp, i64, i64, i32, i32, i32, vp, vp, vp, vp]
+    L.qlora_quantize_user.restype = i32
+    L.qlora_quantize_user.argtypes = [vp, i64, i64, i32, vp, i32, i32, vp, vp, vp, vp]
+    L.qlora_user_table.restype = i32
+    L.qlora_user_table.argtypes = [i32, vp, vp]
     L.nf4_dequantize.restype = i32
     L.nf4_dequantize.argtypes = [ctypes.POINTER(Nf4Tensor), vp, vp]
     L.qlora_workspace_size.restype = sz

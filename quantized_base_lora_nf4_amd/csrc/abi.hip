@@ -71,16 +71,56 @@ bool nf4_ok(const nf4_tensor_t* w) {
   return w && w->codes && w->q8 && w->step;
 }
 
-// The layer kernels address the packed codes with 32-bit buffer offsets.
-bool state_fits(const nf4_tensor_t* w) {
-  const int64_t bits =
-      with_code(w->code_type, [](auto ct) { return (int64_t)decltype(ct)::kBits; });
-  return w->N * w->K / 8 * bits < ((int64_t)1 << 31);
-}
-
 inline bool code_ok(int32_t code_type) {
   return code_type == QLORA_CODE_NF4 || code_type == QLORA_CODE_FP4 ||
          code_type == QLORA_CODE_NF3 || code_type == QLORA_CODE_NF2;
+}
+
+inline bool user_type(int32_t code_type) {
+  return code_type == QLORA_CODE_USER4 || code_type == QLORA_CODE_USER3 ||
+         code_type == QLORA_CODE_USER2;
+}
+
+// Built-in or caller-codebook code type.
+inline bool any_code_ok(int32_t code_type) { return code_ok(code_type) || user_type(code_type); }
+
+inline int code_bits(int32_t code_type) {
+  return with_any_code(code_type, [](auto ct) { return decltype(ct)::kBits; });
+}
+
+// The table of a caller's codebook (user_type(code_type)): the values must
+// be finite, |v| <= 1, and 0 or |v| >= 2^-20, so that the sum of any two is
+// exact in fp64 and each threshold is its exact midpoint rounded down.  The
+// rest is the built-in tables' construction over the first 2^k codes.
+// Returns the number of thresholds, or -1 if the values break the contract.
+int user_table(int32_t code_type, const float* levels, UserTable* out) {
+  if (!levels) return -1;
+  const int n = 1 << code_bits(code_type);
+  uint32_t lv[16] = {};
+  for (int c = 0; c < n; ++c) {
+    const float v = levels[c];
+    if (!isfinite(v) || fabsf(v) > 1.0f || (v != 0.0f && fabsf(v) < QLORA_USER_MIN_MAGNITUDE))
+      return -1;
+    lv[c] = __builtin_bit_cast(uint32_t, v);
+  }
+  const CodeTable t = make_code_table(lv, n);
+  if (!code_table_sound(t)) return -1;  // not reached under the contract
+  UserTable u{};
+  for (int c = 0; c < 16; ++c) u.level[c] = __builtin_bit_cast(float, t.level[c]);
+  for (int i = 0; i < 15; ++i)
+    u.thr[i] = i + 1 < t.ndist ? __builtin_bit_cast(float, t.thr[i]) : __builtin_inff();
+  uint64_t map = 0;
+  for (int k = 0; k < t.ndist; ++k) map |= (uint64_t)t.dist_code[k] << (4 * k);
+  u.code_lo = (uint32_t)map;
+  u.code_hi = (uint32_t)(map >> 32);
+  if (out) *out = u;
+  return t.ndist - 1;
+}
+
+// The layer kernels address the packed codes with 32-bit buffer offsets.
+bool state_fits(const nf4_tensor_t* w) {
+  const int64_t bits = code_bits(w->code_type);
+  return w->N * w->K / 8 * bits < ((int64_t)1 << 31);
 }
 
 // Block sizes 64, 128, 256 as 64 << shift; -1 for others.
@@ -89,25 +129,31 @@ inline int bshift_of(int32_t blocksize) {
 }
 
 // Configuration of a quantized weight: a supported block size, DQ block
-// size and code type (else QLORA_ERR_UNSUPPORTED), and K a multiple of the
-// block size (else QLORA_ERR_INVALID).
+// size and code type (else QLORA_ERR_UNSUPPORTED), K a multiple of the
+// block size and, for a caller's codebook, values within the contract (else
+// QLORA_ERR_INVALID).
 int32_t nf4_supported(const nf4_tensor_t* w) {
   if (bshift_of(w->blocksize) < 0 || w->dq_blocksize != QLORA_NF4_DQ_BLOCKSIZE ||
-      !code_ok(w->code_type))
+      !any_code_ok(w->code_type))
     return QLORA_ERR_UNSUPPORTED;
+  if (user_type(w->code_type) && user_table(w->code_type, w->levels, nullptr) < 0)
+    return QLORA_ERR_INVALID;
   return (w->K % w->blocksize) == 0 ? QLORA_OK : QLORA_ERR_INVALID;
 }
 
+// For a tensor nf4_supported accepted.
 inline Nf4View view_of(const nf4_tensor_t* w) {
-  return Nf4View{w->codes, w->q8, w->step, w->N, w->K, w->code_type, bshift_of(w->blocksize)};
+  Nf4View v{w->codes, w->q8, w->step, w->N, w->K, w->code_type, bshift_of(w->blocksize), {}};
+  if (user_type(w->code_type)) user_table(w->code_type, w->levels, &v.ut);
+  return v;
 }
 
 size_t config_bytes(int32_t code_type, int32_t blocksize, int64_t N, int64_t K) {
-  if (!code_ok(code_type) || bshift_of(blocksize) < 0 || N < 1 || K < 64 || (K % 64) != 0 ||
+  if (!any_code_ok(code_type) || bshift_of(blocksize) < 0 || N < 1 || K < 64 || (K % 64) != 0 ||
       (K % blocksize) != 0)
     return 0;
   const int64_t nb = N * K / blocksize;
-  const int64_t bits = with_code(code_type, [](auto ct) { return decltype(ct)::kBits; });
+  const int64_t bits = code_bits(code_type);
   return (size_t)(N * K / 8 * bits) + (size_t)nb + 4 * (size_t)((nb + 255) / 256);
 }
 
@@ -125,19 +171,22 @@ int32_t copy_table(float* levels16, float* thresholds15) {
   return CT::table.ndist - 1;
 }
 
-int32_t quantize(const float* W, int64_t N, int64_t K, int32_t code_type, int32_t blocksize,
-                 int32_t dq_blocksize, uint8_t* codes, uint8_t* q8, float* step,
-                 hipStream_t stream) {
+// levels: the caller's codebook for a user code type, else null.
+int32_t quantize(const float* W, int64_t N, int64_t K, int32_t code_type, const float* levels,
+                 int32_t blocksize, int32_t dq_blocksize, uint8_t* codes, uint8_t* q8,
+                 float* step, hipStream_t stream) {
   if (!W || !codes || !q8 || !step) return QLORA_ERR_INVALID;
   if (N < 1 || K < 64 || (K % 64) != 0 || N > ((int64_t)1 << 40) / K) return QLORA_ERR_INVALID;
   const int bs = bshift_of(blocksize);
-  if (bs < 0 || dq_blocksize != QLORA_NF4_DQ_BLOCKSIZE || !code_ok(code_type))
+  if (bs < 0 || dq_blocksize != QLORA_NF4_DQ_BLOCKSIZE || !any_code_ok(code_type))
     return QLORA_ERR_UNSUPPORTED;
   if ((K % blocksize) != 0) return QLORA_ERR_INVALID;
+  UserTable ut{};
+  if (user_type(code_type) && user_table(code_type, levels, &ut) < 0) return QLORA_ERR_INVALID;
   if (!aligned16(W) || !aligned16(codes) || !aligned16(q8) || !aligned16(step))
     return QLORA_ERR_INVALID;
   return launch_status(
-      launch_nf4_quantize(W, N * K / blocksize, codes, q8, step, code_type, bs, stream));
+      launch_nf4_quantize(W, N * K / blocksize, codes, q8, step, code_type, bs, &ut, stream));
 }
 
 }  // namespace
@@ -185,13 +234,31 @@ size_t nf4_storage_bytes(int64_t N, int64_t K) {
 int32_t nf4_quantize(const float* W, int64_t N, int64_t K, int32_t blocksize,
                      int32_t dq_blocksize, uint8_t* codes, uint8_t* q8, float* step,
                      hipStream_t stream) {
-  return quantize(W, N, K, QLORA_CODE_NF4, blocksize, dq_blocksize, codes, q8, step, stream);
+  return quantize(W, N, K, QLORA_CODE_NF4, nullptr, blocksize, dq_blocksize, codes, q8, step,
+                  stream);
 }
 
 int32_t qlora_quantize(const float* W, int64_t N, int64_t K, int32_t code_type,
                        int32_t blocksize, int32_t dq_blocksize, uint8_t* codes, uint8_t* q8,
                        float* step, hipStream_t stream) {
-  return quantize(W, N, K, code_type, blocksize, dq_blocksize, codes, q8, step, stream);
+  return quantize(W, N, K, code_type, nullptr, blocksize, dq_blocksize, codes, q8, step, stream);
+}
+
+int32_t qlora_quantize_user(const float* W, int64_t N, int64_t K, int32_t code_type,
+                            const float* levels, int32_t blocksize, int32_t dq_blocksize,
+                            uint8_t* codes, uint8_t* q8, float* step, hipStream_t stream) {
+  if (!user_type(code_type)) return QLORA_ERR_UNSUPPORTED;
+  return quantize(W, N, K, code_type, levels, blocksize, dq_blocksize, codes, q8, step, stream);
+}
+
+int32_t qlora_user_table(int32_t code_type, const float* levels, float* thresholds15) {
+  if (!user_type(code_type)) return QLORA_ERR_UNSUPPORTED;
+  UserTable u;
+  const int n = user_table(code_type, levels, &u);
+  if (n < 0) return QLORA_ERR_INVALID;
+  if (thresholds15)
+    for (int i = 0; i < 15; ++i) thresholds15[i] = i < n ? u.thr[i] : 0.0f;
+  return n;
 }
 
 int32_t nf4_dequantize(const nf4_tensor_t* w, uint16_t* W_bf16, hipStream_t stream) {
@@ -201,8 +268,9 @@ int32_t nf4_dequantize(const nf4_tensor_t* w, uint16_t* W_bf16, hipStream_t stre
   if (sup != QLORA_OK) return sup;
   if (!aligned16(w->codes) || !aligned16(w->q8) || !aligned16(w->step) || !aligned16(W_bf16))
     return QLORA_ERR_INVALID;
+  const Nf4View v = view_of(w);
   return launch_status(launch_nf4_dequantize(w->codes, w->q8, w->step, w->N * w->K, W_bf16,
-                                             w->code_type, bshift_of(w->blocksize), stream));
+                                             w->code_type, v.bshift, &v.ut, stream));
 }
 
 size_t qlora_workspace_size(int64_t M, int64_t N, int64_t K, int32_t r, int32_t for_bwd) {

@@ -59,15 +59,16 @@ struct CodeTable {
   uint8_t zero_code;     // code of an all-zero block
 };
 
-constexpr CodeTable make_code_table(const uint32_t (&lv)[16]) {
+// Over the first n codes (the others keep value +0 and take no part).
+constexpr CodeTable make_code_table(const uint32_t (&lv)[16], int n = 16) {
   CodeTable t{};
-  for (int c = 0; c < 16; ++c) t.level[c] = lv[c];
+  for (int c = 0; c < n; ++c) t.level[c] = lv[c];
   // distinct values in ascending order (selection by value, lowest code wins)
   t.ndist = 0;
   float last = 0.0f;
-  for (int k = 0; k < 16; ++k) {
+  for (int k = 0; k < n; ++k) {
     int best = -1;
-    for (int c = 0; c < 16; ++c) {
+    for (int c = 0; c < n; ++c) {
       const float v = __builtin_bit_cast(float, lv[c]);
       if (t.ndist > 0 && !(v > last)) continue;
       if (best < 0 || v < __builtin_bit_cast(float, lv[best])) best = c;
@@ -92,7 +93,8 @@ constexpr bool code_table_sound(const CodeTable& t) {
     if (!(lo < hi)) return false;
     const double mid = ((double)lo + (double)hi) * 0.5;
     const float th = __builtin_bit_cast(float, t.thr[i]);
-    if ((double)th > mid || th == 0.0f) return false;  // at or below the midpoint
+    if (t.thr[i] == 0x80000000u) return false;         // never -0 (+0 for a midpoint of 0)
+    if ((double)th > mid) return false;                 // at or below the midpoint
     const uint32_t nb = t.thr[i] + ((th >= 0.0f) ? 1u : (uint32_t)-1);
     if ((double)__builtin_bit_cast(float, nb) <= mid) return false;  // next float above it
     if (!(lo <= th && th < hi)) return false;
@@ -132,24 +134,28 @@ constexpr uint32_t kNf2Bits[16] = {0xbf800000u, 0x00000000u, 0x3edf238fu, 0x3f80
 // Each code type also gives the code for a threshold count in closed form
 // (checked against the table below) and its width in bits.
 struct CodeNF4 {
+  static constexpr bool kUser = false;
   static constexpr int kId = 0;
   static constexpr int kBits = 4;
   static constexpr CodeTable table = make_code_table(kLevelBits);
   __host__ __device__ static constexpr uint32_t code_of_count(uint32_t n) { return n; }
 };
 struct CodeNF3 {
+  static constexpr bool kUser = false;
   static constexpr int kId = 2;
   static constexpr int kBits = 3;
   static constexpr CodeTable table = make_code_table(kNf3Bits);
   __host__ __device__ static constexpr uint32_t code_of_count(uint32_t n) { return n; }
 };
 struct CodeNF2 {
+  static constexpr bool kUser = false;
   static constexpr int kId = 3;
   static constexpr int kBits = 2;
   static constexpr CodeTable table = make_code_table(kNf2Bits);
   __host__ __device__ static constexpr uint32_t code_of_count(uint32_t n) { return n; }
 };
 struct CodeFP4 {
+  static constexpr bool kUser = false;
   static constexpr int kId = 1;
   static constexpr int kBits = 4;
   static constexpr CodeTable table = make_code_table(kFp4Bits.b);
@@ -186,6 +192,38 @@ __host__ __device__ constexpr float code_value(int c) {
   return __builtin_bit_cast(float, CT::table.level[c]);
 }
 
+// ---------------------------------------------------------------------------
+// A caller's codebook (the ModuLoRA abstract finetunes through weights
+// materialized from a black-box quantizer: any 2^k values behind the codes).
+// The values and the quantizer's rule are derived on the host with the same
+// construction as the built-in tables (make_code_table over the first 2^k
+// codes) and travel by value in the kernel arguments, so the code words stay
+// uniform (scalar registers).
+// ---------------------------------------------------------------------------
+struct UserTable {
+  float level[16];    // value of each code (0 past 2^k)
+  float thr[15];      // decision thresholds ascending; +inf past the last
+  uint32_t code_lo;   // code for threshold count n: nibble n of code_hi:code_lo
+  uint32_t code_hi;
+};
+
+template <int K, int Id>
+struct CodeUser {
+  static constexpr bool kUser = true;
+  static constexpr int kId = Id;
+  static constexpr int kBits = K;
+};
+using CodeUser4 = CodeUser<4, 4>;
+using CodeUser3 = CodeUser<3, 5>;
+using CodeUser2 = CodeUser<2, 6>;
+
+// Value of code c: the built-in table, or the caller's.
+template <class CT>
+__host__ __device__ __forceinline__ float level_of(const UserTable& u, int c) {
+  if constexpr (CT::kUser) return u.level[c];
+  else return code_value<CT>(c);
+}
+
 // Call f(CT{}) for the code type with this id (NF4 for an unknown id; the C
 // ABI rejects unknown ids before any launch).
 template <class F>
@@ -195,6 +233,17 @@ __host__ auto with_code(int id, F&& f) {
     case CodeNF3::kId: return f(CodeNF3{});
     case CodeNF2::kId: return f(CodeNF2{});
     default: return f(CodeNF4{});
+  }
+}
+
+// with_code, also for the caller-codebook types.
+template <class F>
+__host__ auto with_any_code(int id, F&& f) {
+  switch (id) {
+    case CodeUser4::kId: return f(CodeUser4{});
+    case CodeUser3::kId: return f(CodeUser3{});
+    case CodeUser2::kId: return f(CodeUser2{});
+    default: return with_code(id, f);
   }
 }
 

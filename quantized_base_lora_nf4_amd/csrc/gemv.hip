@@ -109,6 +109,7 @@ struct GemvArgs {
   uint16_t* Y;
   uint16_t* U_out;  // nullable, bf16 [M][r]
   int bshift;       // block size 64 << bshift
+  UserTable ut;     // the caller's codebook (CodeUser types only)
 };
 
 #ifndef QN_GEMV_PD
@@ -233,7 +234,7 @@ __global__ __launch_bounds__(64 * KW) void k_qgemv(GemvArgs p) {
   // of a thread's loads are issued before any is used (one latency).
   for (int e = tid; e < kLutWords; e += NT) {
     const int b = e >> 4;  // copy e % 16 of entry b
-    lut[e] = pack_bf16x2(code_value<CT>(b & 15), code_value<CT>(b >> 4));
+    lut[e] = pack_bf16x2(level_of<CT>(p.ut, b & 15), level_of<CT>(p.ut, b >> 4));
   }
   if (p.bshift > 0) {
     // blocks of 64 << bshift: each 64-element block takes the constant of
@@ -381,7 +382,7 @@ hipError_t launch_qgemv_g(const GemvArgs& a, int code, hipStream_t stream) {
   constexpr int KW = 8, PD = QN_GEMV_PD;
   const size_t lds = 4 * (size_t)gemv_lds_words(G, KW, a.M, a.r, a.K / 64);
   const dim3 grid((unsigned)((a.N + 16 * G - 1) / (16 * G)));
-  return with_code(code, [&](auto ct) {
+  return with_any_code(code, [&](auto ct) {
     const void* fn = reinterpret_cast<const void*>(&k_qgemv<G, KW, PD, decltype(ct)>);
     // dynamic LDS above the default 64 KB needs the limit raised; the call is
     // cheap and idempotent, and made for the device the launch goes to
@@ -404,7 +405,7 @@ hipError_t launch_qgemv(const Nf4View& w, const uint16_t* X, int64_t M, const ui
   if (e != hipSuccess) return e;
   if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
   const GemvArgs a{w.codes, w.q8, w.step, X,     M, w.N, w.K,  upart, (int32_t)gu.x,
-                   B,       r,    s,      Y, U_out, w.bshift};
+                   B,       r,    s,      Y, U_out, w.bshift, w.ut};
   const int64_t kblocks = w.K / 64;
   // 16 G weight rows per workgroup, K split over its 8 waves.
   //  - G = 7 when the 16-row groups make exactly one workgroup of 7 per CU

@@ -129,7 +129,8 @@ hipError_t launch_quant_error(const float* W, int64_t N, int64_t K, int code, in
   float* step = reinterpret_cast<float*>(base + pl.step_off);
   double* part = reinterpret_cast<double*>(base + pl.part_off);
   hipError_t e =
-      launch_nf4_quantize(R, N * K / (64 << bshift), codes, q8, step, code, bshift, stream);
+      launch_nf4_quantize(R, N * K / (64 << bshift), codes, q8, step, code, bshift, nullptr,
+                          stream);
   if (e != hipSuccess) return e;
   with_code(code, [&](auto ct) {
     hipLaunchKernelGGL(k_sq_error<decltype(ct)>, dim3(kErrBlocks), dim3(256), 0, stream, R, codes,

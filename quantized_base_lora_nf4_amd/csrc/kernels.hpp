@@ -6,14 +6,16 @@
 
 namespace qn {
 
-// ---- nf4_quant.hip ----  (code: kId of CodeNF4, CodeFP4, CodeNF3 or CodeNF2)
+// ---- nf4_quant.hip ----  (code: kId of any code type; ut: the caller's
+// codebook for the CodeUser types, else unused and may be null)
 // Blocks of 64 << bshift elements (bshift 0, 1, 2: block size 64, 128, 256);
 // nblocks counts those blocks.
 hipError_t launch_nf4_quantize(const float* W, int64_t nblocks, uint8_t* codes, uint8_t* q8,
-                               float* step, int code, int bshift, hipStream_t stream);
+                               float* step, int code, int bshift, const UserTable* ut,
+                               hipStream_t stream);
 hipError_t launch_nf4_dequantize(const uint8_t* codes, const uint8_t* q8, const float* step,
                                  int64_t nelem, uint16_t* out, int code, int bshift,
-                                 hipStream_t stream);
+                                 const UserTable* ut, hipStream_t stream);
 
 // ---- qgemm.hip: MFMA tile kernels with the NF4 dequantization in the prologue ----
 struct Nf4View {
@@ -21,8 +23,9 @@ struct Nf4View {
   const uint8_t* q8;
   const float* step;
   int64_t N, K;
-  int code;    // kId of CodeNF4, CodeFP4, CodeNF3 or CodeNF2
-  int bshift;  // block size 64 << bshift (K is a multiple of it)
+  int code;     // kId of the code type
+  int bshift;   // block size 64 << bshift (K is a multiple of it)
+  UserTable ut; // the caller's codebook (CodeUser types only)
 };
 
 // Y[M,N] = X[M,K] W^T + bf16(s U)[M,r] B[N,r]^T.  U has row stride ldu (a

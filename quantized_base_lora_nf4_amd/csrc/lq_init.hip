@@ -754,7 +754,7 @@ hipError_t launch_lq_init(const LqArgs& a, hipStream_t stream) {
     return mul_xm(Y2, N, Mm, r, a.L1) && mul_xm(Z, K, Mm + (size_t)l * r, r, a.L2t);
   };
   auto q_step = [&](const float* R) {
-    return (e = launch_nf4_quantize(R, nblocks, a.codes, a.q8, a.step, a.code, 0, stream)) ==
+    return (e = launch_nf4_quantize(R, nblocks, a.codes, a.q8, a.step, a.code, 0, nullptr, stream)) ==
            hipSuccess;
   };
   auto residual = [&]() {

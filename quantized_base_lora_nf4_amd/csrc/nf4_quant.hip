@@ -84,18 +84,37 @@ __device__ __forceinline__ float div_refined(float a, float b, float r) {
 }
 
 // Block size 64 << BS (BS = 0, 1, 2: 64, 128, 256 elements per constant).
+// Code of x under a caller's codebook: the count of thresholds below x,
+// one compare per threshold (they may lie arbitrarily close together, so
+// the bucket table does not apply), mapped to the lowest code of that value.
+__device__ __forceinline__ uint32_t user_code(float x, const UserTable& u) {
+  uint32_t n = 0;
+#pragma unroll
+  for (int i = 0; i < 15; ++i) n += (x > u.thr[i]) ? 1u : 0u;
+  const uint64_t map = ((uint64_t)u.code_hi << 32) | u.code_lo;
+  return (uint32_t)(map >> (4 * n)) & 15u;
+}
+
+template <class CT>
+__device__ __forceinline__ uint32_t zero_code() {
+  if constexpr (CT::kUser) return 0u;  // not reached: user blocks take user_code
+  else return CT::table.zero_code;
+}
+
 template <class CT, int BS>
 __global__ __launch_bounds__(256) void k_nf4_quantize(const float* __restrict__ W,
                                                       int64_t nblocks,
                                                       uint8_t* __restrict__ codes,
                                                       uint8_t* __restrict__ q8,
-                                                      float* __restrict__ step) {
+                                                      float* __restrict__ step, UserTable ut) {
   constexpr int kLanesPerBlock = 16 << BS;  // four elements per lane
   __shared__ float cabs[256];
   __shared__ float wmax[4];
   __shared__ uint2 bucket[kBuckets];
-  build_buckets<CT>(bucket);
-  __syncthreads();
+  if constexpr (!CT::kUser) {
+    build_buckets<CT>(bucket);
+    __syncthreads();
+  }
   const int64_t g = blockIdx.x;
   const int64_t b0 = g * 256;  // first block of the group
   const int nb = (int)((nblocks - b0) < 256 ? (nblocks - b0) : 256);
@@ -117,7 +136,15 @@ __global__ __launch_bounds__(256) void k_nf4_quantize(const float* __restrict__ 
       for (int off = kLanesPerBlock / 2; off >= 1; off >>= 1)
         m = fmaxf(m, __shfl_xor(m, off, kLanesPerBlock));
       uint32_t c0, c1, c2, c3;
-      if (m >= 0x1p-60f && m <= 0x1p126f) {
+      if constexpr (CT::kUser) {
+        // IEEE-correct division for every block (the refined quotient is
+        // checked only near the built-in thresholds); x = 0 in an all-zero
+        // block, which then takes the code of the value nearest to zero
+        c0 = user_code(m > 0.0f ? v[0] / m : 0.0f, ut);
+        c1 = user_code(m > 0.0f ? v[1] / m : 0.0f, ut);
+        c2 = user_code(m > 0.0f ? v[2] / m : 0.0f, ut);
+        c3 = user_code(m > 0.0f ? v[3] / m : 0.0f, ut);
+      } else if (m >= 0x1p-60f && m <= 0x1p126f) {
         const float r = 1.0f / m;  // IEEE-correct fp32 division
         c0 = quant_code<CT>(div_refined(v[0], m, r), bucket);
         c1 = quant_code<CT>(div_refined(v[1], m, r), bucket);
@@ -130,7 +157,7 @@ __global__ __launch_bounds__(256) void k_nf4_quantize(const float* __restrict__ 
         c2 = quant_code<CT>(v[2] / m, bucket);
         c3 = quant_code<CT>(v[3] / m, bucket);
       } else {
-        c0 = c1 = c2 = c3 = CT::table.zero_code;  // all-zero block: the zero level
+        c0 = c1 = c2 = c3 = zero_code<CT>();  // all-zero block: the zero level
       }
       if constexpr (CT::kBits == 4) {
         const uint16_t packed = (uint16_t)(c0 | (c1 << 4) | (c2 << 8) | (c3 << 12));
@@ -191,9 +218,10 @@ __global__ __launch_bounds__(256) void k_nf4_dequantize(const uint8_t* __restric
                                                         const uint8_t* __restrict__ q8,
                                                         const float* __restrict__ step,
                                                         int64_t n8, int bshift,
-                                                        uint16_t* __restrict__ out) {
+                                                        uint16_t* __restrict__ out,
+                                                        UserTable ut) {
   __shared__ float lv[16];
-  if (threadIdx.x < 16) lv[threadIdx.x] = code_value<CT>(threadIdx.x);
+  if (threadIdx.x < 16) lv[threadIdx.x] = level_of<CT>(ut, threadIdx.x);
   __syncthreads();
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n8;
        i += (int64_t)gridDim.x * blockDim.x) {
@@ -219,32 +247,35 @@ __global__ __launch_bounds__(256) void k_nf4_dequantize(const uint8_t* __restric
 }
 
 hipError_t launch_nf4_quantize(const float* W, int64_t nblocks, uint8_t* codes, uint8_t* q8,
-                               float* step, int code, int bshift, hipStream_t stream) {
+                               float* step, int code, int bshift, const UserTable* ut,
+                               hipStream_t stream) {
   const int64_t ngroups = (nblocks + 255) / 256;
-  return with_code(code, [&](auto ct) {
+  const UserTable u = ut ? *ut : UserTable{};
+  return with_any_code(code, [&](auto ct) {
     using CT = decltype(ct);
     if (bshift == 2)
       hipLaunchKernelGGL((k_nf4_quantize<CT, 2>), dim3((unsigned)ngroups), dim3(256), 0, stream, W,
-                         nblocks, codes, q8, step);
+                         nblocks, codes, q8, step, u);
     else if (bshift == 1)
       hipLaunchKernelGGL((k_nf4_quantize<CT, 1>), dim3((unsigned)ngroups), dim3(256), 0, stream, W,
-                         nblocks, codes, q8, step);
+                         nblocks, codes, q8, step, u);
     else
       hipLaunchKernelGGL((k_nf4_quantize<CT, 0>), dim3((unsigned)ngroups), dim3(256), 0, stream, W,
-                         nblocks, codes, q8, step);
+                         nblocks, codes, q8, step, u);
     return hipGetLastError();
   });
 }
 
 hipError_t launch_nf4_dequantize(const uint8_t* codes, const uint8_t* q8, const float* step,
                                  int64_t nelem, uint16_t* out, int code, int bshift,
-                                 hipStream_t stream) {
+                                 const UserTable* ut, hipStream_t stream) {
   const int64_t n8 = nelem / 8;
   int64_t grid = (n8 + 255) / 256;
   if (grid > 65536) grid = 65536;
-  return with_code(code, [&](auto ct) {
+  const UserTable u = ut ? *ut : UserTable{};
+  return with_any_code(code, [&](auto ct) {
     hipLaunchKernelGGL(k_nf4_dequantize<decltype(ct)>, dim3((unsigned)grid), dim3(256), 0, stream,
-                       codes, q8, step, n8, bshift, out);
+                       codes, q8, step, n8, bshift, out, u);
     return hipGetLastError();
   });
 }

@@ -63,14 +63,14 @@ struct LevelTable {
 };
 
 template <class CT>
-__device__ __forceinline__ LevelTable make_table(float chat) {
+__device__ __forceinline__ LevelTable make_table(float chat, const UserTable& ut) {
   LevelTable t;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const uint32_t p0 =
-        pack_bf16x2(code_value<CT>(4 * q) * chat, code_value<CT>(4 * q + 1) * chat);
+        pack_bf16x2(level_of<CT>(ut, 4 * q) * chat, level_of<CT>(ut, 4 * q + 1) * chat);
     const uint32_t p1 =
-        pack_bf16x2(code_value<CT>(4 * q + 2) * chat, code_value<CT>(4 * q + 3) * chat);
+        pack_bf16x2(level_of<CT>(ut, 4 * q + 2) * chat, level_of<CT>(ut, 4 * q + 3) * chat);
     t.lo[q] = perm(p1, p0, 0x06040200u);
     t.hi[q] = perm(p1, p0, 0x07050301u);
   }
@@ -341,8 +341,9 @@ struct StepRegs {
 };
 
 template <class CT>
-__device__ __forceinline__ void dequant_block(uint16_t* dst, const StepRegs<CT>& r) {
-  const LevelTable t = make_table<CT>((float)r.q * r.st);
+__device__ __forceinline__ void dequant_block(uint16_t* dst, const StepRegs<CT>& r,
+                                              const UserTable& ut) {
+  const LevelTable t = make_table<CT>((float)r.q * r.st, ut);
 #pragma unroll
   for (int w = 0; w < 8; ++w)
     *reinterpret_cast<u32x4*>(dst + 8 * w) = lookup8(nibbles<CT>(r.c[w / 4], w % 4), t);
@@ -362,11 +363,12 @@ __device__ __forceinline__ void dequant_block(uint16_t* dst, const StepRegs<CT>&
 template <class C, bool kTransB, class CT, bool kD>
 __device__ __forceinline__ void step_interleaved(const uint16_t* As, const uint16_t* Bs,
                                                  uint16_t* Bw_n, const StepRegs<CT>& rn, int wm,
-                                                 int wn, int lane, AccT<C>& acc) {
+                                                 int wn, int lane, AccT<C>& acc,
+                                                 const UserTable& ut) {
   Frags<C> f[2];
   read_frags<C, kTransB>(f[0], As, Bs, wm, wn, lane, 0);
   LevelTable t;
-  if constexpr (kD) t = make_table<CT>((float)rn.q * rn.st);
+  if constexpr (kD) t = make_table<CT>((float)rn.q * rn.st, ut);
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
     if (kk < 3) read_frags<C, kTransB>(f[(kk + 1) & 1], As, Bs, wm, wn, lane, kk + 1);
@@ -394,6 +396,7 @@ struct FwdArgs {
   float s;
   uint16_t* Y;
   int64_t M, N, K;
+  UserTable ut;  // the caller's codebook (CodeUser types only)
 };
 
 // kQ4: K is a multiple of 256 (and q8 16-byte aligned, as the C ABI
@@ -498,7 +501,8 @@ __global__ __launch_bounds__(C::NT, 1) void k_qgemm_fwd(FwdArgs p) {
         rnext.st = sg;
       }
       __builtin_amdgcn_sched_barrier(0);
-      step_interleaved<C, false, CT, D>(As, Bs, Bs_n + wrow * LDA, rnext, wm, wn, lane, acc);
+      step_interleaved<C, false, CT, D>(As, Bs, Bs_n + wrow * LDA, rnext, wm, wn, lane, acc,
+                                        p.ut);
       // loads after the tile loads: two code loads (>= 2 instructions),
       // plus q8 and step unless kQ4 (where a group start adds the word of
       // constants and the step); none in an MFMA-only thread
@@ -519,7 +523,7 @@ __global__ __launch_bounds__(C::NT, 1) void k_qgemm_fwd(FwdArgs p) {
       ra.st = s0;
     }
     load_x(xs0, 0);
-    if constexpr (D) dequant_block<CT>(ws0 + wrow * LDA, ra);
+    if constexpr (D) dequant_block<CT>(ws0 + wrow * LDA, ra, p.ut);
     wait_vmem();
     __syncthreads();
     int64_t kt = 0;
@@ -609,6 +613,7 @@ struct BwdArgs {
   int32_t r;
   uint16_t* dX;
   int64_t M, N, K;
+  UserTable ut;  // the caller's codebook (CodeUser types only)
 };
 
 // Output tile BM tokens x BN input features; contraction over the weight's
@@ -691,7 +696,7 @@ __global__ __launch_bounds__(C::NT, 1) void k_qgemm_bwd(BwdArgs p) {
       load_w(rload, ns + 2);   // ... then the weight loads, which outlive the step
       __builtin_amdgcn_sched_barrier(0);
       step_interleaved<C, true, CT, D>(As, Bs, Bs_n + wr * C::LDTB + wb * C::BSTR, rnext, wm,
-                                       wn, lane, acc);
+                                       wn, lane, acc, p.ut);
       // two code loads, q8 and step after the tile loads (>= kWLoads); none
       // in an MFMA-only thread
       if constexpr (D)
@@ -703,7 +708,7 @@ __global__ __launch_bounds__(C::NT, 1) void k_qgemm_bwd(BwdArgs p) {
     load_w(ra, 0);
     load_w(rb, 1);
     load_x(xs0, 0);
-    if constexpr (D) dequant_block<CT>(ws0 + wr * C::LDTB + wb * C::BSTR, ra);
+    if constexpr (D) dequant_block<CT>(ws0 + wr * C::LDTB + wb * C::BSTR, ra, p.ut);
     wait_vmem();
     __syncthreads();
     int64_t ns = 0;
@@ -752,10 +757,10 @@ hipError_t launch_qgemm_fwd(const Nf4View& w, const uint16_t* X, int64_t M, cons
                             int64_t ldu, const uint16_t* B, int32_t r, float s, uint16_t* Y,
                             hipStream_t stream) {
   using C = GemmCfg;
-  FwdArgs a{X, w.codes, w.q8, w.step, U, ldu, B, r, s, Y, M, w.N, w.K};
+  FwdArgs a{X, w.codes, w.q8, w.step, U, ldu, B, r, s, Y, M, w.N, w.K, w.ut};
   dim3 grid((unsigned)(((w.N + C::BN - 1) / C::BN) * ((M + C::BM - 1) / C::BM)));
   const bool q4 = (w.K % 256) == 0 && w.bshift == 0;
-  with_code(w.code, [&](auto ct) {
+  with_any_code(w.code, [&](auto ct) {
     using CT = decltype(ct);
     if (q4)
       hipLaunchKernelGGL((k_qgemm_fwd<C, CT, true, 0>), grid, dim3(C::NT), 0, stream, a);
@@ -774,9 +779,9 @@ hipError_t launch_qgemm_bwd(const Nf4View& w, const uint16_t* dY, int64_t M, con
                             int64_t lddu, const uint16_t* A, int32_t r, uint16_t* dX,
                             hipStream_t stream) {
   using C = GemmCfg;
-  BwdArgs a{dY, w.codes, w.q8, w.step, dU, lddu, A, r, dX, M, w.N, w.K};
+  BwdArgs a{dY, w.codes, w.q8, w.step, dU, lddu, A, r, dX, M, w.N, w.K, w.ut};
   dim3 grid((unsigned)(((w.K + C::BN - 1) / C::BN) * ((M + C::BM - 1) / C::BM)));
-  with_code(w.code, [&](auto ct) {
+  with_any_code(w.code, [&](auto ct) {
     using CT = decltype(ct);
     if (w.bshift == 2)
       hipLaunchKernelGGL((k_qgemm_bwd<C, CT, 2>), grid, dim3(C::NT), 0, stream, a);

@@ -13,13 +13,17 @@ from typing import Optional, Tuple
 import torch
 
 from ._lib import (QLORA_CODE_FP4, QLORA_CODE_NF2, QLORA_CODE_NF3, QLORA_CODE_NF4,
-                   QLORA_ERR_INFEASIBLE, Nf4Tensor, check, lib)
+                   QLORA_CODE_USER2, QLORA_CODE_USER3, QLORA_CODE_USER4, QLORA_ERR_INFEASIBLE,
+                   Nf4Tensor, check, lib)
 
 BLOCKSIZE = 64
 DQ_BLOCKSIZE = 256
 CODE_TYPES = {"nf4": QLORA_CODE_NF4, "fp4": QLORA_CODE_FP4, "nf3": QLORA_CODE_NF3,
-              "nf2": QLORA_CODE_NF2}
-CODE_BITS = {"nf4": 4, "fp4": 4, "nf3": 3, "nf2": 2}
+              "nf2": QLORA_CODE_NF2, "user4": QLORA_CODE_USER4, "user3": QLORA_CODE_USER3,
+              "user2": QLORA_CODE_USER2}
+CODE_BITS = {"nf4": 4, "fp4": 4, "nf3": 3, "nf2": 2, "user4": 4, "user3": 3, "user2": 2}
+# code types whose values the caller supplies (a codebook of 2^bits values)
+USER_CODES = ("user4", "user3", "user2")
 
 
 def _code_id(code: str) -> int:
@@ -27,6 +31,19 @@ def _code_id(code: str) -> int:
         return CODE_TYPES[code]
     except KeyError:
         raise ValueError(f"code must be one of {sorted(CODE_TYPES)}, got {code!r}") from None
+
+
+def _levels_array(code: str, levels) -> "ctypes.Array":
+    """Host fp32 copy of a caller's codebook (2^bits values in code order)."""
+    if levels is None:
+        raise ValueError(f"code type {code!r} needs its 2^{CODE_BITS[code]} values (levels=)")
+    vals = [float(v) for v in (levels.tolist() if hasattr(levels, "tolist") else levels)]
+    if len(vals) != 2 ** CODE_BITS[code]:
+        raise ValueError(f"{code!r} takes {2 ** CODE_BITS[code]} values, got {len(vals)}")
+    arr = (ctypes.c_float * 16)()
+    for i, v in enumerate(vals):
+        arr[i] = v
+    return arr
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -57,12 +74,14 @@ class NF4Weight:
     step: torch.Tensor    # float32 [ceil(N*K/16384)]
     N: int
     K: int
-    code: str = "nf4"     # the code table the codes index: "nf4", "fp4", "nf3", "nf2"
+    code: str = "nf4"     # the code table: "nf4", "fp4", "nf3", "nf2" or "user4/3/2"
     blocksize: int = BLOCKSIZE  # elements per 8-bit constant: 64, 128 or 256
+    levels: Optional[object] = None  # user code types: host fp32 [16] codebook (ctypes)
 
     def struct(self) -> Nf4Tensor:
+        lv = ctypes.cast(self.levels, ctypes.c_void_p).value if self.levels is not None else None
         return Nf4Tensor(_ptr(self.codes), _ptr(self.q8), _ptr(self.step), self.N, self.K,
-                         self.blocksize, DQ_BLOCKSIZE, _code_id(self.code))
+                         self.blocksize, DQ_BLOCKSIZE, _code_id(self.code), lv)
 
     def nbytes(self) -> int:
         return self.codes.numel() + self.q8.numel() + 4 * self.step.numel()
@@ -77,6 +96,18 @@ def code_table(code: str = "nf4") -> Tuple[list, list]:
                                ctypes.cast(th, ctypes.c_void_p))
     check(min(n, 0), "qlora_code_table")
     return list(lv)[:2 ** CODE_BITS[code]], list(th)[:n]
+
+
+def user_table(code: str, levels) -> list:
+    """The decision thresholds the library derives from a caller's codebook
+    (code "user4", "user3" or "user2"); raises if the values break the
+    contract (finite, |v| <= 1, and 0 or |v| >= 2^-20)."""
+    arr = _levels_array(code, levels)
+    th = (ctypes.c_float * 15)()
+    n = lib().qlora_user_table(_code_id(code), ctypes.cast(arr, ctypes.c_void_p),
+                               ctypes.cast(th, ctypes.c_void_p))
+    check(min(n, 0), "qlora_user_table")
+    return list(th)[:n]
 
 
 BLOCKSIZES = (64, 128, 256)
@@ -101,14 +132,23 @@ def alloc_nf4(N: int, K: int, device="cuda", code: str = "nf4",
 
 
 def nf4_quantize(W: torch.Tensor, out: Optional[NF4Weight] = None, stream=None,
-                 code: str = "nf4", blocksize: int = BLOCKSIZE) -> NF4Weight:
+                 code: str = "nf4", blocksize: int = BLOCKSIZE, levels=None) -> NF4Weight:
     """Quantize an fp32 [N, K] device tensor to block codes (NF4 by default,
-    or FP4, NF3, NF2) with double-quantized constants, one per `blocksize`
-    elements (64, 128 or 256)."""
+    or FP4, NF3, NF2, or a caller's codebook: code "user4"/"user3"/"user2"
+    with its 2^bits values in code order as `levels`) with double-quantized
+    constants, one per `blocksize` elements (64, 128 or 256)."""
     if W.dtype != torch.float32 or W.dim() != 2:
         raise TypeError("W must be a 2-D float32 tensor")
+    if not W.is_cuda:
+        raise ValueError("W must be a device tensor")
     N, K = W.shape
     cid = _code_id(code)
+    if code in USER_CODES:
+        arr = _levels_array(code, levels)
+    elif levels is not None:
+        raise ValueError(f"code type {code!r} has built-in values; levels= is for user codes")
+    else:
+        arr = None
     if out is None:
         out = alloc_nf4(N, K, W.device, code, blocksize)
     elif (out.codes.numel() != N * K * CODE_BITS[code] // 8 or
@@ -117,7 +157,12 @@ def nf4_quantize(W: torch.Tensor, out: Optional[NF4Weight] = None, stream=None,
     else:
         out.code = code
         out.blocksize = blocksize
-    if cid == QLORA_CODE_NF4:
+    out.levels = arr
+    if arr is not None:
+        st = lib().qlora_quantize_user(_ptr(W), N, K, cid, ctypes.cast(arr, ctypes.c_void_p),
+                                       blocksize, DQ_BLOCKSIZE, _ptr(out.codes), _ptr(out.q8),
+                                       _ptr(out.step), _stream(stream))
+    elif cid == QLORA_CODE_NF4:
         st = lib().nf4_quantize(_ptr(W), N, K, blocksize, DQ_BLOCKSIZE, _ptr(out.codes),
                                 _ptr(out.q8), _ptr(out.step), _stream(stream))
     else:
@@ -181,6 +226,8 @@ def _check_weight(w: NF4Weight) -> torch.device:
         raise TypeError("codes and q8 must be uint8, step float32")
     if w.codes.numel() != w.N * w.K * CODE_BITS[w.code] // 8:
         raise ValueError("codes do not match the weight's shape and code width")
+    if w.code in USER_CODES and w.levels is None:
+        raise ValueError(f"code type {w.code!r} needs its codebook (NF4Weight.levels)")
     if w.blocksize not in BLOCKSIZES:
         raise ValueError(f"block size must be one of {BLOCKSIZES}")
     if w.q8.numel() != w.N * w.K // w.blocksize or w.step.numel() != -(-w.q8.numel() // DQ_BLOCKSIZE):

@@ -178,8 +178,16 @@ def test_workspace_size_rules():
 FAKE = 1 << 20  # an aligned non-null address that is never dereferenced
 
 
-def _w(N=64, K=64, bs=64, dq=256, codes=FAKE, code_type=_lib.QLORA_CODE_NF4):
-    return _lib.Nf4Tensor(codes, FAKE, FAKE, N, K, bs, dq, code_type)
+def _w(N=64, K=64, bs=64, dq=256, codes=FAKE, code_type=_lib.QLORA_CODE_NF4, levels=None):
+    return _lib.Nf4Tensor(codes, FAKE, FAKE, N, K, bs, dq, code_type,
+                          None if levels is None else ctypes.cast(levels, ctypes.c_void_p).value)
+
+
+def _levels(vals):
+    arr = (ctypes.c_float * 16)()
+    for i, v in enumerate(vals):
+        arr[i] = v
+    return arr
 
 
 def test_quantize_rejects_bad_arguments_without_launching():
@@ -197,9 +205,21 @@ def test_quantize_rejects_bad_arguments_without_launching():
     assert call(bs=32) == _lib.QLORA_ERR_UNSUPPORTED
     assert call(dq=128) == _lib.QLORA_ERR_UNSUPPORTED
     assert call(W=FAKE + 4) == _lib.QLORA_ERR_INVALID
-    # the code-type variant: unknown types are rejected, the checks above apply
-    for ct, want in ((4, _lib.QLORA_ERR_UNSUPPORTED), (-1, _lib.QLORA_ERR_UNSUPPORTED)):
+    # the code-type variant: unknown types are rejected, user types need
+    # their values (qlora_quantize_user), the checks above apply
+    for ct, want in ((7, _lib.QLORA_ERR_UNSUPPORTED), (-1, _lib.QLORA_ERR_UNSUPPORTED),
+                     (_lib.QLORA_CODE_USER4, _lib.QLORA_ERR_INVALID)):
         assert L.qlora_quantize(FAKE, 4, 128, ct, 64, 256, FAKE, FAKE, FAKE, None) == want
+    good = _levels([-1.0, -0.5, 0.0, 0.5])
+    bad = _levels([-1.0, -0.5, 0.0, 1e-7])
+
+    def user(ct=_lib.QLORA_CODE_USER2, lv=good, K=128):
+        return L.qlora_quantize_user(FAKE, 4, K, ct, ctypes.cast(lv, ctypes.c_void_p) if lv else None,
+                                     64, 256, FAKE, FAKE, FAKE, None)
+    assert user(ct=_lib.QLORA_CODE_NF4) == _lib.QLORA_ERR_UNSUPPORTED
+    assert user(lv=None) == _lib.QLORA_ERR_INVALID
+    assert user(lv=bad) == _lib.QLORA_ERR_INVALID
+    assert user(K=96) == _lib.QLORA_ERR_INVALID
     assert L.qlora_quantize(None, 4, 128, _lib.QLORA_CODE_FP4, 64, 256, FAKE, FAKE, FAKE,
                             None) == _lib.QLORA_ERR_INVALID
     assert L.qlora_quantize(FAKE, 4, 96, _lib.QLORA_CODE_FP4, 64, 256, FAKE, FAKE, FAKE,
@@ -222,7 +242,11 @@ def test_linear_rejects_bad_arguments_without_launching():
     assert fwd(w=_w(60, 128)) == _lib.QLORA_ERR_INVALID
     assert fwd(w=_w(64, 128, bs=96)) == _lib.QLORA_ERR_UNSUPPORTED
     assert fwd(w=_w(64, 192, bs=128)) == _lib.QLORA_ERR_INVALID   # K not a multiple of it
-    assert fwd(w=_w(64, 128, code_type=5)) == _lib.QLORA_ERR_UNSUPPORTED
+    assert fwd(w=_w(64, 128, code_type=7)) == _lib.QLORA_ERR_UNSUPPORTED
+    # a caller's codebook: missing, or outside the contract
+    assert fwd(w=_w(64, 128, code_type=_lib.QLORA_CODE_USER3)) == _lib.QLORA_ERR_INVALID
+    lv = _levels([0.0, 0.5, -0.5, 1.0, -1.0, 0.25, -0.25, float("inf")])
+    assert fwd(w=_w(64, 128, code_type=_lib.QLORA_CODE_USER3, levels=lv)) == _lib.QLORA_ERR_INVALID
     assert fwd(w=_w(64, 128, codes=None)) == _lib.QLORA_ERR_INVALID
     assert fwd(nbytes=need - 1) == _lib.QLORA_ERR_WORKSPACE
     assert fwd(ws=None) == _lib.QLORA_ERR_INVALID
@@ -248,7 +272,7 @@ def test_linear_rejects_bad_arguments_without_launching():
 
     w = _w(64, 128)
     assert L.nf4_dequantize(ctypes.byref(w), None, None) == _lib.QLORA_ERR_INVALID
-    w = _w(64, 128, code_type=6)
+    w = _w(64, 128, code_type=9)
     assert L.nf4_dequantize(ctypes.byref(w), FAKE, None) == _lib.QLORA_ERR_UNSUPPORTED
     assert L.qlora_linear_bwd(ctypes.byref(w), FAKE, FAKE, 32, FAKE, FAKE, None, 8, 1.0, None,
                               FAKE, FAKE, FAKE, needb, None) == _lib.QLORA_ERR_UNSUPPORTED
@@ -328,3 +352,53 @@ def test_status_strings():
     for st in (0, -1, -2, -3, -4, -5):
         assert qn.lib().qlora_status_str(st)
     assert "workspace" in _lib.status_str(-3)
+
+
+def _next_up(f):
+    return np.nextafter(np.float32(f), np.float32(np.inf))
+
+
+@pytest.mark.parametrize("code,ct", [("user4", _lib.QLORA_CODE_USER4),
+                                     ("user3", _lib.QLORA_CODE_USER3),
+                                     ("user2", _lib.QLORA_CODE_USER2)])
+def test_user_table_thresholds_are_exact_midpoints_rounded_down(code, ct):
+    """For random codebooks (any order, repeats, zero-free, 1-ulp neighbours)
+    each threshold the library derives is the largest fp32 at or below the
+    exact midpoint of two consecutive distinct values, one per gap."""
+    from fractions import Fraction
+    rng = np.random.default_rng(ct)
+    n = 2 ** qn.ops.CODE_BITS[code]
+    for trial in range(40):
+        v = rng.uniform(-1, 1, n).astype(np.float32)
+        if trial % 4 == 1:
+            v[0] = v[1]
+        if trial % 4 == 2:
+            v[2] = np.nextafter(v[3], np.float32(2))
+        if trial % 4 == 3:
+            v[: n // 2] = -v[n // 2:]
+        th = qn.user_table(code, v)
+        d = sorted(set(float(x) for x in v))
+        assert len(th) == len(d) - 1
+        for t, a, b in zip(th, d[:-1], d[1:]):
+            mid = (Fraction(a) + Fraction(b)) / 2
+            assert Fraction(float(t)) <= mid < Fraction(float(_next_up(t))), (t, a, b)
+
+
+def test_user_table_of_a_builtin_table_is_the_builtin_rule():
+    for code, user in (("nf4", "user4"), ("fp4", "user4"), ("nf3", "user3"), ("nf2", "user2")):
+        lv, th = qn.code_table(code)
+        assert qn.user_table(user, lv) == th
+
+
+def test_user_table_rejects_values_outside_the_contract():
+    L = qn.lib()
+    for vals in ([1.5, 0, 0, 0], [1e-7, 0, 0, 0], [float("nan"), 0, 0, 0]):
+        arr = _levels(vals)
+        assert L.qlora_user_table(_lib.QLORA_CODE_USER2, ctypes.cast(arr, ctypes.c_void_p),
+                                  None) == _lib.QLORA_ERR_INVALID
+    assert L.qlora_user_table(_lib.QLORA_CODE_NF4, ctypes.cast(_levels([0] * 16), ctypes.c_void_p),
+                              None) == _lib.QLORA_ERR_UNSUPPORTED
+    assert L.qlora_user_table(_lib.QLORA_CODE_USER4, None, None) == _lib.QLORA_ERR_INVALID
+    # the smallest nonzero magnitude allowed, and +-0 together
+    arr = _levels([-2.0 ** -20, 0.0, -0.0, 2.0 ** -20])
+    assert L.qlora_user_table(_lib.QLORA_CODE_USER2, ctypes.cast(arr, ctypes.c_void_p), None) == 2

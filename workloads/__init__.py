@@ -179,3 +179,37 @@ def draw_lq_inputs(N: int, K: int, r: int, l: int, *, sigma: float = 0.02, rank0
     Omega = rng.standard_normal((K, l), dtype=np.float32)
     return LqInputs(W=W, Omega=Omega, r=r, l=l)
 
+
+
+CODEBOOK_KINDS = ("plain", "with_zero", "repeats", "symmetric", "clustered")
+
+
+def draw_codebook(rng: np.random.Generator, bits: int, kind: str = "plain") -> np.ndarray:
+    """A caller's codebook of 2^bits fp32 values in shuffled code order,
+    within the contract (|v| <= 1, and 0 or |v| >= 2^-20):
+      plain      uniform on [-1, 1]
+      with_zero  one value exactly 0
+      repeats    two pairs of equal values
+      symmetric  no zero, every value mirrored (a midpoint at 0)
+      clustered  values 1 ulp apart and their negatives
+    """
+    n = 2 ** bits
+    v = rng.uniform(-1.0, 1.0, n).astype(np.float32)
+    v[(v != 0) & (np.abs(v) < 2.0 ** -20)] = np.float32(2.0 ** -20)
+    if kind == "with_zero":
+        v[rng.integers(n)] = 0.0
+    elif kind == "repeats":
+        v[1] = v[0]
+        v[-1] = v[-2]
+    elif kind == "symmetric":
+        h = np.abs(v[: n // 2]) + np.float32(2.0 ** -20)
+        v = np.concatenate([-h, h]).astype(np.float32)
+    elif kind == "clustered":
+        base = np.float32(rng.uniform(0.1, 0.9))
+        v = np.array([base] * n, np.float32)
+        for i in range(1, n):
+            v[i] = np.nextafter(v[i - 1], np.float32(2.0)) if i % 2 else -v[i - 1]
+    elif kind != "plain":
+        raise ValueError(kind)
+    rng.shuffle(v)
+    return v
