@@ -736,7 +736,9 @@ def _time_gemv(L, torch, ev, structs, inp, M, N, K, g, A, B, d16, dev, sp, wbyte
         "weight_bytes": wbytes, "copies_rotated": ncopy,
         "roofline": {"bound": "hbm", "kernel": "k_qgemv", "achieved": round(gbs, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBPS, 4), "avg_launch_us": round(k_avg * 1e3, 2)}}
+                     "frac": round(gbs / HBM_PEAK_GBPS, 4), "avg_launch_us": round(k_avg * 1e3, 2),
+                     "traffic": load_traffic("k_qgemv", f"skinny_gemv_{N}x{K}_M{M}",
+                                             kernel_source_hash(["gemv.hip", "common.hpp"]))}}
 
 
 def hbm_read_ceiling(qn, torch, ev, sp, sizes, reps=40):
