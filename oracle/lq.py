@@ -2,10 +2,10 @@
 Test infrastructure only.
 
 "LQ-LoRA: Low-rank Plus Quantized Matrix Decomposition for Efficient
-Language Model Finetuning", abstract: an iterative algorithm splits each
-pretrained matrix into a high-precision low-rank component and a
-memory-efficient quantized component; in finetuning the quantized component
-stays fixed and only the low-rank one is trained.
+Language Model Finetuning", abstract: each weight is written, by an
+iteration, as a quantized part plus a low-rank part held in high precision;
+finetuning then trains the low-rank part and leaves the quantized part
+frozen.
 
 The abstract gives no steps.  Readings taken (listed in the design notes):
 

@@ -1,8 +1,8 @@
 // Low-rank plus quantized decomposition of a frozen weight, W ~ Q + L1 L2
 // ("LQ-LoRA: Low-rank Plus Quantized Matrix Decomposition for Efficient
-// Language Model Finetuning", abstract: an iterative algorithm splits each
-// pretrained matrix into a high-precision low-rank component, trained as the
-// adapter, and a fixed quantized component).
+// Language Model Finetuning", abstract: the weight becomes, by an iteration,
+// a frozen quantized part plus a high-precision low-rank part that finetuning
+// trains as the adapter).
 //
 // Alternating minimization of ||W - Q - L1 L2||_F:
 //   L step  rank-r approximation of E = W - Q: randomized subspace iteration
