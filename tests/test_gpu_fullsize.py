@@ -11,6 +11,9 @@ Per weight of every workload:
   every 256-row tile boundary, the first and last row, and seeded rows
   spread so that every 256-row tile holds at least one more; the few-token
   workload is compared in full.
+* The same for the LLaMA-7B up_proj under every other configuration the
+  benchmark times: FP4, NF3, NF2, a caller's codebook, block sizes 128 and
+  256.
 * The adapter terms alone (W = 0: Y = s U B^T, dX = dU A) at two full
   shapes with r = 64, where they are about 1 % of Y and so cannot be judged
   inside the full output: the LLaMA-7B up_proj (11008 x 4096) and the
@@ -77,36 +80,36 @@ def _sample_rows(M, seed):
     return out
 
 
-def _quantize_and_check(W, tag):
+def _quantize_and_check(W, tag, code="nf4", blocksize=64, levels=None):
     """GPU quantize + dequantize, bit-exact against the oracle over the
     whole weight; returns the GPU weight and the oracle's W_hat (fp32)."""
     N, K = W.shape
-    say(f"[fullsize] {tag}: quantize {N}x{K}")
+    say(f"[fullsize] {tag}: quantize {N}x{K} ({code}, block {blocksize})")
     Wd = torch.from_numpy(W).cuda()
-    w = qn.nf4_quantize(Wd)
+    w = qn.nf4_quantize(Wd, code=code, blocksize=blocksize, levels=levels)
     torch.cuda.synchronize()
     del Wd
     codes, q8, step = nf4_host(w)
-    oc, oq, os_ = nf4.quantize(W)
+    oc, oq, os_ = nf4.quantize(W, blocksize=blocksize, code=code, levels=levels)
     assert np.array_equal(codes, oc), f"{tag}: codes differ at bytes {np.nonzero(codes != oc)[0][:8]}"
     assert np.array_equal(q8, oq), f"{tag}: q8 differ at blocks {np.nonzero(q8 != oq)[0][:8]}"
     assert np.array_equal(step.view(np.uint32), os_.view(np.uint32)), f"{tag}: steps differ"
     say(f"[fullsize] {tag}: dequantize")
     deq = host_u16(qn.nf4_dequantize(w))
     torch.cuda.synchronize()
-    od = nf4.dequantize(oc, oq, os_, N, K)
+    od = nf4.dequantize(oc, oq, os_, N, K, blocksize=blocksize, code=code, levels=levels)
     assert np.array_equal(deq, od), f"{tag}: dequantized bits differ at {np.argwhere(deq != od)[:4]}"
     del deq, codes, oc
     return w, f32(od)
 
 
-@pytest.mark.parametrize("wl,wi", _cases(fwd_only=False))
-def test_fullsize_fwd_bwd(wl, wi):
+def _fwd_bwd_check(wl, wi, code="nf4", blocksize=64, levels=None):
     spec = wl.weights[wi]
-    tag = f"{wl.name}/{spec.name}"
+    tag = f"{wl.name}/{spec.name}" + ("" if (code, blocksize) == ("nf4", 64) else
+                                      f"/{code}/{blocksize}")
     inp = wl_mod.draw_workload_weight(wl, wi)
     M, N, K, r, s = inp.X.shape[0], spec.N, spec.K, wl.r, wl.s
-    w, What = _quantize_and_check(inp.W, tag)
+    w, What = _quantize_and_check(inp.W, tag, code, blocksize, levels)
 
     say(f"[fullsize] {tag}: fwd + bwd M={M} r={r}")
     X, dY, A, B = dev_u16(inp.X), dev_u16(inp.dY), dev_u16(inp.A), dev_u16(inp.B)
@@ -130,6 +133,28 @@ def test_fullsize_fwd_bwd(wl, wi):
     say(f"[fullsize] {tag}: rel err U {e_u:.2e} Y {e_y:.2e} dX {e_dx:.2e} dA {e_da:.2e} dB {e_db:.2e}")
 
 
+@pytest.mark.parametrize("wl,wi", _cases(fwd_only=False))
+def test_fullsize_fwd_bwd(wl, wi):
+    _fwd_bwd_check(wl, wi)
+
+
+# The other configurations the benchmark times on the headline step: code
+# types, a caller's codebook (the benchmark's own draw) and block sizes, on
+# the LLaMA-7B up_proj (11008 x 4096, 4096 tokens, r = 64).
+OTHER_CONFIGS = [("fp4", 64, None), ("nf3", 64, None), ("nf2", 64, None),
+                 ("user4", 64, (77, 0)), ("nf4", 128, None), ("nf4", 256, None)]
+
+
+@pytest.mark.parametrize("code,blocksize,book", OTHER_CONFIGS,
+                         ids=[f"{c}-{b}" for c, b, _ in OTHER_CONFIGS])
+def test_fullsize_other_configurations(code, blocksize, book):
+    wl = next(w for w in wl_mod.WORKLOADS if w.name == "llama7b_q_up_M4096_r64")
+    levels = None
+    if book is not None:
+        levels = wl_mod.draw_codebook(wl_mod.rng_for(*book), nf4.CODE_BITS[code], "plain")
+    _fwd_bwd_check(wl, 1, code, blocksize, levels)
+
+
 @pytest.mark.parametrize("wl,wi", _cases(fwd_only=True))
 def test_fullsize_few_token_forward(wl, wi):
     spec = wl.weights[wi]
@@ -149,6 +174,25 @@ def test_fullsize_few_token_forward(wl, wi):
         ref = linear.forward(f32(inp.X[:M]), What, Af, Bf, s)
         e = assert_close(f"Y M={M}", Yh, ref)
         say(f"[fullsize] {tag}: M={M} rel err Y {e:.2e}")
+
+
+@pytest.mark.parametrize("code", ["fp4", "nf3", "nf2"])
+def test_fullsize_few_token_forward_other_code_types(code):
+    """The benchmark's other code types on the few-token path, one token,
+    at the 28672 x 8192 weight."""
+    wl = next(w for w in wl_mod.WORKLOADS if w.fwd_only)
+    wi = max(range(len(wl.weights)), key=lambda i: wl.weights[i].N)
+    spec = wl.weights[wi]
+    tag = f"{wl.name}/{spec.name}/{code}"
+    inp = wl_mod.draw_workload_weight(wl, wi, M=max(wl.M))
+    w, What = _quantize_and_check(inp.W, tag, code)
+    A, B = dev_u16(inp.A), dev_u16(inp.B)
+    X = dev_u16(inp.X[:1])
+    Y = qn.qlora_linear_fwd(w, X, A, B, wl.s)
+    torch.cuda.synchronize()
+    ref = linear.forward(f32(inp.X[:1]), What, f32(inp.A), f32(inp.B), wl.s)
+    e = assert_close("Y M=1", f32(host_u16(Y)), ref)
+    say(f"[fullsize] {tag}: M=1 rel err Y {e:.2e}")
 
 
 ADAPTER_ONLY = [
