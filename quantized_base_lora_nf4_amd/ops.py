@@ -76,9 +76,11 @@ class NF4Weight:
     K: int
     code: str = "nf4"     # the code table: "nf4", "fp4", "nf3", "nf2" or "user4/3/2"
     blocksize: int = BLOCKSIZE  # elements per 8-bit constant: 64, 128 or 256
-    levels: Optional[object] = None  # user code types: host fp32 [16] codebook (ctypes)
+    levels: Optional[object] = None  # user code types: the codebook (2^bits values, host)
 
     def struct(self) -> Nf4Tensor:
+        if self.levels is not None and not isinstance(self.levels, ctypes.Array):
+            self.levels = _levels_array(self.code, self.levels)  # kept alive on self
         lv = ctypes.cast(self.levels, ctypes.c_void_p).value if self.levels is not None else None
         return Nf4Tensor(_ptr(self.codes), _ptr(self.q8), _ptr(self.step), self.N, self.K,
                          self.blocksize, DQ_BLOCKSIZE, _code_id(self.code), lv)
@@ -139,8 +141,6 @@ def nf4_quantize(W: torch.Tensor, out: Optional[NF4Weight] = None, stream=None,
     constants, one per `blocksize` elements (64, 128 or 256)."""
     if W.dtype != torch.float32 or W.dim() != 2:
         raise TypeError("W must be a 2-D float32 tensor")
-    if not W.is_cuda:
-        raise ValueError("W must be a device tensor")
     N, K = W.shape
     cid = _code_id(code)
     if code in USER_CODES:
@@ -149,6 +149,8 @@ def nf4_quantize(W: torch.Tensor, out: Optional[NF4Weight] = None, stream=None,
         raise ValueError(f"code type {code!r} has built-in values; levels= is for user codes")
     else:
         arr = None
+    if not W.is_cuda:
+        raise ValueError("W must be a device tensor")
     if out is None:
         out = alloc_nf4(N, K, W.device, code, blocksize)
     elif (out.codes.numel() != N * K * CODE_BITS[code] // 8 or

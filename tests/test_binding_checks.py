@@ -77,3 +77,23 @@ def test_weight_arrays_must_match_the_shape_and_code_width():
     w.q8 = w.q8[:-1]
     with pytest.raises(ValueError, match="q8 / step"):
         qn.qlora_linear_fwd(w, _bf(M, K), _bf(R, K), _bf(N, R), 2.0)
+
+
+def test_codebook_is_marshalled_from_a_list_and_checked_by_the_library():
+    """NF4Weight.levels may be any sequence: the binding copies it into a
+    host fp32 array that the struct points to; the library's own check
+    refuses values outside the contract (no device is touched)."""
+    import ctypes
+    from quantized_base_lora_nf4_amd import _lib
+    w = qn.NF4Weight(codes=torch.empty(0, dtype=torch.uint8), q8=torch.empty(0, dtype=torch.uint8),
+                     step=torch.empty(0), N=8, K=64, code="user2", levels=[-1.0, 0.0, 0.25, 1.0])
+    st = w.struct()
+    got = (ctypes.c_float * 4).from_address(st.levels)
+    assert list(got) == [-1.0, 0.0, 0.25, 1.0]
+    assert qn.user_table("user2", [-1.0, 0.0, 0.25, 1.0]) == [-0.5, 0.125, 0.625]
+    with pytest.raises(_lib.QloraError):
+        qn.user_table("user2", [-1.0, 0.0, 1e-9, 1.0])
+    with pytest.raises(ValueError, match="takes 4 values"):
+        qn.nf4_quantize(torch.zeros(8, 64), code="user2", levels=[0.0, 1.0, -1.0])
+    with pytest.raises(ValueError, match="device tensor"):
+        qn.nf4_quantize(torch.zeros(8, 64), code="user2", levels=[0.0, 1.0, -1.0, 0.5])
