@@ -8,8 +8,9 @@
 // Fp4 Data Types And Lora Adapters", NF4 entry (block-wise absmax scaling).
 //
 // Layout: one workgroup per group of 256 consecutive blocks (blocks of 64,
-// 128 or 256 elements: 64, 128 or 256 KB of W).  Each wave walks a quarter
-// of the group, 256 elements per load instruction (1 KB of contiguous W):
+// 128 or 256 elements: 64, 128 or 256 KB of W), with 4, 8 or 16 waves.
+// Each wave walks 16 KB of the group, 256 elements per load instruction
+// (1 KB of contiguous W):
 // each lane owns four consecutive elements, and the 16, 32 or 64 lanes of a
 // block reduce its absmax by butterfly shuffles.  Codes are packed in
 // 64-element units whatever the block size.  4-bit codes are
@@ -101,8 +102,11 @@ __device__ __forceinline__ uint32_t zero_code() {
   else return CT::table.zero_code;
 }
 
+// 256 << BS threads (4 << BS waves): every wave walks 16 instructions of
+// 256 elements whatever the block size, so larger blocks get more waves per
+// group instead of longer walks.
 template <class CT, int BS>
-__global__ __launch_bounds__(256) void k_nf4_quantize(const float* __restrict__ W,
+__global__ __launch_bounds__(256 << BS) void k_nf4_quantize(const float* __restrict__ W,
                                                       int64_t nblocks,
                                                       uint8_t* __restrict__ codes,
                                                       uint8_t* __restrict__ q8,
@@ -122,10 +126,10 @@ __global__ __launch_bounds__(256) void k_nf4_quantize(const float* __restrict__ 
   const int wave = threadIdx.x >> 6;
   const int sub = lane & 15;  // lane within its 64-element unit: elements 4*sub .. 4*sub+3
 
-  // Each wave walks a quarter of the group, 256 elements (a 64-lane
-  // instruction of 16 bytes each) per iteration.
-  for (int it = 0; it < (16 << BS); ++it) {
-    const int64_t e0 = (((int64_t)wave << (4 + BS)) + it) * 256 + 4 * lane;  // element in group
+  // Wave w walks elements 4096 w .. 4096 w + 4095 of the group, 256
+  // elements (a 64-lane instruction of 16 bytes each) per iteration.
+  for (int it = 0; it < 16; ++it) {
+    const int64_t e0 = ((int64_t)(wave << 4) + it) * 256 + 4 * lane;  // element in group
     const int bi = (int)(e0 >> (6 + BS));                                    // block in group
     if (bi < nb) {
       const int64_t e = (b0 << (6 + BS)) + e0;  // element index in W
@@ -191,12 +195,13 @@ __global__ __launch_bounds__(256) void k_nf4_quantize(const float* __restrict__ 
   }
   __syncthreads();
 
-  // Double quantization of this group's constants.
+  // Double quantization of this group's constants, by the first four
+  // waves (one thread per block); the others hold c = 0.
   const int t = threadIdx.x;
   float c = (t < nb) ? cabs[t] : 0.0f;
   float m = c;
   for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-  if (lane == 0) wmax[wave] = m;
+  if (lane == 0 && wave < 4) wmax[wave] = m;
   __syncthreads();
   const float smax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
   const float st = smax / 255.0f;
@@ -254,14 +259,14 @@ hipError_t launch_nf4_quantize(const float* W, int64_t nblocks, uint8_t* codes, 
   return with_any_code(code, [&](auto ct) {
     using CT = decltype(ct);
     if (bshift == 2)
-      hipLaunchKernelGGL((k_nf4_quantize<CT, 2>), dim3((unsigned)ngroups), dim3(256), 0, stream, W,
-                         nblocks, codes, q8, step, u);
+      hipLaunchKernelGGL((k_nf4_quantize<CT, 2>), dim3((unsigned)ngroups), dim3(1024), 0, stream,
+                         W, nblocks, codes, q8, step, u);
     else if (bshift == 1)
-      hipLaunchKernelGGL((k_nf4_quantize<CT, 1>), dim3((unsigned)ngroups), dim3(256), 0, stream, W,
-                         nblocks, codes, q8, step, u);
+      hipLaunchKernelGGL((k_nf4_quantize<CT, 1>), dim3((unsigned)ngroups), dim3(512), 0, stream,
+                         W, nblocks, codes, q8, step, u);
     else
-      hipLaunchKernelGGL((k_nf4_quantize<CT, 0>), dim3((unsigned)ngroups), dim3(256), 0, stream, W,
-                         nblocks, codes, q8, step, u);
+      hipLaunchKernelGGL((k_nf4_quantize<CT, 0>), dim3((unsigned)ngroups), dim3(256), 0, stream,
+                         W, nblocks, codes, q8, step, u);
     return hipGetLastError();
   });
 }
