@@ -151,14 +151,25 @@ def nf4_quantize(W: torch.Tensor, out: Optional[NF4Weight] = None, stream=None,
         arr = None
     if not W.is_cuda:
         raise ValueError("W must be a device tensor")
+    if not W.is_contiguous():
+        raise ValueError("W must be contiguous")
+    if blocksize not in BLOCKSIZES or K % blocksize:
+        raise ValueError(f"block size must be one of {BLOCKSIZES} and divide K")
     if out is None:
-        out = alloc_nf4(N, K, W.device, code, blocksize)
-    elif (out.codes.numel() != N * K * CODE_BITS[code] // 8 or
-          out.q8.numel() != N * K // blocksize):
-        raise ValueError("out was allocated for another code width or block size")
+        with torch.cuda.stream(_stream_obj(stream)):  # allocated where the kernel writes
+            out = alloc_nf4(N, K, W.device, code, blocksize)
     else:
-        out.code = code
-        out.blocksize = blocksize
+        nb = N * K // blocksize
+        if (out.codes.numel() != N * K * CODE_BITS[code] // 8 or out.q8.numel() != nb or
+                out.step.numel() != -(-nb // DQ_BLOCKSIZE)):
+            raise ValueError("out was allocated for another shape, code width or block size")
+        _check_tensors([("out.codes", out.codes, out.codes.shape, False),
+                        ("out.q8", out.q8, out.q8.shape, False),
+                        ("out.step", out.step, out.step.shape, False)], W.device)
+        if (out.codes.dtype != torch.uint8 or out.q8.dtype != torch.uint8 or
+                out.step.dtype != torch.float32):
+            raise TypeError("out: codes and q8 must be uint8, step float32")
+        out.N, out.K, out.code, out.blocksize = N, K, code, blocksize
     out.levels = arr
     if arr is not None:
         st = lib().qlora_quantize_user(_ptr(W), N, K, cid, ctypes.cast(arr, ctypes.c_void_p),
@@ -176,8 +187,12 @@ def nf4_quantize(W: torch.Tensor, out: Optional[NF4Weight] = None, stream=None,
 
 def nf4_dequantize(w: NF4Weight, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Materialize the bf16 [N, K] weight (for checks and interop)."""
+    dev = _check_weight(w)
+    _check_tensors([("codes", w.codes, w.codes.shape, False), ("q8", w.q8, w.q8.shape, False),
+                    ("step", w.step, w.step.shape, False), ("out", out, (w.N, w.K), True)], dev)
     if out is None:
-        out = torch.empty(w.N, w.K, dtype=torch.bfloat16, device=w.codes.device)
+        with torch.cuda.stream(_stream_obj(stream)):
+            out = torch.empty(w.N, w.K, dtype=torch.bfloat16, device=dev)
     s = w.struct()
     check(lib().nf4_dequantize(ctypes.byref(s), _ptr(_bf16_view(out)), _stream(stream)),
           "nf4_dequantize")

@@ -97,3 +97,13 @@ def test_codebook_is_marshalled_from_a_list_and_checked_by_the_library():
         qn.nf4_quantize(torch.zeros(8, 64), code="user2", levels=[0.0, 1.0, -1.0])
     with pytest.raises(ValueError, match="device tensor"):
         qn.nf4_quantize(torch.zeros(8, 64), code="user2", levels=[0.0, 1.0, -1.0, 0.5])
+
+
+def test_dequantize_checks_the_weight_and_its_device_before_the_c_abi():
+    w = qn.NF4Weight(codes=torch.empty(8 * 64 // 2, dtype=torch.uint8),
+                     q8=torch.empty(8, dtype=torch.uint8), step=torch.empty(1), N=8, K=64)
+    with pytest.raises(ValueError, match="is on cpu"):
+        qn.nf4_dequantize(w)
+    w.q8 = torch.empty(7, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="q8 / step"):
+        qn.nf4_dequantize(w)
