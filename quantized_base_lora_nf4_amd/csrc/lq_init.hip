@@ -239,8 +239,18 @@ __global__ __launch_bounds__(256) void k_lq_reduce(const T* __restrict__ part, i
                                                    int64_t count, T* __restrict__ out) {
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < count;
        i += (int64_t)gridDim.x * blockDim.x) {
+    // slices added in order; eight loads issued before their adds, so that
+    // they are in flight together (the order, and so the sum, is unchanged)
     T v = part[i];
-    for (int64_t s = 1; s < S; ++s) v += part[s * count + i];
+    int64_t s = 1;
+    for (; s + 8 <= S; s += 8) {
+      T x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = part[(s + j) * count + i];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v += x[j];
+    }
+    for (; s < S; ++s) v += part[s * count + i];
     out[i] = v;
   }
 }
