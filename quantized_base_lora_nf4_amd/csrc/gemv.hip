@@ -7,16 +7,17 @@
 // section "Where the memory goes".  A memory-bound stream leaves only a few
 // lane operations per weight, so the codes are expanded to *unscaled* bf16
 // levels (a 256-entry byte table in LDS, one lookup per code byte), the
-// MFMA sums one 64-element block at a time, and the block constant
-// fl32(q8 * step) multiplies that block's fp32 partial sum.  The result
+// MFMA sums one 64-element code block at a time, and the block constant
+// fl32(q8 * step) (of the 64-, 128- or 256-element constant block it lies
+// in) multiplies that block's fp32 partial sum.  The result
 // differs from using the bf16-rounded dequantized weight only by the bf16
 // rounding of the levels (relative 2^-9 per weight); accumulation is fp32.
 //
 // Two launches per call:
 //  1. k_lora_down_part: fp32 partial sums of U = X A^T over S slices of K.
 //  2. k_qgemv: Y = X W^T + s U B^T.  A workgroup owns 16 G weight rows and
-//     all of K; its KW waves each take a contiguous range of K, and their
-//     partial sums are added in LDS.  The epilogue sums the U partials,
+//     all of K; its KW waves split K (wave pairs share a range and take its
+//     even and odd double steps), and their partial sums are added in LDS.  The epilogue sums the U partials,
 //     adds the LoRA term and stores bf16 Y (and bf16 U when asked for).
 //
 // Operand layout (MFMA 16x16x32 bf16, A = X rows, B = weight rows, so that
