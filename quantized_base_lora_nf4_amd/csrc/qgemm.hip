@@ -30,6 +30,7 @@
 // Backward: the weight slice is written to LDS in its natural [n][k] layout
 // and read as the MFMA B operand with ds_read_b64_tr_b16, which hands each
 // lane 4 consecutive rows of one column.
+#include <atomic>
 #include <type_traits>
 
 #include "kernels.hpp"
@@ -750,14 +751,33 @@ __global__ __launch_bounds__(C::NT, 1) void k_qgemm_bwd(BwdArgs p) {
 #define QN_GEMM_CFG 2, 4, 4, 2
 #endif
 using GemmCfg = Cfg<QN_GEMM_CFG>;
+// 128 x 128 tiles, the same 8 waves (each 64 x 32): for grids the 256 x 256
+// tiles would leave mostly idle (few tokens times a narrow weight), where
+// four times as many workgroups still fit in at most two rounds.
+using SmallCfg = Cfg<2, 4, 2, 1>;
 
-}  // namespace
+// Compute units of the current device (the one the launch goes to), asked
+// once per device; 0 if the query fails, which keeps the large tiles.
+int device_cus() {
+  static std::atomic<int> known[64];
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < 64 && (cus = known[dev].load(std::memory_order_relaxed)) > 0) return cus;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  if (dev >= 0 && dev < 64) known[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
 
-hipError_t launch_qgemm_fwd(const Nf4View& w, const uint16_t* X, int64_t M, const uint16_t* U,
-                            int64_t ldu, const uint16_t* B, int32_t r, float s, uint16_t* Y,
-                            hipStream_t stream) {
-  using C = GemmCfg;
-  FwdArgs a{X, w.codes, w.q8, w.step, U, ldu, B, r, s, Y, M, w.N, w.K, w.ut};
+// The small tiles when the 256 x 256 grid of an M x cols output fills at
+// most half the compute units.
+bool small_tiles(int64_t M, int64_t cols) {
+  const int64_t big = ((M + GemmCfg::BM - 1) / GemmCfg::BM) * ((cols + GemmCfg::BN - 1) / GemmCfg::BN);
+  return 2 * big <= device_cus();
+}
+
+template <class C>
+hipError_t launch_fwd(const FwdArgs& a, const Nf4View& w, int64_t M, hipStream_t stream) {
   dim3 grid((unsigned)(((w.N + C::BN - 1) / C::BN) * ((M + C::BM - 1) / C::BM)));
   const bool q4 = (w.K % 256) == 0 && w.bshift == 0;
   with_any_code(w.code, [&](auto ct) {
@@ -775,11 +795,8 @@ hipError_t launch_qgemm_fwd(const Nf4View& w, const uint16_t* X, int64_t M, cons
   return hipGetLastError();
 }
 
-hipError_t launch_qgemm_bwd(const Nf4View& w, const uint16_t* dY, int64_t M, const uint16_t* dU,
-                            int64_t lddu, const uint16_t* A, int32_t r, uint16_t* dX,
-                            hipStream_t stream) {
-  using C = GemmCfg;
-  BwdArgs a{dY, w.codes, w.q8, w.step, dU, lddu, A, r, dX, M, w.N, w.K, w.ut};
+template <class C>
+hipError_t launch_bwd(const BwdArgs& a, const Nf4View& w, int64_t M, hipStream_t stream) {
   dim3 grid((unsigned)(((w.K + C::BN - 1) / C::BN) * ((M + C::BM - 1) / C::BM)));
   with_any_code(w.code, [&](auto ct) {
     using CT = decltype(ct);
@@ -792,6 +809,24 @@ hipError_t launch_qgemm_bwd(const Nf4View& w, const uint16_t* dY, int64_t M, con
     return 0;
   });
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_qgemm_fwd(const Nf4View& w, const uint16_t* X, int64_t M, const uint16_t* U,
+                            int64_t ldu, const uint16_t* B, int32_t r, float s, uint16_t* Y,
+                            hipStream_t stream) {
+  const FwdArgs a{X, w.codes, w.q8, w.step, U, ldu, B, r, s, Y, M, w.N, w.K, w.ut};
+  return small_tiles(M, w.N) ? launch_fwd<SmallCfg>(a, w, M, stream)
+                             : launch_fwd<GemmCfg>(a, w, M, stream);
+}
+
+hipError_t launch_qgemm_bwd(const Nf4View& w, const uint16_t* dY, int64_t M, const uint16_t* dU,
+                            int64_t lddu, const uint16_t* A, int32_t r, uint16_t* dX,
+                            hipStream_t stream) {
+  const BwdArgs a{dY, w.codes, w.q8, w.step, dU, lddu, A, r, dX, M, w.N, w.K, w.ut};
+  return small_tiles(M, w.K) ? launch_bwd<SmallCfg>(a, w, M, stream)
+                             : launch_bwd<GemmCfg>(a, w, M, stream);
 }
 
 }  // namespace qn
