@@ -46,8 +46,16 @@ __device__ __forceinline__ u32x4 levels8_lut(uint32_t w, const uint32_t* lutl) {
 }
 constexpr int kLutWords = 256 * 16;
 
+// At most this many U partial slices (gemv_lora_slices).
+constexpr int kGemvMaxSlices = 32;
+// A per-lane buffer offset past every buffer this file reads through a
+// buffer resource (each under 2^31 bytes): such a load returns 0.
+constexpr int kPastEnd = INT32_MIN;
+
 // ---------------------------------------------------------------------------
-// U partial sums: part[s][m][j] = sum over k in slice s of X[m][k] A[j][k].
+// U partial sums: part[m][j][s] (slices padded to kGemvMaxSlices, so that
+// the slices of one sum are one contiguous 128-byte row) = sum over k in
+// slice s of X[m][k] A[j][k].
 // Grid (S, ceil(r / 64)); wave w of a workgroup owns adapter rows
 // 64 blockIdx.y + 16 w .. +15.  MFMA 16x16x32: A = X rows, B = A rows.
 // ---------------------------------------------------------------------------
@@ -88,11 +96,10 @@ __global__ __launch_bounds__(256) void k_lora_down_part(const uint16_t* __restri
     acc = mfma16(as_bf16x8(mvalid ? xa : zero), as_bf16x8(jvalid ? aa : zero), acc);
   }
   // D[m = 4 q + v][j]
-  float* out = part + (int64_t)blockIdx.x * M * r;
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     const int m = 4 * q + v;
-    if (m < M && jvalid) out[m * r + j] = acc[v];
+    if (m < M && jvalid) part[(m * r + j) * kGemvMaxSlices + blockIdx.x] = acc[v];
   }
 }
 
@@ -102,7 +109,7 @@ struct GemvArgs {
   const float* step;
   const uint16_t* X;
   int64_t M, N, K;
-  const float* upart;  // [us][M][r]
+  const float* upart;  // [M][r][kGemvMaxSlices], the first us slices written
   int32_t us;
   const uint16_t* B;
   int32_t r;
@@ -207,32 +214,58 @@ __global__ __launch_bounds__(64 * KW) void k_qgemv(GemvArgs p) {
 #pragma unroll
   for (int g = 0; g < G; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // One step as 2 G chains (group g, block h of the double step): table
+  // lookups -> two MFMAs -> scaling by the block constant.  The chains are
+  // software-pipelined: the lookups of chain c + 1 are issued before the
+  // MFMAs of chain c and the scaling of chain c - 1, so the LDS latency of
+  // a chain overlaps the work of its neighbours (one chain after another
+  // left the wave waiting on the LDS once per chain).
   auto compute = [&](const Slot& S, int64_t d, bool tail) {
     if (!tail) d = base + 2 * d;
     const int64_t kb = 2 * d;
+    constexpr int NC = 2 * G;
+    u32x4 cw[G];  // per group: words 0, 1 of block kb and 2, 3 of block kb + 1
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       u32x4 c;
 #pragma unroll
       for (int j = 0; j < 4; ++j) c[j] = nibbles<CT>(S.c[g], j);
       // lanes 0-31: (block kb words 0, 1 | words 2, 3) -> keep 0, 1, take the
-      // other half's 0, 1 into 2, 3; lanes 32-63 the mirror image.
+      // other half's 0, 1 into 2, 3; lanes 32-63 the mirror image.  The
+      // swap overwrites both operands: the copies keep it from tying up the
+      // loaded registers (which made the compiler wait for loads still in
+      // flight for later steps).
+#pragma unroll
+      for (int j = 0; j < 2; ++j) c[j] = __builtin_amdgcn_mov_dpp(c[j], 0xE4, 0xf, 0xf, false);
       const auto s02 = __builtin_amdgcn_permlane32_swap(c[0], c[2], false, false);
       const auto s13 = __builtin_amdgcn_permlane32_swap(c[1], c[3], false, false);
-      c[0] = s02[0];
-      c[2] = s02[1];
-      c[1] = s13[0];
-      c[3] = s13[1];
+      cw[g] = u32x4{s02[0], s13[0], s02[1], s13[1]};
+    }
+    u32x4 wl[2][2];  // looked-up levels of two chains
+    float ch[2];     // their block constants
+    f32x4 pq[2];     // MFMA sums of two chains
+    auto lookup = [&](int c) {
+      const int g = c >> 1, h = c & 1;
+      wl[c & 1][0] = levels8_lut(cw[g][2 * h], lut + i16);
+      wl[c & 1][1] = levels8_lut(cw[g][2 * h + 1], lut + i16);
+      ch[c & 1] = (h && tail) ? 0.0f : crow_t[g][kb + h];
+    };
+    auto mma = [&](int c) {
+      const int h = c & 1;
+      const f32x4 pb = mfma16(as_bf16x8(S.x[2 * h]), as_bf16x8(wl[c & 1][0]), f32x4{0.f, 0.f, 0.f, 0.f});
+      pq[c & 1] = mfma16(as_bf16x8(S.x[2 * h + 1]), as_bf16x8(wl[c & 1][1]), pb);
+    };
+    auto scale = [&](int c) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const u32x4 w0 = levels8_lut(c[2 * h], lut + i16);
-        const u32x4 w1 = levels8_lut(c[2 * h + 1], lut + i16);
-        f32x4 pb = mfma16(as_bf16x8(S.x[2 * h]), as_bf16x8(w0), f32x4{0.f, 0.f, 0.f, 0.f});
-        pb = mfma16(as_bf16x8(S.x[2 * h + 1]), as_bf16x8(w1), pb);
-        const float chat = (h && tail) ? 0.0f : crow_t[g][kb + h];
+      for (int v = 0; v < 4; ++v) acc[c >> 1][v] += ch[c & 1] * pq[c & 1][v];
+    };
+    lookup(0);
 #pragma unroll
-        for (int v = 0; v < 4; ++v) acc[g][v] += chat * pb[v];
-      }
+    for (int c = 0; c <= NC; ++c) {
+      if (c >= 1) scale(c - 1);  // reads ch of chain c - 1 before lookup(c + 1) reuses it
+      if (c + 1 < NC) lookup(c + 1);
+      if (c < NC) mma(c);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -241,14 +274,29 @@ __global__ __launch_bounds__(64 * KW) void k_qgemv(GemvArgs p) {
 #pragma unroll
     for (int u = 0; u < PD - 1; ++u) issue(sl[u], d0 + u, false);
   }
-  // Prologue, overlapping the first loads: the byte table, the block
-  // constants fl32(q8 * step) of rows n0 .. n0 + 16 G - 1, and the U sums of
-  // the partial slices written by the previous launch on this stream.  All
-  // of a thread's loads are issued before any is used (one latency).
-  for (int e = tid; e < kLutWords; e += NT) {
-    const int b = e >> 4;  // copy e % 16 of entry b
-    lut[e] = pack_bf16x2(level_of<CT>(p.ut, b & 15), level_of<CT>(p.ut, b >> 4));
-  }
+  // Prologue, overlapping the first loads: the U sums of the partial slices
+  // written by the previous launch on this stream, the block constants
+  // fl32(q8 * step) of rows n0 .. n0 + 16 G - 1, and the byte table.  The
+  // loads go through buffer resources (an offset past the end reads 0), so
+  // none sits behind a branch, and all of them are issued before the first
+  // use: the prologue costs about one memory latency.
+  const int64_t ur = (int64_t)M * p.r;
+  const __amdgpu_buffer_rsrc_t urs = bytes_rsrc(p.upart, 4 * kGemvMaxSlices * ur);
+  // the slices of U sum e: one 128-byte row (zeros for sums past M r).
+  // Kept as raw words until they are added: converting each loaded word to
+  // float where it is loaded made the compiler keep only the first word of
+  // every 16-byte load.
+  auto load_slices = [&](uint32_t (&uv)[kGemvMaxSlices], int64_t e) {
+    const int off = e < ur ? (int)(4 * kGemvMaxSlices * e) : kPastEnd;
+#pragma unroll
+    for (int i = 0; i < kGemvMaxSlices / 4; ++i) {
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(urs, off, 16 * i, 0);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) uv[4 * i + t] = v[t];
+    }
+  };
+  uint32_t uv[kGemvMaxSlices];
+  load_slices(uv, tid);
   if (p.bshift > 0) {
     // blocks of 64 << bshift: each 64-element block takes the constant of
     // the block it lies in (rows past N take the last row's)
@@ -262,61 +310,73 @@ __global__ __launch_bounds__(64 * KW) void k_qgemv(GemvArgs p) {
     }
   } else {
     // The workgroup's constants are the contiguous q8 range starting at
-    // n0 kblocks (a multiple of 16 bytes), 16 G kblocks bytes long; rows
-    // past N read clamped bytes (their results are dropped).
+    // n0 kblocks (a multiple of 16 bytes), 16 G kblocks bytes long, read in
+    // 16-byte chunks, kCq per thread per pass.  Bytes past the weight's
+    // q8 (rows past N, whose results are dropped) read 0.
+    constexpr int kCq = 4;
     const int64_t qtot = N * kblocks, qbase = n0 * kblocks;
     const int64_t nchunk = (16 * G * kblocks + 15) / 16;
-    for (int64_t c = tid; c < nchunk; c += NT) {
-      const int64_t o = qbase + 16 * c;
-      u32x4 qv;
-      if (o + 16 <= qtot) {
-        qv = *reinterpret_cast<const u32x4*>(p.q8 + o);
-      } else {
-        uint32_t b[16];
+    const int64_t ng = (qtot + 255) >> 8;
+    const __amdgpu_buffer_rsrc_t qrs = bytes_rsrc(p.q8, qtot);
+    for (int64_t cp = 0; cp < nchunk; cp += kCq * NT) {
+      u32x4 qv[kCq];
+      float st0[kCq], st1[kCq];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) b[i] = p.q8[o + i < qtot ? o + i : qtot - 1];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          qv[i] = b[4 * i] | (b[4 * i + 1] << 8) | (b[4 * i + 2] << 16) | (b[4 * i + 3] << 24);
+      for (int j = 0; j < kCq; ++j) {
+        const int64_t c = cp + tid + (int64_t)j * NT;
+        const int64_t o = qbase + 16 * (c < nchunk ? c : nchunk - 1);
+        qv[j] = __builtin_amdgcn_raw_buffer_load_b128(qrs, c < nchunk ? (int)o : kPastEnd, 0, 0);
+        const int64_t g0 = o >> 8 < ng ? o >> 8 : ng - 1;
+        const int64_t g1 = (o + 15) >> 8 < ng ? (o + 15) >> 8 : ng - 1;
+        st0[j] = p.step[g0];
+        st1[j] = p.step[g1];
       }
-      const int64_t ng = (qtot + 255) >> 8;
-      const int64_t g0 = o >> 8 < ng ? o >> 8 : ng - 1;
-      const int64_t g1 = (o + 15) >> 8 < ng ? (o + 15) >> 8 : ng - 1;
-      const float st0 = p.step[g0], st1 = p.step[g1];
-      const int64_t split = (g0 + 1) << 8;  // first block of group g0 + 1
-      float cv[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        cv[i] = (float)((qv[i >> 2] >> (8 * (i & 3))) & 0xffu) * (o + i < split ? st0 : st1);
-      // element 16 c + i is block kb of table row `row`
-      int64_t row = (16 * c) / kblocks, kb = 16 * c - row * kblocks;
+      for (int j = 0; j < kCq; ++j) {
+        const int64_t c = cp + tid + (int64_t)j * NT;
+        if (c < nchunk) {
+          const int64_t o = qbase + 16 * c;
+          const int64_t split = ((o >> 8) + 1) << 8;  // first block of the next group
+          // element 16 c + i is block kb of table row `row`
+          int64_t row = (16 * c) / kblocks, kb = 16 * c - row * kblocks;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        if (row < 16 * G) chat_t[row * kbs + kb] = cv[i];
-        if (++kb == kblocks) {
-          kb = 0;
-          ++row;
+          for (int i = 0; i < 16; ++i) {
+            const float cv = (float)((qv[j][i >> 2] >> (8 * (i & 3))) & 0xffu) *
+                             (o + i < split ? st0[j] : st1[j]);
+            if (row < 16 * G) chat_t[row * kbs + kb] = cv;
+            if (++kb == kblocks) {
+              kb = 0;
+              ++row;
+            }
+          }
         }
       }
     }
   }
   {
-    const int64_t ur = (int64_t)M * p.r;
-    // slices in order, eight loads in flight at a time
-    constexpr int kBatch = 8;
-    for (int64_t e = tid; e < ur; e += NT) {
-      float u = 0.0f;
-      for (int sp0 = 0; sp0 < p.us; sp0 += kBatch) {
-        float v[kBatch];
+    // byte table: thread t writes words t + NT i, i.e. copy t % 16 of
+    // entries b = t / 16 + 32 i, whose low code t / 16 % 16 is the same for
+    // every i and whose high code t / 256 + 2 i is uniform over the wave
+    static_assert(NT == 512 && kLutWords == 8 * NT, "table split assumes 8 waves");
+    const float lo = level_of<CT>(p.ut, (tid >> 4) & 15);
+    const int hi0 = __builtin_amdgcn_readfirstlane(tid >> 8);
 #pragma unroll
-        for (int i = 0; i < kBatch; ++i)
-          v[i] = p.upart[(int64_t)(sp0 + i < p.us ? sp0 + i : sp0) * ur + e];
+    for (int i = 0; i < 8; ++i) lut[tid + NT * i] = pack_bf16x2(lo, level_of<CT>(p.ut, hi0 + 2 * i));
+  }
+  if (tid < ur) {
+    float u = 0.0f;  // slices in order
 #pragma unroll
-        for (int i = 0; i < kBatch; ++i)
-          if (sp0 + i < p.us) u += v[i];
-      }
-      ush[e] = u;
-    }
+    for (int i = 0; i < kGemvMaxSlices; ++i)
+      if (i < p.us) u += __builtin_bit_cast(float, uv[i]);
+    ush[tid] = u;
+  }
+  for (int64_t e = tid + NT; e < ur; e += NT) {  // M r > NT: the other sums
+    load_slices(uv, e);
+    float u = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kGemvMaxSlices; ++i)
+      if (i < p.us) u += __builtin_bit_cast(float, uv[i]);
+    ush[e] = u;
   }
   __syncthreads();
 
@@ -350,19 +410,84 @@ __global__ __launch_bounds__(64 * KW) void k_qgemv(GemvArgs p) {
     for (int v = 0; v < 4; ++v) red[((wave * G + g) * 4 + v) * 64 + lane] = acc[g][v];
   __syncthreads();
 
-  for (int o = tid; o < G * 4 * 64; o += NT) {
+  // Outputs o = tid + NT k: the waves' partial sums added in order, then
+  // the LoRA term.  The adapter rows are read JB columns at a time for all
+  // of the thread's outputs at once (one latency per JB columns instead of
+  // one per output and column batch); columns past r and outputs that are
+  // not stored read 0.
+  constexpr int KO = (G * 4 * 64 + NT - 1) / NT;
+  constexpr int JB = 32;
+  const __amdgpu_buffer_rsrc_t brs = bytes_rsrc(p.B, 2 * N * (int64_t)p.r);
+  float yk[KO], lk[KO];
+  int64_t mk[KO], nk[KO];
+  bool vk[KO];
+#pragma unroll
+  for (int k = 0; k < KO; ++k) {
+    const int o = tid + NT * k;
     const int l = o & 63, v = (o >> 6) & 3, g = o >> 8;
     float y = 0.0f;
+    if (o < G * 4 * 64) {
 #pragma unroll
-    for (int w = 0; w < KW; ++w) y += red[((w * G + g) * 4 + v) * 64 + l];
-    const int64_t m = 4 * (l >> 4) + v, n = n0 + 16 * g + (l & 15);
-    if (m < M && n < N) {
-      float lora = 0.0f;
-      const uint16_t* brw = p.B + n * p.r;
-      for (int j = 0; j < p.r; ++j) lora += ush[m * p.r + j] * bf16_to_f32(brw[j]);
-      p.Y[m * N + n] = f32_to_bf16(y + p.s * lora);
+      for (int w = 0; w < KW; ++w) y += red[((w * G + g) * 4 + v) * 64 + l];
+    }
+    mk[k] = 4 * (l >> 4) + v;
+    nk[k] = n0 + 16 * g + (l & 15);
+    vk[k] = o < G * 4 * 64 && mk[k] < M && nk[k] < N;
+    yk[k] = y;
+    lk[k] = 0.0f;
+  }
+  if ((p.r & 7) == 0) {
+    // r a multiple of 8: 16-byte adapter loads (8 columns) and 16-byte U
+    // reads; JB columns per batch.  Outputs that are not stored read U row
+    // 0 and adapter zeros (their sums are dropped).
+    for (int j0 = 0; j0 < p.r; j0 += JB) {
+      u32x4 bq[KO][JB / 8];
+#pragma unroll
+      for (int k = 0; k < KO; ++k)
+#pragma unroll
+        for (int q = 0; q < JB / 8; ++q)
+          bq[k][q] = __builtin_amdgcn_raw_buffer_load_b128(
+              brs, (vk[k] && j0 + 8 * q < p.r) ? (int)(2 * (nk[k] * p.r + j0 + 8 * q)) : kPastEnd, 0,
+              0);
+      __builtin_amdgcn_sched_barrier(0);  // every load of the batch before the first use
+#pragma unroll
+      for (int q = 0; q < JB / 8; ++q) {
+        if (j0 + 8 * q >= p.r) break;  // uniform
+#pragma unroll
+        for (int k = 0; k < KO; ++k) {
+          const float* ur8 = ush + (vk[k] ? mk[k] * p.r : 0) + j0 + 8 * q;
+          const f32x4 u0 = *reinterpret_cast<const f32x4*>(ur8);
+          const f32x4 u1 = *reinterpret_cast<const f32x4*>(ur8 + 4);
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            const uint32_t wd = bq[k][q][t >> 1];
+            const float b = bf16_to_f32((uint16_t)((t & 1) ? wd >> 16 : wd & 0xffffu));
+            lk[k] += (t < 4 ? u0[t] : u1[t - 4]) * b;
+          }
+        }
+      }
+    }
+  } else {
+    for (int j0 = 0; j0 < p.r; j0 += JB) {
+      uint16_t bv[KO][JB];
+#pragma unroll
+      for (int k = 0; k < KO; ++k)
+#pragma unroll
+        for (int t = 0; t < JB; ++t)
+          bv[k][t] = __builtin_amdgcn_raw_buffer_load_b16(
+              brs, (vk[k] && j0 + t < p.r) ? (int)(2 * (nk[k] * p.r + j0 + t)) : kPastEnd, 0, 0);
+#pragma unroll
+      for (int k = 0; k < KO; ++k)
+        if (vk[k]) {
+#pragma unroll
+          for (int t = 0; t < JB; ++t)
+            if (j0 + t < p.r) lk[k] += ush[mk[k] * p.r + j0 + t] * bf16_to_f32(bv[k][t]);
+        }
     }
   }
+#pragma unroll
+  for (int k = 0; k < KO; ++k)
+    if (vk[k]) p.Y[mk[k] * N + nk[k]] = f32_to_bf16(yk[k] + p.s * lk[k]);
   if (p.U_out && blockIdx.x == 0) {
     for (int64_t e = tid; e < (int64_t)M * p.r; e += NT) p.U_out[e] = f32_to_bf16(ush[e]);
   }
@@ -376,6 +501,7 @@ bool gemv_fits(int64_t M, int32_t r, int64_t K) {
 }
 
 int gemv_lora_slices(int64_t M, int32_t r, int64_t K) {
+  static_assert(kGemvMaxSlices == 32, "at most 32 slices below");
   // Slices of at least 256 columns (one batch of loads per wave), at most
   // 32, and at most 8192 partial values in all: k_qgemv's prologue sums
   // them, M r values per slice.
@@ -387,7 +513,8 @@ int gemv_lora_slices(int64_t M, int32_t r, int64_t K) {
 }
 
 size_t gemv_workspace_bytes(int64_t M, int32_t r, int64_t K) {
-  return (size_t)gemv_lora_slices(M, r, K) * M * r * sizeof(float);
+  (void)K;
+  return (size_t)kGemvMaxSlices * M * r * sizeof(float);
 }
 
 template <int G>
