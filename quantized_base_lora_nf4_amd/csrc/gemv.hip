@@ -519,7 +519,9 @@ size_t gemv_workspace_bytes(int64_t M, int32_t r, int64_t K) {
 
 template <int G>
 hipError_t launch_qgemv_g(const GemvArgs& a, int code, hipStream_t stream) {
-  constexpr int KW = 8, PD = QN_GEMV_PD;
+  // seven row groups keep one step (7 KB per wave) in flight: at 28672 x 8192
+  // two were about 3 % slower (and take 45 more registers)
+  constexpr int KW = 8, PD = G == 7 ? 2 : QN_GEMV_PD;
   const size_t lds = 4 * (size_t)gemv_lds_words(G, KW, a.M, a.r, a.K / 64);
   const dim3 grid((unsigned)((a.N + 16 * G - 1) / (16 * G)));
   return with_any_code(code, [&](auto ct) {
