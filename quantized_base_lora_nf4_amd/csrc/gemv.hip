@@ -17,8 +17,11 @@
 //  1. k_lora_down_part: fp32 partial sums of U = X A^T over S slices of K.
 //  2. k_qgemv: Y = X W^T + s U B^T.  A workgroup owns 16 G weight rows and
 //     all of K; its KW waves split K (wave pairs share a range and take its
-//     even and odd double steps), and their partial sums are added in LDS.  The epilogue sums the U partials,
-//     adds the LoRA term and stores bf16 Y (and bf16 U when asked for).
+//     even and odd double steps), and their partial sums are added in LDS.
+//     With G = 7 each wave walks its steps in chunks, one row group after
+//     another within a chunk; otherwise step by step over all groups.  The
+//     epilogue sums the U partials, adds the LoRA term and stores bf16 Y
+//     (and bf16 U when asked for).
 //
 // Operand layout (MFMA 16x16x32 bf16, A = X rows, B = weight rows, so that
 // the four results of a lane share one weight row and one block constant):
@@ -146,6 +149,8 @@ __global__ __launch_bounds__(64 * KW) void k_qgemv(GemvArgs p) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i16 = lane & 15, q = lane >> 4;
+  // seven row groups: row-group-major main loop (below)
+  constexpr bool kRowMajor = G == 7;
   const int64_t M = p.M, N = p.N, K = p.K;
   const int64_t kblocks = K >> 6;
   const int64_t kbs = kblocks | 1;  // row stride of the constant table
@@ -278,7 +283,7 @@ __global__ __launch_bounds__(64 * KW) void k_qgemv(GemvArgs p) {
   // (17.5 against 20.0 us at 8192 x 8192).
   constexpr bool kLateFirst = G >= 2;
   auto issue_first = [&]() {
-    if (active) {
+    if (active && !kRowMajor) {
 #pragma unroll
       for (int u = 0; u < PD - 1; ++u) issue(sl[u], d0 + u, false);
     }
@@ -392,24 +397,128 @@ __global__ __launch_bounds__(64 * KW) void k_qgemv(GemvArgs p) {
   }
   __syncthreads();
 
-  // A ring of PD register slots keeps PD - 1 steps of loads in flight while
-  // a step is consumed.  Loads are counted in issue order, so codes and X
-  // fragments travel in the same slot, and the scheduling barriers keep each
-  // step's loads ahead of the arithmetic of the step before it: the wait
-  // before a step then covers that step's own loads only.
-  int64_t d = d0;
-  for (; d + PD <= d1; d += PD) {  // slots 0 .. PD-2 hold steps d .. d+PD-2 on entry
+  if constexpr (kRowMajor) {
+    // Row-group-major order: the wave takes its double steps in chunks of
+    // DW, and within a chunk one row group after another (all DW double
+    // steps of that group's 16 rows), so that the workgroup reads 2 KB of
+    // each row of one group at a time instead of 512 bytes of all 16 G rows
+    // per step (a read-only stream in this order took 22-26 us at
+    // 28672 x 8192 against 27 in the step-major one).  The X fragments of a
+    // chunk are loaded once and serve every group; the codes of the next
+    // group are in flight while one is consumed (a third slot did not fit
+    // in 256 registers with four double steps per chunk).
+    constexpr int DW = 4;
+    typedef HalfRaw<CT::kBits> Codes[DW];
+    u32x4 xf[DW][4];
+    Codes cs[2];
+    auto step_kb = [&](int64_t c, int j) {  // first block of local step DW c + j (clamped)
+      int64_t dd = DW * c + j;
+      if (dd >= d1) dd = d1 - 1;
+      return 2 * (base + 2 * dd);
+    };
+    // Buffer loads: a per-lane 32-bit offset (the lane's row) plus the
+    // step's offset, which is uniform, so no 64-bit address per load is
+    // kept in vector registers (the codes are under 2 GiB by the C ABI, X
+    // is at most 16 K bf16 rows of K).
+    const __amdgpu_buffer_rsrc_t crs = bytes_rsrc(p.codes, N * kblocks * block_bytes<CT>());
+    const __amdgpu_buffer_rsrc_t xrs = bytes_rsrc(p.X, 2 * M * K);
+    int cvo[G];
 #pragma unroll
-    for (int u = 0; u < PD; ++u) {
-      issue(sl[(u + PD - 1) % PD], d + u + PD - 1, false);
+    for (int g = 0; g < G; ++g) cvo[g] = (int)(crow[g] - p.codes);
+    const int xvo = (int)(2 * (xrow - p.X));
+    auto issue_x = [&](int64_t c) {
+#pragma unroll
+      for (int j = 0; j < DW; ++j) {
+        const int kb = (int)step_kb(c, j);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          xf[j][i] = __builtin_amdgcn_raw_buffer_load_b128(
+              xrs, xvo, 2 * (64 * (kb + (i >> 1)) + 8 * (i & 1)), 0);
+      }
+    };
+    auto issue_c = [&](Codes& cd, int64_t c, int g) {
+#pragma unroll
+      for (int j = 0; j < DW; ++j)
+        cd[j] = load_half<CT>(crs, cvo[g], (int)(step_kb(c, j) * block_bytes<CT>()));
+    };
+    // The 2 DW chains (double step j, block h) of group g, software-pipelined
+    // as in the step-major order.
+    auto compute_g = [&](const Codes& cd, int64_t c, int g) {
+      constexpr int NC = 2 * DW;
+      const int nvalid = (int)(d1 - DW * c < DW ? d1 - DW * c : DW);  // uniform
+      u32x4 cw[DW];
+#pragma unroll
+      for (int j = 0; j < DW; ++j) {
+        u32x4 t;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) t[i] = nibbles<CT>(cd[j], i);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) t[i] = __builtin_amdgcn_mov_dpp(t[i], 0xE4, 0xf, 0xf, false);
+        const auto s02 = __builtin_amdgcn_permlane32_swap(t[0], t[2], false, false);
+        const auto s13 = __builtin_amdgcn_permlane32_swap(t[1], t[3], false, false);
+        cw[j] = u32x4{s02[0], s13[0], s02[1], s13[1]};
+      }
+      u32x4 wl[2][2];
+      float ch[2];
+      f32x4 pq[2];
+      auto lookup = [&](int t) {
+        const int j = t >> 1, h = t & 1;
+        wl[t & 1][0] = levels8_lut(cw[j][2 * h], lut + i16);
+        wl[t & 1][1] = levels8_lut(cw[j][2 * h + 1], lut + i16);
+        ch[t & 1] = j < nvalid ? crow_t[g][step_kb(c, j) + h] : 0.0f;
+      };
+      auto mma = [&](int t) {
+        const int j = t >> 1, h = t & 1;
+        const f32x4 pb = mfma16(as_bf16x8(xf[j][2 * h]), as_bf16x8(wl[t & 1][0]),
+                                f32x4{0.f, 0.f, 0.f, 0.f});
+        pq[t & 1] = mfma16(as_bf16x8(xf[j][2 * h + 1]), as_bf16x8(wl[t & 1][1]), pb);
+      };
+      auto scale = [&](int t) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[g][v] += ch[t & 1] * pq[t & 1][v];
+      };
+      lookup(0);
+#pragma unroll
+      for (int t = 0; t <= NC; ++t) {
+        if (t >= 1) scale(t - 1);
+        if (t + 1 < NC) lookup(t + 1);
+        if (t < NC) mma(t);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    const int64_t nch = (d1 + DW - 1) / DW;  // 0 for a wave without full steps
+    for (int64_t c = 0; c < nch; ++c) {
+      issue_x(c);
+      issue_c(cs[0], c, 0);
       __builtin_amdgcn_sched_barrier(0);
-      compute(sl[u], d + u, false);
-      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        if (g + 1 < G) issue_c(cs[(g + 1) % 2], c, g + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_g(cs[g % 2], c, g);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
-  }
+  } else {
+    // A ring of PD register slots keeps PD - 1 steps of loads in flight while
+    // a step is consumed.  Loads are counted in issue order, so codes and X
+    // fragments travel in the same slot, and the scheduling barriers keep each
+    // step's loads ahead of the arithmetic of the step before it: the wait
+    // before a step then covers that step's own loads only.
+    int64_t d = d0;
+    for (; d + PD <= d1; d += PD) {  // slots 0 .. PD-2 hold steps d .. d+PD-2 on entry
 #pragma unroll
-  for (int u = 0; u < PD - 1; ++u)
-    if (d + u < d1) compute(sl[u], d + u, false);
+      for (int u = 0; u < PD; ++u) {
+        issue(sl[(u + PD - 1) % PD], d + u + PD - 1, false);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(sl[u], d + u, false);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < PD - 1; ++u)
+      if (d + u < d1) compute(sl[u], d + u, false);
+  }
   if (odd_tail) {
     issue(sl[PD - 1], T, true);
     compute(sl[PD - 1], T, true);
@@ -531,8 +640,8 @@ size_t gemv_workspace_bytes(int64_t M, int32_t r, int64_t K) {
 
 template <int G>
 hipError_t launch_qgemv_g(const GemvArgs& a, int code, hipStream_t stream) {
-  // seven row groups keep one step (7 KB per wave) in flight: at 28672 x 8192
-  // two were about 3 % slower (and take 45 more registers)
+  // seven row groups run the row-group-major loop; their ring of steps only
+  // serves an odd tail block, one slot in flight
   constexpr int KW = 8, PD = G == 7 ? 2 : QN_GEMV_PD;
   const size_t lds = 4 * (size_t)gemv_lds_words(G, KW, a.M, a.r, a.K / 64);
   const dim3 grid((unsigned)((a.N + 16 * G - 1) / (16 * G)));
