@@ -753,7 +753,7 @@ __global__ __launch_bounds__(C::NT, 1) void k_qgemm_bwd(BwdArgs p) {
 using GemmCfg = Cfg<QN_GEMM_CFG>;
 // 128 x 128 tiles, the same 8 waves (each 64 x 32): for grids the 256 x 256
 // tiles would leave mostly idle (few tokens times a narrow weight), where
-// four times as many workgroups still fit in at most two rounds.
+// four times as many workgroups still run in at most two passes over the CUs.
 using SmallCfg = Cfg<2, 4, 2, 1>;
 
 // Compute units of the current device (the one the launch goes to), asked
