@@ -127,6 +127,7 @@ LSHAPES = [  # (M, N, K, r)
     (3, 28672, 64, 4),         # one block per row: the odd tail step alone
     (16, 28672, 192, 16),      # three blocks: one double step and the tail
     (7, 28672, 576, 8),
+    (5, 28672, 2560, 16),      # 20 double steps: partial chunks of the row-group-major loop
     (2, 1000, 1088, 8),        # two tokens: one row group per workgroup, ragged rows, odd block count
     (3, 64, 41024, 4),         # few tokens, K past the few-token kernel's LDS tables: tile path
     (70000, 136, 192, 8),      # 274 row tiles (ragged, not a multiple of 8): the XCD tile order's
