@@ -282,10 +282,50 @@ __global__ __launch_bounds__(64 * KW) void k_qgemv(GemvArgs p) {
   // one group (two workgroups per CU) issuing them first was faster
   // (17.5 against 20.0 us at 8192 x 8192).
   constexpr bool kLateFirst = G >= 2;
-  auto issue_first = [&]() {
-    if (active && !kRowMajor) {
+  // Row-group-major state (G = 7; unused otherwise): chunks of DW double
+  // steps, one row group after another within a chunk (see the main loop).
+  constexpr int DW = 4;
+  typedef HalfRaw<CT::kBits> Codes[DW];
+  u32x4 xf[DW][4];
+  Codes cs[2];
+  auto step_kb = [&](int64_t c, int j) {  // first block of local step DW c + j (clamped)
+    int64_t dd = DW * c + j;
+    if (dd >= d1) dd = d1 - 1;
+    return 2 * (base + 2 * dd);
+  };
+  // Buffer loads: a per-lane 32-bit offset (the lane's row) plus the
+  // step's offset, which is uniform, so no 64-bit address per load is
+  // kept in vector registers (the codes are under 2 GiB by the C ABI, X
+  // is at most 16 K bf16 rows of K).
+  const __amdgpu_buffer_rsrc_t crs = bytes_rsrc(p.codes, N * kblocks * block_bytes<CT>());
+  const __amdgpu_buffer_rsrc_t xrs = bytes_rsrc(p.X, 2 * M * K);
+  int cvo[G];
 #pragma unroll
-      for (int u = 0; u < PD - 1; ++u) issue(sl[u], d0 + u, false);
+  for (int g = 0; g < G; ++g) cvo[g] = (int)(crow[g] - p.codes);
+  const int xvo = (int)(2 * (xrow - p.X));
+  auto issue_x = [&](int64_t c) {
+#pragma unroll
+    for (int j = 0; j < DW; ++j) {
+      const int kb = (int)step_kb(c, j);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        xf[j][i] = __builtin_amdgcn_raw_buffer_load_b128(
+            xrs, xvo, 2 * (64 * (kb + (i >> 1)) + 8 * (i & 1)), 0);
+    }
+  };
+  auto issue_c = [&](Codes& cd, int64_t c, int g) {
+#pragma unroll
+    for (int j = 0; j < DW; ++j)
+      cd[j] = load_half<CT>(crs, cvo[g], (int)(step_kb(c, j) * block_bytes<CT>()));
+  };
+  auto issue_first = [&]() {
+    if (active) {
+      if constexpr (kRowMajor) {
+        issue_c(cs[0], 0, 0);  // the first group's codes of the first chunk
+      } else {
+#pragma unroll
+        for (int u = 0; u < PD - 1; ++u) issue(sl[u], d0 + u, false);
+      }
     }
   };
   if constexpr (!kLateFirst) issue_first();
@@ -407,40 +447,6 @@ __global__ __launch_bounds__(64 * KW) void k_qgemv(GemvArgs p) {
     // chunk are loaded once and serve every group; the codes of the next
     // group are in flight while one is consumed (a third slot did not fit
     // in 256 registers with four double steps per chunk).
-    constexpr int DW = 4;
-    typedef HalfRaw<CT::kBits> Codes[DW];
-    u32x4 xf[DW][4];
-    Codes cs[2];
-    auto step_kb = [&](int64_t c, int j) {  // first block of local step DW c + j (clamped)
-      int64_t dd = DW * c + j;
-      if (dd >= d1) dd = d1 - 1;
-      return 2 * (base + 2 * dd);
-    };
-    // Buffer loads: a per-lane 32-bit offset (the lane's row) plus the
-    // step's offset, which is uniform, so no 64-bit address per load is
-    // kept in vector registers (the codes are under 2 GiB by the C ABI, X
-    // is at most 16 K bf16 rows of K).
-    const __amdgpu_buffer_rsrc_t crs = bytes_rsrc(p.codes, N * kblocks * block_bytes<CT>());
-    const __amdgpu_buffer_rsrc_t xrs = bytes_rsrc(p.X, 2 * M * K);
-    int cvo[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) cvo[g] = (int)(crow[g] - p.codes);
-    const int xvo = (int)(2 * (xrow - p.X));
-    auto issue_x = [&](int64_t c) {
-#pragma unroll
-      for (int j = 0; j < DW; ++j) {
-        const int kb = (int)step_kb(c, j);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          xf[j][i] = __builtin_amdgcn_raw_buffer_load_b128(
-              xrs, xvo, 2 * (64 * (kb + (i >> 1)) + 8 * (i & 1)), 0);
-      }
-    };
-    auto issue_c = [&](Codes& cd, int64_t c, int g) {
-#pragma unroll
-      for (int j = 0; j < DW; ++j)
-        cd[j] = load_half<CT>(crs, cvo[g], (int)(step_kb(c, j) * block_bytes<CT>()));
-    };
     // The 2 DW chains (double step j, block h) of group g, software-pipelined
     // as in the step-major order.
     auto compute_g = [&](const Codes& cd, int64_t c, int g) {
@@ -489,7 +495,7 @@ __global__ __launch_bounds__(64 * KW) void k_qgemv(GemvArgs p) {
     const int64_t nch = (d1 + DW - 1) / DW;  // 0 for a wave without full steps
     for (int64_t c = 0; c < nch; ++c) {
       issue_x(c);
-      issue_c(cs[0], c, 0);
+      if (c > 0) issue_c(cs[0], c, 0);  // chunk 0's went out in the prologue
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int g = 0; g < G; ++g) {
