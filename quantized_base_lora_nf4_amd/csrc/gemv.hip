@@ -58,7 +58,7 @@ constexpr int kPastEnd = INT32_MIN;
 // ---------------------------------------------------------------------------
 // U partial sums: part[m][j][s] (slices padded to kGemvMaxSlices, so that
 // the slices of one sum are one contiguous 128-byte row) = sum over k in
-// slice s of X[m][k] A[j][k].
+// slice s of X[m][k] A[j][k] for s < S, and 0 for the padding slices.
 // Grid (S, ceil(r / 64)); wave w of a workgroup owns adapter rows
 // 64 blockIdx.y + 16 w .. +15.  MFMA 16x16x32: A = X rows, B = A rows.
 // ---------------------------------------------------------------------------
@@ -104,6 +104,17 @@ __global__ __launch_bounds__(256) void k_lora_down_part(const uint16_t* __restri
     const int m = 4 * q + v;
     if (m < M && jvalid) part[(m * r + j) * kGemvMaxSlices + blockIdx.x] = acc[v];
   }
+  // the slices past the grid read as zeros, so that a sum may take all of
+  // them in order
+  if (blockIdx.x == 0) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int m = 4 * q + v;
+      if (m < M && jvalid)
+        for (int s = gridDim.x; s < kGemvMaxSlices; ++s)
+          part[(m * r + j) * kGemvMaxSlices + s] = 0.0f;
+    }
+  }
 }
 
 struct GemvArgs {
@@ -112,8 +123,7 @@ struct GemvArgs {
   const float* step;
   const uint16_t* X;
   int64_t M, N, K;
-  const float* upart;  // [M][r][kGemvMaxSlices], the first us slices written
-  int32_t us;
+  const float* upart;  // [M][r][kGemvMaxSlices]: the slices, then zeros
   const uint16_t* B;
   int32_t r;
   float s;
@@ -131,21 +141,34 @@ struct GemvArgs {
 // (M r), then a region holding the block constants of the workgroup's rows
 // during the main loop (16 G rows of odd stride kblocks | 1, so that the 16
 // rows a wave reads at once sit in 16 different banks) and the waves'
-// partial sums after it (KW G 256).
+// partial sums after it (KW G 256); with seven groups, the workgroup's
+// adapter rows last, 16-byte aligned.
+__host__ __device__ constexpr int64_t gemv_b_words(int G, int64_t r) {
+  // 16 G x r bf16 in whole KB (one direct-to-LDS copy instruction each)
+  return G == 7 ? (16 * G * r * 2 + 1023) / 1024 * 256 : 0;
+}
 __host__ __device__ constexpr int64_t gemv_lds_words(int G, int KW, int64_t M, int64_t r,
                                                      int64_t kblocks) {
   const int64_t chat = 16 * G * (kblocks | 1), red = (int64_t)KW * G * 256;
-  return kLutWords + M * r + (chat > red ? chat : red);
+  const int64_t base = kLutWords + M * r + (chat > red ? chat : red);
+  return G == 7 ? ((base + 3) & ~(int64_t)3) + gemv_b_words(G, r) : base;
 }
 
+// One row group runs two workgroups per CU (16 waves): the register budget
+// is held to 128 so that both fit.
 template <int G, int KW, int PD, class CT>
-__global__ __launch_bounds__(64 * KW) void k_qgemv(GemvArgs p) {
+__global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(G == 1 ? 4 : 1)))
+void k_qgemv(GemvArgs p) {
   constexpr int NT = 64 * KW;
   extern __shared__ float lds[];
   uint32_t* lut = reinterpret_cast<uint32_t*>(lds);
   float* ush = lds + kLutWords;
   float* chat_t = ush + p.M * p.r;  // [16 G][kblocks | 1] during the main loop
   float* red = chat_t;              // [KW][G][4][64] after it
+  // G = 7: the workgroup's adapter rows, copied in by the prologue (bf16 [16 G][r])
+  const int64_t chat_words = 16 * G * ((p.K >> 6) | 1), red_words = (int64_t)KW * G * 256;
+  const int64_t cr_words = chat_words > red_words ? chat_words : red_words;
+  uint16_t* bsh = reinterpret_cast<uint16_t*>(lds + ((kLutWords + p.M * p.r + cr_words + 3) & ~3));
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i16 = lane & 15, q = lane >> 4;
@@ -335,6 +358,17 @@ __global__ __launch_bounds__(64 * KW) void k_qgemv(GemvArgs p) {
   // loads go through buffer resources (an offset past the end reads 0), so
   // none sits behind a branch, and all of them are issued before the first
   // use: the prologue costs about one memory latency.
+  const bool b_lds = kRowMajor && (p.r & 7) == 0;  // uniform
+  if (b_lds) {
+    // direct-to-LDS copy of rows n0 .. n0 + 16 G - 1 of B (1 KB per wave
+    // instruction; bytes past B read 0), waited for before the epilogue
+    const __amdgpu_buffer_rsrc_t brs0 = bytes_rsrc(p.B + n0 * p.r, 2 * (N - n0) * (int64_t)p.r);
+    const int nkb = (int)gemv_b_words(G, p.r) / 256;
+    for (int i = wave; i < nkb; i += KW)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          brs0, (__attribute__((address_space(3))) void*)(bsh + 512 * i), 16, 1024 * i + 16 * lane,
+          0, 0, 0);
+  }
   const int64_t ur = (int64_t)M * p.r;
   const __amdgpu_buffer_rsrc_t urs = bytes_rsrc(p.upart, 4 * kGemvMaxSlices * ur);
   // the slices of U sum e: one 128-byte row (zeros for sums past M r).
@@ -366,44 +400,62 @@ __global__ __launch_bounds__(64 * KW) void k_qgemv(GemvArgs p) {
     }
   } else {
     // The workgroup's constants are the contiguous q8 range starting at
-    // n0 kblocks (a multiple of 16 bytes), 16 G kblocks bytes long, read in
-    // 16-byte chunks, kCq per thread per pass.  Bytes past the weight's
-    // q8 (rows past N, whose results are dropped) read 0.
+    // n0 kblocks, 16 G kblocks bytes long (both multiples of 16), read in
+    // 16-byte chunks, kCq per thread per pass.  A chunk starts at a
+    // multiple of 16, so its 16 constants share one step (groups of 256).
+    // Bytes past the weight's q8 (rows past N, whose results are dropped)
+    // read 0.
+    // Index math in 32 bits: the workgroup's table has 16 G kblocks < 2^24
+    // entries, so an entry index converts to float exactly, and its row
+    // (at most 16 G) comes from one multiplication by 1 / kblocks, which
+    // is off by well under one; truncating it gives the row or a neighbour,
+    // which two comparisons correct.
     constexpr int kCq = 4;
-    const int64_t qtot = N * kblocks, qbase = n0 * kblocks;
-    const int64_t nchunk = (16 * G * kblocks + 15) / 16;
-    const int64_t ng = (qtot + 255) >> 8;
+    const int kbl = (int)kblocks;
+    const int64_t qtot = N * kblocks;
+    const int qbase = (int)(n0 * kblocks);  // < 2^31: q8 is under 2 GiB
+    const int nchunk = G * kbl;             // 16 G kblocks / 16
+    const int glast = (int)((qtot + 255) >> 8) - 1;
     const __amdgpu_buffer_rsrc_t qrs = bytes_rsrc(p.q8, qtot);
-    for (int64_t cp = 0; cp < nchunk; cp += kCq * NT) {
+    const int skip = (int)(kbs - kblocks);  // 1 where the row stride is padded
+    const float rkb = 1.0f / (float)kbl;
+    auto row_of = [&](int e) {  // e / kblocks
+      int r = (int)((float)e * rkb);
+      const int m = e - r * kbl;
+      return m < 0 ? r - 1 : m >= kbl ? r + 1 : r;
+    };
+    for (int cp = 0; cp < nchunk; cp += kCq * NT) {
       u32x4 qv[kCq];
-      float st0[kCq], st1[kCq];
+      float st[kCq];
 #pragma unroll
       for (int j = 0; j < kCq; ++j) {
-        const int64_t c = cp + tid + (int64_t)j * NT;
-        const int64_t o = qbase + 16 * (c < nchunk ? c : nchunk - 1);
-        qv[j] = __builtin_amdgcn_raw_buffer_load_b128(qrs, c < nchunk ? (int)o : kPastEnd, 0, 0);
-        const int64_t g0 = o >> 8 < ng ? o >> 8 : ng - 1;
-        const int64_t g1 = (o + 15) >> 8 < ng ? (o + 15) >> 8 : ng - 1;
-        st0[j] = p.step[g0];
-        st1[j] = p.step[g1];
+        const int c = cp + tid + j * NT;
+        const int o = qbase + 16 * (c < nchunk ? c : nchunk - 1);
+        qv[j] = __builtin_amdgcn_raw_buffer_load_b128(qrs, c < nchunk ? o : kPastEnd, 0, 0);
+        st[j] = p.step[o >> 8 < glast ? o >> 8 : glast];
       }
       if (kLateFirst && cp == 0) issue_first();
 #pragma unroll
       for (int j = 0; j < kCq; ++j) {
-        const int64_t c = cp + tid + (int64_t)j * NT;
+        const int c = cp + tid + j * NT;
         if (c < nchunk) {
-          const int64_t o = qbase + 16 * c;
-          const int64_t split = ((o >> 8) + 1) << 8;  // first block of the next group
-          // element 16 c + i is block kb of table row `row`
-          int64_t row = (16 * c) / kblocks, kb = 16 * c - row * kblocks;
+          // element 16 c + i is block kb0 + i of table row row0, or, from
+          // i = kblocks - kb0 on, of the next row (at most one row break
+          // per chunk when kblocks >= 16)
+          const int row0 = row_of(16 * c), kb0 = 16 * c - row0 * kbl;
+          float* const dst = chat_t + row0 * (kbl + skip) + kb0;
+          if (kbl >= 16) {  // uniform
+            const int brk = kbl - kb0;
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float cv = (float)((qv[j][i >> 2] >> (8 * (i & 3))) & 0xffu) *
-                             (o + i < split ? st0[j] : st1[j]);
-            if (row < 16 * G) chat_t[row * kbs + kb] = cv;
-            if (++kb == kblocks) {
-              kb = 0;
-              ++row;
+            for (int i = 0; i < 16; ++i)
+              dst[i + (i >= brk ? skip : 0)] =
+                  (float)((qv[j][i >> 2] >> (8 * (i & 3))) & 0xffu) * st[j];
+          } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int e = 16 * c + i;
+              chat_t[e + skip * row_of(e)] =
+                  (float)((qv[j][i >> 2] >> (8 * (i & 3))) & 0xffu) * st[j];
             }
           }
         }
@@ -421,18 +473,16 @@ __global__ __launch_bounds__(64 * KW) void k_qgemv(GemvArgs p) {
     for (int i = 0; i < 8; ++i) lut[tid + NT * i] = pack_bf16x2(lo, level_of<CT>(p.ut, hi0 + 2 * i));
   }
   if (tid < ur) {
-    float u = 0.0f;  // slices in order
+    float u = 0.0f;  // slices in order (those past us are zeros)
 #pragma unroll
-    for (int i = 0; i < kGemvMaxSlices; ++i)
-      if (i < p.us) u += __builtin_bit_cast(float, uv[i]);
+    for (int i = 0; i < kGemvMaxSlices; ++i) u += __builtin_bit_cast(float, uv[i]);
     ush[tid] = u;
   }
   for (int64_t e = tid + NT; e < ur; e += NT) {  // M r > NT: the other sums
     load_slices(uv, e);
     float u = 0.0f;
 #pragma unroll
-    for (int i = 0; i < kGemvMaxSlices; ++i)
-      if (i < p.us) u += __builtin_bit_cast(float, uv[i]);
+    for (int i = 0; i < kGemvMaxSlices; ++i) u += __builtin_bit_cast(float, uv[i]);
     ush[e] = u;
   }
   __syncthreads();
@@ -529,6 +579,7 @@ __global__ __launch_bounds__(64 * KW) void k_qgemv(GemvArgs p) {
     issue(sl[PD - 1], T, true);
     compute(sl[PD - 1], T, true);
   }
+  if (b_lds) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the adapter rows are in LDS
   __syncthreads();  // the constant table becomes the reduction buffer
 
 #pragma unroll
@@ -564,18 +615,24 @@ __global__ __launch_bounds__(64 * KW) void k_qgemv(GemvArgs p) {
     lk[k] = 0.0f;
   }
   if ((p.r & 7) == 0) {
-    // r a multiple of 8: 16-byte adapter loads (8 columns) and 16-byte U
-    // reads; JB columns per batch.  Outputs that are not stored read U row
-    // 0 and adapter zeros (their sums are dropped).
+    // r a multiple of 8: 16-byte adapter reads (8 columns, from LDS with
+    // seven groups) and 16-byte U reads; JB columns per batch.  Outputs
+    // that are not stored read U row 0 and adapter zeros or the first
+    // row (their sums are dropped); columns past r are never used.
     for (int j0 = 0; j0 < p.r; j0 += JB) {
       u32x4 bq[KO][JB / 8];
 #pragma unroll
       for (int k = 0; k < KO; ++k)
 #pragma unroll
-        for (int q = 0; q < JB / 8; ++q)
-          bq[k][q] = __builtin_amdgcn_raw_buffer_load_b128(
-              brs, (vk[k] && j0 + 8 * q < p.r) ? (int)(2 * (nk[k] * p.r + j0 + 8 * q)) : kPastEnd, 0,
-              0);
+        for (int q = 0; q < JB / 8; ++q) {
+          const bool jv = j0 + 8 * q < p.r;
+          if (b_lds)  // uniform
+            bq[k][q] = *reinterpret_cast<const u32x4*>(bsh + (vk[k] ? nk[k] - n0 : 0) * p.r +
+                                                       (jv ? j0 + 8 * q : 0));
+          else
+            bq[k][q] = __builtin_amdgcn_raw_buffer_load_b128(
+                brs, vk[k] && jv ? (int)(2 * (nk[k] * p.r + j0 + 8 * q)) : kPastEnd, 0, 0);
+        }
       __builtin_amdgcn_sched_barrier(0);  // every load of the batch before the first use
 #pragma unroll
       for (int q = 0; q < JB / 8; ++q) {
@@ -656,7 +713,8 @@ hipError_t launch_qgemv_g(const GemvArgs& a, int code, hipStream_t stream) {
     // dynamic LDS above the default 64 KB needs the limit raised; the call is
     // cheap and idempotent, and made for the device the launch goes to
     // (a per-process cache would only cover the first device)
-    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (G == 7 ? 160 : 96) * 1024);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((k_qgemv<G, KW, PD, decltype(ct)>), grid, dim3(64 * KW), lds, stream, a);
     return hipGetLastError();
@@ -673,7 +731,7 @@ hipError_t launch_qgemv(const Nf4View& w, const uint16_t* X, int64_t M, const ui
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
-  const GemvArgs a{w.codes, w.q8, w.step, X,     M, w.N, w.K,  upart, (int32_t)gu.x,
+  const GemvArgs a{w.codes, w.q8, w.step, X,     M, w.N, w.K,  upart,
                    B,       r,    s,      Y, U_out, w.bshift, w.ut};
   const int64_t kblocks = w.K / 64;
   // 16 G weight rows per workgroup, K split over its 8 waves.
@@ -692,7 +750,7 @@ hipError_t launch_qgemv(const Nf4View& w, const uint16_t* X, int64_t M, const ui
     cus = 0;
   const int64_t groups = (w.N + 15) / 16;
   const bool g7 = cus > 0 && groups % (7 * (int64_t)cus) == 0 &&
-                  4 * gemv_lds_words(7, 8, M, r, kblocks) <= 96 * 1024;
+                  4 * gemv_lds_words(7, 8, M, r, kblocks) <= 160 * 1024;
   const bool g1 = !g7 && M <= 2 && cus > 0 && groups <= 2 * (int64_t)cus;
   e = g7   ? launch_qgemv_g<7>(a, w.code, stream)
       : g1 ? launch_qgemv_g<1>(a, w.code, stream)
