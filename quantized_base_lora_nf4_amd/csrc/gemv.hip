@@ -543,13 +543,22 @@ void k_qgemv(GemvArgs p) {
       }
     };
     const int64_t nch = (d1 + DW - 1) / DW;  // 0 for a wave without full steps
+    static_assert(G % 2 == 1, "the next chunk's first group goes to slot 1");
     for (int64_t c = 0; c < nch; ++c) {
       issue_x(c);
-      if (c > 0) issue_c(cs[0], c, 0);  // chunk 0's went out in the prologue
+      // group 0's codes: chunk 0's went out in the prologue, the others
+      // during the previous chunk's last group (into slot 1)
+      if (c > 0) {
+#pragma unroll
+        for (int j = 0; j < DW; ++j) cs[0][j] = cs[1][j];
+      }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        if (g + 1 < G) issue_c(cs[(g + 1) % 2], c, g + 1);
+        // the last group issues the next chunk's first (on the last chunk a
+        // clamped re-read of the last step, unused), without a branch so
+        // that the wait for this group's codes does not cover those loads
+        issue_c(cs[(g + 1) % 2], g + 1 < G ? c : c + 1, g + 1 < G ? g + 1 : 0);
         __builtin_amdgcn_sched_barrier(0);
         compute_g(cs[g % 2], c, g);
         __builtin_amdgcn_sched_barrier(0);
