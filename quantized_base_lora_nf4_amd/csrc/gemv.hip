@@ -747,10 +747,11 @@ hipError_t launch_qgemv(const Nf4View& w, const uint16_t* X, int64_t M, const ui
   //  - G = 7 when the 16-row groups make exactly one workgroup of 7 per CU
   //    (a 28672-row weight on 256 CUs): no CU gets more rows than another,
   //    and each CU loads the X fragments once.
-  //  - G = 1 for one or two tokens when G = 2 would leave at most one
-  //    workgroup (8 waves) per CU: twice the waves keep more loads in
-  //    flight.  With more tokens the X fragments, loaded once per
-  //    workgroup, cost more than that gains.
+  //  - G = 1 for one or two tokens when G = 2 would leave CUs without a
+  //    workgroup (fewer than 32 rows per CU): every CU then streams.  With
+  //    one workgroup per CU or more, G = 2 is faster (8192 x 8192 on 256
+  //    CUs at one token: 15.6 against 17.9 us), and with more tokens the
+  //    X fragments, loaded once per workgroup, favour G = 2 further.
   //  - G = 2 otherwise.
   // compute units of the current device, the one the launch goes to
   int dev = 0, cus = 0;
@@ -760,7 +761,7 @@ hipError_t launch_qgemv(const Nf4View& w, const uint16_t* X, int64_t M, const ui
   const int64_t groups = (w.N + 15) / 16;
   const bool g7 = cus > 0 && groups % (7 * (int64_t)cus) == 0 &&
                   4 * gemv_lds_words(7, 8, M, r, kblocks) <= 160 * 1024;
-  const bool g1 = !g7 && M <= 2 && cus > 0 && groups <= 2 * (int64_t)cus;
+  const bool g1 = !g7 && M <= 2 && cus > 0 && groups < 2 * (int64_t)cus;
   e = g7   ? launch_qgemv_g<7>(a, w.code, stream)
       : g1 ? launch_qgemv_g<1>(a, w.code, stream)
            : launch_qgemv_g<2>(a, w.code, stream);
