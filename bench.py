@@ -69,6 +69,63 @@ def parse():
 HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
 
 
+class ClockSampler:
+    """The GPU's shader (GFX) clock while work runs: amdsmi (the library
+    behind amd-smi and rocm-smi) polled from a thread every few
+    milliseconds.  The value it returns is refreshed by the GPU's power
+    management firmware only about once a second, so only a run of a few
+    seconds gives readings taken under that load.  `mhz(after)` is the
+    median of the samples taken `after` seconds or later into the run, None
+    when amdsmi is not usable here."""
+
+    def __init__(self, period_s=0.005):
+        import threading
+        self.period, self.samples, self.handle = period_s, [], None
+        self._stop, self._thread = threading.Event(), None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self.amdsmi = amdsmi
+            self.handle = amdsmi.amdsmi_get_processor_handles()[0]
+            self._read()
+        except Exception:
+            self.handle = None
+
+    def _read(self):
+        a = self.amdsmi
+        return a.amdsmi_get_clock_info(self.handle, a.AmdSmiClkType.GFX)["clk"]
+
+    def _loop(self):
+        t0 = time.perf_counter()
+        while not self._stop.is_set():
+            try:
+                v = self._read()
+                if isinstance(v, (int, float)) and v > 0:
+                    self.samples.append((time.perf_counter() - t0, float(v)))
+            except Exception:
+                pass
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self.handle is not None:
+            import threading
+            self._stop.clear()
+            self._thread = threading.Thread(target=self._loop, daemon=True)
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join()
+            self._thread = None
+        return False
+
+    def mhz(self, after=0.0):
+        v = [c for t, c in self.samples if t >= after]
+        return float(np.median(v)) if v else None
+
+
 class HipEvents:
     """hipEvent_t pairs through the HIP runtime's C API (the library's
     measurement calls record them around the dominant kernel).  They only
@@ -190,6 +247,14 @@ def main():
 
     extra = {}
     if not args.no_extra:
+        # The spec peak is 4096 flop per CU per clock at 2.4 GHz; next to it,
+        # the same peak at the shader clock the GPU holds under this step
+        mhz = clock_under_load(fx, sp)
+        roofline["observed_clock_ghz"] = None if mhz is None else round(mhz / 1e3, 3)
+        roofline["peak_at_observed_clock"] = (
+            None if mhz is None else round(fx.cus * 4096 * mhz * 1e6 / 1e12, 1))
+        roofline["frac_at_observed_clock"] = (
+            None if mhz is None else round(roofline["achieved"] / roofline["peak_at_observed_clock"], 4))
         # the same step without rotation (weights may be served from the
         # Infinity Cache), labeled as such
         extra["warm_step"] = fx.run(args.steps, args.warmup, 0, sp, rotate=False)["summary"]
@@ -259,6 +324,7 @@ class FusedWorkload:
     def __init__(self, qn, torch, ev, wl, d16, dev, rotate=True, keep_host=True):
         import workloads as wl_mod
         self.qn, self.torch, self.ev, self.wl = qn, torch, ev, wl
+        self.cus = torch.cuda.get_device_properties(0).multi_processor_count
         M, r = wl.M[0], wl.r
         self.layers = []
         self.host_inputs = []
@@ -392,6 +458,20 @@ class FusedWorkload:
                       "events_on_every_nth_step": events_every},
         }
         return out
+
+
+def clock_under_load(fx, sp, seconds=3.0, settle=1.5):
+    """Median shader clock (MHz) while the step runs back to back for
+    `seconds` (untimed, rotated weight copies), from the readings taken
+    after the first `settle` seconds; None without amdsmi."""
+    clock = ClockSampler()
+    if clock.handle is None:
+        return None
+    t0 = time.perf_counter()
+    with clock:
+        while time.perf_counter() - t0 < seconds:
+            fx.run(100, 0, 0, sp)
+    return clock.mhz(after=settle)
 
 
 # The other forward + backward workloads, reported under extra.workloads:
