@@ -819,6 +819,7 @@ def _time_gemv(L, torch, ev, structs, inp, M, N, K, g, A, B, d16, dev, sp, wbyte
     return {
         "weight": f"{N}x{K}", "M": M, "r": g.r,
         "kernel_us": round(k_ms * 1e3, 2),
+        "kernel_us_p10_p90": [round(float(np.percentile(kern, q)) * 1e3, 2) for q in (10, 90)],
         "kernel_GB/s": round(wbytes / (k_ms * 1e-3) / 1e9, 1),
         "kernel_frac_hbm": round(wbytes / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "call_us": round(call_ms * 1e3, 2),
@@ -860,6 +861,7 @@ def hbm_read_ceiling(qn, torch, ev, sp, sizes, reps=40):
             ev.destroy(b)
         ms = float(np.median(ts))
         out.append({"bytes": nb, "us": round(ms * 1e3, 2),
+                    "us_p10_p90": [round(float(np.percentile(ts, q)) * 1e3, 2) for q in (10, 90)],
                     "GB/s": round(nb / (ms * 1e-3) / 1e9, 1),
                     "frac_hbm": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                     "copies_rotated": ncopy})
